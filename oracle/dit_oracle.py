@@ -1,0 +1,427 @@
+"""Test infrastructure: plain fp64 CPU oracle of the DiT denoise step.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` import this module.  It shares no code with the HIP library.
+
+What it computes, and which passage of the source pages each part follows:
+
+* First-Block-Cache (FBC): the unsloth studio ``diffusion.py`` commit log,
+  commit "Add opt-in step caching (First-Block-Cache)": run the first block,
+  compare its residual with the cached one, and when it barely changes skip
+  the remaining blocks and reuse their cached output; the threshold is raised
+  for a quantised transformer.  The devotd.net VisualGen article (section on
+  why the speed-ups differ, Cache-DiT paragraph) names the same test a
+  "residual difference threshold".
+* Fused QKV projection: same commit log, speed-profile commit ("fused QKV").
+* RoPE as its own step: the vflash "Optimization ledger" page, table
+  "Accepted or exposed" (strict Triton RoPE row).
+* Flow-matching schedule with a flow shift and an Euler solver: the ledger
+  page, section "Fewer steps require a new contract" (scheduler, flow shift,
+  solver tuned together).
+* CFG with scale 3.5 on a positive/negative prompt pair: the VisualGen
+  article, stage-latency table conditions.
+* fp8 W8A8 with dynamic activation scales: runinfra.ai image-gen runbook,
+  "Optimization stack" table, first row.
+
+The pages give no formulas, so every formula below is a reading; each one
+carries its reading number (R1..R32) as listed in the design notes.
+
+Everything is fp64 numpy.  Parameters are ``dict[str, ndarray]`` with weights
+in ``torch.nn.Linear`` layout ``[out, in]``: ``y = x @ W.T + b``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+from .numerics import quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX
+
+__all__ = [
+    "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
+    "linear", "rope_table", "apply_rope", "attention", "attention_naive",
+    "double_block", "single_block", "final_layer", "fbcache_rel",
+    "fbcache_decide", "euler_update", "cfg_combine", "time_embed",
+    "modulation_vectors", "denoise_step", "FBCacheState", "to64",
+    "linear_fp8", "attention_fp8", "image_positions",
+]
+
+LN_EPS = 1e-6
+ROPE_THETA = 10000.0
+TIME_PERIOD = 10000.0
+TIME_SCALE = 1000.0
+
+
+def to64(t) -> np.ndarray:
+    """torch tensor / array -> fp64 ndarray (exact for bf16 and fp32 inputs)."""
+    if hasattr(t, "detach"):
+        t = t.detach().to("cpu").double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# schedule and embeddings
+# --------------------------------------------------------------------------
+
+def sigmas(num_steps: int, shift: float) -> np.ndarray:
+    """Shifted flow-matching sigmas (R14): tau_i = 1 - i/N, sigma = s*tau / (1 + (s-1)*tau)."""
+    tau = 1.0 - np.arange(num_steps + 1, dtype=np.float64) / num_steps
+    return shift * tau / (1.0 + (shift - 1.0) * tau)
+
+
+def timestep_sinusoid(t, dim: int = 256) -> np.ndarray:
+    """[cos(1000 t w_k), sin(1000 t w_k)], w_k = 10000^(-k/(dim/2)) (R5). t: [M] -> [M, dim]."""
+    t = np.atleast_1d(np.asarray(t, dtype=np.float64))
+    half = dim // 2
+    w = TIME_PERIOD ** (-np.arange(half, dtype=np.float64) / half)
+    arg = TIME_SCALE * t[:, None] * w[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x):
+    """GELU, tanh approximation (R9)."""
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def linear(x, w, b):
+    """y = x W^T + b over the last axis."""
+    return x @ w.T + b
+
+
+def time_embed(P: Dict[str, np.ndarray], t) -> np.ndarray:
+    """Timestep MLP (R5): c = W2 SiLU(W1 e + b1) + b2."""
+    e = timestep_sinusoid(t)
+    h = silu(linear(e, P["time.w1"], P["time.b1"]))
+    return linear(h, P["time.w2"], P["time.b2"])
+
+
+def modulation_vectors(c: np.ndarray, w: np.ndarray, b: np.ndarray, D: int) -> np.ndarray:
+    """mu = W SiLU(c) + b, split into D-wide chunks (R4, R6). c: [M, D] -> [M, k, D]."""
+    mu = linear(silu(c), w, b)
+    return mu.reshape(mu.shape[0], -1, D)
+
+
+# --------------------------------------------------------------------------
+# normalisation, modulation, RoPE
+# --------------------------------------------------------------------------
+
+def layer_norm(u: np.ndarray, eps: float = LN_EPS) -> np.ndarray:
+    """LayerNorm over the last axis, no affine, biased variance (R3)."""
+    mu = u.mean(axis=-1, keepdims=True)
+    var = ((u - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (u - mu) / np.sqrt(var + eps)
+
+
+def modulate(u, shift, scale):
+    """LN(u) * (1 + scale) + shift (R3, R4); shift/scale broadcast over tokens."""
+    return layer_norm(u) * (1.0 + scale) + shift
+
+
+def image_positions(grid_h: int, grid_w: int, Lt: int) -> np.ndarray:
+    """(row, col) of every joint token: text tokens at (0, 0), image row-major (R7, R8)."""
+    pos = np.zeros((Lt + grid_h * grid_w, 2), dtype=np.float64)
+    ii = np.arange(grid_h * grid_w)
+    pos[Lt:, 0] = ii // grid_w
+    pos[Lt:, 1] = ii % grid_w
+    return pos
+
+
+def rope_table(pos: np.ndarray, d: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """Angles [L, d/2] of the 2-D RoPE (R7).
+
+    Pair p < d/4 rotates with the row coordinate, pair p >= d/4 with the column;
+    inside an axis, pair j turns at theta^(-j/(d/4)) radians per position.
+    """
+    q = d // 4
+    p = np.arange(d // 2)
+    j = p % q
+    freq = theta ** (-j / q)
+    axis = (p >= q).astype(np.int64)
+    return pos[:, axis] * freq[None, :]
+
+
+def apply_rope(x: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """Rotate interleaved pairs (x[2p], x[2p+1]) by ang[t, p].  x: [..., L, d]."""
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    c = np.cos(ang)
+    s = np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def attention(q, k, v, scale: Optional[float] = None) -> np.ndarray:
+    """softmax(q k^T * scale) v per (batch, head), no mask (R8).  q,k,v: [B, H, L, d]."""
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    B, H, L, _ = q.shape
+    out = np.empty_like(q)
+    for bi in range(B):
+        for h in range(H):
+            s = (q[bi, h] @ k[bi, h].T) * scale
+            s = s - s.max(axis=1, keepdims=True)     # exact shift; softmax unchanged
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[bi, h] = p @ v[bi, h]
+    return out
+
+
+def attention_naive(q, k, v, scale: Optional[float] = None) -> np.ndarray:
+    """Triple-loop attention for tiny shapes (a brute-force second opinion)."""
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    B, H, L, _ = q.shape
+    Lk = k.shape[2]
+    out = np.zeros_like(q)
+    for bi in range(B):
+        for h in range(H):
+            for i in range(L):
+                s = [sum(q[bi, h, i, c] * k[bi, h, j, c] for c in range(d)) * scale
+                     for j in range(Lk)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                for c in range(d):
+                    out[bi, h, i, c] = sum(e[j] * v[bi, h, j, c] for j in range(Lk)) / z
+    return out
+
+
+def _heads(x, H):
+    """[B, L, D] -> [B, H, L, d]."""
+    B, L, D = x.shape
+    return x.reshape(B, L, H, D // H).transpose(0, 2, 1, 3)
+
+
+def _merge(x):
+    """[B, H, L, d] -> [B, L, D]."""
+    B, H, L, d = x.shape
+    return x.transpose(0, 2, 1, 3).reshape(B, L, H * d)
+
+
+# --------------------------------------------------------------------------
+# fp8 W8A8 (R24-R28)
+# --------------------------------------------------------------------------
+
+def linear_fp8(x, w, b):
+    """fp8 linear: per-token e4m3 activations x per-channel e4m3 weights (R25, R26).
+
+    Both operands are quantised with scale amax/448 and the product is taken
+    on the dequantised values in fp64.
+    """
+    shp = x.shape
+    x2 = x.reshape(-1, shp[-1])
+    qx, sx = quantize_rows_e4m3(x2)
+    qw, sw = quantize_rows_e4m3(w)
+    y = (qx @ qw.T) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + b
+    return y.reshape(*shp[:-1], w.shape[0])
+
+
+def attention_fp8(q, k, v, scale: Optional[float] = None) -> np.ndarray:
+    """fp8 attention (R27).
+
+    q, k: per-(batch, head, token) e4m3 scales; v: per-(batch, head, channel)
+    scales.  Scores use the dequantised operands; P = exp(s - max) in (0, 1] is
+    quantised as e4m3(448 P) / 448 and the row sum is taken from the quantised
+    P, so identical keys still return the mean of V.
+    """
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    B, H, L, _ = q.shape
+    out = np.empty_like(q)
+    for bi in range(B):
+        for h in range(H):
+            qq, sq = quantize_rows_e4m3(q[bi, h])
+            kq, sk = quantize_rows_e4m3(k[bi, h])
+            vq_t, sv = quantize_rows_e4m3(v[bi, h].T)          # per channel
+            qd = qq * sq.astype(np.float64)[:, None]
+            kd = kq * sk.astype(np.float64)[:, None]
+            vd = (vq_t * sv.astype(np.float64)[:, None]).T
+            s = (qd @ kd.T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            pq = round_e4m3(p * E4M3_MAX) / E4M3_MAX
+            out[bi, h] = (pq @ vd) / pq.sum(axis=1, keepdims=True)
+    return out
+
+
+# --------------------------------------------------------------------------
+# blocks
+# --------------------------------------------------------------------------
+
+def _lin(x, P, name, fp8):
+    if fp8:
+        return linear_fp8(x, P[name + ".w"], P[name + ".b"])
+    return linear(x, P[name + ".w"], P[name + ".b"])
+
+
+def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
+    """Double-stream block (R1, R2, R4, R8): separate weights per stream, joint attention.
+
+    x_txt [B, Lt, D], x_img [B, Li, D]; mod_* [B or 1, 6, D] in the order
+    shift1, scale1, gate1, shift2, scale2, gate2; P keys "img.qkv.w" etc.;
+    ang: RoPE angles [Lt + Li, d/2].  Returns the updated (x_txt, x_img).
+    """
+    attn_fn = attention_fp8 if fp8 else attention
+    Lt = x_txt.shape[1]
+    streams = {"txt": (x_txt, mod_txt), "img": (x_img, mod_img)}
+    qkv = {}
+    for s, (x, m) in streams.items():
+        u = modulate(x, m[:, 0:1], m[:, 1:2])
+        qkv[s] = _lin(u, P, f"{s}.qkv", fp8)
+    D = x_img.shape[-1]
+    q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
+    k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
+    v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
+    q = apply_rope(_heads(q, H), ang)
+    k = apply_rope(_heads(k, H), ang)
+    a = _merge(attn_fn(q, k, _heads(v, H)))
+    out = {}
+    for s, (x, m) in streams.items():
+        a_s = a[:, :Lt] if s == "txt" else a[:, Lt:]
+        x = x + m[:, 2:3] * _lin(a_s, P, f"{s}.proj", fp8)
+        u = modulate(x, m[:, 3:4], m[:, 4:5])
+        hdn = gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8))
+        x = x + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
+        out[s] = x
+    return out["txt"], out["img"]
+
+
+def single_block(x, mod, P, ang, H, fp8=False):
+    """Single-stream block (R10): one modulated LN feeding attention and MLP in parallel.
+
+    x [B, L, D]; mod [B or 1, 3, D] = shift, scale, gate; P keys "lin1.w" ...
+    """
+    attn_fn = attention_fp8 if fp8 else attention
+    D = x.shape[-1]
+    u = modulate(x, mod[:, 0:1], mod[:, 1:2])
+    h = _lin(u, P, "lin1", fp8)
+    q = apply_rope(_heads(h[..., :D], H), ang)
+    k = apply_rope(_heads(h[..., D:2 * D], H), ang)
+    v = _heads(h[..., 2 * D:3 * D], H)
+    a = _merge(attn_fn(q, k, v))
+    cat = np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1)
+    return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8)
+
+
+def final_layer(x_img, shift, scale, w, b):
+    """Velocity head (R11): Mod(x_img) W_out^T + b_out, image tokens only."""
+    return linear(modulate(x_img, shift, scale), w, b)
+
+
+# --------------------------------------------------------------------------
+# First-Block-Cache (R18-R22), Euler (R14-R17)
+# --------------------------------------------------------------------------
+
+def fbcache_rel(r: np.ndarray, anchor: np.ndarray) -> float:
+    """Relative L1 change of the first block's residual (R20), in fp64.
+
+    sum|r - a| / sum|a|; a zero denominator gives +inf (never skips).
+    """
+    num = float(np.sum(np.abs(np.asarray(r, np.float64) - np.asarray(anchor, np.float64))))
+    den = float(np.sum(np.abs(np.asarray(anchor, np.float64))))
+    if den == 0.0:
+        return math.inf if num == num else math.nan
+    return num / den
+
+
+def fbcache_decide(rel: float, threshold: float) -> bool:
+    """Skip iff rel < threshold, strictly; NaN never skips (R20, R21)."""
+    return bool(rel < threshold)
+
+
+def euler_update(x, v, sigma_i, sigma_next):
+    """x <- x + (sigma_{i+1} - sigma_i) v, integrating sigma from 1 to 0 (R16)."""
+    return x + (sigma_next - sigma_i) * v
+
+
+def cfg_combine(v_pos, v_neg, g):
+    """v_neg + g (v_pos - v_neg) (R17)."""
+    return v_neg + g * (v_pos - v_neg)
+
+
+class FBCacheState:
+    """Caller-held First-Block-Cache state (anchor residual + cached tail residual)."""
+
+    def __init__(self, enabled: bool, threshold: float):
+        self.enabled = enabled
+        self.threshold = threshold
+        self.has_anchor = False
+        self.anchor = None     # first block's residual at the last full step
+        self.cached = None     # final image hidden - image hidden after block 0
+
+
+def _block_params(P, prefix):
+    n = len(prefix) + 1
+    return {k[n:]: v for k, v in P.items() if k.startswith(prefix + ".")}
+
+
+def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = None,
+                 force_skip: Optional[bool] = None, fp8: bool = False):
+    """One flow-matching Euler step of the whole model (steps 1-11 of the oracle definition).
+
+    P: parameters keyed as in ``dit_inputs.param_specs`` (fp64 arrays);
+    w: the workload (B, grid, Lt, guidance); lat [1, Li, C_in]; txt [B, Lt, D].
+    ``force_skip`` replays a decision taken elsewhere (decision replay).
+    Returns (new latents, info dict with rel / skip / velocity).
+    """
+    D, H = dims.D, dims.H
+    B = txt.shape[0]
+    t = sig[i]
+    c = time_embed(P, np.array([t]))                           # [1, D]
+    ang = rope_table(image_positions(w.grid_h, w.grid_w, w.Lt), D // H)
+    h_img = linear(lat, P["img_in.w"], P["img_in.b"])         # [1, Li, D]
+    x_img = np.broadcast_to(h_img, (B,) + h_img.shape[1:]).copy()
+    x_txt = txt.copy()
+    before = x_img.copy()
+
+    def mods(prefix, k):
+        return modulation_vectors(c, P[prefix + ".mod.w"], P[prefix + ".mod.b"], D)
+
+    info = {"rel": math.inf, "skip": False}
+    for j in range(dims.n_double):
+        bp = _block_params(P, f"double{j}")
+        m_img = mods(f"double{j}.img", 6)
+        m_txt = mods(f"double{j}.txt", 6)
+        x_txt, x_img = double_block(x_txt, x_img, m_img, m_txt, bp, ang, H, fp8)
+        if j == 0 and cache is not None and cache.enabled:
+            r = x_img - before
+            rel = fbcache_rel(r, cache.anchor) if cache.has_anchor else math.inf
+            skip = fbcache_decide(rel, cache.threshold)
+            if force_skip is not None:
+                skip = bool(force_skip)
+            info["rel"], info["skip"] = rel, skip
+            after0 = x_img.copy()
+            if skip:
+                break
+    if info["skip"]:
+        x_img = after0 + cache.cached
+    else:
+        if dims.n_single:
+            x = np.concatenate([x_txt, x_img], axis=1)
+            for j in range(dims.n_single):
+                x = single_block(x, mods(f"single{j}", 3), _block_params(P, f"single{j}"),
+                                 ang, H, fp8)
+            x_img = x[:, w.Lt:]
+        if cache is not None and cache.enabled:
+            cache.cached = x_img - after0
+            cache.anchor = r
+            cache.has_anchor = True
+    mf = mods("final", 2)
+    v = final_layer(x_img, mf[:, 0:1], mf[:, 1:2], P["final.out.w"], P["final.out.b"])
+    if B == 2 and w.guidance:
+        v = cfg_combine(v[0:1], v[1:2], w.guidance)
+    info["v"] = v
+    return euler_update(lat, v, sig[i], sig[i + 1]), info

@@ -1,0 +1,89 @@
+"""Test infrastructure: number-format rounding used by the oracle (fp64 numpy).
+
+Formats (from their public definitions, not from any page):
+  * bfloat16: 1 sign, 8 exponent, 7 stored mantissa bits (fp32 exponent range).
+  * OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, no infinities, the all-ones code S.1111.111 is NaN; largest finite
+    magnitude 1.75 * 2^8 = 448, smallest normal 2^-6, smallest subnormal 2^-9.
+
+The fp8 W8A8 recipe the pages name ("FP8 W8A8 dynamic precision" in the
+runinfra.ai image-generation runbook, Optimization stack table) fixes no
+rounding rule; the reading used here is round-to-nearest-even with saturation
+to +-448 and a scale of amax/448 (amax = 0 gives scale 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["round_bf16", "round_e4m3", "E4M3_MAX", "quant_scale_f32",
+           "quantize_rows_e4m3", "quantize_cols_e4m3"]
+
+E4M3_MAX = 448.0
+
+
+def _round_sig(x: np.ndarray, sig_bits: int, min_exp: int) -> np.ndarray:
+    """Round to the nearest value with ``sig_bits`` significant bits, ties to even.
+
+    Below 2**min_exp the spacing stays 2**(min_exp - sig_bits + 1) (gradual
+    underflow).  Works in fp64, where every step below is exact.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    m, e = np.frexp(ax)                      # ax = m * 2**e, m in [0.5, 1)
+    # exponent of the leading bit is e - 1; clamp to the subnormal range
+    lead = np.maximum(e - 1, min_exp)
+    ulp_exp = lead - (sig_bits - 1)
+    q = np.rint(np.ldexp(ax, -ulp_exp))      # rint rounds half to even
+    out = np.ldexp(q, ulp_exp)
+    out = np.where(ax == 0, 0.0, out)
+    return np.copysign(out, x)
+
+
+def round_bf16(x) -> np.ndarray:
+    """fp64 -> nearest bfloat16 value (as fp64), ties to even; overflow -> inf."""
+    x = np.asarray(x, dtype=np.float64)
+    out = _round_sig(x, 8, -126)
+    bf16_max = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    # halfway above max rounds to inf (ties-to-even lands on the next binade)
+    out = np.where(np.abs(out) > bf16_max, np.copysign(np.inf, x), out)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def round_e4m3(x) -> np.ndarray:
+    """fp64 -> nearest OCP e4m3 value (as fp64), ties to even, saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    out = _round_sig(x, 4, -6)
+    out = np.clip(out, -E4M3_MAX, E4M3_MAX)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def quant_scale_f32(amax) -> tuple:
+    """Per-row scale and its reciprocal, both taken in fp32 as a kernel does.
+
+    scale = amax / 448 and inv = 448 / amax, each one correctly rounded fp32
+    division; amax == 0 gives scale = inv = 1.
+    """
+    a = np.asarray(amax, dtype=np.float32)
+    safe = np.where(a > 0, a, np.float32(1.0))
+    scale = np.where(a > 0, safe / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    inv = np.where(a > 0, np.float32(E4M3_MAX) / safe, np.float32(1.0)).astype(np.float32)
+    return scale, inv
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """Dynamic per-row (per-token) quantisation of a 2-D array.
+
+    Returns (codes as fp64 values, scale [rows] fp32).  The value fed to the
+    rounding is fp32(x) * inv in fp32, the precision a kernel takes the
+    decision in.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    scale, inv = quant_scale_f32(amax)
+    y = (x32 * inv[..., None]).astype(np.float32)
+    return round_e4m3(y.astype(np.float64)), scale
+
+
+def quantize_cols_e4m3(w: np.ndarray):
+    """Per-output-channel quantisation of a weight [out, in] (one scale per row)."""
+    return quantize_rows_e4m3(w)

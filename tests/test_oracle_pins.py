@@ -1,0 +1,516 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names the mistake it is meant to catch.  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.numerics import round_bf16, round_e4m3, quantize_rows_e4m3
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append([float(t) for t in line.split()])
+    return rows
+
+
+# ---------------------------------------------------------------- schedule
+
+def test_sigmas_golden_shift3():
+    want = np.array(_golden_rows("sigmas_shift3_n4.txt")[0])
+    np.testing.assert_allclose(O.sigmas(4, 3.0), want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,s", [(4, 1.0), (28, 3.0), (50, 3.0), (7, 0.5)])
+def test_sigmas_endpoints_monotone(n, s):
+    sg = O.sigmas(n, s)
+    assert sg[0] == 1.0 and sg[-1] == 0.0
+    assert np.all(np.diff(sg) < 0)
+
+
+def test_sigmas_shift1_is_linear():
+    np.testing.assert_allclose(O.sigmas(10, 1.0), np.linspace(1, 0, 11), atol=1e-15)
+
+
+def test_euler_constant_velocity_total_displacement():
+    # sum of d(sigma) is exactly -1: a wrong sign or a dropped step shows here
+    sg = O.sigmas(28, 3.0)
+    x = np.array([0.3, -1.2])
+    u = np.array([2.0, 0.5])
+    for i in range(28):
+        x = O.euler_update(x, u, sg[i], sg[i + 1])
+    np.testing.assert_allclose(x, np.array([0.3, -1.2]) - u, atol=1e-13)
+
+
+def test_euler_lands_on_target_for_exact_velocity():
+    # v(x, sigma) = (x - x*) / sigma is the exact rectified-flow velocity of a
+    # point mass at x*; Euler then hits x* at sigma = 0 for any schedule
+    rng = np.random.default_rng(0)
+    xs = rng.standard_normal(5)
+    x = rng.standard_normal(5)
+    sg = O.sigmas(13, 2.3)
+    for i in range(13):
+        x = O.euler_update(x, (x - xs) / sg[i], sg[i], sg[i + 1])
+    np.testing.assert_allclose(x, xs, atol=1e-12)
+
+
+def test_cfg_combine_cases():
+    vp, vn = np.array([1.0, 2.0]), np.array([-1.0, 0.5])
+    np.testing.assert_array_equal(O.cfg_combine(vp, vn, 1.0), vp)
+    np.testing.assert_array_equal(O.cfg_combine(vp, vn, 0.0), vn)
+    np.testing.assert_array_equal(O.cfg_combine(vp, vp, 3.5), vp)
+
+
+# ---------------------------------------------------------------- embeddings
+
+def test_timestep_sinusoid_t0():
+    e = O.timestep_sinusoid(0.0)
+    assert e.shape == (1, 256)
+    np.testing.assert_array_equal(e[0, :128], 1.0)
+    np.testing.assert_array_equal(e[0, 128:], 0.0)
+
+
+def test_timestep_sinusoid_frequencies():
+    # k = 0 turns once per unit of 1000 t; k = 64 at 10000^-0.5 = 1/100 of it
+    t = math.pi / 2000.0          # 1000 t = pi/2
+    e = O.timestep_sinusoid(t)[0]
+    assert abs(e[0]) < 1e-15 and abs(e[128] - 1.0) < 1e-15
+    np.testing.assert_allclose(e[64], math.cos(math.pi / 200.0), atol=1e-15)
+    np.testing.assert_allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- LN / GELU
+
+def test_layer_norm_vs_torch_and_moments():
+    rng = np.random.default_rng(1)
+    u = rng.standard_normal((7, 96)) * 3 + 1.5
+    ln = O.layer_norm(u)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(u), (96,), eps=1e-6).numpy()
+    np.testing.assert_allclose(ln, ref, atol=1e-12)
+    np.testing.assert_allclose(ln.mean(-1), 0, atol=1e-13)
+    var = u.var(-1)
+    np.testing.assert_allclose(ln.var(-1), var / (var + 1e-6), rtol=1e-12)
+
+
+def test_modulate_identity_and_affine():
+    rng = np.random.default_rng(2)
+    u = rng.standard_normal((3, 5, 64))
+    z = np.zeros((1, 1, 64))
+    np.testing.assert_array_equal(O.modulate(u, z, z), O.layer_norm(u))
+    sh = rng.standard_normal((1, 1, 64))
+    np.testing.assert_array_equal(O.modulate(u, sh, z - 1.0), np.broadcast_to(sh, u.shape))
+
+
+def test_gelu_tanh_vs_torch_and_erf():
+    x = np.linspace(-12, 12, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(x), ref, atol=1e-14)
+    exact = 0.5 * x * (1 + np.vectorize(math.erf)(x / math.sqrt(2)))
+    assert np.max(np.abs(O.gelu_tanh(x) - exact)) < 1e-3   # tanh form is within ~5e-4
+    assert O.gelu_tanh(np.array(0.0)) == 0.0
+    np.testing.assert_allclose(O.gelu_tanh(np.array([30.0, -30.0])), [30.0, 0.0], atol=1e-12)
+
+
+def test_silu_vs_torch():
+    x = np.linspace(-20, 20, 801)
+    np.testing.assert_allclose(O.silu(x), torch.nn.functional.silu(torch.from_numpy(x)).numpy(),
+                               atol=1e-14)
+
+
+# ---------------------------------------------------------------- linear
+
+def test_linear_vs_triple_loop():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 6))
+    w = rng.standard_normal((5, 6))
+    b = rng.standard_normal(5)
+    y = O.linear(x, w, b)
+    for i in range(4):
+        for n in range(5):
+            assert abs(y[i, n] - (sum(x[i, k] * w[n, k] for k in range(6)) + b[n])) < 1e-12
+
+
+def test_linear_one_hot_weight_selects_column():
+    x = np.arange(12.0).reshape(3, 4)
+    w = np.zeros((2, 4))
+    w[0, 2] = 1.0
+    w[1, 0] = 1.0
+    np.testing.assert_array_equal(O.linear(x, w, np.zeros(2)), x[:, [2, 0]])
+
+
+# ---------------------------------------------------------------- RoPE
+
+def _complex_rope(x, ang):
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def test_rope_matches_complex_rotation_and_keeps_pair_norms():
+    rng = np.random.default_rng(4)
+    pos = O.image_positions(5, 7, 3)
+    ang = O.rope_table(pos, 64)
+    x = rng.standard_normal((2, 3, pos.shape[0], 64))
+    y = O.apply_rope(x, ang)
+    np.testing.assert_allclose(y, _complex_rope(x, ang), atol=1e-13)
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12)
+    # text tokens sit at (0, 0): identity
+    np.testing.assert_array_equal(y[:, :, :3], x[:, :, :3])
+
+
+def test_rope_relative_position_per_axis():
+    # <R(q, p + delta), R(k, p' + delta)> == <R(q, p), R(k, p')> for a shift
+    # along either axis; a wrong frequency or pairing breaks it
+    rng = np.random.default_rng(5)
+    d = 128
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d)
+    for delta in ([3, 0], [0, 5], [2, 7]):
+        p = np.array([[1.0, 4.0], [6.0, 2.0]])
+        p2 = p + np.array(delta, dtype=float)
+        a = O.rope_table(p, d)
+        a2 = O.rope_table(p2, d)
+        s1 = O.apply_rope(q[None], a[0:1])[0] @ O.apply_rope(k[None], a[1:2])[0]
+        s2 = O.apply_rope(q[None], a2[0:1])[0] @ O.apply_rope(k[None], a2[1:2])[0]
+        assert abs(s1 - s2) < 1e-10
+
+
+def test_rope_axis_split():
+    # moving along columns leaves the row pairs (p < d/4) untouched and vice versa
+    d = 64
+    a_row = O.rope_table(np.array([[3.0, 0.0]]), d)[0]
+    a_col = O.rope_table(np.array([[0.0, 3.0]]), d)[0]
+    assert np.all(a_row[:d // 4] != 0) and np.all(a_col[d // 4:] != 0)
+    assert np.all(a_col[:d // 4] == 0)
+    assert np.all(a_row[d // 4:] == 0)
+    # pair j = 0 of each axis turns by exactly the position
+    assert a_row[0] == 3.0 and a_col[d // 4] == 3.0
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_rows_are_a_distribution():
+    # with V = identity the output row is the softmax row itself
+    rng = np.random.default_rng(6)
+    L = 40
+    q = rng.standard_normal((1, 2, L, 64)) * 2
+    k = rng.standard_normal((1, 2, L, 64)) * 2
+    v = np.broadcast_to(np.eye(L, 64), (1, 2, L, 64)).copy()
+    p = O.attention(q, k, v)[..., :L]
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    assert np.all(p > 0)
+
+
+def test_attention_identical_keys_gives_mean_of_v():
+    rng = np.random.default_rng(7)
+    L = 33
+    q = rng.standard_normal((2, 2, L, 64))
+    k = np.broadcast_to(rng.standard_normal((1, 1, 1, 64)), (2, 2, L, 64)).copy()
+    v = rng.standard_normal((2, 2, L, 64))
+    out = O.attention(q, k, v)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=2, keepdims=True), out.shape),
+                               atol=1e-13)
+    vv = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    np.testing.assert_allclose(O.attention(q, k, vv), vv, atol=1e-13)
+
+
+def test_attention_dominant_key():
+    rng = np.random.default_rng(8)
+    L, d = 17, 64
+    k = rng.standard_normal((1, 1, L, d))
+    v = rng.standard_normal((1, 1, L, d))
+    q = 200.0 * k[:, :, 5:6].repeat(L, axis=2)
+    out = O.attention(q, k, v)
+    np.testing.assert_allclose(out[0, 0], np.broadcast_to(v[0, 0, 5], (L, d)), atol=1e-8)
+
+
+@pytest.mark.parametrize("B,H,L,d", [(1, 1, 7, 64), (2, 2, 33, 64), (1, 1, 9, 128)])
+def test_attention_vs_naive_triple_loop(B, H, L, d):
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    np.testing.assert_allclose(O.attention(q, k, v), O.attention_naive(q, k, v), rtol=1e-9,
+                               atol=1e-12)
+
+
+def test_attention_vs_torch_sdpa():
+    rng = np.random.default_rng(10)
+    q, k, v = (rng.standard_normal((2, 3, 50, 64)) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(O.attention(q, k, v), ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- blocks
+
+def _tiny_double(rng, D=64, H=2, F=256, Lt=3, gh=2, gw=3, B=2):
+    P = {}
+    for s in ("img", "txt"):
+        for name, shp in (("qkv", (3 * D, D)), ("proj", (D, D)), ("mlp1", (F, D)), ("mlp2", (D, F))):
+            P[f"{s}.{name}.w"] = rng.standard_normal(shp) * 0.05
+            P[f"{s}.{name}.b"] = rng.standard_normal(shp[0]) * 0.05
+    x_txt = rng.standard_normal((B, Lt, D))
+    x_img = rng.standard_normal((B, gh * gw, D))
+    m_img = rng.standard_normal((B, 6, D)) * 0.1
+    m_txt = rng.standard_normal((B, 6, D)) * 0.1
+    ang = O.rope_table(O.image_positions(gh, gw, Lt), D // H)
+    return P, x_txt, x_img, m_img, m_txt, ang, H
+
+
+def test_double_block_zero_gates_is_identity():
+    rng = np.random.default_rng(11)
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng)
+    for m in (mi, mt):
+        m[:, 2] = 0.0
+        m[:, 5] = 0.0
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H)
+    np.testing.assert_array_equal(ot, xt)
+    np.testing.assert_array_equal(oi, xi)
+
+
+def test_double_block_zero_value_weights():
+    # W_v = b_v = 0 and mlp gate 0: the attention branch is exactly gate1 * b_o
+    rng = np.random.default_rng(12)
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng)
+    D = xt.shape[-1]
+    for s in ("img", "txt"):
+        P[f"{s}.qkv.w"][2 * D:] = 0.0
+        P[f"{s}.qkv.b"][2 * D:] = 0.0
+    for m in (mi, mt):
+        m[:, 5] = 0.0
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H)
+    np.testing.assert_allclose(oi, xi + mi[:, 2:3] * P["img.proj.b"], atol=1e-14)
+    np.testing.assert_allclose(ot, xt + mt[:, 2:3] * P["txt.proj.b"], atol=1e-14)
+
+
+def test_double_block_stream_isolation():
+    # text gates 0: text rows unchanged, image rows still move
+    rng = np.random.default_rng(13)
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng)
+    mt[:, 2] = 0.0
+    mt[:, 5] = 0.0
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H)
+    np.testing.assert_array_equal(ot, xt)
+    assert np.max(np.abs(oi - xi)) > 1e-3
+
+
+def test_double_block_brute_force_small():
+    # the joint attention written out token by token, no reshapes, no rope
+    # helpers: catches a transposed head split or a swapped stream order
+    rng = np.random.default_rng(14)
+    D, H, F, Lt, gh, gw, B = 8, 2, 16, 2, 1, 3, 1
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng, D, H, F, Lt, gh, gw, B)
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H)
+    d = D // H
+    L = Lt + gh * gw
+    x = np.concatenate([xt, xi], axis=1)[0]
+    mods = [mt[0]] * Lt + [mi[0]] * (gh * gw)
+    names = ["txt"] * Lt + ["img"] * (gh * gw)
+    pos = [(0, 0)] * Lt + [(r, c) for r in range(gh) for c in range(gw)]
+
+    def ln(u):
+        mu = sum(u) / len(u)
+        var = sum((t - mu) ** 2 for t in u) / len(u)
+        return [(t - mu) / math.sqrt(var + 1e-6) for t in u]
+
+    def lin(u, w, b):
+        return [sum(u[k] * w[n][k] for k in range(len(u))) + b[n] for n in range(len(b))]
+
+    def rot(vec, p):
+        out = list(vec)
+        for pr in range(d // 2):
+            ax = 0 if pr < d // 4 else 1
+            j = pr % (d // 4)
+            th = p[ax] * 10000.0 ** (-j / (d // 4))
+            a, b = vec[2 * pr], vec[2 * pr + 1]
+            out[2 * pr] = a * math.cos(th) - b * math.sin(th)
+            out[2 * pr + 1] = a * math.sin(th) + b * math.cos(th)
+        return out
+
+    qs, ks, vs = [], [], []
+    for t in range(L):
+        m = mods[t]
+        u = [ln(list(x[t]))[c] * (1 + m[1][c]) + m[0][c] for c in range(D)]
+        h = lin(u, P[f"{names[t]}.qkv.w"], P[f"{names[t]}.qkv.b"])
+        qs.append(h[:D]); ks.append(h[D:2 * D]); vs.append(h[2 * D:])
+    att = [[0.0] * D for _ in range(L)]
+    for hh in range(H):
+        sl = slice(hh * d, (hh + 1) * d)
+        qh = [rot(qs[t][sl], pos[t]) for t in range(L)]
+        kh = [rot(ks[t][sl], pos[t]) for t in range(L)]
+        for t in range(L):
+            s = [sum(a * b for a, b in zip(qh[t], kh[u])) / math.sqrt(d) for u in range(L)]
+            mx = max(s)
+            e = [math.exp(z - mx) for z in s]
+            z = sum(e)
+            for c in range(d):
+                att[t][hh * d + c] = sum(e[u] * vs[u][sl][c] for u in range(L)) / z
+    gelu = lambda z: 0.5 * z * (1 + math.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+    out = []
+    for t in range(L):
+        m, nm = mods[t], names[t]
+        y = lin(att[t], P[f"{nm}.proj.w"], P[f"{nm}.proj.b"])
+        xr = [x[t][c] + m[2][c] * y[c] for c in range(D)]
+        u = [ln(xr)[c] * (1 + m[4][c]) + m[3][c] for c in range(D)]
+        hid = [gelu(z) for z in lin(u, P[f"{nm}.mlp1.w"], P[f"{nm}.mlp1.b"])]
+        y2 = lin(hid, P[f"{nm}.mlp2.w"], P[f"{nm}.mlp2.b"])
+        out.append([xr[c] + m[5][c] * y2[c] for c in range(D)])
+    out = np.array(out)
+    np.testing.assert_allclose(ot[0], out[:Lt], atol=1e-12)
+    np.testing.assert_allclose(oi[0], out[Lt:], atol=1e-12)
+
+
+def test_single_block_zero_gate_and_wiring():
+    rng = np.random.default_rng(15)
+    D, H, F, L, B = 32, 2, 64, 7, 2
+    P = {"lin1.w": rng.standard_normal((3 * D + F, D)) * 0.1, "lin1.b": rng.standard_normal(3 * D + F) * 0.1,
+         "lin2.w": rng.standard_normal((D, D + F)) * 0.1, "lin2.b": rng.standard_normal(D) * 0.1}
+    x = rng.standard_normal((B, L, D))
+    mod = rng.standard_normal((B, 3, D)) * 0.1
+    ang = O.rope_table(O.image_positions(2, 3, 1), D // H)
+    m0 = mod.copy(); m0[:, 2] = 0
+    np.testing.assert_array_equal(O.single_block(x, m0, P, ang, H), x)
+    # zero the attention half of lin2: the block reduces to a gated GELU MLP
+    P2 = dict(P); P2["lin2.w"] = P["lin2.w"].copy(); P2["lin2.w"][:, :D] = 0
+    u = O.modulate(x, mod[:, 0:1], mod[:, 1:2])
+    mlp = O.gelu_tanh(u @ P["lin1.w"][3 * D:].T + P["lin1.b"][3 * D:]) @ P["lin2.w"][:, D:].T
+    np.testing.assert_allclose(O.single_block(x, mod, P2, ang, H),
+                               x + mod[:, 2:3] * (mlp + P["lin2.b"]), atol=1e-13)
+
+
+# ---------------------------------------------------------------- FBC
+
+def test_fbcache_rel_vs_python_loop():
+    rng = np.random.default_rng(16)
+    r = rng.standard_normal(1000)
+    a = r + 0.05 * rng.standard_normal(1000)
+    num = 0.0
+    den = 0.0
+    for x, y in zip(r.tolist(), a.tolist()):
+        num += abs(x - y)
+        den += abs(y)
+    assert abs(O.fbcache_rel(r, a) - num / den) < 1e-12
+    assert O.fbcache_rel(r, r) == 0.0
+    assert O.fbcache_rel(r, np.zeros_like(r)) == math.inf
+    assert not O.fbcache_decide(math.nan, 1.0)
+    assert not O.fbcache_decide(0.12, 0.12)     # strict
+    assert O.fbcache_decide(0.1199, 0.12)
+    assert not O.fbcache_decide(0.0, 0.0)
+    assert not O.fbcache_decide(math.inf, math.inf)
+
+
+# ---------------------------------------------------------------- number formats
+
+def _e4m3_table():
+    vals = []
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append((s * v, code))
+    return vals
+
+
+def test_e4m3_code_table_bruteforce():
+    table = _e4m3_table()
+    pos = sorted((v, c) for v, c in table if v >= 0 and not (v == 0 and c & 0x80))
+    assert len(pos) == 127 and pos[-1][0] == 448.0
+    rng = np.random.default_rng(17)
+    xs = np.concatenate([rng.standard_normal(4000) * 30, rng.standard_normal(2000) * 0.01,
+                         [p[0] for p in pos],
+                         [(pos[i][0] + pos[i + 1][0]) / 2 for i in range(126)]])
+    vals = np.array([p[0] for p in pos])
+    codes = np.array([p[1] for p in pos])
+    for x in xs:
+        ax = min(abs(x), 448.0)
+        dist = np.abs(vals - ax)
+        best = np.flatnonzero(dist == dist.min())
+        if len(best) > 1:                   # tie: the even code
+            best = [b for b in best if codes[b] % 2 == 0]
+        want = math.copysign(vals[best[0]], x)
+        assert round_e4m3(np.array(x)) == want, x
+
+
+def test_e4m3_golden_points():
+    for x, want in _golden_rows("e4m3_points.txt"):
+        assert round_e4m3(np.array(x)) == want, (x, want)
+
+
+def test_e4m3_representable_values_are_fixed_points():
+    vals = np.array([v for v, _ in _e4m3_table()])
+    np.testing.assert_array_equal(round_e4m3(vals), vals)
+
+
+def test_bf16_rounding_vs_torch_cast():
+    rng = np.random.default_rng(18)
+    x32 = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 100,
+                          (rng.standard_normal(2000) * 1e-39).astype(np.float32),
+                          np.array([3.0e38, -3.0e38, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], np.float32)])
+    want = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(round_bf16(x32.astype(np.float64)), want)
+
+
+def test_quantize_rows_scale_and_roundtrip():
+    # rows whose amax is 448 and whose entries are e4m3 values quantise exactly
+    rng = np.random.default_rng(19)
+    vals = np.array([v for v, _ in _e4m3_table()])
+    x = rng.choice(vals, size=(6, 40))
+    x[:, 0] = 448.0
+    q, s = quantize_rows_e4m3(x)
+    np.testing.assert_array_equal(s, np.float32(1.0))
+    np.testing.assert_array_equal(q, x)
+    z, sz = quantize_rows_e4m3(np.zeros((2, 5)))
+    np.testing.assert_array_equal(sz, 1.0)
+    np.testing.assert_array_equal(z, 0.0)
+
+
+def test_linear_fp8_exact_on_representable_inputs():
+    rng = np.random.default_rng(20)
+    vals = np.array([v for v, _ in _e4m3_table()])
+    vals = vals[np.abs(vals) <= 4]
+    x = rng.choice(vals, size=(5, 32)); x[:, 0] = 448.0
+    w = rng.choice(vals, size=(7, 32)); w[:, 0] = 448.0
+    b = rng.standard_normal(7)
+    np.testing.assert_allclose(O.linear_fp8(x, w, b), O.linear(x, w, b), rtol=1e-15)
+
+
+def test_attention_fp8_identical_keys_mean_of_v():
+    rng = np.random.default_rng(21)
+    vals = np.array([v for v, _ in _e4m3_table()])
+    L, d = 20, 64
+    v = rng.choice(vals[np.abs(vals) < 100], size=(1, 1, L, d))
+    v[0, 0, 0, :] = 448.0                  # per-channel amax 448 -> scale 1
+    k = np.broadcast_to(rng.standard_normal((1, 1, 1, d)), (1, 1, L, d)).copy()
+    q = rng.standard_normal((1, 1, L, d))
+    out = O.attention_fp8(q, k, v)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=2, keepdims=True), out.shape),
+                               rtol=1e-14)
+
+
+def test_attention_fp8_close_to_exact():
+    # each P_j V_j term carries at most a few e4m3 half-ulps (2^-4 each) of
+    # relative error, so the deviation is bounded by a small multiple of the
+    # attention-weighted mean of |V| (the output itself can be much smaller)
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((1, 2, 64, 64)) for _ in range(3))
+    ex = O.attention(q, k, v)
+    wabs = O.attention(q, k, np.abs(v))
+    assert np.max(np.abs(O.attention_fp8(q, k, v) - ex) / wabs) < 0.3
