@@ -1,0 +1,86 @@
+// Device-side helpers shared by the HIP kernels of the DiT denoise step (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;   // bfloat16 storage
+typedef uint8_t fp8_t;     // OCP e4m3 storage
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) int i32x4;   // 16-byte load/store unit
+
+__device__ __forceinline__ float bf2f(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (the gfx950 convert instruction).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// Two floats -> two packed bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// x * sigmoid(x)
+__device__ __forceinline__ float silu_f(float x) {
+  return x * fast_rcp(1.0f + fast_exp2(-x * 1.4426950408889634f));
+}
+
+// tanh-approximated GELU written as x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3):
+// 0.5 x (1 + tanh u) = x / (1 + e^{-2u}).
+__device__ __forceinline__ float gelu_tanh_f(float x) {
+  const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  float u = k0 * (x + k1 * x * x * x);
+  return x * fast_rcp(1.0f + fast_exp2(-2.0f * 1.4426950408889634f * u));
+}
+
+template <typename T> struct XIO;
+template <> struct XIO<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct XIO<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Row map of the "stream-major" row space used inside a double-stream block:
+// rows [0, B*Li) are image tokens (batch-major), rows [B*Li, B*(Li+Lt)) are text
+// tokens; a single-stream block uses the joint order directly (stream_major = 0).
+struct RowMap {
+  int B, Lt, Li, L;
+  int stream_major;  // 1: image rows first then text rows; 0: joint [b][t] order
+  int base;          // added to a row index before mapping (row offset of a GEMM group)
+  __device__ __forceinline__ void token(int r, int& b, int& t) const {
+    r += base;
+    if (!stream_major) { b = r / L; t = r - b * L; return; }
+    const int ni = B * Li;
+    if (r < ni) { b = r / Li; t = Lt + (r - b * Li); }
+    else { const int q = r - ni; b = q / Lt; t = q - b * Lt; }
+  }
+  // Joint-buffer row (b * L + t) of row r.
+  __device__ __forceinline__ int joint_row(int r) const {
+    int b, t; token(r, b, t); return b * L + t;
+  }
+  // Inverse (ignores base): row of token (b, t) in this map's row space.
+  __device__ __forceinline__ int stream_row(int b, int t) const {
+    if (!stream_major) return b * L + t;
+    if (t >= Lt) return b * Li + (t - Lt);
+    return B * Li + b * Lt + t;
+  }
+};
+
+}  // namespace dit

@@ -1,0 +1,537 @@
+// C ABI of libdit: argument validation, workspace layout and the host-side
+// sequencing of the HIP kernels for a block, a denoise step, the modulation
+// precompute and the First-Block-Cache test.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dit.h"
+#include "common.h"
+#include "kernels.h"
+#include "ops.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define DIT_CHECK_HIP(expr)                                                              \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(DIT_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));           \
+  } while (0)
+
+// Arch check, cached per device (the answer never changes for a device).
+int check_device() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DIT_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(DIT_ERR_UNSUPPORTED, "device index %d", dev);
+  int v = cache[dev].load();
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(DIT_ERR_HIP, "hipGetDeviceProperties failed");
+    v = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(v);
+  }
+  if (v != 1) return fail(DIT_ERR_UNSUPPORTED, "libdit runs on gfx950 only");
+  return DIT_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct Dims {
+  int B, Lt, Li, L, D, H, d, F, gw;
+};
+
+int make_dims(const dit_dims* in, Dims* o) {
+  if (!in) return fail(DIT_ERR_INVALID_ARG, "dims is NULL");
+  if (in->B < 1 || in->Lt < 0 || in->grid_h < 1 || in->grid_w < 1 || in->D < 1 || in->H < 1 ||
+      in->F < 1)
+    return fail(DIT_ERR_INVALID_ARG, "non-positive dimension");
+  o->B = in->B;
+  o->Lt = in->Lt;
+  o->Li = in->grid_h * in->grid_w;
+  o->L = o->Lt + o->Li;
+  o->D = in->D;
+  o->H = in->H;
+  o->F = in->F;
+  o->gw = in->grid_w;
+  if (o->D % o->H) return fail(DIT_ERR_INVALID_ARG, "D %% H != 0");
+  o->d = o->D / o->H;
+  if (o->Lt % 8 || o->Li % 8)
+    return fail(DIT_ERR_INVALID_ARG, "text and image token counts must be multiples of 8");
+  if ((long long)o->B * o->L * (o->D + o->F) > (1LL << 31) - 1)
+    return fail(DIT_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  return DIT_OK;
+}
+
+int check_bf16_dims(const Dims& dm) {
+  if (dm.d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d (this build runs 128)", dm.d);
+  if (dm.D % 256 || dm.D > 3072)
+    return fail(DIT_ERR_UNSUPPORTED, "hidden size %d (needs a multiple of 256, <= 3072)", dm.D);
+  if (dm.F % 64) return fail(DIT_ERR_UNSUPPORTED, "MLP size %d (needs a multiple of 64)", dm.F);
+  return DIT_OK;
+}
+
+// ---- workspace layout (256-byte aligned carving)
+struct Carver {
+  char* base;
+  size_t off;
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* r = (T*)(base + off);
+    off += n * sizeof(T);
+    return r;
+  }
+};
+
+struct BlockWS {
+  bf16_t* u;    // LN-modulate output [B*L, D] (row order of the block)
+  bf16_t* q;    // [B, H, L, d]
+  bf16_t* k;    // [B, H, L, d]
+  bf16_t* vt;   // [B, H, d, L]
+  bf16_t* cat;  // [B*L, D + F]: attention output | MLP hidden
+};
+
+BlockWS carve_block(Carver& c, const Dims& dm) {
+  const size_t n = (size_t)dm.B * dm.L * dm.D;
+  BlockWS w;
+  w.u = c.take<bf16_t>(n);
+  w.q = c.take<bf16_t>(n);
+  w.k = c.take<bf16_t>(n);
+  w.vt = c.take<bf16_t>(n);
+  w.cat = c.take<bf16_t>((size_t)dm.B * dm.L * (dm.D + dm.F));
+  return w;
+}
+
+struct StepWS {
+  BlockWS blk;
+  float* x;         // joint residual stream [B, L, D]
+  float* before;    // image hidden before block 0 [B, Li, D]
+  float* staging;   // first block's residual [B, Li, D]
+  float* v;         // velocity [B * Li, 64]
+  float* rope;      // [L, d/2, 2]
+  double* part;     // [2 * FBC_PARTS]
+  FbcResult* res;
+};
+
+StepWS carve_step(Carver& c, const Dims& dm) {
+  StepWS w;
+  w.blk = carve_block(c, dm);
+  w.x = c.take<float>((size_t)dm.B * dm.L * dm.D);
+  w.before = c.take<float>((size_t)dm.B * dm.Li * dm.D);
+  w.staging = c.take<float>((size_t)dm.B * dm.Li * dm.D);
+  w.v = c.take<float>((size_t)dm.B * dm.Li * 64);
+  w.rope = c.take<float>((size_t)dm.L * dm.d);
+  w.part = c.take<double>(2 * FBC_PARTS);
+  w.res = c.take<FbcResult>(1);
+  return w;
+}
+
+struct ModWS {
+  bf16_t* emb;  // [n, 256]
+  bf16_t* h;    // [n, D]
+  bf16_t* cs;   // [n, D]
+};
+
+ModWS carve_mod(Carver& c, const Dims& dm, int n) {
+  ModWS w;
+  w.emb = c.take<bf16_t>((size_t)n * 256);
+  w.h = c.take<bf16_t>((size_t)n * dm.D);
+  w.cs = c.take<bf16_t>((size_t)n * dm.D);
+  return w;
+}
+
+size_t ws_size(const Dims& dm, int purpose, int n) {
+  Carver c{nullptr, 0};
+  switch (purpose) {
+    case DIT_WS_ATTENTION: return 0;
+    case DIT_WS_BLOCK: carve_block(c, dm); break;
+    case DIT_WS_STEP: carve_step(c, dm); break;
+    case DIT_WS_MODULATION: carve_mod(c, dm, n); break;
+    case DIT_WS_FBCACHE:
+      c.take<double>(2 * FBC_PARTS);
+      c.take<FbcResult>(1);
+      break;
+    default: return 0;
+  }
+  return (c.off + 255) & ~(size_t)255;
+}
+
+int check_linear(const dit_linear& l, const char* name) {
+  if (!l.w || !l.b) return fail(DIT_ERR_INVALID_ARG, "%s: NULL weight or bias", name);
+  if (!aligned16(l.w) || !aligned16(l.b))
+    return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", name);
+  return DIT_OK;
+}
+
+int check_block(const dit_block* blk) {
+  if (!blk) return fail(DIT_ERR_INVALID_ARG, "block is NULL");
+  int rc;
+  if (blk->kind == DIT_BLOCK_DOUBLE) {
+    for (int s = 0; s < 2; ++s) {
+      if ((rc = check_linear(blk->qkv[s], "qkv")) || (rc = check_linear(blk->proj[s], "proj")) ||
+          (rc = check_linear(blk->mlp1[s], "mlp1")) || (rc = check_linear(blk->mlp2[s], "mlp2")))
+        return rc;
+    }
+  } else if (blk->kind == DIT_BLOCK_SINGLE) {
+    if ((rc = check_linear(blk->lin1, "lin1")) || (rc = check_linear(blk->lin2, "lin2"))) return rc;
+  } else {
+    return fail(DIT_ERR_INVALID_ARG, "unknown block kind %d", blk->kind);
+  }
+  return DIT_OK;
+}
+
+GemmProblem gp(const bf16_t* A, int lda, const dit_linear& l, int K, int M, int N) {
+  GemmProblem g;
+  g.A = A;
+  g.lda = lda;
+  g.W = (const bf16_t*)l.w;
+  g.ldw = K;
+  g.bias = l.b;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return g;
+}
+
+// ---- one block, already validated
+template <class XT>
+hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* mod, int bs,
+                      const float* rope, const BlockWS& w, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
+  const int DF = D + F;
+  const QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  const float scale = 1.0f / sqrtf((float)dm.d);
+  hipError_t e;
+  if (blk.kind == DIT_BLOCK_DOUBLE) {
+    const RowMap sm{B, Lt, Li, L, 1, 0};
+    RowMap st_txt = sm;
+    st_txt.base = B * Li;
+    const RowMap maps[2] = {sm, st_txt};
+    const int ng = (B * Lt > 0) ? 2 : 1;
+    const float* mi = mod;
+    const float* mt = mod + 6 * (size_t)D;
+    const size_t ti = (size_t)B * Li;   // first text row of the stream-major row space
+
+    if ((e = ln_modulate<XT>(x, w.u, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs, st))) return e;
+    GemmProblem g[2] = {gp(w.u, D, blk.qkv[0], D, B * Li, 3 * D),
+                        gp(w.u + ti * D, D, blk.qkv[1], D, B * Lt, 3 * D)};
+    if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
+    if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, sm, B, dm.H, L, dm.d, scale, st))) return e;
+    g[0] = gp(w.cat, DF, blk.proj[0], D, B * Li, D);
+    g[1] = gp(w.cat + ti * DF, DF, blk.proj[1], D, B * Lt, D);
+    const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
+    if ((e = gemm_gated_residual<XT>(g, ng, x, D, gate1, bs, maps, st))) return e;
+    if ((e = ln_modulate<XT>(x, w.u, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D, mt + 3 * D,
+                             mt + 4 * D, bs, st)))
+      return e;
+    g[0] = gp(w.u, D, blk.mlp1[0], D, B * Li, F);
+    g[1] = gp(w.u + ti * D, D, blk.mlp1[1], D, B * Lt, F);
+    bf16_t* hid[2] = {w.cat + D, w.cat + ti * DF + D};
+    const int ldh[2] = {DF, DF};
+    if ((e = gemm_gelu_bf16(g, ng, hid, ldh, st))) return e;
+    g[0] = gp(w.cat + D, DF, blk.mlp2[0], F, B * Li, D);
+    g[1] = gp(w.cat + ti * DF + D, DF, blk.mlp2[1], F, B * Lt, D);
+    const float* gate2[2] = {mi + 5 * D, mt + 5 * D};
+    return gemm_gated_residual<XT>(g, ng, x, D, gate2, bs, maps, st);
+  }
+  // single-stream block, joint row order
+  const RowMap jm{B, Lt, Li, L, 0, 0};
+  if ((e = ln_modulate<XT>(x, w.u, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st))) return e;
+  const GemmProblem g1 = gp(w.u, D, blk.lin1, D, B * L, 3 * D + F);
+  if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
+  if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, jm, B, dm.H, L, dm.d, scale, st))) return e;
+  const GemmProblem g2 = gp(w.cat, DF, blk.lin2, DF, B * L, D);
+  const float* gate[1] = {mod + 2 * D};
+  return gemm_gated_residual<XT>(&g2, 1, x, D, gate, bs, &jm, st);
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* dit_status_string(int status) {
+  switch (status) {
+    case DIT_OK: return "ok";
+    case DIT_ERR_INVALID_ARG: return "invalid argument";
+    case DIT_ERR_UNSUPPORTED: return "unsupported";
+    case DIT_ERR_WORKSPACE: return "workspace too small";
+    case DIT_ERR_HIP: return "HIP runtime error";
+    case DIT_ERR_NONFINITE: return "non-finite value in the cache test";
+    default: return "unknown status";
+  }
+}
+
+const char* dit_last_error(void) { return g_last_error.c_str(); }
+
+size_t dit_workspace_bytes(const dit_dims* dims, int purpose, int n_steps) {
+  Dims dm;
+  if (make_dims(dims, &dm) != DIT_OK) return 0;
+  if (purpose == DIT_WS_MODULATION && n_steps < 1) return 0;
+  return ws_size(dm, purpose, n_steps);
+}
+
+int dit_sigmas(int n_steps, double shift, double* out_host) {
+  if (n_steps < 1 || !out_host || !(shift > 0.0) || !std::isfinite(shift))
+    return fail(DIT_ERR_INVALID_ARG, "dit_sigmas: n_steps >= 1, shift > 0, out non-NULL");
+  for (int i = 0; i <= n_steps; ++i) {
+    const double tau = 1.0 - (double)i / (double)n_steps;
+    out_host[i] = shift * tau / (1.0 + (shift - 1.0) * tau);
+  }
+  return DIT_OK;
+}
+
+int dit_rope_table(int grid_h, int grid_w, int Lt, int head_dim, double theta, float* table,
+                   void* stream) {
+  if (grid_h < 1 || grid_w < 1 || Lt < 0 || head_dim < 4 || head_dim % 4 || !table ||
+      !(theta > 0.0))
+    return fail(DIT_ERR_INVALID_ARG, "dit_rope_table: bad argument");
+  int rc = check_device();
+  if (rc) return rc;
+  DIT_CHECK_HIP(rope_table(table, grid_w, Lt, Lt + grid_h * grid_w, head_dim, theta,
+                           (hipStream_t)stream));
+  return DIT_OK;
+}
+
+int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
+                  int head_dim, int dtype, float softmax_scale, void* stream) {
+  if (!q || !k || !vt || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: pointers must be 16-byte aligned");
+  if (B < 1 || H < 1 || L < 8 || L % 8)
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H >= 1 and L a multiple of 8");
+  if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dit_attention: dtype %d", dtype);
+  if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "dit_attention: head_dim %d", head_dim);
+  if (!std::isfinite(softmax_scale))
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: softmax_scale must be finite");
+  if ((long long)B * H * L * head_dim > (1LL << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "dit_attention: problem too large");
+  int rc = check_device();
+  if (rc) return rc;
+  const RowMap jm{B, 0, L, L, 0, 0};
+  DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
+                               H * head_dim, jm, B, H, L, head_dim, softmax_scale,
+                               (hipStream_t)stream));
+  return DIT_OK;
+}
+
+int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
+                      const float* mod, long mod_bstride, const float* rope, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  Dims dm;
+  int rc;
+  if ((rc = make_dims(dims, &dm))) return rc;
+  if ((rc = check_block(blk))) return rc;
+  if (!x || !mod || !rope || !workspace)
+    return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: NULL pointer");
+  if (!aligned16(x) || !aligned16(mod) || !aligned16(rope) || !aligned16(workspace))
+    return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: pointers must be 16-byte aligned");
+  if (mod_bstride < 0 || mod_bstride % 4 || mod_bstride > (1L << 30))
+    return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: mod_bstride must be >= 0, a multiple of 4");
+  if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dit_block_forward: dtype %d", dtype);
+  if (x_dtype != DIT_F32 && x_dtype != DIT_BF16)
+    return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: x_dtype %d", x_dtype);
+  if ((rc = check_bf16_dims(dm))) return rc;
+  const size_t need = ws_size(dm, DIT_WS_BLOCK, 0);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "dit_block_forward: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_device())) return rc;
+  Carver c{(char*)workspace, 0};
+  const BlockWS w = carve_block(c, dm);
+  hipStream_t st = (hipStream_t)stream;
+  if (x_dtype == DIT_F32)
+    DIT_CHECK_HIP(block_impl<float>(dm, *blk, (float*)x, mod, (int)mod_bstride, rope, w, st));
+  else
+    DIT_CHECK_HIP(block_impl<bf16_t>(dm, *blk, (bf16_t*)x, mod, (int)mod_bstride, rope, w, st));
+  return DIT_OK;
+}
+
+int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* out,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  if (!m || !sigmas_host || !out || !workspace || n < 1)
+    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: NULL pointer or n < 1");
+  Dims dm;
+  int rc;
+  if ((rc = make_dims(&m->dims, &dm))) return rc;
+  if ((rc = check_linear(m->time1, "time1")) || (rc = check_linear(m->time2, "time2")) ||
+      (rc = check_linear(m->mod, "mod")))
+    return rc;
+  if (!aligned16(out) || !aligned16(workspace))
+    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: pointers must be 16-byte aligned");
+  if (m->n_double < 0 || m->n_single < 0)
+    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: negative block count");
+  if (dm.D % 64) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: D %% 64 != 0");
+  for (int i = 0; i < n; ++i)
+    if (!std::isfinite(sigmas_host[i]))
+      return fail(DIT_ERR_INVALID_ARG, "dit_modulation: non-finite sigma");
+  const size_t need = ws_size(dm, DIT_WS_MODULATION, n);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "dit_modulation: workspace %zu < %zu bytes", ws_bytes, need);
+  const long long nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm.D;
+  if (nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: too many vectors");
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c{(char*)workspace, 0};
+  const ModWS w = carve_mod(c, dm, n);
+  DIT_CHECK_HIP(sinusoid_host(sigmas_host, w.emb, n, 128, st));
+  DIT_CHECK_HIP(gemm_silu_bf16(gp(w.emb, 256, m->time1, 256, n, dm.D), w.h, dm.D, st));
+  DIT_CHECK_HIP(gemm_silu_bf16(gp(w.h, dm.D, m->time2, dm.D, n, dm.D), w.cs, dm.D, st));
+  DIT_CHECK_HIP(gemm_store_f32(gp(w.cs, dm.D, m->mod, dm.D, n, (int)nmod), out, (int)nmod, st));
+  return DIT_OK;
+}
+
+int fbcache_should_skip(const float* x_after, const float* x_before, const float* anchor,
+                        float* staging, int B, int Lt, int Li, int D, float threshold,
+                        int has_anchor, void* workspace, size_t ws_bytes, void* stream,
+                        double* rel_out, int* skip_out) {
+  if (!x_after || !x_before || !staging || !workspace || !rel_out || !skip_out ||
+      (has_anchor && !anchor))
+    return fail(DIT_ERR_INVALID_ARG, "fbcache_should_skip: NULL pointer");
+  if (!aligned16(x_after) || !aligned16(x_before) || !aligned16(staging) ||
+      !aligned16(workspace) || (anchor && !aligned16(anchor)))
+    return fail(DIT_ERR_INVALID_ARG, "fbcache_should_skip: pointers must be 16-byte aligned");
+  if (B < 1 || Lt < 0 || Li < 1 || D < 4 || D % 4)
+    return fail(DIT_ERR_INVALID_ARG, "fbcache_should_skip: bad shape");
+  if (std::isnan(threshold)) return fail(DIT_ERR_INVALID_ARG, "fbcache_should_skip: NaN threshold");
+  dit_dims dd{B, Lt, 1, Li, D, 1, 1};
+  Dims dm;
+  int rc;
+  if ((rc = make_dims(&dd, &dm))) return rc;
+  const size_t need = ws_size(dm, DIT_WS_FBCACHE, 0);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "fbcache_should_skip: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c{(char*)workspace, 0};
+  double* part = c.take<double>(2 * FBC_PARTS);
+  FbcResult* res = c.take<FbcResult>(1);
+  DIT_CHECK_HIP(fbc_reduce(x_after, x_before, anchor, staging, part, FBC_PARTS, res, B, Lt, Li, D,
+                           has_anchor ? 1 : 0, (double)threshold, st));
+  FbcResult h;
+  DIT_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(h), hipMemcpyDeviceToHost, st));
+  DIT_CHECK_HIP(hipStreamSynchronize(st));
+  *rel_out = h.rel;
+  *skip_out = h.skip;
+  if (h.nonfinite) return fail(DIT_ERR_NONFINITE, "fbcache_should_skip: non-finite residual");
+  return DIT_OK;
+}
+
+int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt, float* latents,
+                     double sigma, double sigma_next, dit_fbcache* cache, void* workspace,
+                     size_t ws_bytes, void* stream, dit_step_info* info_out) {
+  if (!m || !mod_step || !latents || !workspace || (m->dims.Lt > 0 && !txt))
+    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: NULL pointer");
+  Dims dm;
+  int rc;
+  if ((rc = make_dims(&m->dims, &dm))) return rc;
+  if ((rc = check_bf16_dims(dm))) return rc;
+  if (m->n_double < 1 || m->n_single < 0 || !m->blocks)
+    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: needs >= 1 double block");
+  for (int j = 0; j < m->n_double + m->n_single; ++j) {
+    if ((rc = check_block(&m->blocks[j]))) return rc;
+    const int want = j < m->n_double ? DIT_BLOCK_DOUBLE : DIT_BLOCK_SINGLE;
+    if (m->blocks[j].kind != want)
+      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: block %d has the wrong kind", j);
+  }
+  if ((rc = check_linear(m->img_in, "img_in")) || (rc = check_linear(m->final_out, "final_out")))
+    return rc;
+  if (m->C_in < 4 || m->C_in > 64 || m->C_in % 4)
+    return fail(DIT_ERR_UNSUPPORTED, "dit_denoise_step: C_in %d (4..64, multiple of 4)", m->C_in);
+  if (dm.B > 2) return fail(DIT_ERR_UNSUPPORTED, "dit_denoise_step: B must be 1 or 2");
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next) ||
+      (dm.B == 2 && !std::isfinite(m->guidance)))
+    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: non-finite sigma or guidance");
+  if (!aligned16(mod_step) || !aligned16(latents) || !aligned16(workspace) ||
+      (txt && !aligned16(txt)))
+    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: pointers must be 16-byte aligned");
+  const bool use_cache = cache && cache->enabled;
+  if (use_cache) {
+    if (!cache->anchor || !cache->cached || !aligned16(cache->anchor) || !aligned16(cache->cached))
+      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: cache buffers NULL or misaligned");
+    if (std::isnan(cache->threshold))
+      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: NaN threshold");
+  }
+  const size_t need = ws_size(dm, DIT_WS_STEP, 0);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "dit_denoise_step: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  Carver c{(char*)workspace, 0};
+  const StepWS w = carve_step(c, dm);
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, D = dm.D;
+  const size_t D12 = 12 * (size_t)D, D3 = 3 * (size_t)D;
+
+  DIT_CHECK_HIP(rope_table(w.rope, dm.gw, Lt, dm.L, dm.d, 10000.0, st));
+  if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st));
+  DIT_CHECK_HIP(embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before, B,
+                              Lt, Li, D, m->C_in, st));
+  DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
+
+  double rel = INFINITY;
+  int skip = 0;
+  if (use_cache) {
+    DIT_CHECK_HIP(fbc_reduce(w.x, w.before, cache->anchor, w.staging, w.part, FBC_PARTS, w.res, B,
+                             Lt, Li, D, cache->has_anchor ? 1 : 0, (double)cache->threshold, st));
+    FbcResult h;
+    DIT_CHECK_HIP(hipMemcpyAsync(&h, w.res, sizeof(h), hipMemcpyDeviceToHost, st));
+    DIT_CHECK_HIP(hipStreamSynchronize(st));
+    if (h.nonfinite) return fail(DIT_ERR_NONFINITE, "dit_denoise_step: non-finite residual");
+    rel = h.rel;
+    skip = h.skip;
+  }
+  if (skip) {
+    DIT_CHECK_HIP(fbc_apply(w.x, cache->cached, B, Lt, Li, D, st));
+  } else {
+    for (int j = 1; j < m->n_double; ++j)
+      DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[j], w.x, mod_step + j * D12, 0, w.rope, w.blk,
+                                      st));
+    const float* ms = mod_step + m->n_double * D12;
+    for (int j = 0; j < m->n_single; ++j)
+      DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[m->n_double + j], w.x, ms + j * D3, 0, w.rope,
+                                      w.blk, st));
+    if (use_cache) {
+      DIT_CHECK_HIP(fbc_commit(w.x, w.before, w.staging, cache->cached, cache->anchor, B, Lt, Li, D,
+                               st));
+      cache->has_anchor = 1;
+    }
+  }
+  // velocity head on the image rows, then the Euler (+CFG) update
+  const float* mf = mod_step + m->n_double * D12 + m->n_single * D3;
+  const RowMap sm{B, Lt, Li, dm.L, 1, 0};
+  DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D, 0,
+                                   st));
+  DIT_CHECK_HIP(gemm_store_f32(gp(w.blk.u, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in, st));
+  DIT_CHECK_HIP(euler_update(latents, w.v, Li * m->C_in, B == 2 ? 1 : 0, m->guidance,
+                             (float)(sigma_next - sigma), st));
+  if (info_out) {
+    info_out->rel = rel;
+    info_out->skipped = skip;
+  }
+  return DIT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,408 @@
+// bf16 MFMA GEMM with fused epilogues for the DiT block linears (gfx950).
+//
+//   C[m, n] = sum_k A[m, k] * W[n, k] + bias[n]      (A: activations, W: [out, in])
+//
+// One workgroup = 4 or 8 wave64s computing a BM x BN tile with
+// v_mfma_f32_32x32x16_bf16.  K is staged through LDS 64 at a time,
+// double-buffered, with the next slab's global loads in flight during the
+// current slab's MFMAs.  Up to two problems (the image and text streams of a
+// double block, each with its own weights) share one launch.
+//
+// Epilogue: each wave parks one 32-column slice of its accumulators in LDS at a
+// time and reads it back either row-wise (4 consecutive columns of one row per
+// lane: coalesced stores, RoPE pairs in-register) or column-wise (4 consecutive
+// rows of one column per lane: the transposed V store), then calls the fused
+// epilogue functor.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+constexpr int GEMM_BK = 64;
+constexpr int GEMM_LDS = GEMM_BK + 8;   // padded LDS row (bf16 elements): 144 B
+constexpr int EPI_LDS = 36;             // padded fp32 row of a parked 32-column slice
+
+// ---------------------------------------------------------------- epilogues
+// row4(r, c, v): v = C[r, c..c+3] (bias added), c % 4 == 0
+// col4(r, c, v): v = C[r..r+3, c] (bias added), r % 4 == 0
+// colmajor(n0, BN): true if the tile starting at column n0 wants col4
+
+struct EpiStoreF32 {
+  float* out; int ldo;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    *(f32x4*)(out + (size_t)r * ldo + c) = v;
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
+  uint2 u;
+  u.x = pack_bf16x2(a, b);
+  u.y = pack_bf16x2(c, d);
+  *(uint2*)p = u;
+}
+
+struct EpiSiluBf16 {
+  bf16_t* out; int ldo;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    store_bf16x4(out + (size_t)r * ldo + c, silu_f(v[0]), silu_f(v[1]), silu_f(v[2]), silu_f(v[3]));
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+struct EpiGeluBf16 {
+  bf16_t* out; int ldo; int col_off;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    store_bf16x4(out + (size_t)r * ldo + col_off + c, gelu_tanh_f(v[0]), gelu_tanh_f(v[1]),
+                 gelu_tanh_f(v[2]), gelu_tanh_f(v[3]));
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+// x[token] += gate[b] * v, x being the joint residual stream [B, L, D].
+template <class XT>
+struct EpiGatedResidual {
+  XT* x; int D; const float* gate; int gate_bstride; RowMap map;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    int b, t; map.token(r, b, t);
+    XT* p = x + ((size_t)b * map.L + t) * D + c;
+    const f32x4 g = *(const f32x4*)(gate + (size_t)b * gate_bstride + c);
+    if constexpr (sizeof(XT) == 4) {
+      f32x4 o = *(f32x4*)p;
+      *(f32x4*)p = o + g * v;
+    } else {
+      uint2 u = *(uint2*)p;
+      float o0 = __uint_as_float(u.x << 16), o1 = __uint_as_float(u.x & 0xffff0000u);
+      float o2 = __uint_as_float(u.y << 16), o3 = __uint_as_float(u.y & 0xffff0000u);
+      store_bf16x4((bf16_t*)p, o0 + g[0] * v[0], o1 + g[1] * v[1], o2 + g[2] * v[2],
+                   o3 + g[3] * v[3]);
+    }
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+// Split the fused projection into head-major Q, K (rotated) and V^T.
+struct EpiQKV {
+  bf16_t* q; bf16_t* k; bf16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
+  int D, H, d; RowMap map;
+  __device__ __forceinline__ bool colmajor(int n0, int bn) const {
+    return n0 >= 2 * D && n0 + bn <= 3 * D;
+  }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    const int which = c / D;
+    const int cc = c - which * D;
+    const int h = cc / d;
+    const int dd = cc - h * d;
+    int b, t; map.token(r, b, t);
+    const size_t bh = (size_t)b * H + h;
+    if (which < 2) {
+      // pairs (dd, dd+1) and (dd+2, dd+3): table entries p = dd/2 and dd/2 + 1
+      const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+      float o0 = v[0] * cs[0] - v[1] * cs[1];
+      float o1 = v[0] * cs[1] + v[1] * cs[0];
+      float o2 = v[2] * cs[2] - v[3] * cs[3];
+      float o3 = v[2] * cs[3] + v[3] * cs[2];
+      bf16_t* dst = which == 0 ? q : k;
+      store_bf16x4(dst + (bh * map.L + t) * d + dd, o0, o1, o2, o3);
+    } else {
+      bf16_t* dst = vt + (bh * d + dd) * map.L + t;
+      const size_t L = map.L;
+      dst[0] = f2bf(v[0]);
+      dst[L] = f2bf(v[1]);
+      dst[2 * L] = f2bf(v[2]);
+      dst[3 * L] = f2bf(v[3]);
+    }
+  }
+  // V columns, 4 consecutive rows (tokens t..t+3 of one batch row)
+  __device__ __forceinline__ void col4(int r, int c, f32x4 v) const {
+    const int cc = c - 2 * D;
+    const int h = cc / d;
+    const int dd = cc - h * d;
+    int b, t; map.token(r, b, t);
+    store_bf16x4(vt + (((size_t)b * H + h) * d + dd) * map.L + t, v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Single-stream linear1: columns [0, 3D) are Q/K/V, the rest the GELU MLP branch.
+struct EpiLinear1 {
+  EpiQKV qkv; EpiGeluBf16 gelu; int n_qkv;
+  __device__ __forceinline__ bool colmajor(int n0, int bn) const { return qkv.colmajor(n0, bn); }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    if (c < n_qkv) qkv.row4(r, c, v);
+    else gelu.row4(r, c - n_qkv, v);
+  }
+  __device__ __forceinline__ void col4(int r, int c, f32x4 v) const { qkv.col4(r, c, v); }
+};
+
+// ---------------------------------------------------------------- kernel
+
+template <class Epi>
+struct GemmParams {
+  GemmProblem g[2];
+  Epi e[2];
+  int ngroups;
+  int tiles[2];     // tiles per group
+  int tiles_n[2];   // n-tiles per group
+};
+
+template <int BM, int BN, int WM, int WN, class Epi>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi> p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM / 32;
+  constexpr int TN = BN / WN / 32;
+  constexpr int RPP = NT / 8;       // slab rows covered per pass (8 threads per 128-B row)
+  constexpr int AIT = BM / RPP;     // 16-byte loads per thread for the A slab
+  constexpr int BIT = BN / RPP;
+  constexpr int WROWS = BM / WM;    // rows of one wave's tile
+  static_assert(AIT * RPP == BM && BIT * RPP == BN, "tile / thread mismatch");
+  static_assert(WM * WN * WROWS * EPI_LDS * 4 <= 2 * (BM + BN) * GEMM_LDS * 2,
+                "epilogue slice does not fit in the operand LDS");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * GEMM_LDS];
+  bf16_t* sA = smem;                         // [2][BM * GEMM_LDS]
+  bf16_t* sB = smem + 2 * BM * GEMM_LDS;     // [2][BN * GEMM_LDS]
+
+  // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
+  // give each XCD a contiguous range of logical tiles so neighbours share L2.
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
+  int lid = xcd * xq + min(xcd, xr) + (bid >> 3);
+
+  const bool g1 = p.ngroups > 1 && lid >= p.tiles[0];
+  if (g1) lid -= p.tiles[0];
+  const GemmProblem g = g1 ? p.g[1] : p.g[0];
+  const int tiles_n = g1 ? p.tiles_n[1] : p.tiles_n[0];
+  const int tiles_m = (g.M + BM - 1) / BM;
+
+  // grouped raster: 8 m-tiles sweep the n-tiles together
+  constexpr int GROUP_M = 8;
+  const int in_group = GROUP_M * tiles_n;
+  const int gid = lid / in_group;
+  const int first_m = gid * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int tm_idx = first_m + (lid % in_group) % gsize;
+  const int tn_idx = (lid % in_group) / gsize;
+  const int m0 = tm_idx * BM;
+  const int n0 = tn_idx * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // global -> register staging: thread covers row (tid/8) + RPP*i, 16-byte chunk tid%8
+  const int lrow = tid >> 3;
+  const int lchk = (tid & 7) * 8;
+  const bf16_t* gA[AIT];
+  const bf16_t* gW[BIT];
+#pragma unroll
+  for (int i = 0; i < AIT; ++i) {
+    int m = min(m0 + lrow + RPP * i, g.M - 1);
+    gA[i] = g.A + (size_t)m * g.lda + lchk;
+  }
+#pragma unroll
+  for (int i = 0; i < BIT; ++i) {
+    int n = min(n0 + lrow + RPP * i, g.N - 1);
+    gW[i] = g.W + (size_t)n * g.ldw + lchk;
+  }
+  i32x4 ra[AIT], rb[BIT];
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = g.K / GEMM_BK;
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  const int wrow = wm * WROWS;
+  const int wcol = wn * (BN / WN);
+
+#define GEMM_GLOAD(kt)                                                           \
+  {                                                                              \
+    const int ko_ = (kt) * GEMM_BK;                                              \
+    _Pragma("unroll") for (int i = 0; i < AIT; ++i) ra[i] = *(const i32x4*)(gA[i] + ko_); \
+    _Pragma("unroll") for (int i = 0; i < BIT; ++i) rb[i] = *(const i32x4*)(gW[i] + ko_); \
+  }
+#define GEMM_SSTORE(s)                                                           \
+  {                                                                              \
+    bf16_t* a_ = sA + (s) * BM * GEMM_LDS;                                       \
+    bf16_t* b_ = sB + (s) * BN * GEMM_LDS;                                       \
+    _Pragma("unroll") for (int i = 0; i < AIT; ++i)                              \
+        *(i32x4*)&a_[(lrow + RPP * i) * GEMM_LDS + lchk] = ra[i];                \
+    _Pragma("unroll") for (int i = 0; i < BIT; ++i)                              \
+        *(i32x4*)&b_[(lrow + RPP * i) * GEMM_LDS + lchk] = rb[i];                \
+  }
+
+  GEMM_GLOAD(0);
+  GEMM_SSTORE(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) GEMM_GLOAD(kt + 1);
+    const bf16_t* a_s = sA + s * BM * GEMM_LDS;
+    const bf16_t* b_s = sB + s * BN * GEMM_LDS;
+#pragma unroll
+    for (int kk = 0; kk < GEMM_BK / 16; ++kk) {
+      bf16x8 af[TM], bw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *(const bf16x8*)&a_s[(wrow + i * 32 + frow) * GEMM_LDS + kk * 16 + fk];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bw[j] = *(const bf16x8*)&b_s[(wcol + j * 32 + frow) * GEMM_LDS + kk * 16 + fk];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) GEMM_SSTORE(s ^ 1);
+    __syncthreads();
+  }
+#undef GEMM_GLOAD
+#undef GEMM_SSTORE
+
+  // ---- epilogue (the loop above ended with a barrier: operand LDS is free)
+  const Epi epi = g1 ? p.e[1] : p.e[0];
+  float* slice = (float*)smem + wave * WROWS * EPI_LDS;
+  const bool cmaj = epi.colmajor(n0, BN);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    // accumulator element e of block (i, j): row i*32 + (e/4)*8 + (lane/32)*4 + e%4,
+    // column lane%32 of the slice
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        slice[(i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * EPI_LDS + (lane & 31)] =
+            acc[i][j][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cbase = n0 + wcol + j * 32;
+    if (!cmaj) {
+      // 8 lanes per row, 4 columns each
+#pragma unroll
+      for (int ps = 0; ps < WROWS / 8; ++ps) {
+        const int rl = ps * 8 + (lane >> 3);
+        const int cl = (lane & 7) * 4;
+        const int row = m0 + wrow + rl;
+        const int col = cbase + cl;
+        if (row < g.M && col < g.N) {
+          f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
+          if (g.bias) v += *(const f32x4*)(g.bias + col);
+          epi.row4(row, col, v);
+        }
+      }
+    } else {
+      // 32 row-quads x 2 columns per pass: lanes 0..31 write 32 consecutive quads
+#pragma unroll
+      for (int ps = 0; ps < WROWS / 4 * 32 / 64; ++ps) {
+        const int idx = ps * 64 + lane;
+        const int rq = idx % (WROWS / 4);
+        const int cl = idx / (WROWS / 4);
+        const int row = m0 + wrow + rq * 4;
+        const int col = cbase + cl;
+        if (row < g.M && col < g.N) {
+          f32x4 v;
+          v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
+          v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
+          v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
+          v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
+          if (g.bias) v += g.bias[col];
+          epi.col4(row, col, v);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int BM, int BN, int WM, int WN, class Epi>
+static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
+  GemmParams<Epi> p{};
+  int total = 0;
+  p.ngroups = ng;
+  for (int i = 0; i < ng; ++i) {
+    p.g[i] = gp[i];
+    p.e[i] = ep[i];
+    p.tiles_n[i] = (gp[i].N + BN - 1) / BN;
+    p.tiles[i] = ((gp[i].M + BM - 1) / BM) * p.tiles_n[i];
+    total += p.tiles[i];
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi>), dim3(total), dim3(WM * WN * 64), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
+template <class Epi>
+static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
+  int maxM = 0, minN = 1 << 30;
+  for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
+  if (maxM <= 64) return launch_cfg<32, 256, 1, 4>(gp, ep, ng, st);
+  if (maxM >= 1024 && minN >= 1024) return launch_cfg<256, 256, 2, 4>(gp, ep, ng, st);
+  return launch_cfg<128, 128, 2, 2>(gp, ep, ng, st);
+}
+
+hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
+  EpiStoreF32 e{out, ldo};
+  return launch(&g, &e, 1, st);
+}
+
+hipError_t gemm_silu_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st) {
+  EpiSiluBf16 e{out, ldo};
+  return launch(&g, &e, 1, st);
+}
+
+hipError_t gemm_gelu_bf16(const GemmProblem* g, int ng, bf16_t* const* out, const int* ldo,
+                          hipStream_t st) {
+  EpiGeluBf16 e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiGeluBf16{out[i], ldo[i], 0};
+  return launch(g, e, ng, st);
+}
+
+template <class XT>
+hipError_t gemm_gated_residual(const GemmProblem* g, int ng, XT* x, int D,
+                               const float* const* gate, int gate_bstride, const RowMap* map,
+                               hipStream_t st) {
+  EpiGatedResidual<XT> e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiGatedResidual<XT>{x, D, gate[i], gate_bstride, map[i]};
+  return launch(g, e, ng, st);
+}
+template hipError_t gemm_gated_residual<float>(const GemmProblem*, int, float*, int,
+                                               const float* const*, int, const RowMap*, hipStream_t);
+template hipError_t gemm_gated_residual<bf16_t>(const GemmProblem*, int, bf16_t*, int,
+                                                const float* const*, int, const RowMap*, hipStream_t);
+
+hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap* map,
+                    hipStream_t st) {
+  EpiQKV e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i]};
+  return launch(g, e, ng, st);
+}
+
+hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
+                        bf16_t* cat, int ldcat, hipStream_t st) {
+  EpiLinear1 e;
+  e.qkv = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map};
+  e.gelu = EpiGeluBf16{cat, ldcat, o.D};
+  e.n_qkv = 3 * o.D;
+  return launch(&g, &e, 1, st);
+}
+
+}  // namespace dit

@@ -1,0 +1,55 @@
+// Host-side launch interface of the HIP kernels (internal to libdit).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace dit {
+
+// One GEMM problem: C[M, N] = A[M, K] W[N, K]^T + bias.  bf16 operands, K % 64 == 0,
+// lda / ldw multiples of 8 elements, 16-byte aligned base pointers.
+struct GemmProblem {
+  const bf16_t* A; int lda;
+  const bf16_t* W; int ldw;
+  const float* bias;
+  int M, N, K;
+};
+
+// Destinations of the fused QKV epilogue.
+struct QKVOut {
+  bf16_t* q;          // [B, H, L, d]
+  bf16_t* k;          // [B, H, L, d]
+  bf16_t* vt;         // [B, H, d, L]
+  const float* rope;  // [L, d/2, 2] (cos, sin)
+  int D, H, d;
+};
+
+hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st);
+hipError_t gemm_silu_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
+hipError_t gemm_gelu_bf16(const GemmProblem* g, int ng, bf16_t* const* out, const int* ldo,
+                          hipStream_t st);
+template <class XT>
+hipError_t gemm_gated_residual(const GemmProblem* g, int ng, XT* x, int D,
+                               const float* const* gate, int gate_bstride, const RowMap* map,
+                               hipStream_t st);
+hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap* map,
+                    hipStream_t st);
+hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
+                        bf16_t* cat, int ldcat, hipStream_t st);
+
+// Flash attention, bf16: q, k [B, H, L, d], vt [B, H, d, L]; output token (b, t),
+// head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
+                          int ldo, const RowMap& map, int B, int H, int L, int d,
+                          float softmax_scale, hipStream_t st);
+
+// LayerNorm (eps 1e-6, no affine) + modulate: out[r] = LN(x[map(r)]) * (1 + scale) + shift.
+// Rows r < n_img take the image vectors, the rest the text vectors; per batch b
+// the vectors sit at mod + b * mod_bstride.
+template <class XT>
+hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& map,
+                       int n_img_rows, const float* shift_img, const float* scale_img,
+                       const float* shift_txt, const float* scale_txt, int mod_bstride,
+                       hipStream_t st);
+
+}  // namespace dit

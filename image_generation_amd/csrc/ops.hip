@@ -1,0 +1,390 @@
+// Bandwidth-bound kernels of the DiT denoise step (gfx950): adaLN LayerNorm-modulate,
+// embeddings, the First-Block-Cache relative-L1 reduction, cache commit/apply and
+// the Euler / CFG update.
+#include "common.h"
+#include "kernels.h"
+#include "ops.h"
+
+namespace dit {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------- LN + modulate
+// One wave per output row; the row (D <= 64 * 4 * LN_MAXCH) stays in registers
+// between the mean pass, the variance pass and the output pass.
+constexpr int LN_MAXCH = 12;
+
+template <class XT>
+__device__ __forceinline__ f32x4 load4(const XT* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) { return *(const f32x4*)p; }
+template <>
+__device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
+  uint2 u = *(const uint2*)p;
+  f32x4 v;
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xffff0000u);
+  return v;
+}
+
+template <class XT>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(
+    const XT* __restrict__ x, bf16_t* __restrict__ out, int rows, int D, RowMap map, int n_img,
+    const float* __restrict__ sh_i, const float* __restrict__ sc_i,
+    const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  int b, t;
+  map.token(r, b, t);
+  const XT* xr = x + ((size_t)b * map.L + t) * D;
+  const int nch = D >> 8;
+  f32x4 v[LN_MAXCH];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < LN_MAXCH; ++c) {
+    if (c < nch) {
+      v[c] = load4<XT>(xr + c * 256 + lane * 4);
+      s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
+    }
+  }
+  const float inv_d = 1.0f / (float)D;
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < LN_MAXCH; ++c) {
+    if (c < nch) {
+      v[c] -= mean;
+      q += (v[c][0] * v[c][0] + v[c][1] * v[c][1]) + (v[c][2] * v[c][2] + v[c][3] * v[c][3]);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + 1e-6f);
+  const bool img = r < n_img;
+  const float* sh = (img ? sh_i : sh_t) + (size_t)b * bstride;
+  const float* sc = (img ? sc_i : sc_t) + (size_t)b * bstride;
+  bf16_t* orow = out + (size_t)r * D;
+#pragma unroll
+  for (int c = 0; c < LN_MAXCH; ++c) {
+    if (c < nch) {
+      const int col = c * 256 + lane * 4;
+      const f32x4 a = *(const f32x4*)(sc + col);
+      const f32x4 z = *(const f32x4*)(sh + col);
+      const f32x4 y = v[c] * rstd * (1.0f + a) + z;
+      uint2 u;
+      u.x = pack_bf16x2(y[0], y[1]);
+      u.y = pack_bf16x2(y[2], y[3]);
+      *(uint2*)(orow + col) = u;
+    }
+  }
+}
+
+template <class XT>
+hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& map,
+                       int n_img_rows, const float* shift_img, const float* scale_img,
+                       const float* shift_txt, const float* scale_txt, int mod_bstride,
+                       hipStream_t st) {
+  if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(ln_modulate_kernel<XT>, dim3((rows + 3) / 4), dim3(256), 0, st, x, out, rows, D,
+                     map, n_img_rows, shift_img, scale_img, shift_txt, scale_txt, mod_bstride);
+  return hipGetLastError();
+}
+template hipError_t ln_modulate<float>(const float*, bf16_t*, int, int, const RowMap&, int,
+                                       const float*, const float*, const float*, const float*, int,
+                                       hipStream_t);
+template hipError_t ln_modulate<bf16_t>(const bf16_t*, bf16_t*, int, int, const RowMap&, int,
+                                        const float*, const float*, const float*, const float*, int,
+                                        hipStream_t);
+
+// ---------------------------------------------------------------- embeddings
+
+// Image tokens: x[b, Lt + i, :] = before[b, i, :] = lat[i] W_in^T + b_in for every
+// batch row b (a CFG pair shares its latents).  16 tokens x 256 columns per block.
+__global__ __launch_bounds__(256) void embed_latents_kernel(
+    const float* __restrict__ lat, const bf16_t* __restrict__ W, const float* __restrict__ bias,
+    float* __restrict__ x, float* __restrict__ before, int B, int Lt, int Li, int L, int D,
+    int Cin) {
+  __shared__ float sl[16][64];
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * 16;
+  const int n = blockIdx.y * 256 + tid;
+  for (int e = tid; e < 16 * Cin; e += 256) {
+    const int i = e / Cin, k = e - i * Cin;
+    sl[i][k] = (i0 + i < Li) ? lat[(size_t)(i0 + i) * Cin + k] : 0.f;
+  }
+  __syncthreads();
+  if (n >= D) return;
+  float w[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) w[k] = k < Cin ? bf2f(W[(size_t)n * Cin + k]) : 0.f;
+  const float bn = bias[n];
+  for (int i = 0; i < 16 && i0 + i < Li; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) acc = fmaf(sl[i][k], w[k], acc);
+    acc += bn;
+    for (int b = 0; b < B; ++b) {
+      x[((size_t)b * L + Lt + i0 + i) * D + n] = acc;
+      before[((size_t)b * Li + i0 + i) * D + n] = acc;
+    }
+  }
+}
+
+// Text tokens: x[b, t, :] = txt[b, t, :] (bf16 -> fp32 residual stream).
+__global__ __launch_bounds__(256) void text_to_stream_kernel(
+    const bf16_t* __restrict__ txt, float* __restrict__ x, int B, int Lt, int L, int D) {
+  const size_t n4 = (size_t)B * Lt * D / 4;
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
+    const size_t e = j * 4;
+    const size_t row = e / D;
+    const int c = (int)(e - row * D);
+    const int b = (int)(row / Lt), t = (int)(row - (size_t)b * Lt);
+    *(f32x4*)(x + ((size_t)b * L + t) * D + c) = load4<bf16_t>(txt + e);
+  }
+}
+
+// Sinusoidal timestep embedding of t = sigma_m, in fp64: [cos(1000 t w_k), sin(1000 t w_k)],
+// w_k = 10000^(-k/half); bf16 out [M, 2*half].  Sigmas travel in the kernel
+// arguments, up to SIG_CHUNK per launch.
+__global__ void sinusoid_kernel(SigChunk sig, bf16_t* __restrict__ e, int half) {
+  const int m = blockIdx.x;
+  for (int k = threadIdx.x; k < half; k += blockDim.x) {
+    const double w = exp(-log(10000.0) * (double)k / (double)half);
+    const double a = 1000.0 * sig.s[m] * w;
+    e[(size_t)m * 2 * half + k] = f2bf((float)cos(a));
+    e[(size_t)m * 2 * half + half + k] = f2bf((float)sin(a));
+  }
+}
+
+// 2-D RoPE table [L, d/2, 2] (cos, sin), fp64 angles: pair p < d/4 turns with the
+// patch row, p >= d/4 with the patch column, at 10000^(-j/(d/4)) per position.
+__global__ void rope_table_kernel(float* __restrict__ tab, int grid_w, int Lt, int L, int d,
+                                  double theta) {
+  const int t = blockIdx.x;
+  if (t >= L) return;
+  const int q = d / 4;
+  double row = 0.0, col = 0.0;
+  if (t >= Lt) {
+    row = (double)((t - Lt) / grid_w);
+    col = (double)((t - Lt) % grid_w);
+  }
+  for (int p = threadIdx.x; p < d / 2; p += blockDim.x) {
+    const int j = p % q;
+    const double f = exp(-log(theta) * (double)j / (double)q);
+    const double a = (p < q ? row : col) * f;
+    tab[((size_t)t * (d / 2) + p) * 2 + 0] = (float)cos(a);
+    tab[((size_t)t * (d / 2) + p) * 2 + 1] = (float)sin(a);
+  }
+}
+
+// ---------------------------------------------------------------- First-Block-Cache
+
+// Pass 1: r = x_img(after block 0) - x_img(before); staging = r; per-block sums of
+// |r - anchor| and |anchor| in fp64 (fixed assignment of elements to blocks).
+__global__ __launch_bounds__(256) void fbc_partial_kernel(
+    const float* __restrict__ x, const float* __restrict__ before,
+    const float* __restrict__ anchor, float* __restrict__ staging, double* __restrict__ part,
+    int B, int Lt, int Li, int L, int D, int has_anchor) {
+  const size_t n4 = (size_t)B * Li * D / 4;
+  float num = 0.f, den = 0.f;
+  double dnum = 0.0, dden = 0.0;
+  int cnt = 0;
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
+    const size_t e = j * 4;
+    const size_t row = e / D;
+    const int c = (int)(e - row * D);
+    const int b = (int)(row / Li), i = (int)(row - (size_t)b * Li);
+    const f32x4 xa = *(const f32x4*)(x + ((size_t)b * L + Lt + i) * D + c);
+    const f32x4 r = xa - *(const f32x4*)(before + e);
+    *(f32x4*)(staging + e) = r;
+    if (has_anchor) {
+      const f32x4 a = *(const f32x4*)(anchor + e);
+      num += (fabsf(r[0] - a[0]) + fabsf(r[1] - a[1])) + (fabsf(r[2] - a[2]) + fabsf(r[3] - a[3]));
+      den += (fabsf(a[0]) + fabsf(a[1])) + (fabsf(a[2]) + fabsf(a[3]));
+      if (++cnt == 16) {   // flush fp32 partials into fp64 every 64 elements
+        dnum += num; dden += den; num = 0.f; den = 0.f; cnt = 0;
+      }
+    }
+  }
+  dnum += num;
+  dden += den;
+  __shared__ double sn[256], sd[256];
+  sn[threadIdx.x] = dnum;
+  sd[threadIdx.x] = dden;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      sn[threadIdx.x] += sn[threadIdx.x + o];
+      sd[threadIdx.x] += sd[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = sn[0];
+    part[2 * blockIdx.x + 1] = sd[0];
+  }
+}
+
+// Pass 2 (one block): fixed-order fp64 sum of the partials and the decision
+// skip = has_anchor && rel < threshold (strict; NaN and a zero denominator never skip).
+__global__ __launch_bounds__(256) void fbc_final_kernel(const double* __restrict__ part, int nparts,
+                                                        int has_anchor, double threshold,
+                                                        FbcResult* __restrict__ res) {
+  __shared__ double sn[256], sd[256];
+  double a = 0.0, c = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    a += part[2 * i];
+    c += part[2 * i + 1];
+  }
+  sn[threadIdx.x] = a;
+  sd[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      sn[threadIdx.x] += sn[threadIdx.x + o];
+      sd[threadIdx.x] += sd[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double num = sn[0], den = sd[0];
+    double rel;
+    int nonfinite = 0;
+    if (!has_anchor) {
+      rel = INFINITY;
+    } else {
+      nonfinite = !(isfinite(num) && isfinite(den));
+      rel = den > 0.0 ? num / den : (num == num ? INFINITY : NAN);
+    }
+    res->rel = rel;
+    res->skip = (has_anchor && !nonfinite && rel < threshold) ? 1 : 0;
+    res->nonfinite = nonfinite;
+  }
+}
+
+// After a fully computed step: cached = (x_final - before) - r, anchor = r.
+__global__ __launch_bounds__(256) void fbc_commit_kernel(
+    const float* __restrict__ x, const float* __restrict__ before,
+    const float* __restrict__ staging, float* __restrict__ cached, float* __restrict__ anchor,
+    int B, int Lt, int Li, int L, int D) {
+  const size_t n4 = (size_t)B * Li * D / 4;
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
+    const size_t e = j * 4;
+    const size_t row = e / D;
+    const int c = (int)(e - row * D);
+    const int b = (int)(row / Li), i = (int)(row - (size_t)b * Li);
+    const f32x4 xf = *(const f32x4*)(x + ((size_t)b * L + Lt + i) * D + c);
+    const f32x4 r = *(const f32x4*)(staging + e);
+    *(f32x4*)(cached + e) = (xf - *(const f32x4*)(before + e)) - r;
+    *(f32x4*)(anchor + e) = r;
+  }
+}
+
+// Skipped step: x_img += cached.
+__global__ __launch_bounds__(256) void fbc_apply_kernel(float* __restrict__ x,
+                                                        const float* __restrict__ cached, int B,
+                                                        int Lt, int Li, int L, int D) {
+  const size_t n4 = (size_t)B * Li * D / 4;
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
+    const size_t e = j * 4;
+    const size_t row = e / D;
+    const int c = (int)(e - row * D);
+    const int b = (int)(row / Li), i = (int)(row - (size_t)b * Li);
+    f32x4* p = (f32x4*)(x + ((size_t)b * L + Lt + i) * D + c);
+    *p = *p + *(const f32x4*)(cached + e);
+  }
+}
+
+// ---------------------------------------------------------------- Euler + CFG
+// lat += dt * v, with v = v_neg + g (v_pos - v_neg) for a CFG pair (pos = batch row 0).
+__global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ lat,
+                                                    const float* __restrict__ v, int n, int cfg,
+                                                    float g, float dt) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) {
+    float vv = v[j];
+    if (cfg) {
+      const float vn = v[n + j];
+      vv = vn + g * (vv - vn);
+    }
+    lat[j] += dt * vv;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static int grid_for(size_t n4) {
+  size_t g = (n4 + 255) / 256;
+  return (int)(g < 2048 ? (g == 0 ? 1 : g) : 2048);
+}
+
+hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, float* x,
+                         float* before, int B, int Lt, int Li, int D, int Cin, hipStream_t st) {
+  if (Cin > 64) return hipErrorInvalidValue;
+  dim3 grid((Li + 15) / 16, (D + 255) / 256);
+  hipLaunchKernelGGL(embed_latents_kernel, grid, dim3(256), 0, st, lat, W, bias, x, before, B, Lt,
+                     Li, Lt + Li, D, Cin);
+  return hipGetLastError();
+}
+
+hipError_t text_to_stream(const bf16_t* txt, float* x, int B, int Lt, int L, int D,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(text_to_stream_kernel, dim3(grid_for((size_t)B * Lt * D / 4)), dim3(256), 0,
+                     st, txt, x, B, Lt, L, D);
+  return hipGetLastError();
+}
+
+hipError_t sinusoid_host(const double* sig_host, bf16_t* e, int M, int half, hipStream_t st) {
+  for (int m0 = 0; m0 < M; m0 += SIG_CHUNK) {
+    SigChunk c;
+    const int n = M - m0 < SIG_CHUNK ? M - m0 : SIG_CHUNK;
+    for (int i = 0; i < SIG_CHUNK; ++i) c.s[i] = i < n ? sig_host[m0 + i] : 0.0;
+    hipLaunchKernelGGL(sinusoid_kernel, dim3(n), dim3(128), 0, st, c, e + (size_t)m0 * 2 * half,
+                       half);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t rope_table(float* tab, int grid_w, int Lt, int L, int d, double theta, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(L), dim3(64), 0, st, tab, grid_w, Lt, L, d, theta);
+  return hipGetLastError();
+}
+
+hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, float* staging,
+                      double* part, int nparts, FbcResult* res, int B, int Lt, int Li, int D,
+                      int has_anchor, double threshold, hipStream_t st) {
+  hipLaunchKernelGGL(fbc_partial_kernel, dim3(nparts), dim3(256), 0, st, x, before, anchor, staging,
+                     part, B, Lt, Li, Lt + Li, D, has_anchor);
+  hipLaunchKernelGGL(fbc_final_kernel, dim3(1), dim3(256), 0, st, part, nparts, has_anchor,
+                     threshold, res);
+  return hipGetLastError();
+}
+
+hipError_t fbc_commit(const float* x, const float* before, const float* staging, float* cached,
+                      float* anchor, int B, int Lt, int Li, int D, hipStream_t st) {
+  hipLaunchKernelGGL(fbc_commit_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
+                     x, before, staging, cached, anchor, B, Lt, Li, Lt + Li, D);
+  return hipGetLastError();
+}
+
+hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D, hipStream_t st) {
+  hipLaunchKernelGGL(fbc_apply_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
+                     x, cached, B, Lt, Li, Lt + Li, D);
+  return hipGetLastError();
+}
+
+hipError_t euler_update(float* lat, const float* v, int n, int cfg, float g, float dt,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(euler_kernel, dim3(grid_for((size_t)n / 4 + 1)), dim3(256), 0, st, lat, v, n,
+                     cfg, g, dt);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,330 @@
+"""ctypes binding of libdit (include/dit.h): argument marshalling only.
+
+Every function here checks shapes and dtypes of torch tensors, turns them into
+pointers and calls the C entry point of the same name.  All arithmetic runs in
+the HIP kernels of libdit.so; importing this module fails if the library is
+missing (build it with ``python -m image_generation_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, Structure, c_double, c_float, c_int, c_long, c_size_t, c_void_p
+from typing import List, Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit.so")
+
+DIT_OK = 0
+DIT_ERR_INVALID_ARG = -1
+DIT_ERR_UNSUPPORTED = -2
+DIT_ERR_WORKSPACE = -3
+DIT_ERR_HIP = -4
+DIT_ERR_NONFINITE = -5
+
+DIT_F32, DIT_BF16, DIT_FP8 = 0, 1, 2
+DIT_BLOCK_DOUBLE, DIT_BLOCK_SINGLE = 0, 1
+DIT_WS_ATTENTION, DIT_WS_BLOCK, DIT_WS_STEP, DIT_WS_MODULATION, DIT_WS_FBCACHE = range(5)
+
+
+class DitDims(Structure):
+    _fields_ = [("B", c_int), ("Lt", c_int), ("grid_h", c_int), ("grid_w", c_int),
+                ("D", c_int), ("H", c_int), ("F", c_int)]
+
+
+class DitLinear(Structure):
+    _fields_ = [("w", c_void_p), ("b", c_void_p)]
+
+
+class DitBlock(Structure):
+    _fields_ = [("kind", c_int), ("qkv", DitLinear * 2), ("proj", DitLinear * 2),
+                ("mlp1", DitLinear * 2), ("mlp2", DitLinear * 2),
+                ("lin1", DitLinear), ("lin2", DitLinear)]
+
+
+class DitModel(Structure):
+    _fields_ = [("dims", DitDims), ("n_double", c_int), ("n_single", c_int),
+                ("blocks", POINTER(DitBlock)), ("time1", DitLinear), ("time2", DitLinear),
+                ("img_in", DitLinear), ("final_out", DitLinear), ("mod", DitLinear),
+                ("C_in", c_int), ("guidance", c_float)]
+
+
+class DitFBCache(Structure):
+    _fields_ = [("enabled", c_int), ("threshold", c_float), ("has_anchor", c_int),
+                ("anchor", c_void_p), ("cached", c_void_p)]
+
+
+class DitStepInfo(Structure):
+    _fields_ = [("rel", c_double), ("skipped", c_int)]
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libdit status {status}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m image_generation_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = c_void_p
+    sig = {
+        "dit_status_string": (ctypes.c_char_p, [c_int]),
+        "dit_last_error": (ctypes.c_char_p, []),
+        "dit_workspace_bytes": (c_size_t, [POINTER(DitDims), c_int, c_int]),
+        "dit_sigmas": (c_int, [c_int, c_double, POINTER(c_double)]),
+        "dit_rope_table": (c_int, [c_int, c_int, c_int, c_int, c_double, P, P]),
+        "dit_attention": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_float, P]),
+        "dit_block_forward": (c_int, [POINTER(DitDims), POINTER(DitBlock), c_int, P, c_int, P,
+                                      c_long, P, P, c_size_t, P]),
+        "dit_modulation": (c_int, [POINTER(DitModel), POINTER(c_double), c_int, P, P, c_size_t, P]),
+        "fbcache_should_skip": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_float, c_int,
+                                        P, c_size_t, P, POINTER(c_double), POINTER(c_int)]),
+        "dit_denoise_step": (c_int, [POINTER(DitModel), P, P, P, c_double, c_double,
+                                     POINTER(DitFBCache), P, c_size_t, P, POINTER(DitStepInfo)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
+            "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
+            "fbcache_should_skip", "dit_denoise_step")
+
+
+def _check(rc: int) -> None:
+    if rc != DIT_OK:
+        raise DitError(rc, LIB.dit_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdit must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, shape: Sequence[int], name: str) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda:
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def dims_of(B: int, Lt: int, grid_h: int, grid_w: int, D: int, H: int, F: int) -> DitDims:
+    return DitDims(B, Lt, grid_h, grid_w, D, H, F)
+
+
+# ------------------------------------------------------------------ helpers
+
+def dit_workspace_bytes(dims: DitDims, purpose: int, n_steps: int = 0) -> int:
+    return int(LIB.dit_workspace_bytes(ctypes.byref(dims), purpose, n_steps))
+
+
+def workspace(dims: DitDims, purpose: int, n_steps: int = 0, device="cuda") -> torch.Tensor:
+    n = dit_workspace_bytes(dims, purpose, n_steps)
+    if n == 0 and purpose != DIT_WS_ATTENTION:
+        raise DitError(DIT_ERR_INVALID_ARG, "invalid dims for the workspace query")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def dit_sigmas(n_steps: int, shift: float) -> List[float]:
+    out = (c_double * (n_steps + 1))()
+    _check(LIB.dit_sigmas(n_steps, float(shift), out))
+    return list(out)
+
+
+def dit_rope_table(grid_h: int, grid_w: int, Lt: int, head_dim: int, theta: float = 10000.0,
+                   device="cuda", stream=None) -> torch.Tensor:
+    tab = torch.empty((Lt + grid_h * grid_w, head_dim // 2, 2), dtype=torch.float32, device=device)
+    _check(LIB.dit_rope_table(grid_h, grid_w, Lt, head_dim, float(theta), _ptr(tab),
+                              _stream(stream)))
+    return tab
+
+
+# ------------------------------------------------------------------ entry points
+
+def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.Tensor,
+                  softmax_scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """q, k [B, H, L, d] bf16; vt [B, H, d, L] bf16; o [B, L, H*d] bf16 (written)."""
+    B, H, L, d = q.shape
+    _need(q, torch.bfloat16, (B, H, L, d), "q")
+    _need(k, torch.bfloat16, (B, H, L, d), "k")
+    _need(vt, torch.bfloat16, (B, H, d, L), "vt")
+    _need(o, torch.bfloat16, (B, L, H * d), "o")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), B, H, L, d, DIT_BF16,
+                             float(softmax_scale), _stream(stream)))
+    return o
+
+
+def _lin(w: torch.Tensor, b: torch.Tensor) -> DitLinear:
+    if w.dtype != torch.bfloat16 or b.dtype != torch.float32 or not (w.is_cuda and b.is_cuda):
+        raise ValueError("linear: weight bf16 and bias fp32 on the GPU")
+    return DitLinear(_ptr(w), _ptr(b))
+
+
+def make_double_block(p: dict, prefix: str = "") -> DitBlock:
+    """p: '<prefix>img.qkv.w' ... device tensors (weights bf16, biases fp32)."""
+    blk = DitBlock()
+    blk.kind = DIT_BLOCK_DOUBLE
+    for i, s in enumerate(("img", "txt")):
+        blk.qkv[i] = _lin(p[f"{prefix}{s}.qkv.w"], p[f"{prefix}{s}.qkv.b"])
+        blk.proj[i] = _lin(p[f"{prefix}{s}.proj.w"], p[f"{prefix}{s}.proj.b"])
+        blk.mlp1[i] = _lin(p[f"{prefix}{s}.mlp1.w"], p[f"{prefix}{s}.mlp1.b"])
+        blk.mlp2[i] = _lin(p[f"{prefix}{s}.mlp2.w"], p[f"{prefix}{s}.mlp2.b"])
+    return blk
+
+
+def make_single_block(p: dict, prefix: str = "") -> DitBlock:
+    blk = DitBlock()
+    blk.kind = DIT_BLOCK_SINGLE
+    blk.lin1 = _lin(p[f"{prefix}lin1.w"], p[f"{prefix}lin1.b"])
+    blk.lin2 = _lin(p[f"{prefix}lin2.w"], p[f"{prefix}lin2.b"])
+    return blk
+
+
+def dit_block_forward(dims: DitDims, blk: DitBlock, x: torch.Tensor, mod: torch.Tensor,
+                      rope: torch.Tensor, ws: torch.Tensor, mod_bstride: Optional[int] = None,
+                      stream=None) -> torch.Tensor:
+    """x [B, L, D] (fp32 or bf16) updated in place; mod [B or 1, k, D] fp32."""
+    L = dims.Lt + dims.grid_h * dims.grid_w
+    if tuple(x.shape) != (dims.B, L, dims.D) or x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x: expected fp32/bf16 {(dims.B, L, dims.D)}, got {x.dtype} {tuple(x.shape)}")
+    nk = 12 if blk.kind == DIT_BLOCK_DOUBLE else 3
+    if mod.dtype != torch.float32 or mod.shape[-2:] != (nk, dims.D) or mod.shape[0] not in (1, dims.B):
+        raise ValueError(f"mod: expected fp32 [B or 1, {nk}, {dims.D}]")
+    if mod_bstride is None:
+        mod_bstride = 0 if mod.shape[0] == 1 else nk * dims.D
+    xd = DIT_F32 if x.dtype == torch.float32 else DIT_BF16
+    _check(LIB.dit_block_forward(ctypes.byref(dims), ctypes.byref(blk), DIT_BF16, _ptr(x), xd,
+                                 _ptr(mod), int(mod_bstride), _ptr(rope), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+    return x
+
+
+def fbcache_should_skip(x_after: torch.Tensor, x_before: torch.Tensor,
+                        anchor: Optional[torch.Tensor], staging: torch.Tensor, Lt: int,
+                        threshold: float, has_anchor: bool, ws: torch.Tensor, stream=None):
+    """x_after [B, Lt+Li, D] fp32; x_before, anchor, staging [B, Li, D] fp32.  -> (rel, skip)."""
+    B, Li, D = x_before.shape
+    _need(x_after, torch.float32, (B, Lt + Li, D), "x_after")
+    _need(x_before, torch.float32, (B, Li, D), "x_before")
+    _need(staging, torch.float32, (B, Li, D), "staging")
+    if anchor is not None:
+        _need(anchor, torch.float32, (B, Li, D), "anchor")
+    rel = c_double()
+    skip = c_int()
+    _check(LIB.fbcache_should_skip(_ptr(x_after), _ptr(x_before), _ptr(anchor), _ptr(staging),
+                                   B, Lt, Li, D, float(threshold), int(bool(has_anchor)), _ptr(ws),
+                                   ws.numel(), _stream(stream), ctypes.byref(rel),
+                                   ctypes.byref(skip)))
+    return rel.value, bool(skip.value)
+
+
+class GPUModel:
+    """Device copy of a whole model plus the ctypes struct that points into it.
+
+    params: name -> tensor in the enumeration of ``dit_inputs.param_specs``
+    (weights bf16, biases any float dtype; moved to the GPU here).
+    """
+
+    def __init__(self, dims, B: int, Lt: int, grid_h: int, grid_w: int, params: dict,
+                 guidance: float = 0.0, device="cuda"):
+        self.dims_py = dims
+        D = dims.D
+        self.n_double, self.n_single = dims.n_double, dims.n_single
+        self.t = {}
+        for name, t in params.items():
+            if name.endswith(".b"):
+                self.t[name] = t.to(device=device, dtype=torch.float32).contiguous()
+            elif name.endswith(".mod.w"):
+                continue
+            else:
+                self.t[name] = t.to(device=device, dtype=torch.bfloat16).contiguous()
+        # stacked modulation weights in the order the library expects
+        order = []
+        for j in range(self.n_double):
+            order += [f"double{j}.img.mod", f"double{j}.txt.mod"]
+        order += [f"single{j}.mod" for j in range(self.n_single)]
+        order += ["final.mod"]
+        self.mod_w = torch.cat([params[n + ".w"].to(device=device, dtype=torch.bfloat16)
+                                for n in order]).contiguous()
+        self.mod_b = torch.cat([self.t[n + ".b"] for n in order]).contiguous()
+        self.n_mod = self.mod_w.shape[0]
+        assert self.n_mod == (12 * self.n_double + 3 * self.n_single + 2) * D
+        blocks = [make_double_block(self.t, f"double{j}.") for j in range(self.n_double)]
+        blocks += [make_single_block(self.t, f"single{j}.") for j in range(self.n_single)]
+        self._blocks = (DitBlock * max(1, len(blocks)))(*blocks)
+        m = DitModel()
+        m.dims = dims_of(B, Lt, grid_h, grid_w, D, dims.H, dims.F)
+        m.n_double, m.n_single = self.n_double, self.n_single
+        m.blocks = ctypes.cast(self._blocks, POINTER(DitBlock))
+        m.time1 = _lin(self.t["time.w1"], self.t["time.b1"])
+        m.time2 = _lin(self.t["time.w2"], self.t["time.b2"])
+        m.img_in = _lin(self.t["img_in.w"], self.t["img_in.b"])
+        m.final_out = _lin(self.t["final.out.w"], self.t["final.out.b"])
+        m.mod = _lin(self.mod_w, self.mod_b)
+        m.C_in = dims.C_in
+        m.guidance = float(guidance)
+        self.model = m
+
+
+def dit_modulation(gm: GPUModel, sigmas: Sequence[float], out: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    n = len(sigmas)
+    if out is None:
+        out = torch.empty((n, gm.n_mod), dtype=torch.float32, device="cuda")
+    _need(out, torch.float32, (n, gm.n_mod), "out")
+    if ws is None:
+        ws = workspace(gm.model.dims, DIT_WS_MODULATION, n)
+    sig = (c_double * n)(*[float(s) for s in sigmas])
+    _check(LIB.dit_modulation(ctypes.byref(gm.model), sig, n, _ptr(out), _ptr(ws), ws.numel(),
+                              _stream(stream)))
+    return out
+
+
+class FBCache:
+    """Caller-held First-Block-Cache state (device buffers + the ctypes struct)."""
+
+    def __init__(self, B: int, Li: int, D: int, threshold: float, enabled: bool = True,
+                 device="cuda"):
+        self.anchor = torch.zeros((B, Li, D), dtype=torch.float32, device=device)
+        self.cached = torch.zeros((B, Li, D), dtype=torch.float32, device=device)
+        self.c = DitFBCache(int(enabled), float(threshold), 0, _ptr(self.anchor), _ptr(self.cached))
+
+    @property
+    def has_anchor(self) -> bool:
+        return bool(self.c.has_anchor)
+
+
+def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,
+                     latents: torch.Tensor, sigma: float, sigma_next: float,
+                     cache: Optional[FBCache], ws: torch.Tensor, stream=None):
+    """One Euler step in place on latents [Li, C_in] fp32.  -> (rel, skipped)."""
+    dm = gm.model.dims
+    Li = dm.grid_h * dm.grid_w
+    _need(mod_step, torch.float32, (gm.n_mod,), "mod_step")
+    _need(txt, torch.bfloat16, (dm.B, dm.Lt, dm.D), "txt")
+    _need(latents, torch.float32, (Li, gm.model.C_in), "latents")
+    info = DitStepInfo()
+    cp = ctypes.byref(cache.c) if cache is not None else None
+    _check(LIB.dit_denoise_step(ctypes.byref(gm.model), _ptr(mod_step), _ptr(txt), _ptr(latents),
+                                float(sigma), float(sigma_next), cp, _ptr(ws), ws.numel(),
+                                _stream(stream), ctypes.byref(info)))
+    return info.rel, bool(info.skipped)

@@ -1,0 +1,230 @@
+/*
+ * dit.h - C ABI of libdit, the MI355X (gfx950) DiT denoise-step library.
+ *
+ * What it computes.  One flow-matching Euler step of a FLUX-shaped diffusion
+ * transformer over joint text + image tokens: adaLN-modulated LayerNorm, fused
+ * QKV projection with 2-D RoPE, joint softmax attention, output projection and
+ * GELU-tanh MLP with gated residuals, repeated over double-stream and
+ * single-stream blocks; then the velocity head and the Euler (and CFG) update.
+ * The First-Block-Cache test decides, after the first block, whether the
+ * remaining blocks are skipped and their cached residual reused.
+ *
+ * Sources.  The step is the one the pages on image-generation speed keep
+ * returning to: the denoising stage dominates the pipeline and attention plus
+ * matrix products dominate it (devotd.net VisualGen article on FLUX Klein,
+ * stage-latency table and the section on why the speed-ups differ); the
+ * First-Block-Cache test is the unsloth studio diffusion.py commit "Add opt-in
+ * step caching (First-Block-Cache)"; RoPE as its own step and the scheduler /
+ * flow shift / solver triple come from the vflash "Optimization ledger" page
+ * (table "Accepted or exposed"; section "Fewer steps require a new contract");
+ * fp8 W8A8 with dynamic scales from the runinfra.ai image-gen runbook,
+ * "Optimization stack" table.  The pages give no formulas: the exact
+ * definitions implemented here are the readings listed in the design notes
+ * shipped with the library (LN eps 1e-6 without affine, (1 + scale) modulation,
+ * interleaved-pair 2-D RoPE with base 10000, tanh GELU, shifted sigmas
+ * s*t / (1 + (s-1) t), rel-L1 = sum|r - a| / sum|a| with a strict "<").
+ *
+ * Conventions (every entry point).
+ *   - The caller owns all memory.  Pointers named "device" are HIP device
+ *     pointers (e.g. torch tensor data_ptr()), 16-byte aligned, contiguous,
+ *     row-major.  The library allocates nothing and keeps no state between
+ *     calls; scratch comes from a caller workspace sized by
+ *     dit_workspace_bytes().
+ *   - stream: a hipStream_t (NULL = default stream).  Work is enqueued
+ *     asynchronously; only fbcache_should_skip() and dit_denoise_step() with an
+ *     enabled cache synchronise that stream, to hand the skip decision to the
+ *     host.
+ *   - Return value: DIT_OK (0) or a negative DIT_ERR_* code.  All arguments are
+ *     validated before anything is enqueued; on an error nothing has been
+ *     launched (except DIT_ERR_HIP, raised by the runtime mid-way, and
+ *     DIT_ERR_NONFINITE, raised after the cache test ran).  Nothing throws or
+ *     aborts across the ABI.  dit_last_error() gives a message for the calling
+ *     thread's last failure.
+ *   - Weights follow torch.nn.Linear: W is [out, in], y = x W^T + b, with the
+ *     bias always fp32 [out].
+ *   - Runs only on gfx950; any other device gives DIT_ERR_UNSUPPORTED.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols (the library is built with hidden default visibility). */
+#define DIT_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ status */
+#define DIT_OK 0
+#define DIT_ERR_INVALID_ARG (-1)  /* bad pointer, shape, alignment or value        */
+#define DIT_ERR_UNSUPPORTED (-2)  /* dtype / shape / device this build does not run */
+#define DIT_ERR_WORKSPACE (-3)    /* workspace smaller than dit_workspace_bytes()   */
+#define DIT_ERR_HIP (-4)          /* the HIP runtime reported an error              */
+#define DIT_ERR_NONFINITE (-5)    /* NaN / Inf reached the First-Block-Cache test   */
+
+/* ------------------------------------------------------------------ dtypes */
+#define DIT_F32 0
+#define DIT_BF16 1
+#define DIT_FP8 2   /* OCP e4m3 ("e4m3fn") */
+
+#define DIT_BLOCK_DOUBLE 0
+#define DIT_BLOCK_SINGLE 1
+
+/* Workspace purposes for dit_workspace_bytes(). */
+#define DIT_WS_ATTENTION 0
+#define DIT_WS_BLOCK 1
+#define DIT_WS_STEP 2
+#define DIT_WS_MODULATION 3
+#define DIT_WS_FBCACHE 4
+
+/* Token layout of one denoise problem.
+ *   B       batch rows (1, or 2 for a CFG pair: row 0 positive, row 1 negative)
+ *   Lt      text tokens (multiple of 8)
+ *   grid_h, grid_w  patch grid; Li = grid_h * grid_w image tokens (multiple of 8)
+ *   D, H, F hidden size, heads (head dim D / H must be 128), MLP hidden size
+ * Joint token order is [text ; image]: token t < Lt is text, token Lt + i is
+ * image patch (i / grid_w, i % grid_w). */
+typedef struct dit_dims {
+  int B, Lt, grid_h, grid_w, D, H, F;
+} dit_dims;
+
+/* One linear layer on the device: w [out, in] (bf16), b fp32 [out]. */
+typedef struct dit_linear {
+  const void* w;
+  const float* b;
+} dit_linear;
+
+/* A transformer block.
+ * Double-stream (kind DIT_BLOCK_DOUBLE): index 0 = image stream, 1 = text stream;
+ *   qkv [3D, D] (rows: q then k then v, head-major inside each), proj [D, D],
+ *   mlp1 [F, D], mlp2 [D, F].
+ * Single-stream (kind DIT_BLOCK_SINGLE): lin1 [3D + F, D] (q, k, v, MLP-in),
+ *   lin2 [D, D + F] (input: [attention out, GELU(MLP-in)]). */
+typedef struct dit_block {
+  int kind;
+  dit_linear qkv[2], proj[2], mlp1[2], mlp2[2];
+  dit_linear lin1, lin2;
+} dit_block;
+
+/* The whole model.  blocks: host array of n_double double blocks followed by
+ * n_single single blocks.  mod: every modulation linear stacked row-wise into
+ * one [N_mod, D] matrix, N_mod = (12 n_double + 3 n_single + 2) D, in the order
+ * double block j image (shift1, scale1, gate1, shift2, scale2, gate2) then text
+ * (same six), single block j (shift, scale, gate), final layer (shift, scale). */
+typedef struct dit_model {
+  dit_dims dims;
+  int n_double, n_single;
+  const dit_block* blocks;
+  dit_linear time1;      /* [D, 256] */
+  dit_linear time2;      /* [D, D]   */
+  dit_linear img_in;     /* [D, C_in] */
+  dit_linear final_out;  /* [C_in, D] */
+  dit_linear mod;        /* [N_mod, D] */
+  int C_in;              /* patch features, <= 64 */
+  float guidance;        /* CFG scale (B == 2) */
+} dit_model;
+
+/* Caller-held First-Block-Cache state; resuming a loop = passing it back. */
+typedef struct dit_fbcache {
+  int enabled;       /* 0: no test, every block runs, state untouched           */
+  float threshold;   /* skip iff rel < threshold (0: never skip; +inf: always   */
+                     /* after the first full step)                              */
+  int has_anchor;    /* in/out: 0 until a fully computed step stored an anchor  */
+  float* anchor;     /* device fp32 [B, Li, D]: first block's residual at the   */
+                     /* last fully computed step                                */
+  float* cached;     /* device fp32 [B, Li, D]: image hidden after the last     */
+                     /* block minus image hidden after block 0, same step       */
+} dit_fbcache;
+
+typedef struct dit_step_info {
+  double rel;        /* relative L1 change of the first block's residual        */
+                     /* (+inf when there is no anchor or the cache is disabled) */
+  int skipped;       /* 1 if blocks 1.. were skipped                             */
+} dit_step_info;
+
+/* ------------------------------------------------------------------ helpers */
+
+/* Static message for a status code. */
+DIT_API const char* dit_status_string(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+DIT_API const char* dit_last_error(void);
+
+/* Bytes of device workspace an entry point needs.  purpose: DIT_WS_*;
+ * n_steps is used by DIT_WS_MODULATION only.  Returns 0 for invalid dims. */
+DIT_API size_t dit_workspace_bytes(const dit_dims* dims, int purpose, int n_steps);
+
+/* Shifted flow-matching sigmas (host, fp64): tau_i = 1 - i/n,
+ * out[i] = shift tau_i / (1 + (shift - 1) tau_i), i = 0..n (n + 1 values). */
+DIT_API int dit_sigmas(int n_steps, double shift, double* out_host);
+
+/* 2-D RoPE table, device fp32 [Lt + Li, d/2, 2] = (cos, sin) of the angle of
+ * pair p at token t: pairs p < d/4 turn with the patch row, p >= d/4 with the
+ * patch column, pair j of an axis at theta^(-j/(d/4)) radians per position;
+ * text tokens sit at (0, 0). */
+DIT_API int dit_rope_table(int grid_h, int grid_w, int Lt, int head_dim, double theta, float* table,
+                   void* stream);
+
+/* ------------------------------------------------------------------ entry points */
+
+/* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V.
+ *   q, k: device bf16 [B, H, L, 128]; vt: device bf16 [B, H, 128, L] (V
+ *   transposed per head); o: device bf16 [B, L, H * 128] (token-major).
+ *   L % 8 == 0, L >= 8; dtype must be DIT_BF16.  Workspace: none. */
+DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
+                  int head_dim, int dtype, float softmax_scale, void* stream);
+
+/* One transformer block, in place on the joint residual stream.
+ *   x: device [B, Lt + Li, D], dtype x_dtype (DIT_F32 or DIT_BF16), updated.
+ *   mod: device fp32 modulation vectors for batch row b at mod + b * mod_bstride
+ *        (mod_bstride = 0 shares them): double block 12 D-vectors (image
+ *        shift1, scale1, gate1, shift2, scale2, gate2, then text), single 3.
+ *   rope: device table from dit_rope_table() for these dims.
+ *   dtype: compute dtype, DIT_BF16.  workspace >= DIT_WS_BLOCK bytes. */
+DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
+                      const float* mod, long mod_bstride, const float* rope, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Modulation vectors of the whole model for n sigmas at once:
+ *   out[i] = mod.W SiLU(c_i) + mod.b,  c_i = time2(SiLU(time1(emb(sigma_i)))),
+ *   emb(t) = [cos(1000 t w_k), sin(1000 t w_k)], w_k = 10000^(-k/128), k < 128.
+ *   sigmas_host: n fp64 values; out: device fp32 [n, N_mod].
+ *   workspace >= DIT_WS_MODULATION bytes (for n). */
+DIT_API int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* First-Block-Cache test.
+ *   x_after: device fp32 joint stream [B, Lt + Li, D] after the first block
+ *            (Lt may be 0 for a plain image tensor);
+ *   x_before: device fp32 [B, Li, D], image hidden before the first block;
+ *   anchor: device fp32 [B, Li, D] (ignored when has_anchor == 0);
+ *   staging: device fp32 [B, Li, D], receives r = x_after(image) - x_before.
+ *   rel = sum|r - anchor| / sum|anchor| (fp64, fixed-order reduction: the same
+ *   inputs always give the same rel); skip = has_anchor && rel < threshold,
+ *   with a NaN rel or a zero denominator never skipping.  Synchronises the
+ *   stream and writes rel_out / skip_out on the host.  Returns
+ *   DIT_ERR_NONFINITE (with skip 0) if a NaN or Inf reached the sums.
+ *   workspace >= DIT_WS_FBCACHE bytes. */
+DIT_API int fbcache_should_skip(const float* x_after, const float* x_before, const float* anchor,
+                        float* staging, int B, int Lt, int Li, int D, float threshold,
+                        int has_anchor, void* workspace, size_t ws_bytes, void* stream,
+                        double* rel_out, int* skip_out);
+
+/* One Euler step of the whole model:
+ *   latents <- latents + (sigma_next - sigma) v,  v the velocity of the model at
+ *   t = sigma (CFG pair: v = v_neg + guidance (v_pos - v_neg)).
+ *   mod_step: device fp32 [N_mod], this sigma's row of dit_modulation().
+ *   txt: device bf16 [B, Lt, D]; latents: device fp32 [Li, C_in], in place
+ *   (shared by a CFG pair).  cache: NULL or a dit_fbcache (state updated).
+ *   info_out: optional host pointer.  workspace >= DIT_WS_STEP bytes. */
+DIT_API int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt, float* latents,
+                     double sigma, double sigma_next, dit_fbcache* cache, void* workspace,
+                     size_t ws_bytes, void* stream, dit_step_info* info_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

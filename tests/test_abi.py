@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad arguments before touching a device.  CPU only: no compute calls."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit.h")
+LIBPATH = os.path.join(ROOT, "image_generation_amd", "libdit.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"DIT_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIBPATH):
+        pytest.fail("libdit.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIBPATH)
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("dit_attention", "dit_block_forward", "fbcache_should_skip", "dit_denoise_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_declared_symbol():
+    from image_generation_amd import dit
+    assert sorted(dit.EXPORTED) == _declared()
+
+
+def test_status_strings(lib):
+    lib.dit_status_string.restype = ctypes.c_char_p
+    for code, text in ((0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"),
+                       (-5, b"non-finite value in the cache test")):
+        assert lib.dit_status_string(code) == text
+
+
+def test_sigmas_host_helper_matches_closed_form():
+    from image_generation_amd import dit
+    assert dit.dit_sigmas(4, 3.0) == [1.0, 0.9, 0.75, 0.5, 0.0]
+    with pytest.raises(dit.DitError) as e:
+        dit.dit_sigmas(0, 3.0)
+    assert e.value.status == dit.DIT_ERR_INVALID_ARG
+
+
+def test_workspace_query():
+    from image_generation_amd import dit
+    d = dit.dims_of(1, 512, 64, 64, 3072, 24, 12288)
+    blk = dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK)
+    step = dit.dit_workspace_bytes(d, dit.DIT_WS_STEP)
+    L = 4608
+    assert blk >= 2 * L * 3072 * 4 + 2 * L * (3072 + 12288)
+    assert step > blk
+    assert dit.dit_workspace_bytes(dit.dims_of(0, 0, 1, 1, 1, 1, 1), dit.DIT_WS_BLOCK) == 0
+
+
+def test_invalid_arguments_rejected_before_launch():
+    from image_generation_amd import dit
+    L = dit.LIB
+    P = ctypes.c_void_p
+    # NULL pointers
+    rc = L.dit_attention(None, None, None, None, 1, 1, 64, 128, dit.DIT_BF16, 0.1, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # ragged L (not a multiple of 8) with fake aligned pointers: rejected before any launch
+    fake = P(4096)
+    rc = L.dit_attention(fake, fake, fake, fake, 1, 1, 63, 128, dit.DIT_BF16, 0.1, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_attention(fake, fake, fake, fake, 1, 1, 64, 128, dit.DIT_BF16, math.nan, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # misaligned pointer
+    rc = L.dit_attention(P(4098), fake, fake, fake, 1, 1, 64, 128, dit.DIT_BF16, 0.1, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # fbcache: NaN threshold, short workspace
+    rel, skip = ctypes.c_double(), ctypes.c_int()
+    rc = L.fbcache_should_skip(fake, fake, fake, fake, 1, 0, 8, 64, math.nan, 1, fake, 1 << 20,
+                               None, ctypes.byref(rel), ctypes.byref(skip))
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.fbcache_should_skip(fake, fake, fake, fake, 1, 0, 8, 64, 0.1, 1, fake, 16,
+                               None, ctypes.byref(rel), ctypes.byref(skip))
+    assert rc == dit.DIT_ERR_WORKSPACE
+    # block: unknown kind
+    d = dit.dims_of(1, 8, 2, 4, 256, 2, 512)
+    blk = dit.DitBlock()
+    blk.kind = 7
+    rc = L.dit_block_forward(ctypes.byref(d), ctypes.byref(blk), dit.DIT_BF16, fake, dit.DIT_F32,
+                             fake, 0, fake, fake, 1 << 30, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # token counts that are not multiples of 8
+    d = dit.dims_of(1, 7, 2, 4, 256, 2, 512)
+    assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
