@@ -231,6 +231,7 @@ hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf
   const int nblk = B * H * nqt;
   if (nblk == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  KTimerScope timer(KS_ATTENTION, st);
   hipLaunchKernelGGL(attention_bf16_kernel, dim3(nblk), dim3(256), 0, st, q, k, vt, o, ldo, map,
                      H, L, scale_log2);
   return hipGetLastError();

@@ -20,6 +20,7 @@ using namespace dit;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local dit_kernel_timer* g_timer = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -269,6 +270,21 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
 
 }  // namespace
 
+namespace dit {
+void ktimer_start(int site, hipStream_t st) {
+  dit_kernel_timer* t = g_timer;
+  if (!t || !((t->site_mask >> site) & 1u) || t->count >= t->capacity) return;
+  t->sites[t->count] = site;
+  (void)hipEventRecord((hipEvent_t)t->start[t->count], st);
+}
+void ktimer_stop(int site, hipStream_t st) {
+  dit_kernel_timer* t = g_timer;
+  if (!t || !((t->site_mask >> site) & 1u) || t->count >= t->capacity) return;
+  (void)hipEventRecord((hipEvent_t)t->stop[t->count], st);
+  ++t->count;
+}
+}  // namespace dit
+
 // ====================================================================== C ABI
 
 extern "C" {
@@ -286,6 +302,14 @@ const char* dit_status_string(int status) {
 }
 
 const char* dit_last_error(void) { return g_last_error.c_str(); }
+
+int dit_set_kernel_timer(dit_kernel_timer* timer) {
+  if (timer && (timer->capacity < 0 || timer->count < 0 ||
+                (timer->capacity > 0 && (!timer->sites || !timer->start || !timer->stop))))
+    return fail(DIT_ERR_INVALID_ARG, "dit_set_kernel_timer: bad timer");
+  g_timer = timer;
+  return DIT_OK;
+}
 
 size_t dit_workspace_bytes(const dit_dims* dims, int purpose, int n_steps) {
   Dims dm;

@@ -351,7 +351,8 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
 }
 
 template <class Epi>
-static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
+static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st, int site) {
+  KTimerScope timer(site, st);
   int maxM = 0, minN = 1 << 30;
   for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
   if (maxM <= 64) return launch_cfg<32, 256, 1, 4>(gp, ep, ng, st);
@@ -361,19 +362,19 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
   EpiStoreF32 e{out, ldo};
-  return launch(&g, &e, 1, st);
+  return launch(&g, &e, 1, st, KS_GEMM_F32);
 }
 
 hipError_t gemm_silu_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st) {
   EpiSiluBf16 e{out, ldo};
-  return launch(&g, &e, 1, st);
+  return launch(&g, &e, 1, st, KS_GEMM_SILU);
 }
 
 hipError_t gemm_gelu_bf16(const GemmProblem* g, int ng, bf16_t* const* out, const int* ldo,
                           hipStream_t st) {
   EpiGeluBf16 e[2];
   for (int i = 0; i < ng; ++i) e[i] = EpiGeluBf16{out[i], ldo[i], 0};
-  return launch(g, e, ng, st);
+  return launch(g, e, ng, st, KS_GEMM_GELU);
 }
 
 template <class XT>
@@ -382,7 +383,7 @@ hipError_t gemm_gated_residual(const GemmProblem* g, int ng, XT* x, int D,
                                hipStream_t st) {
   EpiGatedResidual<XT> e[2];
   for (int i = 0; i < ng; ++i) e[i] = EpiGatedResidual<XT>{x, D, gate[i], gate_bstride, map[i]};
-  return launch(g, e, ng, st);
+  return launch(g, e, ng, st, KS_GEMM_RESID);
 }
 template hipError_t gemm_gated_residual<float>(const GemmProblem*, int, float*, int,
                                                const float* const*, int, const RowMap*, hipStream_t);
@@ -393,7 +394,7 @@ hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap*
                     hipStream_t st) {
   EpiQKV e[2];
   for (int i = 0; i < ng; ++i) e[i] = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i]};
-  return launch(g, e, ng, st);
+  return launch(g, e, ng, st, KS_GEMM_QKV);
 }
 
 hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
@@ -402,7 +403,7 @@ hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map
   e.qkv = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map};
   e.gelu = EpiGeluBf16{cat, ldcat, o.D};
   e.n_qkv = 3 * o.D;
-  return launch(&g, &e, 1, st);
+  return launch(&g, &e, 1, st, KS_GEMM_LIN1);
 }
 
 }  // namespace dit

@@ -6,6 +6,20 @@
 
 namespace dit {
 
+// Launch sites, numbered as the DIT_SITE_* constants of the public header.
+enum KSite {
+  KS_ATTENTION = 0, KS_GEMM_QKV, KS_GEMM_RESID, KS_GEMM_GELU, KS_GEMM_LIN1, KS_GEMM_F32,
+  KS_GEMM_SILU, KS_LN, KS_FBC, KS_OTHER
+};
+// Bracket a launch with the calling thread's installed event timer (no-op if none).
+void ktimer_start(int site, hipStream_t st);
+void ktimer_stop(int site, hipStream_t st);
+struct KTimerScope {
+  int site; hipStream_t st;
+  KTimerScope(int s, hipStream_t t) : site(s), st(t) { ktimer_start(site, st); }
+  ~KTimerScope() { ktimer_stop(site, st); }
+};
+
 // One GEMM problem: C[M, N] = A[M, K] W[N, K]^T + bias.  bf16 operands, K % 64 == 0,
 // lda / ldw multiples of 8 elements, 16-byte aligned base pointers.
 struct GemmProblem {

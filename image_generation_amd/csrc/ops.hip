@@ -91,6 +91,7 @@ hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& 
                        hipStream_t st) {
   if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
+  KTimerScope timer(KS_LN, st);
   hipLaunchKernelGGL(ln_modulate_kernel<XT>, dim3((rows + 3) / 4), dim3(256), 0, st, x, out, rows, D,
                      map, n_img_rows, shift_img, scale_img, shift_txt, scale_txt, mod_bstride);
   return hipGetLastError();
@@ -325,6 +326,7 @@ static int grid_for(size_t n4) {
 
 hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, float* x,
                          float* before, int B, int Lt, int Li, int D, int Cin, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   if (Cin > 64) return hipErrorInvalidValue;
   dim3 grid((Li + 15) / 16, (D + 255) / 256);
   hipLaunchKernelGGL(embed_latents_kernel, grid, dim3(256), 0, st, lat, W, bias, x, before, B, Lt,
@@ -334,6 +336,7 @@ hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, f
 
 hipError_t text_to_stream(const bf16_t* txt, float* x, int B, int Lt, int L, int D,
                           hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(text_to_stream_kernel, dim3(grid_for((size_t)B * Lt * D / 4)), dim3(256), 0,
                      st, txt, x, B, Lt, L, D);
   return hipGetLastError();
@@ -353,6 +356,7 @@ hipError_t sinusoid_host(const double* sig_host, bf16_t* e, int M, int half, hip
 }
 
 hipError_t rope_table(float* tab, int grid_w, int Lt, int L, int d, double theta, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(rope_table_kernel, dim3(L), dim3(64), 0, st, tab, grid_w, Lt, L, d, theta);
   return hipGetLastError();
 }
@@ -360,6 +364,7 @@ hipError_t rope_table(float* tab, int grid_w, int Lt, int L, int d, double theta
 hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, float* staging,
                       double* part, int nparts, FbcResult* res, int B, int Lt, int Li, int D,
                       int has_anchor, double threshold, hipStream_t st) {
+  KTimerScope timer(KS_FBC, st);
   hipLaunchKernelGGL(fbc_partial_kernel, dim3(nparts), dim3(256), 0, st, x, before, anchor, staging,
                      part, B, Lt, Li, Lt + Li, D, has_anchor);
   hipLaunchKernelGGL(fbc_final_kernel, dim3(1), dim3(256), 0, st, part, nparts, has_anchor,
@@ -369,12 +374,14 @@ hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, 
 
 hipError_t fbc_commit(const float* x, const float* before, const float* staging, float* cached,
                       float* anchor, int B, int Lt, int Li, int D, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(fbc_commit_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
                      x, before, staging, cached, anchor, B, Lt, Li, Lt + Li, D);
   return hipGetLastError();
 }
 
 hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(fbc_apply_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
                      x, cached, B, Lt, Li, Lt + Li, D);
   return hipGetLastError();
@@ -382,6 +389,7 @@ hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D
 
 hipError_t euler_update(float* lat, const float* v, int n, int cfg, float g, float dt,
                         hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(euler_kernel, dim3(grid_for((size_t)n / 4 + 1)), dim3(256), 0, st, lat, v, n,
                      cfg, g, dt);
   return hipGetLastError();

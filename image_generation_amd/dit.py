@@ -60,6 +60,16 @@ class DitStepInfo(Structure):
     _fields_ = [("rel", c_double), ("skipped", c_int)]
 
 
+class DitKernelTimer(Structure):
+    _fields_ = [("site_mask", ctypes.c_uint), ("capacity", c_int), ("count", c_int),
+                ("sites", POINTER(c_int)), ("start", POINTER(c_void_p)),
+                ("stop", POINTER(c_void_p))]
+
+
+SITES = ("attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1", "gemm_f32",
+         "gemm_silu", "ln", "fbc", "other")
+
+
 class DitError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"libdit status {status}: {msg}")
@@ -86,6 +96,7 @@ def _load() -> ctypes.CDLL:
                                         P, c_size_t, P, POINTER(c_double), POINTER(c_int)]),
         "dit_denoise_step": (c_int, [POINTER(DitModel), P, P, P, c_double, c_double,
                                      POINTER(DitFBCache), P, c_size_t, P, POINTER(DitStepInfo)]),
+        "dit_set_kernel_timer": (c_int, [POINTER(DitKernelTimer)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -97,7 +108,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
             "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
-            "fbcache_should_skip", "dit_denoise_step")
+            "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer")
 
 
 def _check(rc: int) -> None:
@@ -251,7 +262,7 @@ class GPUModel:
         self.n_double, self.n_single = dims.n_double, dims.n_single
         self.t = {}
         for name, t in params.items():
-            if name.endswith(".b"):
+            if name.rsplit(".", 1)[-1].startswith("b"):      # b, b1, b2: biases
                 self.t[name] = t.to(device=device, dtype=torch.float32).contiguous()
             elif name.endswith(".mod.w"):
                 continue
@@ -328,3 +339,58 @@ def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,
                                 float(sigma), float(sigma_next), cp, _ptr(ws), ws.numel(),
                                 _stream(stream), ctypes.byref(info)))
     return info.rel, bool(info.skipped)
+
+
+# ------------------------------------------------------------------ launch timing
+
+class KernelTimer:
+    """HIP events recorded by libdit around launches of the selected sites.
+
+    Events are created through the HIP runtime (libamdhip64) directly, so they
+    bracket the kernels on whatever stream the library launches them on.
+    """
+
+    def __init__(self, sites: Sequence[str], capacity: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [POINTER(c_float), c_void_p, c_void_p]
+        self.hip.hipEventDestroy.argtypes = [c_void_p]
+        self.capacity = capacity
+        self.start = (c_void_p * capacity)()
+        self.stop = (c_void_p * capacity)()
+        self.sites = (c_int * capacity)()
+        for i in range(capacity):
+            for arr in (self.start, self.stop):
+                ev = c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise DitError(DIT_ERR_HIP, "hipEventCreate failed")
+                arr[i] = ev
+        mask = 0
+        for s_ in sites:
+            mask |= 1 << SITES.index(s_)
+        self.t = DitKernelTimer(mask, capacity, 0, self.sites,
+                                ctypes.cast(self.start, POINTER(c_void_p)),
+                                ctypes.cast(self.stop, POINTER(c_void_p)))
+
+    def __enter__(self):
+        self.t.count = 0
+        _check(LIB.dit_set_kernel_timer(ctypes.byref(self.t)))
+        return self
+
+    def __exit__(self, *exc):
+        _check(LIB.dit_set_kernel_timer(None))
+
+    def durations_ms(self):
+        """[(site name, ms)] of the recorded launches (call after synchronising)."""
+        out = []
+        for i in range(self.t.count):
+            ms = c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+                raise DitError(DIT_ERR_HIP, "hipEventElapsedTime failed")
+            out.append((SITES[self.sites[i]], ms.value))
+        return out
+
+    def close(self):
+        for i in range(self.capacity):
+            self.hip.hipEventDestroy(self.start[i])
+            self.hip.hipEventDestroy(self.stop[i])

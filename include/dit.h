@@ -167,6 +167,32 @@ DIT_API int dit_sigmas(int n_steps, double shift, double* out_host);
 DIT_API int dit_rope_table(int grid_h, int grid_w, int Lt, int head_dim, double theta, float* table,
                    void* stream);
 
+/* Opt-in launch timing for benchmarks.  While a timer is installed on the
+ * calling thread, every kernel the library launches from a site whose bit is
+ * set in site_mask is bracketed by hipEventRecord(start[i]) / (stop[i]) on the
+ * launch stream, and sites[i] receives the site id, i = count++ (nothing is
+ * recorded once count == capacity).  The caller creates the hipEvent_t
+ * handles and reads the times after synchronising; NULL uninstalls. */
+#define DIT_SITE_ATTENTION 0    /* flash attention                              */
+#define DIT_SITE_GEMM_QKV 1     /* QKV projection + RoPE epilogue (double)      */
+#define DIT_SITE_GEMM_RESID 2   /* proj / mlp2 / lin2 + gated residual          */
+#define DIT_SITE_GEMM_GELU 3    /* mlp1 + GELU (double)                         */
+#define DIT_SITE_GEMM_LIN1 4    /* single-block linear1: QKV + RoPE | GELU      */
+#define DIT_SITE_GEMM_F32 5     /* plain fp32-out GEMM (modulation, final)      */
+#define DIT_SITE_GEMM_SILU 6    /* timestep MLP                                 */
+#define DIT_SITE_LN 7           /* LayerNorm + modulate                         */
+#define DIT_SITE_FBC 8          /* First-Block-Cache reduction                  */
+#define DIT_SITE_OTHER 9        /* embeddings, cache apply/commit, Euler, RoPE  */
+typedef struct dit_kernel_timer {
+  unsigned site_mask;
+  int capacity;
+  int count;
+  int* sites;        /* host [capacity] */
+  void** start;      /* host [capacity] of hipEvent_t */
+  void** stop;       /* host [capacity] of hipEvent_t */
+} dit_kernel_timer;
+DIT_API int dit_set_kernel_timer(dit_kernel_timer* timer);
+
 /* ------------------------------------------------------------------ entry points */
 
 /* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V.

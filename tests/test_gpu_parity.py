@@ -15,10 +15,17 @@ import torch
 import dit_inputs as DI
 import oracle as O
 from _helpers import parity_err
+from oracle.numerics import round_bf16
 
 pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 2e-2
+# Branch-only check (x_out - x_in with an fp32 residual stream): the branch passes
+# through about six bf16 roundings (LN out, Q/K/V, P, O, LN2 out, MLP hidden),
+# each of relative RMS <= 2^-9/sqrt(3) ~ 1.1e-3 and independent, so the branch
+# error has relative RMS ~ sqrt(6) * 1.1e-3 ~ 2.8e-3 and its maximum over ~10^6
+# elements sits near 5 sigma ~ 1.4e-2 .. 3e-2.  Twice that is the bound.
+TOL_BRANCH = 6e-2
 
 
 @pytest.fixture(scope="module")
@@ -153,13 +160,17 @@ def test_block_forward_small(dit, D, H, F, B, Lt, gh, gw, kind, xdt):
     torch.cuda.synchronize()
     ref = _oracle_block(params, inp, w, dims, kind)
     got = x.double().cpu().numpy()
+    if xdt == torch.bfloat16:
+        # a bf16-stored result cannot be closer than its own rounding (half an ulp
+        # of |x| ~ 5 is 1.6e-2 of the RMS): compare with the rounded exact result
+        ref = round_bf16(ref)
     err = parity_err(got, ref)
     _say(f"  x_out err {err:.3e}")
     assert err <= TOL_BF16
     if xdt == torch.float32:
         derr = parity_err(got - x_in.double().cpu().numpy(), ref - O.to64(inp["x"]))
-        _say(f"  delta err {derr:.3e}")
-        assert derr <= TOL_BF16
+        _say(f"  branch err {derr:.3e}")
+        assert derr <= TOL_BRANCH
 
 
 def test_block_forward_flux_1024(dit):
@@ -172,7 +183,7 @@ def test_block_forward_flux_1024(dit):
     torch.cuda.synchronize()
     got = x.double().cpu().numpy()
     del dev, ws
-    ref = _oracle_block(params, inp, w, dims, "double")
+    ref = round_bf16(_oracle_block(params, inp, w, dims, "double"))
     err = parity_err(got, ref)
     _say(f"  err {err:.3e}")
     assert err <= TOL_BF16
