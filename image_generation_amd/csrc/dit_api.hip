@@ -107,6 +107,7 @@ struct Carver {
 };
 
 struct BlockWS {
+  float* xf;    // fp32 residual stream for a bf16-stored x [B, L, D]
   bf16_t* u;    // LN-modulate output [B*L, D] (row order of the block)
   bf16_t* q;    // [B, H, L, d]
   bf16_t* k;    // [B, H, L, d]
@@ -114,9 +115,10 @@ struct BlockWS {
   bf16_t* cat;  // [B*L, D + F]: attention output | MLP hidden
 };
 
-BlockWS carve_block(Carver& c, const Dims& dm) {
+BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   const size_t n = (size_t)dm.B * dm.L * dm.D;
   BlockWS w;
+  w.xf = with_xf ? c.take<float>(n) : nullptr;
   w.u = c.take<bf16_t>(n);
   w.q = c.take<bf16_t>(n);
   w.k = c.take<bf16_t>(n);
@@ -138,7 +140,7 @@ struct StepWS {
 
 StepWS carve_step(Carver& c, const Dims& dm) {
   StepWS w;
-  w.blk = carve_block(c, dm);
+  w.blk = carve_block(c, dm, false);
   w.x = c.take<float>((size_t)dm.B * dm.L * dm.D);
   w.before = c.take<float>((size_t)dm.B * dm.Li * dm.D);
   w.staging = c.take<float>((size_t)dm.B * dm.Li * dm.D);
@@ -167,7 +169,7 @@ size_t ws_size(const Dims& dm, int purpose, int n) {
   Carver c{nullptr, 0};
   switch (purpose) {
     case DIT_WS_ATTENTION: return 0;
-    case DIT_WS_BLOCK: carve_block(c, dm); break;
+    case DIT_WS_BLOCK: carve_block(c, dm, true); break;
     case DIT_WS_STEP: carve_step(c, dm); break;
     case DIT_WS_MODULATION: carve_mod(c, dm, n); break;
     case DIT_WS_FBCACHE:
@@ -384,12 +386,17 @@ int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, voi
     return fail(DIT_ERR_WORKSPACE, "dit_block_forward: workspace %zu < %zu bytes", ws_bytes, need);
   if ((rc = check_device())) return rc;
   Carver c{(char*)workspace, 0};
-  const BlockWS w = carve_block(c, dm);
+  const BlockWS w = carve_block(c, dm, true);
   hipStream_t st = (hipStream_t)stream;
-  if (x_dtype == DIT_F32)
+  if (x_dtype == DIT_F32) {
     DIT_CHECK_HIP(block_impl<float>(dm, *blk, (float*)x, mod, (int)mod_bstride, rope, w, st));
-  else
-    DIT_CHECK_HIP(block_impl<bf16_t>(dm, *blk, (bf16_t*)x, mod, (int)mod_bstride, rope, w, st));
+  } else {
+    // a bf16 residual stream is carried in fp32 through the block and rounded once
+    const size_t n = (size_t)dm.B * dm.L * dm.D;
+    DIT_CHECK_HIP(widen_bf16((const bf16_t*)x, w.xf, n, st));
+    DIT_CHECK_HIP(block_impl<float>(dm, *blk, w.xf, mod, (int)mod_bstride, rope, w, st));
+    DIT_CHECK_HIP(narrow_f32(w.xf, (bf16_t*)x, n, st));
+  }
   return DIT_OK;
 }
 

@@ -387,8 +387,6 @@ hipError_t gemm_gated_residual(const GemmProblem* g, int ng, XT* x, int D,
 }
 template hipError_t gemm_gated_residual<float>(const GemmProblem*, int, float*, int,
                                                const float* const*, int, const RowMap*, hipStream_t);
-template hipError_t gemm_gated_residual<bf16_t>(const GemmProblem*, int, bf16_t*, int,
-                                                const float* const*, int, const RowMap*, hipStream_t);
 
 hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap* map,
                     hipStream_t st) {

@@ -29,6 +29,9 @@ hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, 
 hipError_t fbc_commit(const float* x, const float* before, const float* staging, float* cached,
                       float* anchor, int B, int Lt, int Li, int D, hipStream_t st);
 hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D, hipStream_t st);
+// x (n elements, n % 4 == 0) between bf16 and fp32
+hipError_t widen_bf16(const bf16_t* a, float* b, size_t n, hipStream_t st);
+hipError_t narrow_f32(const float* a, bf16_t* b, size_t n, hipStream_t st);
 hipError_t euler_update(float* lat, const float* v, int n, int cfg, float g, float dt,
                         hipStream_t st);
 

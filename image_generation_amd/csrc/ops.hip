@@ -99,9 +99,6 @@ hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& 
 template hipError_t ln_modulate<float>(const float*, bf16_t*, int, int, const RowMap&, int,
                                        const float*, const float*, const float*, const float*, int,
                                        hipStream_t);
-template hipError_t ln_modulate<bf16_t>(const bf16_t*, bf16_t*, int, int, const RowMap&, int,
-                                        const float*, const float*, const float*, const float*, int,
-                                        hipStream_t);
 
 // ---------------------------------------------------------------- embeddings
 
@@ -317,11 +314,41 @@ __global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ lat,
   }
 }
 
+// ---------------------------------------------------------------- dtype moves
+__global__ __launch_bounds__(256) void bf16_to_f32_kernel(const bf16_t* __restrict__ a,
+                                                          float* __restrict__ b, size_t n4) {
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256)
+    *(f32x4*)(b + 4 * j) = load4<bf16_t>(a + 4 * j);
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ a,
+                                                          bf16_t* __restrict__ b, size_t n4) {
+  for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
+    const f32x4 v = *(const f32x4*)(a + 4 * j);
+    uint2 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    *(uint2*)(b + 4 * j) = u;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int grid_for(size_t n4) {
   size_t g = (n4 + 255) / 256;
   return (int)(g < 2048 ? (g == 0 ? 1 : g) : 2048);
+}
+
+hipError_t widen_bf16(const bf16_t* a, float* b, size_t n, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3(grid_for(n / 4)), dim3(256), 0, st, a, b, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t narrow_f32(const float* a, bf16_t* b, size_t n, hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(n / 4)), dim3(256), 0, st, a, b, n / 4);
+  return hipGetLastError();
 }
 
 hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, float* x,

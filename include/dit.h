@@ -203,7 +203,9 @@ DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
                   int head_dim, int dtype, float softmax_scale, void* stream);
 
 /* One transformer block, in place on the joint residual stream.
- *   x: device [B, Lt + Li, D], dtype x_dtype (DIT_F32 or DIT_BF16), updated.
+ *   x: device [B, Lt + Li, D], dtype x_dtype (DIT_F32 or DIT_BF16), updated;
+ *      a bf16 x is carried in fp32 through both residual updates and rounded
+ *      once at the end.
  *   mod: device fp32 modulation vectors for batch row b at mod + b * mod_bstride
  *        (mod_bstride = 0 shares them): double block 12 D-vectors (image
  *        shift1, scale1, gate1, shift2, scale2, gate2, then text), single 3.
