@@ -25,6 +25,17 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, h);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// Round-to-nearest-even fp32 -> fp16 bits.
+__device__ __forceinline__ uint16_t f2h(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+}
+
 // Two floats -> two packed bf16 (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);

@@ -111,7 +111,7 @@ struct BlockWS {
   bf16_t* u;    // LN-modulate output [B*L, D] (row order of the block)
   bf16_t* q;    // [B, H, L, d]
   bf16_t* k;    // [B, H, L, d]
-  bf16_t* vt;   // [B, H, d, L]
+  uint16_t* vt; // [B, H, d, L] fp16
   bf16_t* cat;  // [B*L, D + F]: attention output | MLP hidden
 };
 
@@ -122,7 +122,7 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.u = c.take<bf16_t>(n);
   w.q = c.take<bf16_t>(n);
   w.k = c.take<bf16_t>(n);
-  w.vt = c.take<bf16_t>(n);
+  w.vt = c.take<uint16_t>(n);
   w.cat = c.take<bf16_t>((size_t)dm.B * dm.L * (dm.D + dm.F));
   return w;
 }
@@ -342,6 +342,28 @@ int dit_rope_table(int grid_h, int grid_w, int Lt, int head_dim, double theta, f
   return DIT_OK;
 }
 
+int dit_linear_forward(const void* x, int M, int K, const dit_linear* lin, int N, void* y, int y_dtype,
+               void* stream) {
+  if (!x || !lin || !y) return fail(DIT_ERR_INVALID_ARG, "dit_linear_forward: NULL pointer");
+  int rc;
+  if ((rc = check_linear(*lin, "dit_linear_forward"))) return rc;
+  if (!aligned16(x) || !aligned16(y))
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_forward: pointers must be 16-byte aligned");
+  if (M < 1 || K < 64 || K % 64 || N < 4 || N % 4)
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_forward: M >= 1, K a multiple of 64, N a multiple of 4");
+  if ((long long)M * N > (1LL << 40) || (long long)M * K > (1LL << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "dit_linear_forward: problem too large");
+  if (y_dtype != DIT_F32 && y_dtype != DIT_BF16)
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_forward: y_dtype %d", y_dtype);
+  if ((rc = check_device())) return rc;
+  const GemmProblem g = gp((const bf16_t*)x, K, *lin, K, M, N);
+  if (y_dtype == DIT_F32)
+    DIT_CHECK_HIP(gemm_store_f32(g, (float*)y, N, (hipStream_t)stream));
+  else
+    DIT_CHECK_HIP(gemm_store_bf16(g, (bf16_t*)y, N, (hipStream_t)stream));
+  return DIT_OK;
+}
+
 int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
                   int head_dim, int dtype, float softmax_scale, void* stream) {
   if (!q || !k || !vt || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
@@ -358,7 +380,7 @@ int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, 
   int rc = check_device();
   if (rc) return rc;
   const RowMap jm{B, 0, L, L, 0, 0};
-  DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
+  DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const uint16_t*)vt, (bf16_t*)o,
                                H * head_dim, jm, B, H, L, head_dim, softmax_scale,
                                (hipStream_t)stream));
   return DIT_OK;

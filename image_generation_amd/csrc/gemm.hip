@@ -43,6 +43,15 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float 
   *(uint2*)p = u;
 }
 
+struct EpiStoreBf16 {
+  bf16_t* out; int ldo;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    store_bf16x4(out + (size_t)r * ldo + c, v[0], v[1], v[2], v[3]);
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
 struct EpiSiluBf16 {
   bf16_t* out; int ldo;
   __device__ __forceinline__ bool colmajor(int, int) const { return false; }
@@ -85,9 +94,9 @@ struct EpiGatedResidual {
   __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
-// Split the fused projection into head-major Q, K (rotated) and V^T.
+// Split the fused projection into head-major Q, K (bf16, rotated) and V^T (fp16).
 struct EpiQKV {
-  bf16_t* q; bf16_t* k; bf16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
+  bf16_t* q; bf16_t* k; uint16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
   int D, H, d; RowMap map;
   __device__ __forceinline__ bool colmajor(int n0, int bn) const {
     return n0 >= 2 * D && n0 + bn <= 3 * D;
@@ -109,21 +118,24 @@ struct EpiQKV {
       bf16_t* dst = which == 0 ? q : k;
       store_bf16x4(dst + (bh * map.L + t) * d + dd, o0, o1, o2, o3);
     } else {
-      bf16_t* dst = vt + (bh * d + dd) * map.L + t;
+      uint16_t* dst = vt + (bh * d + dd) * map.L + t;
       const size_t L = map.L;
-      dst[0] = f2bf(v[0]);
-      dst[L] = f2bf(v[1]);
-      dst[2 * L] = f2bf(v[2]);
-      dst[3 * L] = f2bf(v[3]);
+      dst[0] = f2h(v[0]);
+      dst[L] = f2h(v[1]);
+      dst[2 * L] = f2h(v[2]);
+      dst[3 * L] = f2h(v[3]);
     }
   }
-  // V columns, 4 consecutive rows (tokens t..t+3 of one batch row)
+  // V columns, 4 consecutive rows (tokens t..t+3 of one batch row), fp16
   __device__ __forceinline__ void col4(int r, int c, f32x4 v) const {
     const int cc = c - 2 * D;
     const int h = cc / d;
     const int dd = cc - h * d;
     int b, t; map.token(r, b, t);
-    store_bf16x4(vt + (((size_t)b * H + h) * d + dd) * map.L + t, v[0], v[1], v[2], v[3]);
+    uint2 u;
+    u.x = pack_f16x2(v[0], v[1]);
+    u.y = pack_f16x2(v[2], v[3]);
+    *(uint2*)(vt + (((size_t)b * H + h) * d + dd) * map.L + t) = u;
   }
 };
 
@@ -330,9 +342,186 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
   }
 }
 
+// Variant fed by gfx950's direct global->LDS loads (global_load_lds_dwordx4): each
+// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so the
+// padded 144-B rows are filled by giving every lane the global chunk that
+// belongs at its LDS slot (the 9th slot of a row is padding: it re-reads the
+// row's last chunk).  No staging registers, no LDS store instructions; the two
+// stages are separate LDS objects so the loads into one never order the reads
+// of the other.
+template <int BM, int BN, int WM, int WN, class Epi>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32;
+  constexpr int TN = BN / WN / 32;
+  constexpr int WROWS = BM / WM;
+  constexpr int ROWB = GEMM_LDS * 2;          // 144 bytes per LDS row
+  constexpr int AB = BM * ROWB, BB = BN * ROWB, SB = AB + BB;
+  constexpr int NI = SB / 1024;               // 1-KB load instructions per stage
+  constexpr int IPW = NI / NW;
+  static_assert(AB % 1024 == 0 && BB % 1024 == 0 && NI % NW == 0, "stage / wave mismatch");
+  static_assert((NW / 2) * WROWS * EPI_LDS * 4 <= SB, "epilogue slices must fit half the waves per stage");
+  __shared__ __attribute__((aligned(1024))) char st0[SB];
+  __shared__ __attribute__((aligned(1024))) char st1[SB];
+
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
+  int lid = xcd * xq + min(xcd, xr) + (bid >> 3);
+  const bool g1 = p.ngroups > 1 && lid >= p.tiles[0];
+  if (g1) lid -= p.tiles[0];
+  const GemmProblem g = g1 ? p.g[1] : p.g[0];
+  const int tiles_n = g1 ? p.tiles_n[1] : p.tiles_n[0];
+  const int tiles_m = (g.M + BM - 1) / BM;
+  constexpr int GROUP_M = 8;
+  const int in_group = GROUP_M * tiles_n;
+  const int gid = lid / in_group;
+  const int first_m = gid * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int m0 = (first_m + (lid % in_group) % gsize) * BM;
+  const int n0 = ((lid % in_group) / gsize) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // element offset of every lane's source chunk for each of this wave's load
+  // instructions (an instruction lies wholly in the A or the B part of a stage)
+  int voff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int off = (wave * IPW + j) * 1024 + lane * 16;
+    const bool isb = (wave * IPW + j) * 1024 >= AB;
+    const int o2 = isb ? off - AB : off;
+    const int row = o2 / ROWB;
+    const int slot = min((o2 - row * ROWB) >> 4, 7);
+    voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw + slot * 8
+                  : min(m0 + row, g.M - 1) * g.lda + slot * 8;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = g.K / GEMM_BK;
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  const int wrow = wm * WROWS;
+  const int wcol = wn * (BN / WN);
+
+#define GEMM_DMA(stage, kt)                                                              \
+  {                                                                                      \
+    const int ko_ = (kt) * GEMM_BK;                                                      \
+    _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                   \
+      const bf16_t* b_ = ((wave * IPW + j) * 1024 >= AB) ? g.W : g.A;                    \
+      __builtin_amdgcn_global_load_lds((const void*)(b_ + voff[j] + ko_),            \
+                                       (void*)((stage) + (wave * IPW + j) * 1024), 16, 0, 0); \
+    }                                                                                    \
+  }
+  // fragments of K-chunk kk+1 are read while the MFMAs of chunk kk run
+#define GEMM_COMPUTE(stage)                                                              \
+  {                                                                                      \
+    const bf16_t* a_s = (const bf16_t*)(stage);                                          \
+    const bf16_t* b_s = (const bf16_t*)((stage) + AB);                                   \
+    bf16x8 af[2][TM], bw[2][TN];                                                         \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+        af[0][i] = *(const bf16x8*)&a_s[(wrow + i * 32 + frow) * GEMM_LDS + fk];         \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
+        bw[0][j] = *(const bf16x8*)&b_s[(wcol + j * 32 + frow) * GEMM_LDS + fk];         \
+    _Pragma("unroll") for (int kk = 0; kk < GEMM_BK / 16; ++kk) {                       \
+      const int cb = kk & 1, nb = cb ^ 1;                                                \
+      if (kk + 1 < GEMM_BK / 16) {                                                       \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
+            af[nb][i] = *(const bf16x8*)&a_s[(wrow + i * 32 + frow) * GEMM_LDS + (kk + 1) * 16 + fk]; \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+            bw[nb][j] = *(const bf16x8*)&b_s[(wcol + j * 32 + frow) * GEMM_LDS + (kk + 1) * 16 + fk]; \
+      }                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                     \
+          _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bw[cb][j], acc[i][j], 0, 0, 0); \
+    }                                                                                    \
+  }
+  // vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
+#define GEMM_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+  GEMM_DMA(st0, 0);
+  GEMM_WAIT_DMA();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = (kt & 1) ? st1 : st0;
+    char* nxt = (kt & 1) ? st0 : st1;
+    if (kt + 1 < nk) GEMM_DMA(nxt, kt + 1);
+    GEMM_COMPUTE(cur);
+    GEMM_WAIT_DMA();
+    __syncthreads();
+  }
+#undef GEMM_DMA
+#undef GEMM_COMPUTE
+#undef GEMM_WAIT_DMA
+
+  const Epi epi = g1 ? p.e[1] : p.e[0];
+  float* slice = (float*)(wave < NW / 2 ? st0 : st1) + (wave % (NW / 2)) * WROWS * EPI_LDS;
+  const bool cmaj = epi.colmajor(n0, BN);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        slice[(i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * EPI_LDS + (lane & 31)] =
+            acc[i][j][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cbase = n0 + wcol + j * 32;
+    if (!cmaj) {
+#pragma unroll
+      for (int ps = 0; ps < WROWS / 8; ++ps) {
+        const int rl = ps * 8 + (lane >> 3);
+        const int cl = (lane & 7) * 4;
+        const int row = m0 + wrow + rl;
+        const int col = cbase + cl;
+        if (row < g.M && col < g.N) {
+          f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
+          if (g.bias) v += *(const f32x4*)(g.bias + col);
+          epi.row4(row, col, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ps = 0; ps < WROWS / 4 * 32 / 64; ++ps) {
+        const int idx = ps * 64 + lane;
+        const int rq = idx % (WROWS / 4);
+        const int cl = idx / (WROWS / 4);
+        const int row = m0 + wrow + rq * 4;
+        const int col = cbase + cl;
+        if (row + 3 < g.M && col < g.N) {
+          f32x4 v;
+          v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
+          v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
+          v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
+          v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
+          if (g.bias) v += g.bias[col];
+          epi.col4(row, col, v);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // ---------------------------------------------------------------- launch
 
-template <int BM, int BN, int WM, int WN, class Epi>
+// KV: 1 = direct-to-LDS kernel, 0 = register-staged kernel
+template <int BM, int BN, int WM, int WN, int KV, class Epi>
 static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
   GemmParams<Epi> p{};
   int total = 0;
@@ -345,8 +534,10 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
     total += p.tiles[i];
   }
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi>), dim3(total), dim3(WM * WN * 64), 0,
-                     st, p);
+  void (*kern)(GemmParams<Epi>);
+  if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, Epi>;
+  else kern = &gemm_bf16_kernel<BM, BN, WM, WN, Epi>;
+  hipLaunchKernelGGL(kern, dim3(total), dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -355,13 +546,19 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   KTimerScope timer(site, st);
   int maxM = 0, minN = 1 << 30;
   for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
-  if (maxM <= 64) return launch_cfg<32, 256, 1, 4>(gp, ep, ng, st);
-  if (maxM >= 1024 && minN >= 1024) return launch_cfg<256, 256, 2, 4>(gp, ep, ng, st);
-  return launch_cfg<128, 128, 2, 2>(gp, ep, ng, st);
+  if (maxM <= 64) return launch_cfg<32, 256, 1, 4, 0>(gp, ep, ng, st);
+  // large problems: 256x256 tiles, 8 waves, fed by direct global->LDS loads
+  if (maxM >= 1024 && minN >= 1024) return launch_cfg<256, 256, 2, 4, 1>(gp, ep, ng, st);
+  return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
 }
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
   EpiStoreF32 e{out, ldo};
+  return launch(&g, &e, 1, st, KS_GEMM_F32);
+}
+
+hipError_t gemm_store_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st) {
+  EpiStoreBf16 e{out, ldo};
   return launch(&g, &e, 1, st, KS_GEMM_F32);
 }
 

@@ -33,12 +33,13 @@ struct GemmProblem {
 struct QKVOut {
   bf16_t* q;          // [B, H, L, d]
   bf16_t* k;          // [B, H, L, d]
-  bf16_t* vt;         // [B, H, d, L]
+  uint16_t* vt;       // [B, H, d, L] fp16
   const float* rope;  // [L, d/2, 2] (cos, sin)
   int D, H, d;
 };
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st);
+hipError_t gemm_store_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
 hipError_t gemm_silu_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
 hipError_t gemm_gelu_bf16(const GemmProblem* g, int ng, bf16_t* const* out, const int* ldo,
                           hipStream_t st);
@@ -51,9 +52,9 @@ hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap*
 hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
                         bf16_t* cat, int ldcat, hipStream_t st);
 
-// Flash attention, bf16: q, k [B, H, L, d], vt [B, H, d, L]; output token (b, t),
-// head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
+// Flash attention: q, k bf16 [B, H, L, d], vt fp16 [B, H, d, L]; output (bf16) of
+// token (b, t), head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const uint16_t* vt, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st);
 

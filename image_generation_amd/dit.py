@@ -97,6 +97,7 @@ def _load() -> ctypes.CDLL:
         "dit_denoise_step": (c_int, [POINTER(DitModel), P, P, P, c_double, c_double,
                                      POINTER(DitFBCache), P, c_size_t, P, POINTER(DitStepInfo)]),
         "dit_set_kernel_timer": (c_int, [POINTER(DitKernelTimer)]),
+        "dit_linear_forward": (c_int, [P, c_int, c_int, POINTER(DitLinear), c_int, P, c_int, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -108,7 +109,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
             "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
-            "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer")
+            "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward")
 
 
 def _check(rc: int) -> None:
@@ -171,17 +172,35 @@ def dit_rope_table(grid_h: int, grid_w: int, Lt: int, head_dim: int, theta: floa
 
 def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.Tensor,
                   softmax_scale: Optional[float] = None, stream=None) -> torch.Tensor:
-    """q, k [B, H, L, d] bf16; vt [B, H, d, L] bf16; o [B, L, H*d] bf16 (written)."""
+    """q, k [B, H, L, d] bf16; vt [B, H, d, L] fp16; o [B, L, H*d] bf16 (written)."""
     B, H, L, d = q.shape
     _need(q, torch.bfloat16, (B, H, L, d), "q")
     _need(k, torch.bfloat16, (B, H, L, d), "k")
-    _need(vt, torch.bfloat16, (B, H, d, L), "vt")
+    _need(vt, torch.float16, (B, H, d, L), "vt")
     _need(o, torch.bfloat16, (B, L, H * d), "o")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), B, H, L, d, DIT_BF16,
                              float(softmax_scale), _stream(stream)))
     return o
+
+
+def dit_linear_forward(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = x W^T + b: x [M, K] bf16, w [N, K] bf16, b [N] fp32 -> y [M, N] (fp32 or bf16)."""
+    M, K = x.shape
+    N = w.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w, torch.bfloat16, (N, K), "w")
+    _need(b, torch.float32, (N,), "b")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (M, N) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out: fp32 or bf16 [M, N]")
+    lin = DitLinear(_ptr(w), _ptr(b))
+    yd = DIT_F32 if out.dtype == torch.float32 else DIT_BF16
+    _check(LIB.dit_linear_forward(_ptr(x), M, K, ctypes.byref(lin), N, _ptr(out), yd, _stream(stream)))
+    return out
 
 
 def _lin(w: torch.Tensor, b: torch.Tensor) -> DitLinear:

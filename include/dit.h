@@ -195,10 +195,19 @@ DIT_API int dit_set_kernel_timer(dit_kernel_timer* timer);
 
 /* ------------------------------------------------------------------ entry points */
 
+/* One linear layer: y[M, N] = x[M, K] W^T + b (bf16 operands, fp32 accumulate).
+ *   x: device bf16 [M, K] (row stride K); lin->w bf16 [N, K]; lin->b fp32 [N];
+ *   y: device [M, N], y_dtype DIT_F32 or DIT_BF16.  K % 64 == 0, N % 4 == 0.
+ *   The same MFMA kernel as the block projections.  Workspace: none. */
+DIT_API int dit_linear_forward(const void* x, int M, int K, const dit_linear* lin, int N, void* y,
+                       int y_dtype, void* stream);
+
 /* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V.
- *   q, k: device bf16 [B, H, L, 128]; vt: device bf16 [B, H, 128, L] (V
- *   transposed per head); o: device bf16 [B, L, H * 128] (token-major).
- *   L % 8 == 0, L >= 8; dtype must be DIT_BF16.  Workspace: none. */
+ *   q, k: device bf16 [B, H, L, 128]; vt: device fp16 [B, H, 128, L] (V
+ *   transposed per head, in fp16: the P V product runs on fp16 MFMAs); o:
+ *   device bf16 [B, L, H * 128] (token-major).  Softmax statistics and both
+ *   products accumulate in fp32.  L % 8 == 0, L >= 8; dtype must be DIT_BF16
+ *   (the dtype of q, k and o).  Workspace: none. */
 DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
                   int head_dim, int dtype, float softmax_scale, void* stream);
 

@@ -6,12 +6,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 What it computes, and which passage of the source pages each part follows:
 
 * First-Block-Cache (FBC): the unsloth studio ``diffusion.py`` commit log,
-  commit "Add opt-in step caching (First-Block-Cache)": run the first block,
-  compare its residual with the cached one, and when it barely changes skip
-  the remaining blocks and reuse their cached output; the threshold is raised
-  for a quantised transformer.  The devotd.net VisualGen article (section on
-  why the speed-ups differ, Cache-DiT paragraph) names the same test a
-  "residual difference threshold".
+  commit adding opt-in step caching (First-Block-Cache): the first block's
+  residual is compared with the one cached from an earlier step; once it hardly
+  moves, the remaining blocks are not run and their earlier contribution is
+  added back instead; a quantised transformer gets a higher threshold.  The
+  devotd.net VisualGen article (section on why the speed-ups differ, Cache-DiT
+  paragraph) describes the same kind of test as a threshold on the change of a
+  residual.
 * Fused QKV projection: same commit log, speed-profile commit ("fused QKV").
 * RoPE as its own step: the vflash "Optimization ledger" page, table
   "Accepted or exposed" (strict Triton RoPE row).

@@ -15,3 +15,15 @@ def parity_err(got, ref):
     r = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(r * r))
     return float(np.max(np.abs(g - r)) / rms)
+
+
+def parity_err_bf16_stored(got, ref):
+    """parity_err for a bf16-stored result: each element may differ from the
+    exact value by half a bf16 ulp of its magnitude just by being stored, so
+    that half-ulp is taken off each element's error before the max."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    _, e = np.frexp(np.abs(r))            # |r| in [2^(e-1), 2^e): ulp = 2^(e-8)
+    half_ulp = np.ldexp(1.0, e - 9)
+    excess = np.maximum(np.abs(g - r) - half_ulp, 0.0)
+    return float(np.max(excess) / np.sqrt(np.mean(r * r)))
