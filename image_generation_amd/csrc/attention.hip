@@ -94,21 +94,48 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   float lsum = 0.f;           // this lane's partial row sum, relative to mref
 
   // ---- direct-to-LDS loads of a K / V^T tile pair.  Chunk c of a stage: the
-  // first 64*17 chunks are K rows (16 data chunks + 1 pad), then 128*9 V^T rows.
+  // first 64*17 chunks are K rows (16 data chunks + 1 pad) = load instructions
+  // 0..16, then 128*9 V^T rows = instructions 17..34.  Wave w issues
+  // instructions w, w+8, ...; each lane's source offset inside a tile is fixed,
+  // so it is computed once here.
+  constexpr int ATT_KI = ATT_BN * 17 / 64;        // K instructions (17)
+  constexpr int ATT_IPW = (ATT_NI + ATT_WAVES - 1) / ATT_WAVES;
+  static_assert(ATT_BN * 17 % 64 == 0, "K part must be whole instructions");
+  int doff[ATT_IPW];   // K: row*128 + slot*8 ; V^T: row*L + slot*8
+  int dkv[ATT_IPW];    // K: key row in tile ; V^T: first key of the chunk in tile
+#pragma unroll
+  for (int j = 0; j < ATT_IPW; ++j) {
+    const int inst = wave + j * ATT_WAVES;
+    const int c = inst * 64 + lane;
+    if (inst < ATT_KI) {
+      const int row = c / 17;
+      const int slot = min(c - row * 17, 15);
+      doff[j] = row * ATT_D + slot * 8;
+      dkv[j] = row;
+    } else {
+      const int c2 = c - ATT_BN * 17;
+      const int row = c2 / 9;
+      const int slot = min(c2 - row * 9, 7);
+      doff[j] = row * L + slot * 8;
+      dkv[j] = slot * 8;
+    }
+  }
   auto issue_tile = [&](char* stage, int kt) {
     const int kv0 = kt * ATT_BN;
-    for (int inst = wave; inst < ATT_NI; inst += ATT_WAVES) {
-      const int c = inst * 64 + lane;
+    const bool full = kv0 + ATT_BN <= L;
+#pragma unroll
+    for (int j = 0; j < ATT_IPW; ++j) {
+      const int inst = wave + j * ATT_WAVES;
+      if (inst >= ATT_NI) break;
       const uint16_t* src;
-      if (c < ATT_BN * 17) {
-        const int row = c / 17;
-        const int slot = min(c - row * 17, 15);
-        src = Kb + (size_t)min(kv0 + row, L - 1) * ATT_D + slot * 8;
+      if (inst < ATT_KI) {
+        src = Kb + (size_t)kv0 * ATT_D + doff[j];
+        if (!full && kv0 + dkv[j] > L - 1)   // tail tile: clamp the key row
+          src = Kb + (size_t)(L - 1) * ATT_D + (doff[j] - dkv[j] * ATT_D);
       } else {
-        const int c2 = c - ATT_BN * 17;
-        const int row = c2 / 9;
-        const int slot = min(c2 - row * 9, 7);
-        src = Vb + (size_t)row * L + min(kv0 + slot * 8, L - 8);
+        src = Vb + kv0 + doff[j];
+        if (!full && kv0 + dkv[j] > L - 8)   // tail tile: clamp the key chunk
+          src = Vb + (L - 8) + (doff[j] - dkv[j]);
       }
       __builtin_amdgcn_global_load_lds((const void*)src, (void*)(stage + inst * 1024), 16, 0, 0);
     }
