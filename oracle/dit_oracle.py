@@ -37,7 +37,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .numerics import quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX
+from .numerics import (quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX, round_bf16,
+                       round_fp16, e4m3_tie_mask)
 
 __all__ = [
     "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
@@ -230,37 +231,66 @@ def linear_fp8(x, w, b):
     return y.reshape(*shp[:-1], w.shape[0])
 
 
-def attention_fp8(q, k, v, scale: Optional[float] = None) -> np.ndarray:
+def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
+                  tie_rel: Optional[float] = None):
     """fp8 attention (R27).
 
-    q, k: per-(batch, head, token) e4m3 scales; v: per-(batch, head, channel)
-    scales.  Scores use the dequantised operands; P = exp(s - max) in (0, 1] is
-    quantised as e4m3(448 P) / 448 and the row sum is taken from the quantised
-    P, so identical keys still return the mean of V.
+    Q, K and V each get one e4m3 scale per (batch, head), taken over that head's
+    whole [L, d] slice, so the scales factor out of both products.  Scores use
+    the dequantised operands.  With t = s * log2(e) and the row reference
+    r = ceil(max_j t_j) (the row max rounded up to an integer in log2 units),
+    P = 2^(t - r) lies in (0, 1] with its largest entry above 1/2; P enters the
+    P V product as e4m3(448 P) / 448 and the normaliser is the row sum of that
+    quantised P, so every row of weights sums to one.  A power-of-two reference
+    makes the quantised weights independent of which integer r is used (short
+    of e4m3's subnormal range).  Identical keys give equal weights, so the
+    output is then the mean of the dequantised V.  ``rows`` restricts the
+    output to those query rows (each row is independent of the others).
+
+    With ``tie_rel`` the call returns (out, slack): slack bounds, to first
+    order, how far the output moves when every P code whose 448 P lies within
+    tie_rel (relative) of an e4m3 rounding boundary rounds the other way -- the
+    spread of equally valid results that a computation of P in fp32 can give.
     """
     d = q.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     B, H, L, _ = q.shape
-    out = np.empty_like(q)
+    sel = np.arange(L) if rows is None else np.asarray(rows)
+    out = np.empty((B, H, len(sel), d))
+    slack = np.zeros_like(out) if tie_rel is not None else None
+
+    def deq(t):
+        codes, sc = quantize_rows_e4m3(t.reshape(1, -1))
+        return (codes * float(sc[0])).reshape(t.shape)
+
     for bi in range(B):
         for h in range(H):
-            qq, sq = quantize_rows_e4m3(q[bi, h])
-            kq, sk = quantize_rows_e4m3(k[bi, h])
-            vq_t, sv = quantize_rows_e4m3(v[bi, h].T)          # per channel
-            qd = qq * sq.astype(np.float64)[:, None]
-            kd = kq * sk.astype(np.float64)[:, None]
-            vd = (vq_t * sv.astype(np.float64)[:, None]).T
-            s = (qd @ kd.T) * scale
-            p = np.exp(s - s.max(axis=1, keepdims=True))
+            qd, kd, vd = deq(q[bi, h]), deq(k[bi, h]), deq(v[bi, h])
+            t = (qd[sel] @ kd.T) * (scale / math.log(2.0))
+            p = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)))
             pq = round_e4m3(p * E4M3_MAX) / E4M3_MAX
-            out[bi, h] = (pq @ vd) / pq.sum(axis=1, keepdims=True)
-    return out
+            lq = pq.sum(axis=1, keepdims=True)
+            out[bi, h] = (pq @ vd) / lq
+            if slack is not None:
+                # moving one weight by a step changes the output by step * (v_j - out) / l
+                tie, step = e4m3_tie_mask(p * E4M3_MAX, tie_rel)
+                w = np.where(tie, step / E4M3_MAX, 0.0)
+                slack[bi, h] = (w @ np.abs(vd) + w.sum(axis=1, keepdims=True)
+                                * np.abs(out[bi, h])) / lq
+    return out if slack is None else (out, slack)
 
 
 # --------------------------------------------------------------------------
 # blocks
 # --------------------------------------------------------------------------
+
+def _held(x, fp8, rounding=round_bf16):
+    """fp8 blocks (R33): an activation that is quantised to e4m3 later is first
+    rounded to the 16-bit format it is stored in between the two steps (bf16;
+    fp16 for V), so each e4m3 code is decided on the stored value."""
+    return rounding(x) if fp8 else x
+
 
 def _lin(x, P, name, fp8):
     if fp8:
@@ -286,15 +316,15 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
     q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
     k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
-    q = apply_rope(_heads(q, H), ang)
-    k = apply_rope(_heads(k, H), ang)
-    a = _merge(attn_fn(q, k, _heads(v, H)))
+    q = _held(apply_rope(_heads(q, H), ang), fp8)
+    k = _held(apply_rope(_heads(k, H), ang), fp8)
+    a = _held(_merge(attn_fn(q, k, _held(_heads(v, H), fp8, round_fp16))), fp8)
     out = {}
     for s, (x, m) in streams.items():
         a_s = a[:, :Lt] if s == "txt" else a[:, Lt:]
         x = x + m[:, 2:3] * _lin(a_s, P, f"{s}.proj", fp8)
         u = modulate(x, m[:, 3:4], m[:, 4:5])
-        hdn = gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8))
+        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8)), fp8)
         x = x + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
         out[s] = x
     return out["txt"], out["img"]
@@ -309,11 +339,11 @@ def single_block(x, mod, P, ang, H, fp8=False):
     D = x.shape[-1]
     u = modulate(x, mod[:, 0:1], mod[:, 1:2])
     h = _lin(u, P, "lin1", fp8)
-    q = apply_rope(_heads(h[..., :D], H), ang)
-    k = apply_rope(_heads(h[..., D:2 * D], H), ang)
-    v = _heads(h[..., 2 * D:3 * D], H)
+    q = _held(apply_rope(_heads(h[..., :D], H), ang), fp8)
+    k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), fp8)
+    v = _held(_heads(h[..., 2 * D:3 * D], H), fp8, round_fp16)
     a = _merge(attn_fn(q, k, v))
-    cat = np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1)
+    cat = _held(np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1), fp8)
     return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8)
 
 

@@ -2,6 +2,8 @@
 
 Formats (from their public definitions, not from any page):
   * bfloat16: 1 sign, 8 exponent, 7 stored mantissa bits (fp32 exponent range).
+  * IEEE binary16 (fp16): 1 sign, 5 exponent bits with bias 15, 10 stored
+    mantissa bits; largest finite 65504, smallest normal 2^-14.
   * OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7, 3 mantissa
     bits, no infinities, the all-ones code S.1111.111 is NaN; largest finite
     magnitude 1.75 * 2^8 = 448, smallest normal 2^-6, smallest subnormal 2^-9.
@@ -15,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["round_bf16", "round_e4m3", "E4M3_MAX", "quant_scale_f32",
+__all__ = ["round_bf16", "round_fp16", "e4m3_tie_mask", "round_e4m3", "E4M3_MAX", "quant_scale_f32",
            "quantize_rows_e4m3", "quantize_cols_e4m3"]
 
 E4M3_MAX = 448.0
@@ -47,6 +49,27 @@ def round_bf16(x) -> np.ndarray:
     # halfway above max rounds to inf (ties-to-even lands on the next binade)
     out = np.where(np.abs(out) > bf16_max, np.copysign(np.inf, x), out)
     return np.where(np.isnan(x), np.nan, out)
+
+
+def round_fp16(x) -> np.ndarray:
+    """fp64 -> nearest binary16 value (as fp64), ties to even; overflow -> inf."""
+    x = np.asarray(x, dtype=np.float64)
+    out = _round_sig(x, 11, -14)
+    fp16_max = (2.0 - 2.0 ** -10) * 2.0 ** 15
+    out = np.where(np.abs(out) > fp16_max, np.copysign(np.inf, x), out)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def e4m3_tie_mask(y, rel: float):
+    """(mask, step): mask marks the y (>= 0, <= 448) that lie within rel * y of
+    an e4m3 rounding boundary (a midpoint between neighbouring codes), where a
+    computation carried in a different precision may round the other way;
+    step is the spacing of e4m3 values around y."""
+    y = np.asarray(y, dtype=np.float64)
+    _, e = np.frexp(y)
+    step = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    mid = (np.floor(y / step) + 0.5) * step
+    return np.abs(y - mid) <= rel * y, step
 
 
 def round_e4m3(x) -> np.ndarray:

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from oracle.numerics import round_bf16, round_e4m3, quantize_rows_e4m3
+from oracle.numerics import round_bf16, round_fp16, round_e4m3, quantize_rows_e4m3, e4m3_tie_mask
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -497,12 +497,81 @@ def test_attention_fp8_identical_keys_mean_of_v():
     vals = np.array([v for v, _ in _e4m3_table()])
     L, d = 20, 64
     v = rng.choice(vals[np.abs(vals) < 100], size=(1, 1, L, d))
-    v[0, 0, 0, :] = 448.0                  # per-channel amax 448 -> scale 1
+    v[0, 0, 0, :] = 448.0                  # head amax 448 -> scale 1
     k = np.broadcast_to(rng.standard_normal((1, 1, 1, d)), (1, 1, L, d)).copy()
     q = rng.standard_normal((1, 1, L, d))
     out = O.attention_fp8(q, k, v)
     np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=2, keepdims=True), out.shape),
                                rtol=1e-14)
+
+
+def test_fp16_rounding_vs_numpy_cast():
+    rng = np.random.default_rng(30)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-9, 5, 20000),
+                        [0.0, -0.0, 65504.0, 65519.9, 65520.0, -70000.0, 2.0 ** -24,
+                         2.0 ** -25, 3 * 2.0 ** -26, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]])
+    with np.errstate(over="ignore"):                 # overflow to inf is the point
+        want = x.astype(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(round_fp16(x), want)
+
+
+def test_e4m3_tie_mask_against_code_table():
+    # midpoints between consecutive non-negative e4m3 values, from the enumerated table
+    vals = np.unique([v for v, _ in _e4m3_table() if v >= 0])
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(31)
+    y = np.concatenate([rng.uniform(0, 448, 5000), 2.0 ** rng.uniform(-10, 8.8, 5000),
+                        mids, mids * (1 + 1e-5), mids * (1 - 3e-5)])
+    y = y[y <= 448]
+    rel = 2e-5
+    want = np.min(np.abs(y[:, None] - mids[None, :]), axis=1) <= rel * y
+    got, step = e4m3_tie_mask(y, rel)
+    np.testing.assert_array_equal(got, want)
+    # step: distance to the next code up from the code at or below y
+    lo = vals[np.searchsorted(vals, y, side="right") - 1]
+    hi = vals[np.minimum(np.searchsorted(vals, y, side="right"), len(vals) - 1)]
+    inner = y < 448
+    np.testing.assert_array_equal(step[inner], (hi - lo)[inner])
+
+
+def test_attention_fp8_slack_grows_with_the_band():
+    rng = np.random.default_rng(32)
+    q, k, v = (rng.standard_normal((1, 2, 48, 64)) for _ in range(3))
+    out0, s0 = O.attention_fp8(q, k, v, tie_rel=0.0)
+    _, s1 = O.attention_fp8(q, k, v, tie_rel=1e-3)
+    _, s2 = O.attention_fp8(q, k, v, tie_rel=1e-1)
+    np.testing.assert_array_equal(out0, O.attention_fp8(q, k, v))
+    assert np.all(s0 == 0) and np.all(s1 <= s2) and np.all(s2 >= 0) and s2.max() > 0
+
+
+def test_attention_fp8_identical_values_returned_exactly():
+    # the weights are normalised by the sum of the quantised P, so they sum to
+    # one and a V whose rows are all equal (and representable) comes back as is
+    rng = np.random.default_rng(24)
+    vals = np.array([v for v, _ in _e4m3_table()])
+    L, d = 40, 64
+    row = rng.choice(vals[np.abs(vals) < 100], size=d)
+    row[7] = 448.0
+    v = np.broadcast_to(row, (1, 1, L, d)).copy()
+    q, k = rng.standard_normal((1, 1, L, d)) * 2, rng.standard_normal((1, 1, L, d)) * 2
+    np.testing.assert_allclose(O.attention_fp8(q, k, v), v, rtol=1e-14, atol=0)
+
+
+def test_attention_fp8_exact_when_p_is_representable():
+    # q = 0.875 e0, k_j = -(j mod 8) e0 and softmax scale ln 2 / 0.875 give
+    # P_j = 2^-(j mod 8).  The head scales 0.875/448 = 2^-9, 7/448 = 2^-6 and
+    # 448/448 are exact in fp32, Q, K, V quantise exactly and so does 448 P, so
+    # the fp8 path equals exact attention on the same values
+    rng = np.random.default_rng(23)
+    vals = np.array([v for v, _ in _e4m3_table()])
+    L, d = 16, 64
+    q = np.zeros((1, 1, L, d)); q[..., 0] = 0.875
+    k = np.zeros((1, 1, L, d)); k[0, 0, :, 0] = -(np.arange(L) % 8)
+    v = rng.choice(vals[np.abs(vals) < 100], size=(1, 1, L, d))
+    v[0, 0, 3, 5] = 448.0
+    sc = math.log(2.0) / 0.875
+    got = O.attention_fp8(q, k, v, scale=sc)
+    np.testing.assert_allclose(got, O.attention(q, k, v, scale=sc), rtol=1e-13, atol=1e-13)
 
 
 def test_attention_fp8_close_to_exact():
