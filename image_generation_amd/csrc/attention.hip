@@ -49,7 +49,7 @@ __device__ __forceinline__ int swap23(int r) {
 }
 
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const uint16_t* __restrict__ VT,
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const f16_t* __restrict__ VT,
     bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char st0[ATT_SB];
   __shared__ __attribute__((aligned(1024))) char st1[ATT_SB];
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 
   const bf16_t* Qb = Q + (size_t)bh * L * ATT_D;
   const bf16_t* Kb = K + (size_t)bh * L * ATT_D;
-  const uint16_t* Vb = VT + (size_t)bh * ATT_D * L;
+  const f16_t* Vb = VT + (size_t)bh * ATT_D * L;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[q][c*16 + g*8 .. +8]
   const int q0 = qt * ATT_BM + wave * ATT_QW;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     for (int j = 0; j < ATT_IPW; ++j) {
       const int inst = wave + j * ATT_WAVES;
       if (inst >= ATT_NI) break;
-      const uint16_t* src;
+      const void* src;
       if (inst < ATT_KI) {
         src = Kb + (size_t)kv0 * ATT_D + doff[j];
         if (!full && kv0 + dkv[j] > L - 1)   // tail tile: clamp the key row
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     char* nxt = (kt & 1) ? st0 : st1;
     if (kt + 1 < ntiles) issue_tile(nxt, kt + 1);
     const bf16_t* sK = (const bf16_t*)cur;
-    const uint16_t* sV = (const uint16_t*)(cur + ATT_KB);
+    const f16_t* sV = (const f16_t*)(cur + ATT_KB);
     const int kv0 = kt * ATT_BN;
 
     // S^T for 2 key blocks of 32
@@ -248,7 +248,239 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   }
 }
 
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const uint16_t* vt, bf16_t* o,
+// ---------------------------------------------------------------- fp8 (e4m3)
+// Same work split.  Q, K, V^T are e4m3 with one scale per (b, h) each, so the
+// score scale sq * sk folds into the exp2 constant and sv into the final
+// normalisation.  S^T uses v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales):
+// for key block kb the MFMA row r is fed K row  g(r)*32 + kb*16 + i(r),
+// g(r) = (r/4)&1, i(r) = (r/8)*4 + r%4, so a lane's 32 score registers over the
+// 64-key tile are the 32 consecutive keys its lane group needs as the P operand
+// of the fp8 P V^T MFMA.
+//
+// Softmax reference: in exp2 units the running row max is rounded up to an
+// integer r, so P = 2^(t - r) <= 1 and 448 P never saturates e4m3.  When r
+// moves by k, O and the row sum scale by exactly 2^-k, and the e4m3 rounding of
+// 448 P is the same for every integer r (down to e4m3's subnormals): the result
+// matches quantising against the final row max rounded the same way.  The row
+// sum adds the quantised P (decoded back from the codes), so the weights that
+// multiply V sum to one.
+constexpr int AF8_BN = 64;
+constexpr int AF8_KRB = 144;                      // K row: 128 B + 16 pad (9 chunks)
+constexpr int AF8_VRB = 80;                       // V^T row: 64 B + 16 pad (5 chunks)
+constexpr int AF8_KB = AF8_BN * AF8_KRB;          // 9 KB
+constexpr int AF8_VB = ATT_D * AF8_VRB;           // 10 KB
+constexpr int AF8_SB = AF8_KB + AF8_VB;
+constexpr int AF8_NI = AF8_SB / 1024;             // 19 load instructions per stage
+constexpr int AF8_KI = AF8_KB / 1024;             // 9 of them for K
+static_assert(AF8_KB % 1024 == 0 && AF8_VB % 1024 == 0, "whole 1-KB loads");
+
+__global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
+    const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ VT,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char st0[AF8_SB];
+  __shared__ __attribute__((aligned(1024))) char st1[AF8_SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int nqt = (L + ATT_BM - 1) / ATT_BM;
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
+  const int lid = xcd * xq + min(xcd, xr) + (bid >> 3);
+  const int bh = lid / nqt;
+  const int qt = lid - bh * nqt;
+  const int b = bh / H;
+  const int h = bh - b * H;
+
+  const fp8_t* Qb = Q + (size_t)bh * L * ATT_D;
+  const fp8_t* Kb = K + (size_t)bh * L * ATT_D;
+  const fp8_t* Vb = VT + (size_t)bh * ATT_D * L;
+  const float cs = scale_log2 * sq[bh] * sk[bh];   // raw score -> exp2 units
+
+  // Q fragments: lane holds Q[q][c*64 + g*32 .. +32], c = 0, 1
+  const int q0 = qt * ATT_BM + wave * ATT_QW;
+  i32x8 qf[2];
+  {
+    const int qr = min(q0 + l32, L - 1);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const i32x4 lo = *(const i32x4*)(Qb + (size_t)qr * ATT_D + c * 64 + g * 32);
+      const i32x4 hi = *(const i32x4*)(Qb + (size_t)qr * ATT_D + c * 64 + g * 32 + 16);
+      qf[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+
+  f32x16 oacc[ATT_D / 32];
+#pragma unroll
+  for (int db = 0; db < ATT_D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float mref = -INFINITY;    // integer-valued reference, exp2 units
+  float lsum = 0.f;          // sum of 448 * quantised P, relative to mref
+
+  // per-lane load offsets (bytes inside a tile): K chunk c -> row c/9, slot c%9;
+  // V^T chunk c2 -> row c2/5, slot c2%5 (the last slot of a row is padding)
+  constexpr int IPW = (AF8_NI + ATT_WAVES - 1) / ATT_WAVES;
+  int doff[IPW], dkv[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int inst = wave + j * ATT_WAVES;
+    const int c = inst * 64 + lane;
+    if (inst < AF8_KI) {
+      const int row = c / 9;
+      const int slot = min(c - row * 9, 7);
+      doff[j] = row * ATT_D + slot * 16;
+      dkv[j] = row;
+    } else {
+      const int c2 = c - AF8_KI * 64;
+      const int row = c2 / 5;
+      const int slot = min(c2 - row * 5, 3);
+      doff[j] = row * L + slot * 16;
+      dkv[j] = slot * 16;
+    }
+  }
+  auto issue_tile = [&](char* stage, int kt) {
+    const int kv0 = kt * AF8_BN;
+    const bool full = kv0 + AF8_BN <= L;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int inst = wave + j * ATT_WAVES;
+      if (inst >= AF8_NI) break;
+      const fp8_t* src;
+      if (inst < AF8_KI) {
+        src = Kb + (size_t)kv0 * ATT_D + doff[j];
+        if (!full && kv0 + dkv[j] > L - 1)
+          src = Kb + (size_t)(L - 1) * ATT_D + (doff[j] - dkv[j] * ATT_D);
+      } else {
+        src = Vb + kv0 + doff[j];
+        if (!full && kv0 + dkv[j] > L - 16) src = Vb + (L - 16) + (doff[j] - dkv[j]);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(stage + inst * 1024), 16, 0, 0);
+    }
+  };
+
+  const int ntiles = (L + AF8_BN - 1) / AF8_BN;
+  // K row fed to MFMA row l32 of key block kb
+  const int krow0 = ((l32 >> 2) & 1) * 32 + (l32 >> 3) * 4 + (l32 & 3);
+  issue_tile(st0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    char* cur = (kt & 1) ? st1 : st0;
+    char* nxt = (kt & 1) ? st0 : st1;
+    if (kt + 1 < ntiles) issue_tile(nxt, kt + 1);
+    const char* sK = cur;
+    const char* sV = cur + AF8_KB;
+    const int kv0 = kt * AF8_BN;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const char* q_ = sK + (krow0 + kb * 16) * AF8_KRB + c * 64 + g * 32;
+        const i32x4 lo = *(const i32x4*)q_, hi = *(const i32x4*)(q_ + 16);
+        const i32x8 kf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[c], sacc[kb], 0, 0, 0,
+                                                                   127, 0, 127);
+      }
+    }
+    // element e of sacc[kb] is key kv0 + g*32 + kb*16 + e of query column l32
+    if (kv0 + AF8_BN > L) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kv0 + g * 32 + kb * 16 + e >= L) sacc[kb][e] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxl = mx * cs;
+    if (__any(mxl > mref)) {
+      const float mnew = fmaxf(mref, ceilf(mxl));
+      // 2^(mref - mnew): an exact power of two (0 before the first tile)
+      const float alpha = mref == -INFINITY ? 0.f : ldexpf(1.0f, (int)(mref - mnew));
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < ATT_D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+    int pw[8];   // 32 e4m3 codes of P * 448, keys g*32 + 0..31
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p[e] = fast_exp2(fmaf(sacc[kb][w4 * 4 + e], cs, -mref)) * 448.f;
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+        pw[kb * 4 + w4] = w;
+        const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        lsum += (d0.x + d0.y) + (d1.x + d1.y);
+      }
+    const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+    for (int db = 0; db < ATT_D / 32; ++db) {
+      const char* v_ = sV + (db * 32 + l32) * AF8_VRB + g * 32;
+      const i32x4 lo = *(const i32x4*)v_, hi = *(const i32x4*)(v_ + 16);
+      const i32x8 vf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[db], 0, 0, 0, 127,
+                                                                 0, 127);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = sv[bh] / lt;
+  const int t = q0 + l32;
+  if (t < L) {
+    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * ATT_D;
+#pragma unroll
+    for (int db = 0; db < ATT_D / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int dd = db * 32 + e4 * 8 + g * 4;
+        uint2 u;
+        u.x = pack_bf16x2(oacc[db][e4 * 4 + 0] * inv, oacc[db][e4 * 4 + 1] * inv);
+        u.y = pack_bf16x2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv);
+        *(uint2*)(orow + dd) = u;
+      }
+  }
+}
+
+hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, const float* sq,
+                         const float* sk, const float* sv, bf16_t* o, int ldo, const RowMap& map,
+                         int B, int H, int L, int d, float softmax_scale, hipStream_t st) {
+  if (d != ATT_D || L < 16 || L % 16) return hipErrorInvalidValue;
+  const int nqt = (L + ATT_BM - 1) / ATT_BM;
+  const int nblk = B * H * nqt;
+  if (nblk == 0) return hipSuccess;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  KTimerScope timer(KS_ATTENTION, st);
+  hipLaunchKernelGGL(attention_fp8_kernel, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q8, k8, vt8,
+                     sq, sk, sv, o, ldo, map, H, L, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st) {
   if (d != ATT_D || L < 8 || L % 8) return hipErrorInvalidValue;

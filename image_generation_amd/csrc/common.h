@@ -7,6 +7,7 @@ namespace dit {
 
 typedef uint16_t bf16_t;   // bfloat16 storage
 typedef uint8_t fp8_t;     // OCP e4m3 storage
+typedef _Float16 f16_t;    // fp16 storage
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -29,7 +30,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 // Round-to-nearest-even fp32 -> fp16 bits.
 __device__ __forceinline__ uint16_t f2h(float f) {
-  _Float16 h = (_Float16)f;
+  f16_t h = (f16_t)f;
   return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {

@@ -85,11 +85,18 @@ int make_dims(const dit_dims* in, Dims* o) {
   return DIT_OK;
 }
 
-int check_bf16_dims(const Dims& dm) {
+int check_block_dims(const Dims& dm, int dtype) {
+  if (dtype != DIT_BF16 && dtype != DIT_FP8)
+    return fail(DIT_ERR_UNSUPPORTED, "block dtype %d (DIT_BF16 or DIT_FP8)", dtype);
   if (dm.d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d (this build runs 128)", dm.d);
   if (dm.D % 256 || dm.D > 3072)
     return fail(DIT_ERR_UNSUPPORTED, "hidden size %d (needs a multiple of 256, <= 3072)", dm.D);
   if (dm.F % 64) return fail(DIT_ERR_UNSUPPORTED, "MLP size %d (needs a multiple of 64)", dm.F);
+  if (dtype == DIT_FP8) {
+    // e4m3 K slabs are 128 deep; fp8 attention tiles keys by 16
+    if (dm.F % 128) return fail(DIT_ERR_UNSUPPORTED, "fp8: MLP size %d (multiple of 128)", dm.F);
+    if (dm.L % 16) return fail(DIT_ERR_UNSUPPORTED, "fp8: joint length %d (multiple of 16)", dm.L);
+  }
   return DIT_OK;
 }
 
@@ -111,19 +118,40 @@ struct BlockWS {
   bf16_t* u;    // LN-modulate output [B*L, D] (row order of the block)
   bf16_t* q;    // [B, H, L, d]
   bf16_t* k;    // [B, H, L, d]
-  uint16_t* vt; // [B, H, d, L] fp16
+  f16_t* vt;    // [B, H, d, L] fp16
   bf16_t* cat;  // [B*L, D + F]: attention output | MLP hidden
+  // e4m3 operands of the fp8 blocks and their scales
+  fp8_t* u8;    // [B*L, D], scale su [B*L]
+  fp8_t* q8;    // [B, H, L, d]
+  fp8_t* k8;    // [B, H, L, d]
+  fp8_t* v8;    // [B, H, d, L]
+  fp8_t* cat8;  // [B*L, D + F], scales s_att (attention part or whole row), s_hid
+  float *su, *s_att, *s_hid;
+  float* s_qkv;          // [3, B*H]: q, k, v scales per (b, h)
+  unsigned int* amax;    // [B*H] reduction scratch
 };
 
 BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   const size_t n = (size_t)dm.B * dm.L * dm.D;
+  const size_t rows = (size_t)dm.B * dm.L;
+  const size_t bh = (size_t)dm.B * dm.H;
   BlockWS w;
   w.xf = with_xf ? c.take<float>(n) : nullptr;
   w.u = c.take<bf16_t>(n);
   w.q = c.take<bf16_t>(n);
   w.k = c.take<bf16_t>(n);
-  w.vt = c.take<uint16_t>(n);
-  w.cat = c.take<bf16_t>((size_t)dm.B * dm.L * (dm.D + dm.F));
+  w.vt = c.take<f16_t>(n);
+  w.cat = c.take<bf16_t>(rows * (dm.D + dm.F));
+  w.u8 = c.take<fp8_t>(n);
+  w.q8 = c.take<fp8_t>(n);
+  w.k8 = c.take<fp8_t>(n);
+  w.v8 = c.take<fp8_t>(n);
+  w.cat8 = c.take<fp8_t>(rows * (dm.D + dm.F));
+  w.su = c.take<float>(rows);
+  w.s_att = c.take<float>(rows);
+  w.s_hid = c.take<float>(rows);
+  w.s_qkv = c.take<float>(3 * bh);
+  w.amax = c.take<unsigned int>(bh);
   return w;
 }
 
@@ -181,24 +209,30 @@ size_t ws_size(const Dims& dm, int purpose, int n) {
   return (c.off + 255) & ~(size_t)255;
 }
 
-int check_linear(const dit_linear& l, const char* name) {
+// fp8: the layer must carry its per-channel weight scales
+int check_linear(const dit_linear& l, const char* name, bool fp8 = false) {
   if (!l.w || !l.b) return fail(DIT_ERR_INVALID_ARG, "%s: NULL weight or bias", name);
   if (!aligned16(l.w) || !aligned16(l.b))
     return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", name);
+  if (fp8 && (!l.w_scale || !aligned16(l.w_scale)))
+    return fail(DIT_ERR_INVALID_ARG, "%s: fp8 layer needs a 16-byte aligned w_scale", name);
   return DIT_OK;
 }
 
-int check_block(const dit_block* blk) {
+int check_block(const dit_block* blk, bool fp8) {
   if (!blk) return fail(DIT_ERR_INVALID_ARG, "block is NULL");
   int rc;
   if (blk->kind == DIT_BLOCK_DOUBLE) {
     for (int s = 0; s < 2; ++s) {
-      if ((rc = check_linear(blk->qkv[s], "qkv")) || (rc = check_linear(blk->proj[s], "proj")) ||
-          (rc = check_linear(blk->mlp1[s], "mlp1")) || (rc = check_linear(blk->mlp2[s], "mlp2")))
+      if ((rc = check_linear(blk->qkv[s], "qkv", fp8)) ||
+          (rc = check_linear(blk->proj[s], "proj", fp8)) ||
+          (rc = check_linear(blk->mlp1[s], "mlp1", fp8)) ||
+          (rc = check_linear(blk->mlp2[s], "mlp2", fp8)))
         return rc;
     }
   } else if (blk->kind == DIT_BLOCK_SINGLE) {
-    if ((rc = check_linear(blk->lin1, "lin1")) || (rc = check_linear(blk->lin2, "lin2"))) return rc;
+    if ((rc = check_linear(blk->lin1, "lin1", fp8)) || (rc = check_linear(blk->lin2, "lin2", fp8)))
+      return rc;
   } else {
     return fail(DIT_ERR_INVALID_ARG, "unknown block kind %d", blk->kind);
   }
@@ -217,6 +251,92 @@ GemmProblem gp(const bf16_t* A, int lda, const dit_linear& l, int K, int M, int 
   g.K = K;
   return g;
 }
+
+// e4m3 problem: A8 [M, K] with row scales sa, weight codes with l.w_scale
+GemmProblem gp8(const fp8_t* A8, int lda, const float* sa, const dit_linear& l, int K, int M, int N) {
+  GemmProblem g = gp(nullptr, lda, l, K, M, N);
+  g.W = nullptr;
+  g.A8 = A8;
+  g.W8 = (const fp8_t*)l.w;
+  g.sa = sa;
+  g.sw = l.w_scale;
+  return g;
+}
+
+// per-(b, h) e4m3 copies of the QKV epilogue's Q, K (bf16) and V^T (fp16)
+hipError_t quant_qkv(const Dims& dm, const BlockWS& w, hipStream_t st) {
+  const size_t n = (size_t)dm.L * dm.d;
+  const int bh = dm.B * dm.H;
+  hipError_t e;
+  if ((e = quant_slices<bf16_t>(w.q, n, bh, w.amax, w.q8, w.s_qkv, st))) return e;
+  if ((e = quant_slices<bf16_t>(w.k, n, bh, w.amax, w.k8, w.s_qkv + bh, st))) return e;
+  return quant_slices<f16_t>(w.vt, n, bh, w.amax, w.v8, w.s_qkv + 2 * bh, st);
+}
+
+// fp8 block (x fp32): e4m3 GEMM operands with per-token activation scales, e4m3
+// attention with per-(b, h) scales; the same row spaces and epilogues as bf16.
+hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float* mod, int bs,
+                     const float* rope, const BlockWS& w, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F, H = dm.H;
+  const int DF = D + F, BH = B * H;
+  const QKVOut qo{w.q, w.k, w.vt, rope, D, H, dm.d};
+  const float scale = 1.0f / sqrtf((float)dm.d);
+  const float *sq = w.s_qkv, *sk = w.s_qkv + BH, *sv = w.s_qkv + 2 * BH;
+  hipError_t e;
+  if (blk.kind == DIT_BLOCK_DOUBLE) {
+    const RowMap sm{B, Lt, Li, L, 1, 0};
+    RowMap st_txt = sm;
+    st_txt.base = B * Li;
+    const RowMap maps[2] = {sm, st_txt};
+    const int ng = (B * Lt > 0) ? 2 : 1;
+    const float* mi = mod;
+    const float* mt = mod + 6 * (size_t)D;
+    const size_t ti = (size_t)B * Li;
+
+    if ((e = ln_modulate_fp8(x, w.u8, w.su, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs, st)))
+      return e;
+    GemmProblem g[2] = {gp8(w.u8, D, w.su, blk.qkv[0], D, B * Li, 3 * D),
+                        gp8(w.u8 + ti * D, D, w.su + ti, blk.qkv[1], D, B * Lt, 3 * D)};
+    if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
+    if ((e = quant_qkv(dm, w, st))) return e;
+    if ((e = attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, sm, B, H, L, dm.d, scale, st)))
+      return e;
+    if ((e = quant_rows<bf16_t>(w.cat, DF, w.cat8, DF, w.s_att, B * L, D, st))) return e;
+    g[0] = gp8(w.cat8, DF, w.s_att, blk.proj[0], D, B * Li, D);
+    g[1] = gp8(w.cat8 + ti * DF, DF, w.s_att + ti, blk.proj[1], D, B * Lt, D);
+    const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
+    if ((e = gemm_gated_residual<float>(g, ng, x, D, gate1, bs, maps, st))) return e;
+    if ((e = ln_modulate_fp8(x, w.u8, w.su, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D,
+                             mt + 3 * D, mt + 4 * D, bs, st)))
+      return e;
+    g[0] = gp8(w.u8, D, w.su, blk.mlp1[0], D, B * Li, F);
+    g[1] = gp8(w.u8 + ti * D, D, w.su + ti, blk.mlp1[1], D, B * Lt, F);
+    bf16_t* hid[2] = {w.cat + D, w.cat + ti * DF + D};
+    const int ldh[2] = {DF, DF};
+    if ((e = gemm_gelu_bf16(g, ng, hid, ldh, st))) return e;
+    if ((e = quant_rows<bf16_t>(w.cat + D, DF, w.cat8 + D, DF, w.s_hid, B * L, F, st))) return e;
+    g[0] = gp8(w.cat8 + D, DF, w.s_hid, blk.mlp2[0], F, B * Li, D);
+    g[1] = gp8(w.cat8 + ti * DF + D, DF, w.s_hid + ti, blk.mlp2[1], F, B * Lt, D);
+    const float* gate2[2] = {mi + 5 * D, mt + 5 * D};
+    return gemm_gated_residual<float>(g, ng, x, D, gate2, bs, maps, st);
+  }
+  const RowMap jm{B, Lt, Li, L, 0, 0};
+  if ((e = ln_modulate_fp8(x, w.u8, w.su, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st)))
+    return e;
+  const GemmProblem g1 = gp8(w.u8, D, w.su, blk.lin1, D, B * L, 3 * D + F);
+  if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
+  if ((e = quant_qkv(dm, w, st))) return e;
+  if ((e = attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, jm, B, H, L, dm.d, scale, st)))
+    return e;
+  // linear2 takes [attention | GELU] as one row, so one scale per joint row
+  if ((e = quant_rows<bf16_t>(w.cat, DF, w.cat8, DF, w.s_att, B * L, DF, st))) return e;
+  const GemmProblem g2 = gp8(w.cat8, DF, w.s_att, blk.lin2, DF, B * L, D);
+  const float* gate[1] = {mod + 2 * D};
+  return gemm_gated_residual<float>(&g2, 1, x, D, gate, bs, &jm, st);
+}
+
+hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
+                     int bs, const float* rope, const BlockWS& w, hipStream_t st);
 
 // ---- one block, already validated
 template <class XT>
@@ -268,6 +388,12 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
   const GemmProblem g2 = gp(w.cat, DF, blk.lin2, DF, B * L, D);
   const float* gate[1] = {mod + 2 * D};
   return gemm_gated_residual<XT>(&g2, 1, x, D, gate, bs, &jm, st);
+}
+
+hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
+                     int bs, const float* rope, const BlockWS& w, hipStream_t st) {
+  if (dtype == DIT_FP8) return block_fp8(dm, blk, x, mod, bs, rope, w, st);
+  return block_impl<float>(dm, blk, x, mod, bs, rope, w, st);
 }
 
 }  // namespace
@@ -364,25 +490,56 @@ int dit_linear_forward(const void* x, int M, int K, const dit_linear* lin, int N
   return DIT_OK;
 }
 
-int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
-                  int head_dim, int dtype, float softmax_scale, void* stream) {
+int dit_attention(const void* q, const void* k, const void* vt, void* o, const float* q_scale,
+                  const float* k_scale, const float* v_scale, int B, int H, int L, int head_dim,
+                  int dtype, float softmax_scale, void* stream) {
   if (!q || !k || !vt || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: pointers must be 16-byte aligned");
-  if (B < 1 || H < 1 || L < 8 || L % 8)
-    return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H >= 1 and L a multiple of 8");
-  if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dit_attention: dtype %d", dtype);
+  if (dtype != DIT_BF16 && dtype != DIT_FP8)
+    return fail(DIT_ERR_UNSUPPORTED, "dit_attention: dtype %d", dtype);
+  const int lmul = dtype == DIT_FP8 ? 16 : 8;
+  if (B < 1 || H < 1 || L < lmul || L % lmul)
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H >= 1 and L a positive multiple of %d",
+                lmul);
+  if (dtype == DIT_FP8 && (!q_scale || !k_scale || !v_scale))
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: fp8 needs q, k and v scales");
   if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "dit_attention: head_dim %d", head_dim);
   if (!std::isfinite(softmax_scale))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: softmax_scale must be finite");
-  if ((long long)B * H * L * head_dim > (1LL << 40))
+  if ((long long)B * H * L * head_dim > (1LL << 40) || (long long)B * L > (1LL << 31) - 1)
     return fail(DIT_ERR_UNSUPPORTED, "dit_attention: problem too large");
   int rc = check_device();
   if (rc) return rc;
   const RowMap jm{B, 0, L, L, 0, 0};
-  DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const uint16_t*)vt, (bf16_t*)o,
-                               H * head_dim, jm, B, H, L, head_dim, softmax_scale,
-                               (hipStream_t)stream));
+  if (dtype == DIT_FP8)
+    DIT_CHECK_HIP(attention_fp8((const fp8_t*)q, (const fp8_t*)k, (const fp8_t*)vt, q_scale,
+                                k_scale, v_scale, (bf16_t*)o, H * head_dim, jm, B, H, L, head_dim,
+                                softmax_scale, (hipStream_t)stream));
+  else
+    DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const f16_t*)vt, (bf16_t*)o,
+                                 H * head_dim, jm, B, H, L, head_dim, softmax_scale,
+                                 (hipStream_t)stream));
+  return DIT_OK;
+}
+
+int dit_quantize_rows(const void* src, int src_dtype, int src_ld, int rows, int width, void* dst,
+                      int dst_ld, float* scale, void* stream) {
+  if (!src || !dst || !scale) return fail(DIT_ERR_INVALID_ARG, "dit_quantize_rows: NULL pointer");
+  if (!aligned16(src) || !aligned16(dst) || !aligned16(scale))
+    return fail(DIT_ERR_INVALID_ARG, "dit_quantize_rows: pointers must be 16-byte aligned");
+  if (src_dtype != DIT_BF16)
+    return fail(DIT_ERR_UNSUPPORTED, "dit_quantize_rows: src_dtype %d (DIT_BF16)", src_dtype);
+  if (rows < 0 || width < 8 || width % 8 || src_ld < width || src_ld % 8 || dst_ld < width ||
+      dst_ld % 8)
+    return fail(DIT_ERR_INVALID_ARG,
+                "dit_quantize_rows: width, src_ld, dst_ld multiples of 8, strides >= width");
+  if ((long long)rows * src_ld > (1LL << 40) || (long long)rows * dst_ld > (1LL << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "dit_quantize_rows: problem too large");
+  int rc = check_device();
+  if (rc) return rc;
+  DIT_CHECK_HIP(quant_rows<bf16_t>((const bf16_t*)src, src_ld, (fp8_t*)dst, dst_ld, scale, rows,
+                                   width, (hipStream_t)stream));
   return DIT_OK;
 }
 
@@ -392,17 +549,16 @@ int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, voi
   Dims dm;
   int rc;
   if ((rc = make_dims(dims, &dm))) return rc;
-  if ((rc = check_block(blk))) return rc;
+  if ((rc = check_block_dims(dm, dtype))) return rc;
+  if ((rc = check_block(blk, dtype == DIT_FP8))) return rc;
   if (!x || !mod || !rope || !workspace)
     return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: NULL pointer");
   if (!aligned16(x) || !aligned16(mod) || !aligned16(rope) || !aligned16(workspace))
     return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: pointers must be 16-byte aligned");
   if (mod_bstride < 0 || mod_bstride % 4 || mod_bstride > (1L << 30))
     return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: mod_bstride must be >= 0, a multiple of 4");
-  if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dit_block_forward: dtype %d", dtype);
   if (x_dtype != DIT_F32 && x_dtype != DIT_BF16)
     return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: x_dtype %d", x_dtype);
-  if ((rc = check_bf16_dims(dm))) return rc;
   const size_t need = ws_size(dm, DIT_WS_BLOCK, 0);
   if (ws_bytes < need)
     return fail(DIT_ERR_WORKSPACE, "dit_block_forward: workspace %zu < %zu bytes", ws_bytes, need);
@@ -411,12 +567,12 @@ int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, voi
   const BlockWS w = carve_block(c, dm, true);
   hipStream_t st = (hipStream_t)stream;
   if (x_dtype == DIT_F32) {
-    DIT_CHECK_HIP(block_impl<float>(dm, *blk, (float*)x, mod, (int)mod_bstride, rope, w, st));
+    DIT_CHECK_HIP(run_block(dm, dtype, *blk, (float*)x, mod, (int)mod_bstride, rope, w, st));
   } else {
     // a bf16 residual stream is carried in fp32 through the block and rounded once
     const size_t n = (size_t)dm.B * dm.L * dm.D;
     DIT_CHECK_HIP(widen_bf16((const bf16_t*)x, w.xf, n, st));
-    DIT_CHECK_HIP(block_impl<float>(dm, *blk, w.xf, mod, (int)mod_bstride, rope, w, st));
+    DIT_CHECK_HIP(run_block(dm, dtype, *blk, w.xf, mod, (int)mod_bstride, rope, w, st));
     DIT_CHECK_HIP(narrow_f32(w.xf, (bf16_t*)x, n, st));
   }
   return DIT_OK;
@@ -500,11 +656,12 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   Dims dm;
   int rc;
   if ((rc = make_dims(&m->dims, &dm))) return rc;
-  if ((rc = check_bf16_dims(dm))) return rc;
+  if ((rc = check_block_dims(dm, m->dtype))) return rc;
+  const int dt = m->dtype;
   if (m->n_double < 1 || m->n_single < 0 || !m->blocks)
     return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: needs >= 1 double block");
   for (int j = 0; j < m->n_double + m->n_single; ++j) {
-    if ((rc = check_block(&m->blocks[j]))) return rc;
+    if ((rc = check_block(&m->blocks[j], dt == DIT_FP8))) return rc;
     const int want = j < m->n_double ? DIT_BLOCK_DOUBLE : DIT_BLOCK_SINGLE;
     if (m->blocks[j].kind != want)
       return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: block %d has the wrong kind", j);
@@ -542,7 +699,7 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st));
   DIT_CHECK_HIP(embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before, B,
                               Lt, Li, D, m->C_in, st));
-  DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
+  DIT_CHECK_HIP(run_block(dm, dt, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
 
   double rel = INFINITY;
   int skip = 0;
@@ -560,12 +717,11 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
     DIT_CHECK_HIP(fbc_apply(w.x, cache->cached, B, Lt, Li, D, st));
   } else {
     for (int j = 1; j < m->n_double; ++j)
-      DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[j], w.x, mod_step + j * D12, 0, w.rope, w.blk,
-                                      st));
+      DIT_CHECK_HIP(run_block(dm, dt, m->blocks[j], w.x, mod_step + j * D12, 0, w.rope, w.blk, st));
     const float* ms = mod_step + m->n_double * D12;
     for (int j = 0; j < m->n_single; ++j)
-      DIT_CHECK_HIP(block_impl<float>(dm, m->blocks[m->n_double + j], w.x, ms + j * D3, 0, w.rope,
-                                      w.blk, st));
+      DIT_CHECK_HIP(run_block(dm, dt, m->blocks[m->n_double + j], w.x, ms + j * D3, 0, w.rope,
+                              w.blk, st));
     if (use_cache) {
       DIT_CHECK_HIP(fbc_commit(w.x, w.before, w.staging, cache->cached, cache->anchor, B, Lt, Li, D,
                                st));

@@ -96,7 +96,7 @@ struct EpiGatedResidual {
 
 // Split the fused projection into head-major Q, K (bf16, rotated) and V^T (fp16).
 struct EpiQKV {
-  bf16_t* q; bf16_t* k; uint16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
+  bf16_t* q; bf16_t* k; f16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
   int D, H, d; RowMap map;
   __device__ __forceinline__ bool colmajor(int n0, int bn) const {
     return n0 >= 2 * D && n0 + bn <= 3 * D;
@@ -118,7 +118,7 @@ struct EpiQKV {
       bf16_t* dst = which == 0 ? q : k;
       store_bf16x4(dst + (bh * map.L + t) * d + dd, o0, o1, o2, o3);
     } else {
-      uint16_t* dst = vt + (bh * d + dd) * map.L + t;
+      uint16_t* dst = (uint16_t*)vt + (bh * d + dd) * map.L + t;
       const size_t L = map.L;
       dst[0] = f2h(v[0]);
       dst[L] = f2h(v[1]);
@@ -349,7 +349,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
 // row's last chunk).  No staging registers, no LDS store instructions; the two
 // stages are separate LDS objects so the loads into one never order the reads
 // of the other.
-template <int BM, int BN, int WM, int WN, class Epi>
+//
+// F8: operands are OCP e4m3 with per-row (A) and per-column (W) scales; a K
+// slab is 128 elements (the same 128 bytes per row as a bf16 slab of 64), and
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) takes 32 bytes of K
+// per lane; the epilogue dequantises with sa[row] * sw[col].
+template <int BM, int BN, int WM, int WN, bool F8, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
@@ -387,8 +392,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  // element offset of every lane's source chunk for each of this wave's load
+  // byte offset of every lane's source chunk for each of this wave's load
   // instructions (an instruction lies wholly in the A or the B part of a stage)
+  constexpr int ES = F8 ? 1 : 2;                    // element bytes
+  const char* abase = F8 ? (const char*)g.A8 : (const char*)g.A;
+  const char* wbase = F8 ? (const char*)g.W8 : (const char*)g.W;
   int voff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
@@ -397,8 +405,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     const int o2 = isb ? off - AB : off;
     const int row = o2 / ROWB;
     const int slot = min((o2 - row * ROWB) >> 4, 7);
-    voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw + slot * 8
-                  : min(m0 + row, g.M - 1) * g.lda + slot * 8;
+    voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw * ES + slot * 16
+                  : min(m0 + row, g.M - 1) * g.lda * ES + slot * 16;
   }
 
   f32x16 acc[TM][TN];
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = g.K / GEMM_BK;
+  const int nk = g.K / (GEMM_BK * 2 / ES);          // 128-byte K slabs
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
   const int wrow = wm * WROWS;
@@ -417,9 +425,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 
 #define GEMM_DMA(stage, kt)                                                              \
   {                                                                                      \
-    const int ko_ = (kt) * GEMM_BK;                                                      \
+    const int ko_ = (kt) * 128;                                                          \
     _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                   \
-      const bf16_t* b_ = ((wave * IPW + j) * 1024 >= AB) ? g.W : g.A;                    \
+      const char* b_ = ((wave * IPW + j) * 1024 >= AB) ? wbase : abase;                  \
       __builtin_amdgcn_global_load_lds((const void*)(b_ + voff[j] + ko_),            \
                                        (void*)((stage) + (wave * IPW + j) * 1024), 16, 0, 0); \
     }                                                                                    \
@@ -450,6 +458,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   // vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 #define GEMM_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x0F70)
 
+  // fp8: two 64-deep MFMAs per slab, 32 bytes of K per lane (two 16-byte reads)
+#define GEMM_COMPUTE_F8(stage)                                                           \
+  {                                                                                      \
+    const char* a_s = (const char*)(stage);                                              \
+    const char* b_s = (const char*)(stage) + AB;                                         \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                  \
+      i32x8 af[TM], bw[TN];                                                              \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                   \
+        const char* q_ = a_s + (wrow + i * 32 + frow) * ROWB + kk * 64 + (lane >> 5) * 32; \
+        const i32x4 lo_ = *(const i32x4*)q_, hi_ = *(const i32x4*)(q_ + 16);             \
+        af[i] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};     \
+      }                                                                                  \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                   \
+        const char* q_ = b_s + (wcol + j * 32 + frow) * ROWB + kk * 64 + (lane >> 5) * 32; \
+        const i32x4 lo_ = *(const i32x4*)q_, hi_ = *(const i32x4*)(q_ + 16);             \
+        bw[j] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};     \
+      }                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                     \
+          _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+                  af[i], bw[j], acc[i][j], 0, 0, 0, 127, 0, 127);                        \
+    }                                                                                    \
+  }
+
   GEMM_DMA(st0, 0);
   GEMM_WAIT_DMA();
   __syncthreads();
@@ -457,12 +489,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     char* cur = (kt & 1) ? st1 : st0;
     char* nxt = (kt & 1) ? st0 : st1;
     if (kt + 1 < nk) GEMM_DMA(nxt, kt + 1);
-    GEMM_COMPUTE(cur);
+    if constexpr (F8) GEMM_COMPUTE_F8(cur)
+    else GEMM_COMPUTE(cur)
     GEMM_WAIT_DMA();
     __syncthreads();
   }
 #undef GEMM_DMA
 #undef GEMM_COMPUTE
+#undef GEMM_COMPUTE_F8
 #undef GEMM_WAIT_DMA
 
   const Epi epi = g1 ? p.e[1] : p.e[0];
@@ -489,6 +523,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
         const int col = cbase + cl;
         if (row < g.M && col < g.N) {
           f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
+          if constexpr (F8) v *= *(const f32x4*)(g.sw + col) * g.sa[row];
           if (g.bias) v += *(const f32x4*)(g.bias + col);
           epi.row4(row, col, v);
         }
@@ -507,6 +542,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
           v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
           v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
           v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
+          if constexpr (F8) v *= *(const f32x4*)(g.sa + row) * g.sw[col];
           if (g.bias) v += g.bias[col];
           epi.col4(row, col, v);
         }
@@ -520,7 +556,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 
 // ---------------------------------------------------------------- launch
 
-// KV: 1 = direct-to-LDS kernel, 0 = register-staged kernel
+// KV: 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS bf16 kernel, 0 = register-staged bf16 kernel
 template <int BM, int BN, int WM, int WN, int KV, class Epi>
 static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
   GemmParams<Epi> p{};
@@ -535,7 +571,8 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
   }
   if (total == 0) return hipSuccess;
   void (*kern)(GemmParams<Epi>);
-  if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, Epi>;
+  if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, true, Epi>;
+  else if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, false, Epi>;
   else kern = &gemm_bf16_kernel<BM, BN, WM, WN, Epi>;
   hipLaunchKernelGGL(kern, dim3(total), dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
@@ -546,6 +583,7 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   KTimerScope timer(site, st);
   int maxM = 0, minN = 1 << 30;
   for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
+  if (gp[0].A8) return launch_cfg<256, 256, 2, 4, 2>(gp, ep, ng, st);   // fp8: one config
   if (maxM <= 64) return launch_cfg<32, 256, 1, 4, 0>(gp, ep, ng, st);
   // large problems: 256x256 tiles, 8 waves, fed by direct global->LDS loads
   if (maxM >= 1024 && minN >= 1024) return launch_cfg<256, 256, 2, 4, 1>(gp, ep, ng, st);

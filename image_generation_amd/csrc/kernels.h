@@ -9,7 +9,7 @@ namespace dit {
 // Launch sites, numbered as the DIT_SITE_* constants of the public header.
 enum KSite {
   KS_ATTENTION = 0, KS_GEMM_QKV, KS_GEMM_RESID, KS_GEMM_GELU, KS_GEMM_LIN1, KS_GEMM_F32,
-  KS_GEMM_SILU, KS_LN, KS_FBC, KS_OTHER
+  KS_GEMM_SILU, KS_LN, KS_FBC, KS_OTHER, KS_QUANT
 };
 // Bracket a launch with the calling thread's installed event timer (no-op if none).
 void ktimer_start(int site, hipStream_t st);
@@ -20,20 +20,27 @@ struct KTimerScope {
   ~KTimerScope() { ktimer_stop(site, st); }
 };
 
-// One GEMM problem: C[M, N] = A[M, K] W[N, K]^T + bias.  bf16 operands, K % 64 == 0,
-// lda / ldw multiples of 8 elements, 16-byte aligned base pointers.
+// One GEMM problem: C[M, N] = A[M, K] W[N, K]^T + bias.
+//   bf16: A, W; K % 64 == 0.
+//   fp8 (e4m3): A8, W8 with per-row scales sa[M] and per-output-channel scales
+//   sw[N], C = (A8 W8^T) * sa[m] * sw[n] + bias; K % 128 == 0.
+// lda / ldw in elements, rows 16-byte aligned.
 struct GemmProblem {
   const bf16_t* A; int lda;
   const bf16_t* W; int ldw;
   const float* bias;
   int M, N, K;
+  const fp8_t* A8 = nullptr;
+  const fp8_t* W8 = nullptr;
+  const float* sa = nullptr;
+  const float* sw = nullptr;
 };
 
 // Destinations of the fused QKV epilogue.
 struct QKVOut {
   bf16_t* q;          // [B, H, L, d]
   bf16_t* k;          // [B, H, L, d]
-  uint16_t* vt;       // [B, H, d, L] fp16
+  f16_t* vt;          // [B, H, d, L] fp16
   const float* rope;  // [L, d/2, 2] (cos, sin)
   int D, H, d;
 };
@@ -54,7 +61,7 @@ hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map
 
 // Flash attention: q, k bf16 [B, H, L, d], vt fp16 [B, H, d, L]; output (bf16) of
 // token (b, t), head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const uint16_t* vt, bf16_t* o,
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st);
 
@@ -66,5 +73,27 @@ hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& 
                        int n_img_rows, const float* shift_img, const float* scale_img,
                        const float* shift_txt, const float* scale_txt, int mod_bstride,
                        hipStream_t st);
+
+// LayerNorm + modulate emitting e4m3 with a per-row scale (out8 [rows, D], scale [rows]).
+hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, int D,
+                           const RowMap& map, int n_img_rows, const float* shift_img,
+                           const float* scale_img, const float* shift_txt, const float* scale_txt,
+                           int mod_bstride, hipStream_t st);
+
+// Per-row dynamic quantisation: dst[r, :width] = e4m3(src[r, :width] * 448 / amax_r),
+// scale[r] = amax_r / 448.  T = bf16_t or f16_t.
+template <class T>
+hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, int rows, int width,
+                      hipStream_t st);
+// One scale per contiguous slice of n elements (nslices slices); amax_tmp [nslices].
+template <class T>
+hipError_t quant_slices(const T* src, size_t n, int nslices, unsigned int* amax_tmp, fp8_t* dst,
+                        float* scale, hipStream_t st);
+
+// fp8 attention: q8, k8 e4m3 [B, H, L, d], vt8 e4m3 [B, H, d, L], one fp32 scale per
+// (b, h) for each of q, k, v; output bf16 as attention_bf16.
+hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, const float* sq,
+                         const float* sk, const float* sv, bf16_t* o, int ldo, const RowMap& map,
+                         int B, int H, int L, int d, float softmax_scale, hipStream_t st);
 
 }  // namespace dit

@@ -33,9 +33,10 @@ __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
   return v;
 }
 
-template <class XT>
+template <class XT, bool F8>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(
-    const XT* __restrict__ x, bf16_t* __restrict__ out, int rows, int D, RowMap map, int n_img,
+    const XT* __restrict__ x, bf16_t* __restrict__ out, fp8_t* __restrict__ out8,
+    float* __restrict__ oscale, int rows, int D, RowMap map, int n_img,
     const float* __restrict__ sh_i, const float* __restrict__ sc_i,
     const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride) {
   const int lane = threadIdx.x & 63;
@@ -68,19 +69,48 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
   const bool img = r < n_img;
   const float* sh = (img ? sh_i : sh_t) + (size_t)b * bstride;
   const float* sc = (img ? sc_i : sc_t) + (size_t)b * bstride;
-  bf16_t* orow = out + (size_t)r * D;
+  float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < LN_MAXCH; ++c) {
     if (c < nch) {
       const int col = c * 256 + lane * 4;
       const f32x4 a = *(const f32x4*)(sc + col);
       const f32x4 z = *(const f32x4*)(sh + col);
-      const f32x4 y = v[c] * rstd * (1.0f + a) + z;
-      uint2 u;
-      u.x = pack_bf16x2(y[0], y[1]);
-      u.y = pack_bf16x2(y[2], y[3]);
-      *(uint2*)(orow + col) = u;
+      v[c] = v[c] * rstd * (1.0f + a) + z;
+      if constexpr (F8)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])),
+                                 fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
     }
+  }
+  if constexpr (!F8) {
+    bf16_t* orow = out + (size_t)r * D;
+#pragma unroll
+    for (int c = 0; c < LN_MAXCH; ++c) {
+      if (c < nch) {
+        uint2 u;
+        u.x = pack_bf16x2(v[c][0], v[c][1]);
+        u.y = pack_bf16x2(v[c][2], v[c][3]);
+        *(uint2*)(orow + c * 256 + lane * 4) = u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float scl = 1.f, inv = 1.f;
+    if (amax > 0.f) {
+      scl = amax / 448.0f;
+      inv = 448.0f / amax;
+    }
+    fp8_t* orow = out8 + (size_t)r * D;
+#pragma unroll
+    for (int c = 0; c < LN_MAXCH; ++c) {
+      if (c < nch) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[c][0] * inv, v[c][1] * inv, 0, false);
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[c][2] * inv, v[c][3] * inv, lo, true);
+        *(int*)(orow + c * 256 + lane * 4) = w;
+      }
+    }
+    if (lane == 0) oscale[r] = scl;
   }
 }
 
@@ -92,13 +122,27 @@ hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& 
   if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   KTimerScope timer(KS_LN, st);
-  hipLaunchKernelGGL(ln_modulate_kernel<XT>, dim3((rows + 3) / 4), dim3(256), 0, st, x, out, rows, D,
-                     map, n_img_rows, shift_img, scale_img, shift_txt, scale_txt, mod_bstride);
+  hipLaunchKernelGGL((ln_modulate_kernel<XT, false>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
+                     out, nullptr, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
+                     shift_txt, scale_txt, mod_bstride);
   return hipGetLastError();
 }
 template hipError_t ln_modulate<float>(const float*, bf16_t*, int, int, const RowMap&, int,
                                        const float*, const float*, const float*, const float*, int,
                                        hipStream_t);
+
+hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, int D,
+                           const RowMap& map, int n_img_rows, const float* shift_img,
+                           const float* scale_img, const float* shift_txt, const float* scale_txt,
+                           int mod_bstride, hipStream_t st) {
+  if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  KTimerScope timer(KS_LN, st);
+  hipLaunchKernelGGL((ln_modulate_kernel<float, true>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
+                     nullptr, out8, scale, rows, D, map, n_img_rows, shift_img, scale_img,
+                     shift_txt, scale_txt, mod_bstride);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- embeddings
 

@@ -1,0 +1,170 @@
+// Dynamic fp8 (OCP e4m3) quantisation kernels for the W8A8 path (gfx950).
+//
+// Rows: per-row scale = amax / 448 (amax 0 -> 1); codes = RNE-saturating e4m3 of
+// x * (448 / amax), both factors one correctly rounded fp32 division.  The
+// gfx950 convert (v_cvt_pk_fp8_f32) rounds to nearest even and saturates.
+// Heads: one scale per contiguous slice (a (batch, head) of Q, K or V^T).
+#include "common.h"
+#include "kernels.h"
+#include "ops.h"
+
+namespace dit {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// 8 consecutive source elements -> f32
+template <class T> struct Load8;
+template <> struct Load8<bf16_t> {
+  static __device__ __forceinline__ void get(const bf16_t* p, float* v) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Load8<f16_t> {
+  static __device__ __forceinline__ void get(const f16_t* p, float* v) {
+    const f16x8 h = *(const f16x8*)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+  }
+};
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__device__ __forceinline__ void store_fp8x8(fp8_t* p, const float* v, float inv) {
+  uint2 u;
+  u.x = pack_fp8x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  u.y = pack_fp8x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  *(uint2*)p = u;
+}
+
+__device__ __forceinline__ void scale_of(float amax, float& scale, float& inv) {
+  if (amax > 0.f) {
+    scale = amax / 448.0f;
+    inv = 448.0f / amax;
+  } else {
+    scale = 1.f;
+    inv = 1.f;
+  }
+}
+
+// One wave per row; the row is read twice (amax, then quantise).
+template <class T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ src, int lds,
+                                                         fp8_t* __restrict__ dst, int ldd,
+                                                         float* __restrict__ scale, int rows,
+                                                         int width) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* s = src + (size_t)r * lds;
+  float amax = 0.f;
+  for (int c = lane * 8; c < width; c += 512) {
+    float v[8];
+    Load8<T>::get(s + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = wave_max(amax);
+  float sc, inv;
+  scale_of(amax, sc, inv);
+  fp8_t* d = dst + (size_t)r * ldd;
+  for (int c = lane * 8; c < width; c += 512) {
+    float v[8];
+    Load8<T>::get(s + c, v);
+    store_fp8x8(d + c, v, inv);
+  }
+  if (lane == 0) scale[r] = sc;
+}
+
+// amax of each contiguous slice of n elements (one slice per blockIdx.y); the
+// float bit pattern of a non-negative value orders like the value, so an
+// integer atomic max combines the blocks.  amax must be zeroed beforehand.
+template <class T>
+__global__ __launch_bounds__(256) void amax_slices_kernel(const T* __restrict__ src, size_t n,
+                                                          unsigned int* __restrict__ amax) {
+  const T* s = src + (size_t)blockIdx.y * n;
+  float m = 0.f;
+  for (size_t c = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; c < n; c += (size_t)gridDim.x * 2048) {
+    float v[8];
+    Load8<T>::get(s + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = wave_max(m);
+  __shared__ float sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    atomicMax(amax + blockIdx.y, __float_as_uint(b));
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void quant_slices_kernel(const T* __restrict__ src, size_t n,
+                                                           const unsigned int* __restrict__ amax,
+                                                           fp8_t* __restrict__ dst,
+                                                           float* __restrict__ scale) {
+  float sc, inv;
+  scale_of(__uint_as_float(amax[blockIdx.y]), sc, inv);
+  const T* s = src + (size_t)blockIdx.y * n;
+  fp8_t* d = dst + (size_t)blockIdx.y * n;
+  for (size_t c = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; c < n; c += (size_t)gridDim.x * 2048) {
+    float v[8];
+    Load8<T>::get(s + c, v);
+    store_fp8x8(d + c, v, inv);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) scale[blockIdx.y] = sc;
+}
+
+__global__ void zero_u32_kernel(unsigned int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <class T>
+hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, int rows, int width,
+                      hipStream_t st) {
+  if (width % 8 || lds % 8 || ldd % 8) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  KTimerScope timer(KS_QUANT, st);
+  hipLaunchKernelGGL(quant_rows_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, src, lds, dst,
+                     ldd, scale, rows, width);
+  return hipGetLastError();
+}
+template hipError_t quant_rows<bf16_t>(const bf16_t*, int, fp8_t*, int, float*, int, int, hipStream_t);
+template hipError_t quant_rows<f16_t>(const f16_t*, int, fp8_t*, int, float*, int, int, hipStream_t);
+
+template <class T>
+hipError_t quant_slices(const T* src, size_t n, int nslices, unsigned int* amax_tmp, fp8_t* dst,
+                        float* scale, hipStream_t st) {
+  if (n % 8) return hipErrorInvalidValue;
+  if (nslices == 0 || n == 0) return hipSuccess;
+  KTimerScope timer(KS_QUANT, st);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nslices + 255) / 256), dim3(256), 0, st, amax_tmp,
+                     nslices);
+  size_t blocks = (n / 8 + 255) / 256;
+  const int bx = (int)(blocks < 64 ? blocks : 64);
+  hipLaunchKernelGGL(amax_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax_tmp);
+  hipLaunchKernelGGL(quant_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax_tmp,
+                     dst, scale);
+  return hipGetLastError();
+}
+template hipError_t quant_slices<bf16_t>(const bf16_t*, size_t, int, unsigned int*, fp8_t*, float*,
+                                         hipStream_t);
+template hipError_t quant_slices<f16_t>(const f16_t*, size_t, int, unsigned int*, fp8_t*, float*,
+                                           hipStream_t);
+
+}  // namespace dit

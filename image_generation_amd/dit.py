@@ -35,7 +35,7 @@ class DitDims(Structure):
 
 
 class DitLinear(Structure):
-    _fields_ = [("w", c_void_p), ("b", c_void_p)]
+    _fields_ = [("w", c_void_p), ("b", c_void_p), ("w_scale", c_void_p)]
 
 
 class DitBlock(Structure):
@@ -48,7 +48,7 @@ class DitModel(Structure):
     _fields_ = [("dims", DitDims), ("n_double", c_int), ("n_single", c_int),
                 ("blocks", POINTER(DitBlock)), ("time1", DitLinear), ("time2", DitLinear),
                 ("img_in", DitLinear), ("final_out", DitLinear), ("mod", DitLinear),
-                ("C_in", c_int), ("guidance", c_float)]
+                ("C_in", c_int), ("guidance", c_float), ("dtype", c_int)]
 
 
 class DitFBCache(Structure):
@@ -67,7 +67,7 @@ class DitKernelTimer(Structure):
 
 
 SITES = ("attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1", "gemm_f32",
-         "gemm_silu", "ln", "fbc", "other")
+         "gemm_silu", "ln", "fbc", "other", "quant")
 
 
 class DitError(RuntimeError):
@@ -88,7 +88,9 @@ def _load() -> ctypes.CDLL:
         "dit_workspace_bytes": (c_size_t, [POINTER(DitDims), c_int, c_int]),
         "dit_sigmas": (c_int, [c_int, c_double, POINTER(c_double)]),
         "dit_rope_table": (c_int, [c_int, c_int, c_int, c_int, c_double, P, P]),
-        "dit_attention": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_float, P]),
+        "dit_attention": (c_int, [P, P, P, P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_float,
+                                  P]),
+        "dit_quantize_rows": (c_int, [P, c_int, c_int, c_int, c_int, P, c_int, P, P]),
         "dit_block_forward": (c_int, [POINTER(DitDims), POINTER(DitBlock), c_int, P, c_int, P,
                                       c_long, P, P, c_size_t, P]),
         "dit_modulation": (c_int, [POINTER(DitModel), POINTER(c_double), c_int, P, P, c_size_t, P]),
@@ -109,7 +111,8 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
             "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
-            "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward")
+            "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward",
+            "dit_quantize_rows")
 
 
 def _check(rc: int) -> None:
@@ -170,19 +173,54 @@ def dit_rope_table(grid_h: int, grid_w: int, Lt: int, head_dim: int, theta: floa
 
 # ------------------------------------------------------------------ entry points
 
+def _codes(t: torch.Tensor, shape, name: str) -> None:
+    """e4m3 codes: uint8 (raw bytes) or torch.float8_e4m3fn."""
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or tuple(t.shape) != tuple(shape) \
+            or not t.is_cuda:
+        raise ValueError(f"{name}: expected e4m3 codes (uint8) {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
 def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.Tensor,
-                  softmax_scale: Optional[float] = None, stream=None) -> torch.Tensor:
-    """q, k [B, H, L, d] bf16; vt [B, H, d, L] fp16; o [B, L, H*d] bf16 (written)."""
+                  softmax_scale: Optional[float] = None, q_scale: Optional[torch.Tensor] = None,
+                  k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """bf16: q, k [B, H, L, d] bf16, vt [B, H, d, L] fp16.
+    fp8: q, k, vt e4m3 codes of the same shapes, scales fp32 [B, H].
+    o [B, L, H*d] bf16 (written)."""
     B, H, L, d = q.shape
-    _need(q, torch.bfloat16, (B, H, L, d), "q")
-    _need(k, torch.bfloat16, (B, H, L, d), "k")
-    _need(vt, torch.float16, (B, H, d, L), "vt")
+    fp8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        _codes(q, (B, H, L, d), "q")
+        _codes(k, (B, H, L, d), "k")
+        _codes(vt, (B, H, d, L), "vt")
+        for n_, t_ in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+            if t_ is None:
+                raise ValueError(f"{n_} is required for fp8 attention")
+            _need(t_, torch.float32, (B, H), n_)
+    else:
+        _need(q, torch.bfloat16, (B, H, L, d), "q")
+        _need(k, torch.bfloat16, (B, H, L, d), "k")
+        _need(vt, torch.float16, (B, H, d, L), "vt")
     _need(o, torch.bfloat16, (B, L, H * d), "o")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), B, H, L, d, DIT_BF16,
+    _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(q_scale), _ptr(k_scale),
+                             _ptr(v_scale), B, H, L, d, DIT_FP8 if fp8 else DIT_BF16,
                              float(softmax_scale), _stream(stream)))
     return o
+
+
+def dit_quantize_rows(src: torch.Tensor, stream=None):
+    """Per-row e4m3 quantisation of a bf16 [rows, width] tensor -> (codes uint8, scale fp32 [rows])."""
+    if src.dim() != 2 or src.dtype != torch.bfloat16 or not src.is_cuda:
+        raise ValueError("src: bf16 [rows, width] on the GPU")
+    rows, width = src.shape
+    codes = torch.empty((rows, width), dtype=torch.uint8, device=src.device)
+    scale = torch.empty((rows,), dtype=torch.float32, device=src.device)
+    _check(LIB.dit_quantize_rows(_ptr(src), DIT_BF16, width, rows, width, _ptr(codes), width,
+                                 _ptr(scale), _stream(stream)))
+    return codes, scale
 
 
 def dit_linear_forward(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor,
@@ -197,42 +235,68 @@ def dit_linear_forward(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor,
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if tuple(out.shape) != (M, N) or out.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out: fp32 or bf16 [M, N]")
-    lin = DitLinear(_ptr(w), _ptr(b))
+    lin = DitLinear(_ptr(w), _ptr(b), None)
     yd = DIT_F32 if out.dtype == torch.float32 else DIT_BF16
     _check(LIB.dit_linear_forward(_ptr(x), M, K, ctypes.byref(lin), N, _ptr(out), yd, _stream(stream)))
     return out
 
 
-def _lin(w: torch.Tensor, b: torch.Tensor) -> DitLinear:
-    if w.dtype != torch.bfloat16 or b.dtype != torch.float32 or not (w.is_cuda and b.is_cuda):
-        raise ValueError("linear: weight bf16 and bias fp32 on the GPU")
-    return DitLinear(_ptr(w), _ptr(b))
+def _lin(w: torch.Tensor, b: torch.Tensor, w_scale: Optional[torch.Tensor] = None) -> DitLinear:
+    """bf16 layer (w_scale None) or e4m3 layer (w uint8 codes, w_scale fp32 [out])."""
+    if b.dtype != torch.float32 or not (w.is_cuda and b.is_cuda):
+        raise ValueError("linear: bias fp32, tensors on the GPU")
+    if w_scale is None:
+        if w.dtype != torch.bfloat16:
+            raise ValueError("linear: bf16 weight expected")
+    elif w.dtype not in (torch.uint8, torch.float8_e4m3fn) or w_scale.dtype != torch.float32 \
+            or tuple(w_scale.shape) != (w.shape[0],):
+        raise ValueError("linear: fp8 layer needs e4m3 codes and an fp32 scale per output")
+    return DitLinear(_ptr(w), _ptr(b), _ptr(w_scale))
+
+
+def _lin_of(p: dict, name: str) -> DitLinear:
+    return _lin(p[name + ".w"], p[name + ".b"], p.get(name + ".w_scale"))
 
 
 def make_double_block(p: dict, prefix: str = "") -> DitBlock:
-    """p: '<prefix>img.qkv.w' ... device tensors (weights bf16, biases fp32)."""
+    """p: '<prefix>img.qkv.w' ... device tensors (weights bf16, biases fp32); an fp8
+    layer also has '<name>.w_scale' and its '.w' holds the e4m3 codes."""
     blk = DitBlock()
     blk.kind = DIT_BLOCK_DOUBLE
     for i, s in enumerate(("img", "txt")):
-        blk.qkv[i] = _lin(p[f"{prefix}{s}.qkv.w"], p[f"{prefix}{s}.qkv.b"])
-        blk.proj[i] = _lin(p[f"{prefix}{s}.proj.w"], p[f"{prefix}{s}.proj.b"])
-        blk.mlp1[i] = _lin(p[f"{prefix}{s}.mlp1.w"], p[f"{prefix}{s}.mlp1.b"])
-        blk.mlp2[i] = _lin(p[f"{prefix}{s}.mlp2.w"], p[f"{prefix}{s}.mlp2.b"])
+        blk.qkv[i] = _lin_of(p, f"{prefix}{s}.qkv")
+        blk.proj[i] = _lin_of(p, f"{prefix}{s}.proj")
+        blk.mlp1[i] = _lin_of(p, f"{prefix}{s}.mlp1")
+        blk.mlp2[i] = _lin_of(p, f"{prefix}{s}.mlp2")
     return blk
 
 
 def make_single_block(p: dict, prefix: str = "") -> DitBlock:
     blk = DitBlock()
     blk.kind = DIT_BLOCK_SINGLE
-    blk.lin1 = _lin(p[f"{prefix}lin1.w"], p[f"{prefix}lin1.b"])
-    blk.lin2 = _lin(p[f"{prefix}lin2.w"], p[f"{prefix}lin2.b"])
+    blk.lin1 = _lin_of(p, f"{prefix}lin1")
+    blk.lin2 = _lin_of(p, f"{prefix}lin2")
     return blk
+
+
+def quantize_block_params(p: dict, prefix: str = "", stream=None) -> dict:
+    """Copy of p with every block linear under prefix replaced by its e4m3 codes
+    and per-output-channel scales (computed by dit_quantize_rows on the GPU)."""
+    out = dict(p)
+    for name in list(p):
+        if not name.startswith(prefix) or not name.endswith(".w") or ".mod." in name:
+            continue
+        codes, scale = dit_quantize_rows(p[name], stream)
+        out[name] = codes
+        out[name + "_scale"] = scale
+    return out
 
 
 def dit_block_forward(dims: DitDims, blk: DitBlock, x: torch.Tensor, mod: torch.Tensor,
                       rope: torch.Tensor, ws: torch.Tensor, mod_bstride: Optional[int] = None,
-                      stream=None) -> torch.Tensor:
-    """x [B, L, D] (fp32 or bf16) updated in place; mod [B or 1, k, D] fp32."""
+                      dtype: int = DIT_BF16, stream=None) -> torch.Tensor:
+    """x [B, L, D] (fp32 or bf16) updated in place; mod [B or 1, k, D] fp32.
+    dtype DIT_BF16, or DIT_FP8 for a block built from quantize_block_params()."""
     L = dims.Lt + dims.grid_h * dims.grid_w
     if tuple(x.shape) != (dims.B, L, dims.D) or x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"x: expected fp32/bf16 {(dims.B, L, dims.D)}, got {x.dtype} {tuple(x.shape)}")
@@ -242,7 +306,7 @@ def dit_block_forward(dims: DitDims, blk: DitBlock, x: torch.Tensor, mod: torch.
     if mod_bstride is None:
         mod_bstride = 0 if mod.shape[0] == 1 else nk * dims.D
     xd = DIT_F32 if x.dtype == torch.float32 else DIT_BF16
-    _check(LIB.dit_block_forward(ctypes.byref(dims), ctypes.byref(blk), DIT_BF16, _ptr(x), xd,
+    _check(LIB.dit_block_forward(ctypes.byref(dims), ctypes.byref(blk), dtype, _ptr(x), xd,
                                  _ptr(mod), int(mod_bstride), _ptr(rope), _ptr(ws), ws.numel(),
                                  _stream(stream)))
     return x
@@ -275,7 +339,7 @@ class GPUModel:
     """
 
     def __init__(self, dims, B: int, Lt: int, grid_h: int, grid_w: int, params: dict,
-                 guidance: float = 0.0, device="cuda"):
+                 guidance: float = 0.0, device="cuda", dtype: int = DIT_BF16):
         self.dims_py = dims
         D = dims.D
         self.n_double, self.n_single = dims.n_double, dims.n_single
@@ -298,6 +362,18 @@ class GPUModel:
         self.mod_b = torch.cat([self.t[n + ".b"] for n in order]).contiguous()
         self.n_mod = self.mod_w.shape[0]
         assert self.n_mod == (12 * self.n_double + 3 * self.n_single + 2) * D
+        if dtype == DIT_FP8:
+            # block linears in e4m3 with per-channel scales; the rest stays bf16
+            q = {}
+            for pre in [f"double{j}." for j in range(self.n_double)] + \
+                       [f"single{j}." for j in range(self.n_single)]:
+                q.update(quantize_block_params({n: t for n, t in self.t.items()
+                                                if n.startswith(pre)}, pre))
+            for n, t in q.items():
+                self.t[n] = t
+        elif dtype != DIT_BF16:
+            raise ValueError(f"model dtype {dtype}")
+        self.dtype = dtype
         blocks = [make_double_block(self.t, f"double{j}.") for j in range(self.n_double)]
         blocks += [make_single_block(self.t, f"single{j}.") for j in range(self.n_single)]
         self._blocks = (DitBlock * max(1, len(blocks)))(*blocks)
@@ -312,6 +388,7 @@ class GPUModel:
         m.mod = _lin(self.mod_w, self.mod_b)
         m.C_in = dims.C_in
         m.guidance = float(guidance)
+        m.dtype = dtype
         self.model = m
 
 

@@ -91,10 +91,15 @@ typedef struct dit_dims {
   int B, Lt, grid_h, grid_w, D, H, F;
 } dit_dims;
 
-/* One linear layer on the device: w [out, in] (bf16), b fp32 [out]. */
+/* One linear layer on the device: w [out, in], b fp32 [out].
+ *   bf16 layers: w bf16, w_scale NULL.
+ *   fp8 layers (DIT_FP8 blocks): w OCP e4m3 and w_scale fp32 [out], the
+ *   per-output-channel scale (weight = code * w_scale[n]), as produced by
+ *   dit_quantize_rows() on the bf16 weight. */
 typedef struct dit_linear {
   const void* w;
   const float* b;
+  const float* w_scale;
 } dit_linear;
 
 /* A transformer block.
@@ -125,6 +130,10 @@ typedef struct dit_model {
   dit_linear mod;        /* [N_mod, D] */
   int C_in;              /* patch features, <= 64 */
   float guidance;        /* CFG scale (B == 2) */
+  int dtype;             /* DIT_BF16, or DIT_FP8: the blocks' linears and attention run
+                            in e4m3 with dynamic per-token activation scales; the
+                            modulation, embedders, timestep MLP and velocity head stay
+                            bf16 */
 } dit_model;
 
 /* Caller-held First-Block-Cache state; resuming a loop = passing it back. */
@@ -183,6 +192,7 @@ DIT_API int dit_rope_table(int grid_h, int grid_w, int Lt, int head_dim, double 
 #define DIT_SITE_LN 7           /* LayerNorm + modulate                         */
 #define DIT_SITE_FBC 8          /* First-Block-Cache reduction                  */
 #define DIT_SITE_OTHER 9        /* embeddings, cache apply/commit, Euler, RoPE  */
+#define DIT_SITE_QUANT 10       /* fp8 activation quantisation passes           */
 typedef struct dit_kernel_timer {
   unsigned site_mask;
   int capacity;
@@ -203,13 +213,30 @@ DIT_API int dit_linear_forward(const void* x, int M, int K, const dit_linear* li
                        int y_dtype, void* stream);
 
 /* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V.
- *   q, k: device bf16 [B, H, L, 128]; vt: device fp16 [B, H, 128, L] (V
- *   transposed per head, in fp16: the P V product runs on fp16 MFMAs); o:
- *   device bf16 [B, L, H * 128] (token-major).  Softmax statistics and both
- *   products accumulate in fp32.  L % 8 == 0, L >= 8; dtype must be DIT_BF16
- *   (the dtype of q, k and o).  Workspace: none. */
-DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o, int B, int H, int L,
-                  int head_dim, int dtype, float softmax_scale, void* stream);
+ *   dtype DIT_BF16: q, k device bf16 [B, H, L, 128]; vt device fp16
+ *     [B, H, 128, L] (V transposed per head, fp16: the P V product runs on fp16
+ *     MFMAs); scales NULL; L % 8 == 0, L >= 8.
+ *   dtype DIT_FP8: q, k e4m3 [B, H, L, 128], vt e4m3 [B, H, 128, L], each with
+ *     one fp32 scale per (b, h) in q_scale / k_scale / v_scale [B * H] (value =
+ *     code * scale); P is quantised as e4m3(448 P) against the exact running
+ *     max, the row sum uses the unquantised P; L % 16 == 0, L >= 16.
+ *   o: device bf16 [B, L, H * 128] (token-major).  Softmax statistics and both
+ *   products accumulate in fp32.  Workspace: none. */
+DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          int B, int H, int L, int head_dim, int dtype, float softmax_scale,
+                          void* stream);
+
+/* Dynamic per-row e4m3 quantisation (the W8A8 recipe): for each row r,
+ *   scale[r] = amax_r / 448 (1 if the row is all zero),
+ *   dst[r, c] = e4m3 code of src[r, c] * (448 / amax_r), round to nearest even,
+ *   saturating; both factors are single correctly rounded fp32 divisions.
+ *   src: device [rows, width], row stride src_ld elements, src_dtype DIT_BF16;
+ *   dst: device e4m3 [rows, width], row stride dst_ld; scale: device fp32 [rows].
+ *   width, src_ld, dst_ld multiples of 8.  Used offline for fp8 weights (one
+ *   scale per output channel) and by the fp8 blocks for their activations. */
+DIT_API int dit_quantize_rows(const void* src, int src_dtype, int src_ld, int rows, int width,
+                              void* dst, int dst_ld, float* scale, void* stream);
 
 /* One transformer block, in place on the joint residual stream.
  *   x: device [B, Lt + Li, D], dtype x_dtype (DIT_F32 or DIT_BF16), updated;
@@ -219,7 +246,9 @@ DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
  *        (mod_bstride = 0 shares them): double block 12 D-vectors (image
  *        shift1, scale1, gate1, shift2, scale2, gate2, then text), single 3.
  *   rope: device table from dit_rope_table() for these dims.
- *   dtype: compute dtype, DIT_BF16.  workspace >= DIT_WS_BLOCK bytes. */
+ *   dtype: DIT_BF16, or DIT_FP8 (e4m3 linears with w_scale set, per-token
+ *   activation scales, e4m3 attention with per-(b, h) scales).
+ *   workspace >= DIT_WS_BLOCK bytes. */
 DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,
                       size_t ws_bytes, void* stream);

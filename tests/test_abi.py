@@ -71,17 +71,31 @@ def test_invalid_arguments_rejected_before_launch():
     L = dit.LIB
     P = ctypes.c_void_p
     # NULL pointers
-    rc = L.dit_attention(None, None, None, None, 1, 1, 64, 128, dit.DIT_BF16, 0.1, None)
+    N = None
+    rc = L.dit_attention(N, N, N, N, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
     # ragged L (not a multiple of 8) with fake aligned pointers: rejected before any launch
     fake = P(4096)
-    rc = L.dit_attention(fake, fake, fake, fake, 1, 1, 63, 128, dit.DIT_BF16, 0.1, None)
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 63, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
-    rc = L.dit_attention(fake, fake, fake, fake, 1, 1, 64, 128, dit.DIT_BF16, math.nan, None)
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, math.nan, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
     # misaligned pointer
-    rc = L.dit_attention(P(4098), fake, fake, fake, 1, 1, 64, 128, dit.DIT_BF16, 0.1, None)
+    rc = L.dit_attention(P(4098), fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
+    # fp8: scales required, L a multiple of 16
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_FP8, 0.1, N)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_attention(fake, fake, fake, fake, fake, fake, fake, 1, 1, 72, 128, dit.DIT_FP8,
+                         0.1, N)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # row quantisation: width not a multiple of 8, stride below width, unsupported source
+    rc = L.dit_quantize_rows(fake, dit.DIT_BF16, 12, 4, 12, fake, 16, fake, N)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_quantize_rows(fake, dit.DIT_BF16, 8, 4, 16, fake, 16, fake, N)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_quantize_rows(fake, dit.DIT_F32, 16, 4, 16, fake, 16, fake, N)
+    assert rc == dit.DIT_ERR_UNSUPPORTED
     # fbcache: NaN threshold, short workspace
     rel, skip = ctypes.c_double(), ctypes.c_int()
     rc = L.fbcache_should_skip(fake, fake, fake, fake, 1, 0, 8, 64, math.nan, 1, fake, 1 << 20,
@@ -97,6 +111,23 @@ def test_invalid_arguments_rejected_before_launch():
     rc = L.dit_block_forward(ctypes.byref(d), ctypes.byref(blk), dit.DIT_BF16, fake, dit.DIT_F32,
                              fake, 0, fake, fake, 1 << 30, None)
     assert rc == dit.DIT_ERR_INVALID_ARG
+    # fp8 block whose linears carry no weight scales
+    lin = dit.DitLinear(4096, 4096, None)
+    blk = dit.DitBlock()
+    blk.kind = dit.DIT_BLOCK_SINGLE
+    blk.lin1 = lin
+    blk.lin2 = lin
+    d16 = dit.dims_of(1, 8, 2, 4, 256, 2, 512)
+    rc = L.dit_block_forward(ctypes.byref(d16), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
+                             fake, 0, fake, fake, 1 << 30, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    # fp8 needs the joint length to be a multiple of 16 (8 + 8*2 = 24 is not)
+    d24 = dit.dims_of(1, 8, 2, 8, 256, 2, 512)
+    blk.lin1 = dit.DitLinear(4096, 4096, 4096)
+    blk.lin2 = blk.lin1
+    rc = L.dit_block_forward(ctypes.byref(d24), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
+                             fake, 0, fake, fake, 1 << 30, None)
+    assert rc == dit.DIT_ERR_UNSUPPORTED
     # token counts that are not multiples of 8
     d = dit.dims_of(1, 7, 2, 4, 256, 2, 512)
     assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
