@@ -14,6 +14,11 @@ so no step skips work; the run at the workload's own threshold is reported
 beside it under ``fbcache``.  Per-kernel durations come from HIP events the
 library records around its own launches on the launch stream.
 
+Beside the 1024px line the same JSON carries the 2048px figures: one bf16
+double block of the 2048px CFG-pair shape (16384 + 512 tokens, batch 2:
+attention and GEMM TFLOP/s) and a few steps of the fp8 W8A8 model at 2048px
+(batch 2, CFG 3.5), whose TFLOP/s are taken against the fp8 peak.
+
 Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -28,8 +33,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X published dense fp8 MFMA peak
 PEAK_HBM_GBS = 8000.0
+METRIC = "DiT denoise steps/s at 1024px & 2048px; attention+GEMM TFLOP/s, % MFMA peak"
+ALL_SITES = ["attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1", "gemm_f32",
+             "gemm_silu", "ln", "fbc", "other", "quant"]
+BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 
 
 def log(msg):
@@ -56,16 +66,110 @@ def lin1_flops(B, L, D, F):
     return 2.0 * B * L * D * (3 * D + F)
 
 
-def build_model(dit, DI, w, device):
+def build_model(dit, DI, w, device, dtype=None):
     import torch
     dims = w.dims
     params = {}
     for k, (name, shape) in enumerate(DI.param_specs(dims)):
         params[name] = DI.device_randn(shape, DI.SEED_PARAM_BASE + k, DI.WEIGHT_STD, device)
-    gm = dit.GPUModel(dims, w.B, w.Lt, w.grid_h, w.grid_w, params, guidance=w.guidance)
+    gm = dit.GPUModel(dims, w.B, w.Lt, w.grid_h, w.grid_w, params, guidance=w.guidance,
+                      dtype=dit.DIT_BF16 if dtype is None else dtype)
     del params
     torch.cuda.empty_cache()
     return gm
+
+
+def site_totals(rec):
+    by_site = {}
+    for s_, ms in rec:
+        t = by_site.setdefault(s_, [0, 0.0])
+        t[0] += 1
+        t[1] += ms
+    return by_site
+
+
+def kernel_table(by_site):
+    return {s_: {"launches": n, "total_ms": round(ms, 3), "avg_us": round(1e3 * ms / max(n, 1), 2)}
+            for s_, (n, ms) in sorted(by_site.items())}
+
+
+def block_2048_bf16(dit, DI, device, reps=3):
+    """One bf16 double block at the 2048px CFG-pair shape: attention and GEMM rates."""
+    import torch
+    w = DI.WORKLOADS["block_2048_cfg"]
+    dims = w.dims
+    p = {}
+    for k, (name, shape) in enumerate(DI.double_block_specs(dims, "blk")):
+        t = DI.device_randn(shape, DI.SEED_PARAM_BASE + k, DI.WEIGHT_STD, device)
+        p[name[4:]] = t if name.endswith(".w") else t.float()
+    blk = dit.make_double_block(p)
+    dd = dit.dims_of(w.B, w.Lt, w.grid_h, w.grid_w, dims.D, dims.H, dims.F)
+    rope = dit.dit_rope_table(w.grid_h, w.grid_w, w.Lt, dims.d)
+    ws = dit.workspace(dd, dit.DIT_WS_BLOCK)
+    x = DI.device_randn((w.B, w.L, dims.D), DI.SEED_ACT, 1.0, device, torch.float32)
+    mod = DI.device_randn((w.B, 12, dims.D), DI.SEED_MOD, DI.MOD_STD, device, torch.float32)
+    dit.dit_block_forward(dd, blk, x, mod, rope, ws)            # warmup
+    timer = dit.KernelTimer(ALL_SITES, capacity=64 * reps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with timer:
+        for _ in range(reps):
+            dit.dit_block_forward(dd, blk, x, mod, rope, ws)
+    torch.cuda.synchronize()
+    secs = (time.perf_counter() - t0) / reps
+    by = site_totals(timer.durations_ms())
+    timer.close()
+    L = w.L
+    att_f = attn_flops_per_launch(w.B, dims.H, L, dims.d)
+    gemm_f = 2.0 * w.B * L * dims.D * (3 * dims.D + dims.D + 2 * dims.F)
+    att_ms = by.get("attention", [0, 0.0])[1] / reps
+    gemm_ms = sum(by.get(s_, [0, 0.0])[1] for s_ in BLOCK_GEMM_SITES) / reps
+    return {"workload": w.name, "tokens": [w.Lt, w.Li], "batch": w.B, "dtype": "bf16",
+            "ms_per_block": round(secs * 1e3, 3),
+            "attention_us": round(att_ms * 1e3, 1),
+            "attention_tflops": round(att_f / (att_ms * 1e-3) / 1e12, 1),
+            "attention_frac_peak": round(att_f / (att_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_peak": round(gemm_f / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": kernel_table(by)}
+
+
+def loop_2048_fp8(dit, DI, device, K, warmup):
+    """K steps of the fp8 W8A8 model at 2048px (CFG pair), FBC threshold 0."""
+    import torch
+    w = DI.WORKLOADS["flux_2048_fp8_cfg"]
+    dims = w.dims
+    log(f"[bench] building {w.name} (fp8)")
+    gm = build_model(dit, DI, w, device, dit.DIT_FP8)
+    txt = DI.device_randn((w.B, w.Lt, dims.D), DI.SEED_TEXT, 1.0, device)
+    lat0 = DI.device_randn((w.Li, dims.C_in), DI.SEED_LATENTS, 1.0, device, torch.float32)
+    sig = dit.dit_sigmas(w.steps, w.shift)
+    ws = dit.workspace(gm.model.dims, dit.DIT_WS_STEP)
+    if warmup:
+        run_loop(dit, gm, sig, txt, lat0, ws, 0.0, warmup)
+    timer = dit.KernelTimer(ALL_SITES, capacity=40 * (dims.n_double + dims.n_single) * K + 256)
+    log(f"[bench] fp8 timed: {K} steps")
+    secs, skipped, _ = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
+    by = site_totals(timer.durations_ms())
+    timer.close()
+    del gm, ws
+    torch.cuda.empty_cache()
+    B, L, Li = w.B, w.L, w.Li
+    att_n, att_ms = by.get("attention", [0, 0.0])
+    att_f = attn_flops_per_launch(B, dims.H, L, dims.d)
+    gemm_f = (gemm_flops_per_step(dims, B, w.Lt, Li, dims.C_in) - 2.0 * B * Li * dims.D * dims.C_in) * K
+    gemm_ms = sum(by.get(s_, [0, 0.0])[1] for s_ in BLOCK_GEMM_SITES)
+    att_tf = att_f * att_n / (att_ms * 1e-3) / 1e12
+    gemm_tf = gemm_f / (gemm_ms * 1e-3) / 1e12
+    return {"workload": w.name, "image_px": w.image_px, "tokens": [w.Lt, Li], "batch": B,
+            "guidance": w.guidance, "dtype": "fp8 e4m3 (W8A8)", "steps": K, "warmup": warmup,
+            "steps_per_s": round(K / secs, 4), "ms_per_step": round(1e3 * secs / K, 2),
+            "attention_tflops": round(att_tf, 1),
+            "attention_frac_fp8_peak": round(att_tf / PEAK_FP8_TFLOPS, 4),
+            "block_gemm_tflops": round(gemm_tf, 1),
+            "block_gemm_frac_fp8_peak": round(gemm_tf / PEAK_FP8_TFLOPS, 4),
+            "quant_ms_per_step": round(by.get("quant", [0, 0.0])[1] / K, 3),
+            "kernels": kernel_table(by)}
 
 
 def run_loop(dit, gm, sig, txt, lat0, ws, threshold, K, timer=None):
@@ -128,6 +232,8 @@ def main():
     ap.add_argument("--workload", default="flux_1024_28step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fbcache-run", action="store_true")
+    ap.add_argument("--no-2048", action="store_true", help="skip the 2048px block and fp8 loop")
+    ap.add_argument("--fp8-steps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -163,31 +269,22 @@ def main():
     # timed region: K steps, threshold 0 (every block runs), kernel timers on
     K = args.steps
     per_step_sites = 8 * (dims.n_double + dims.n_single) + 16
-    timer = dit.KernelTimer(["attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1",
-                             "gemm_f32", "gemm_silu", "ln", "fbc", "other"],
-                            capacity=per_step_sites * K + 64)
+    timer = dit.KernelTimer(ALL_SITES, capacity=per_step_sites * K + 64)
     log(f"[bench] timed: {K} steps, FBC threshold 0")
     secs, skipped, rels = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
     assert skipped == 0
-    rec = timer.durations_ms()
+    by_site = site_totals(timer.durations_ms())
     timer.close()
-    by_site = {}
-    for s, ms in rec:
-        t = by_site.setdefault(s, [0, 0.0])
-        t[0] += 1
-        t[1] += ms
 
     B, L, Li = w.B, w.L, w.Li
     steps_per_s = K / secs
     attn_f = attn_flops_per_launch(B, dims.H, L, dims.d)
     gemm_f = gemm_flops_per_step(dims, B, w.Lt, Li, dims.C_in) * K
-    gemm_sites = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
-    gemm_ms = sum(by_site.get(s, [0, 0.0])[1] for s in gemm_sites)
+    gemm_ms = sum(by_site.get(s, [0, 0.0])[1] for s in BLOCK_GEMM_SITES)
     final_gemm = 2.0 * B * Li * dims.D * dims.C_in * K
     attn_n, attn_ms = by_site.get("attention", [0, 0.0])
     lin1_n, lin1_ms = by_site.get("gemm_lin1", [0, 0.0])
-    kernels = {s: {"launches": n, "total_ms": round(ms, 3), "avg_us": round(1e3 * ms / max(n, 1), 2)}
-               for s, (n, ms) in sorted(by_site.items())}
+    kernels = kernel_table(by_site)
     attn_tflops = attn_f * attn_n / (attn_ms * 1e-3) / 1e12 if attn_ms else None
     block_gemm_tflops = (gemm_f - final_gemm) / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
     lin1_avg_s = lin1_ms * 1e-3 / max(lin1_n, 1)
@@ -206,7 +303,7 @@ def main():
                 "flops_per_launch": dom_flops, "avg_launch_us": round(dom_avg * 1e6, 2)}
 
     out = {
-        "metric": "DiT denoise steps/s at 1024px",
+        "metric": METRIC,
         "value": round(steps_per_s, 4),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -241,6 +338,11 @@ def main():
                                      for r in rels_c]}
     del gm, ws
     torch.cuda.empty_cache()
+    if not args.no_2048:
+        log("[bench] 2048px bf16 block")
+        out["block_2048px_bf16"] = block_2048_bf16(dit, DI, device)
+        torch.cuda.empty_cache()
+        out["loop_2048px_fp8"] = loop_2048_fp8(dit, DI, device, args.fp8_steps, 1)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(DI, w)
