@@ -234,6 +234,8 @@ def main():
     ap.add_argument("--no-fbcache-run", action="store_true")
     ap.add_argument("--no-2048", action="store_true", help="skip the 2048px block and fp8 loop")
     ap.add_argument("--fp8-steps", type=int, default=3)
+    ap.add_argument("--only-2048", action="store_true",
+                    help="run only the 2048px block and fp8 loop (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -252,6 +254,12 @@ def main():
         raise SystemExit(f"--steps {args.steps} exceeds the workload's {w.steps} steps")
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.only_2048:
+        out = {"block_2048px_bf16": block_2048_bf16(dit, DI, device)}
+        torch.cuda.empty_cache()
+        out["loop_2048px_fp8"] = loop_2048_fp8(dit, DI, device, args.fp8_steps, 1)
+        print(json.dumps(out), flush=True)
+        return
 
     log(f"[bench] building {w.name}: {dims.n_double}+{dims.n_single} blocks, B={w.B}, "
         f"tokens {w.Lt}+{w.Li}")
