@@ -466,6 +466,92 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   }
 }
 
+// ---------------------------------------------------------------- fp32
+// Reference-precision attention for small models (head dim 32 or 64): one wave
+// per 64 queries of one (b, h), one query per lane, 64-key K and V^T tiles in LDS
+// (every lane reads the same key, so the LDS reads broadcast); online softmax in
+// exp2 units with the scale folded into q.
+template <int HD>
+__global__ __launch_bounds__(64) void attention_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ VT,
+    float* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
+  __shared__ float sK[64][HD];
+  __shared__ float sV[HD][65];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int t = blockIdx.x * 64 + lane;
+  const int tq = min(t, L - 1);
+  const float* Kb = K + (size_t)bh * L * HD;
+  const float* Vb = VT + (size_t)bh * HD * L;
+  float q[HD], acc[HD];
+#pragma unroll
+  for (int c = 0; c < HD; ++c) {
+    q[c] = Q[((size_t)bh * L + tq) * HD + c] * scale_log2;
+    acc[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int k0 = 0; k0 < L; k0 += 64) {
+    const int kr = k0 + lane;
+#pragma unroll
+    for (int c = 0; c < HD; ++c) {
+      sK[lane][c] = kr < L ? Kb[(size_t)kr * HD + c] : 0.f;
+      sV[c][lane] = kr < L ? Vb[(size_t)c * L + kr] : 0.f;
+    }
+    __syncthreads();
+    const int nk = min(64, L - k0);
+    for (int j0 = 0; j0 < nk; j0 += 16) {     // 16 keys per softmax update
+      float sc[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < HD; ++c) d = fmaf(q[c], sK[j0 + j][c], d);
+        sc[j] = j0 + j < nk ? d : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      const float mnew = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int c = 0; c < HD; ++c) acc[c] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pj = fast_exp2(sc[j] - mnew);
+        l += pj;
+#pragma unroll
+        for (int c = 0; c < HD; ++c) acc[c] = fmaf(pj, sV[c][j0 + j], acc[c]);
+      }
+      m = mnew;
+    }
+    __syncthreads();
+  }
+  if (t < L) {
+    float* orow = O + (size_t)map.stream_row(b, t) * ldo + h * HD;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int c = 0; c < HD; ++c) orow[c] = acc[c] * inv;
+  }
+}
+
+hipError_t attention_f32(const float* q, const float* k, const float* vt, float* o, int ldo,
+                         const RowMap& map, int B, int H, int L, int d, float softmax_scale,
+                         hipStream_t st) {
+  if ((d != 32 && d != 64) || L < 1) return hipErrorInvalidValue;
+  if (B * H == 0) return hipSuccess;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  KTimerScope timer(KS_ATTENTION, st);
+  const dim3 grid((L + 63) / 64, B * H);
+  if (d == 64)
+    hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
+                       L, scale_log2);
+  else
+    hipLaunchKernelGGL(attention_f32_kernel<32>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
+                       L, scale_log2);
+  return hipGetLastError();
+}
+
 hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, const float* sq,
                          const float* sk, const float* sv, bf16_t* o, int ldo, const RowMap& map,
                          int B, int H, int L, int d, float softmax_scale, hipStream_t st) {

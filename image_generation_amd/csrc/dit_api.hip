@@ -86,11 +86,17 @@ int make_dims(const dit_dims* in, Dims* o) {
 }
 
 int check_block_dims(const Dims& dm, int dtype) {
-  if (dtype != DIT_BF16 && dtype != DIT_FP8)
-    return fail(DIT_ERR_UNSUPPORTED, "block dtype %d (DIT_BF16 or DIT_FP8)", dtype);
-  if (dm.d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d (this build runs 128)", dm.d);
+  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32)
+    return fail(DIT_ERR_UNSUPPORTED, "block dtype %d", dtype);
   if (dm.D % 256 || dm.D > 3072)
     return fail(DIT_ERR_UNSUPPORTED, "hidden size %d (needs a multiple of 256, <= 3072)", dm.D);
+  if (dtype == DIT_F32) {
+    if (dm.d != 32 && dm.d != 64)
+      return fail(DIT_ERR_UNSUPPORTED, "fp32 blocks: head dim %d (32 or 64)", dm.d);
+    if (dm.F % 4) return fail(DIT_ERR_UNSUPPORTED, "fp32 blocks: MLP size %d (multiple of 4)", dm.F);
+    return DIT_OK;
+  }
+  if (dm.d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d (bf16/fp8 run 128)", dm.d);
   if (dm.F % 64) return fail(DIT_ERR_UNSUPPORTED, "MLP size %d (needs a multiple of 64)", dm.F);
   if (dtype == DIT_FP8) {
     // e4m3 K slabs are 128 deep; fp8 attention tiles keys by 16
@@ -129,6 +135,8 @@ struct BlockWS {
   float *su, *s_att, *s_hid;
   float* s_qkv;          // [3, B*H]: q, k, v scales per (b, h)
   unsigned int* amax;    // [B*H] reduction scratch
+  // fp32 blocks (overlaying the buffers above): LN out, Q, K, V^T, attention | MLP
+  float *u32, *q32, *k32, *vt32, *cat32;
 };
 
 BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
@@ -137,6 +145,7 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   const size_t bh = (size_t)dm.B * dm.H;
   BlockWS w;
   w.xf = with_xf ? c.take<float>(n) : nullptr;
+  Carver c32 = c;   // the fp32 layout reuses the space of the bf16 / fp8 one
   w.u = c.take<bf16_t>(n);
   w.q = c.take<bf16_t>(n);
   w.k = c.take<bf16_t>(n);
@@ -152,6 +161,12 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.s_hid = c.take<float>(rows);
   w.s_qkv = c.take<float>(3 * bh);
   w.amax = c.take<unsigned int>(bh);
+  w.u32 = c32.take<float>(n);
+  w.q32 = c32.take<float>(n);
+  w.k32 = c32.take<float>(n);
+  w.vt32 = c32.take<float>(n);
+  w.cat32 = c32.take<float>(rows * (dm.D + dm.F));
+  if (c32.off > c.off) c.off = c32.off;
   return w;
 }
 
@@ -180,16 +195,16 @@ StepWS carve_step(Carver& c, const Dims& dm) {
 }
 
 struct ModWS {
-  bf16_t* emb;  // [n, 256]
-  bf16_t* h;    // [n, D]
-  bf16_t* cs;   // [n, D]
+  void* emb;  // [n, 256]  (bf16, or fp32 for an fp32 model)
+  void* h;    // [n, D]
+  void* cs;   // [n, D]
 };
 
 ModWS carve_mod(Carver& c, const Dims& dm, int n) {
-  ModWS w;
-  w.emb = c.take<bf16_t>((size_t)n * 256);
-  w.h = c.take<bf16_t>((size_t)n * dm.D);
-  w.cs = c.take<bf16_t>((size_t)n * dm.D);
+  ModWS w;   // sized for fp32 elements, so either element type fits
+  w.emb = c.take<float>((size_t)n * 256);
+  w.h = c.take<float>((size_t)n * dm.D);
+  w.cs = c.take<float>((size_t)n * dm.D);
   return w;
 }
 
@@ -261,6 +276,69 @@ GemmProblem gp8(const fp8_t* A8, int lda, const float* sa, const dit_linear& l, 
   g.sa = sa;
   g.sw = l.w_scale;
   return g;
+}
+
+// fp32 problem: A32 [M, K] (row stride lda), fp32 weight [N, K]
+GemmProblem gp32(const float* A, int lda, const dit_linear& l, int K, int M, int N) {
+  GemmProblem g = gp(nullptr, lda, l, K, M, N);
+  g.W = nullptr;
+  g.A32 = A;
+  g.W32 = (const float*)l.w;
+  return g;
+}
+
+// fp32 block (reference precision): the same sequence as block_impl on fp32 buffers
+hipError_t block_f32(const Dims& dm, const dit_block& blk, float* x, const float* mod, int bs,
+                     const float* rope, const BlockWS& w, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
+  const int DF = D + F;
+  const QKVOut32 qo{w.q32, w.k32, w.vt32, rope, D, dm.H, dm.d};
+  const float scale = 1.0f / sqrtf((float)dm.d);
+  hipError_t e;
+  if (blk.kind == DIT_BLOCK_DOUBLE) {
+    const RowMap sm{B, Lt, Li, L, 1, 0};
+    RowMap st_txt = sm;
+    st_txt.base = B * Li;
+    const RowMap maps[2] = {sm, st_txt};
+    const int ng = (B * Lt > 0) ? 2 : 1;
+    const float* mi = mod;
+    const float* mt = mod + 6 * (size_t)D;
+    const size_t ti = (size_t)B * Li;
+    float* u = w.u32;
+    float* cat = w.cat32;
+    if ((e = ln_modulate<float>(x, u, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs, st))) return e;
+    GemmProblem g[2] = {gp32(u, D, blk.qkv[0], D, B * Li, 3 * D),
+                        gp32(u + ti * D, D, blk.qkv[1], D, B * Lt, 3 * D)};
+    if ((e = gemm32_qkv(g, ng, qo, maps, st))) return e;
+    if ((e = attention_f32(w.q32, w.k32, w.vt32, cat, DF, sm, B, dm.H, L, dm.d, scale, st)))
+      return e;
+    g[0] = gp32(cat, DF, blk.proj[0], D, B * Li, D);
+    g[1] = gp32(cat + ti * DF, DF, blk.proj[1], D, B * Lt, D);
+    const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
+    if ((e = gemm32_gated_residual(g, ng, x, D, gate1, bs, maps, st))) return e;
+    if ((e = ln_modulate<float>(x, u, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D, mt + 3 * D,
+                                mt + 4 * D, bs, st)))
+      return e;
+    g[0] = gp32(u, D, blk.mlp1[0], D, B * Li, F);
+    g[1] = gp32(u + ti * D, D, blk.mlp1[1], D, B * Lt, F);
+    float* hid[2] = {cat + D, cat + ti * DF + D};
+    const int ldh[2] = {DF, DF};
+    if ((e = gemm32_gelu(g, ng, hid, ldh, st))) return e;
+    g[0] = gp32(cat + D, DF, blk.mlp2[0], F, B * Li, D);
+    g[1] = gp32(cat + ti * DF + D, DF, blk.mlp2[1], F, B * Lt, D);
+    const float* gate2[2] = {mi + 5 * D, mt + 5 * D};
+    return gemm32_gated_residual(g, ng, x, D, gate2, bs, maps, st);
+  }
+  const RowMap jm{B, Lt, Li, L, 0, 0};
+  if ((e = ln_modulate<float>(x, w.u32, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st)))
+    return e;
+  const GemmProblem g1 = gp32(w.u32, D, blk.lin1, D, B * L, 3 * D + F);
+  if ((e = gemm32_linear1(g1, qo, jm, w.cat32, DF, st))) return e;
+  if ((e = attention_f32(w.q32, w.k32, w.vt32, w.cat32, DF, jm, B, dm.H, L, dm.d, scale, st)))
+    return e;
+  const GemmProblem g2 = gp32(w.cat32, DF, blk.lin2, DF, B * L, D);
+  const float* gate[1] = {mod + 2 * D};
+  return gemm32_gated_residual(&g2, 1, x, D, gate, bs, &jm, st);
 }
 
 // per-(b, h) e4m3 copies of the QKV epilogue's Q, K (bf16) and V^T (fp16)
@@ -393,6 +471,7 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
 hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
                      int bs, const float* rope, const BlockWS& w, hipStream_t st) {
   if (dtype == DIT_FP8) return block_fp8(dm, blk, x, mod, bs, rope, w, st);
+  if (dtype == DIT_F32) return block_f32(dm, blk, x, mod, bs, rope, w, st);
   return block_impl<float>(dm, blk, x, mod, bs, rope, w, st);
 }
 
@@ -496,15 +575,16 @@ int dit_attention(const void* q, const void* k, const void* vt, void* o, const f
   if (!q || !k || !vt || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: pointers must be 16-byte aligned");
-  if (dtype != DIT_BF16 && dtype != DIT_FP8)
+  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32)
     return fail(DIT_ERR_UNSUPPORTED, "dit_attention: dtype %d", dtype);
-  const int lmul = dtype == DIT_FP8 ? 16 : 8;
+  const int lmul = dtype == DIT_FP8 ? 16 : dtype == DIT_F32 ? 1 : 8;
   if (B < 1 || H < 1 || L < lmul || L % lmul)
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H >= 1 and L a positive multiple of %d",
                 lmul);
   if (dtype == DIT_FP8 && (!q_scale || !k_scale || !v_scale))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: fp8 needs q, k and v scales");
-  if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "dit_attention: head_dim %d", head_dim);
+  if (dtype == DIT_F32 ? (head_dim != 32 && head_dim != 64) : head_dim != 128)
+    return fail(DIT_ERR_UNSUPPORTED, "dit_attention: head_dim %d for dtype %d", head_dim, dtype);
   if (!std::isfinite(softmax_scale))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: softmax_scale must be finite");
   if ((long long)B * H * L * head_dim > (1LL << 40) || (long long)B * L > (1LL << 31) - 1)
@@ -512,7 +592,11 @@ int dit_attention(const void* q, const void* k, const void* vt, void* o, const f
   int rc = check_device();
   if (rc) return rc;
   const RowMap jm{B, 0, L, L, 0, 0};
-  if (dtype == DIT_FP8)
+  if (dtype == DIT_F32)
+    DIT_CHECK_HIP(attention_f32((const float*)q, (const float*)k, (const float*)vt, (float*)o,
+                                H * head_dim, jm, B, H, L, head_dim, softmax_scale,
+                                (hipStream_t)stream));
+  else if (dtype == DIT_FP8)
     DIT_CHECK_HIP(attention_fp8((const fp8_t*)q, (const fp8_t*)k, (const fp8_t*)vt, q_scale,
                                 k_scale, v_scale, (bf16_t*)o, H * head_dim, jm, B, H, L, head_dim,
                                 softmax_scale, (hipStream_t)stream));
@@ -601,14 +685,25 @@ int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* 
     return fail(DIT_ERR_WORKSPACE, "dit_modulation: workspace %zu < %zu bytes", ws_bytes, need);
   const long long nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm.D;
   if (nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: too many vectors");
+  if (m->dtype != DIT_BF16 && m->dtype != DIT_FP8 && m->dtype != DIT_F32)
+    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: model dtype %d", m->dtype);
   if ((rc = check_device())) return rc;
   hipStream_t st = (hipStream_t)stream;
   Carver c{(char*)workspace, 0};
   const ModWS w = carve_mod(c, dm, n);
-  DIT_CHECK_HIP(sinusoid_host(sigmas_host, w.emb, n, 128, st));
-  DIT_CHECK_HIP(gemm_silu_bf16(gp(w.emb, 256, m->time1, 256, n, dm.D), w.h, dm.D, st));
-  DIT_CHECK_HIP(gemm_silu_bf16(gp(w.h, dm.D, m->time2, dm.D, n, dm.D), w.cs, dm.D, st));
-  DIT_CHECK_HIP(gemm_store_f32(gp(w.cs, dm.D, m->mod, dm.D, n, (int)nmod), out, (int)nmod, st));
+  if (m->dtype == DIT_F32) {
+    float *emb = (float*)w.emb, *h = (float*)w.h, *cs = (float*)w.cs;
+    DIT_CHECK_HIP(sinusoid_host(sigmas_host, emb, n, 128, st));
+    DIT_CHECK_HIP(gemm32_silu(gp32(emb, 256, m->time1, 256, n, dm.D), h, dm.D, st));
+    DIT_CHECK_HIP(gemm32_silu(gp32(h, dm.D, m->time2, dm.D, n, dm.D), cs, dm.D, st));
+    DIT_CHECK_HIP(gemm32_store(gp32(cs, dm.D, m->mod, dm.D, n, (int)nmod), out, (int)nmod, st));
+    return DIT_OK;
+  }
+  bf16_t *emb = (bf16_t*)w.emb, *h = (bf16_t*)w.h, *cs = (bf16_t*)w.cs;
+  DIT_CHECK_HIP(sinusoid_host(sigmas_host, emb, n, 128, st));
+  DIT_CHECK_HIP(gemm_silu_bf16(gp(emb, 256, m->time1, 256, n, dm.D), h, dm.D, st));
+  DIT_CHECK_HIP(gemm_silu_bf16(gp(h, dm.D, m->time2, dm.D, n, dm.D), cs, dm.D, st));
+  DIT_CHECK_HIP(gemm_store_f32(gp(cs, dm.D, m->mod, dm.D, n, (int)nmod), out, (int)nmod, st));
   return DIT_OK;
 }
 
@@ -696,9 +791,15 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   const size_t D12 = 12 * (size_t)D, D3 = 3 * (size_t)D;
 
   DIT_CHECK_HIP(rope_table(w.rope, dm.gw, Lt, dm.L, dm.d, 10000.0, st));
-  if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st));
-  DIT_CHECK_HIP(embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before, B,
-                              Lt, Li, D, m->C_in, st));
+  if (dt == DIT_F32) {
+    if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const float*)txt, w.x, B, Lt, dm.L, D, st));
+    DIT_CHECK_HIP(embed_latents(latents, (const float*)m->img_in.w, m->img_in.b, w.x, w.before,
+                                B, Lt, Li, D, m->C_in, st));
+  } else {
+    if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st));
+    DIT_CHECK_HIP(embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before,
+                                B, Lt, Li, D, m->C_in, st));
+  }
   DIT_CHECK_HIP(run_block(dm, dt, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
 
   double rel = INFINITY;
@@ -731,9 +832,17 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   // velocity head on the image rows, then the Euler (+CFG) update
   const float* mf = mod_step + m->n_double * D12 + m->n_single * D3;
   const RowMap sm{B, Lt, Li, dm.L, 1, 0};
-  DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D, 0,
-                                   st));
-  DIT_CHECK_HIP(gemm_store_f32(gp(w.blk.u, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in, st));
+  if (dt == DIT_F32) {
+    DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u32, B * Li, D, sm, B * Li, mf, mf + D, mf,
+                                     mf + D, 0, st));
+    DIT_CHECK_HIP(gemm32_store(gp32(w.blk.u32, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in,
+                               st));
+  } else {
+    DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D,
+                                     0, st));
+    DIT_CHECK_HIP(gemm_store_f32(gp(w.blk.u, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in,
+                                 st));
+  }
   DIT_CHECK_HIP(euler_update(latents, w.v, Li * m->C_in, B == 2 ? 1 : 0, m->guidance,
                              (float)(sigma_next - sigma), st));
   if (info_out) {

@@ -343,31 +343,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
 }
 
 // Variant fed by gfx950's direct global->LDS loads (global_load_lds_dwordx4): each
-// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so the
-// padded 144-B rows are filled by giving every lane the global chunk that
-// belongs at its LDS slot (the 9th slot of a row is padding: it re-reads the
-// row's last chunk).  No staging registers, no LDS store instructions; the two
-// stages are separate LDS objects so the loads into one never order the reads
-// of the other.
+// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so padded
+// rows are filled by giving every lane the global chunk that belongs at its LDS
+// slot (the last 16 B of a row is padding: it re-reads the row's last chunk).
+// No staging registers, no LDS store instructions.
 //
-// F8: operands are OCP e4m3 with per-row (A) and per-column (W) scales; a K
-// slab is 128 elements (the same 128 bytes per row as a bf16 slab of 64), and
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) takes 32 bytes of K
-// per lane; the epilogue dequantises with sa[row] * sw[col].
-template <int BM, int BN, int WM, int WN, bool F8, class Epi>
+// Pipeline: NS stages, each holding a K slab of SLAB bytes per row for the A and
+// the W tile (SLAB / 2 bf16 or SLAB e4m3 values), so NS - 1 slabs are in flight
+// while one is consumed; every stage is its own LDS object so the loads into
+// one never order the reads of another.
+//
+// F8: operands are OCP e4m3 with per-row (A) and per-column (W) scales;
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) takes 32 bytes of K per
+// lane; the epilogue dequantises with sa[row] * sw[col].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt at max
+}
+
+template <int BM, int BN, int WM, int WN, bool F8, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
   constexpr int WROWS = BM / WM;
-  constexpr int ROWB = GEMM_LDS * 2;          // 144 bytes per LDS row
+  constexpr int ROWB = SLAB + 16;             // padded LDS row (bytes)
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per LDS row
   constexpr int AB = BM * ROWB, BB = BN * ROWB, SB = AB + BB;
   constexpr int NI = SB / 1024;               // 1-KB load instructions per stage
   constexpr int IPW = NI / NW;
+  constexpr int SLICE = WROWS * EPI_LDS * 4;  // bytes of one wave's parked epilogue slice
+  constexpr int WPS = SB / SLICE;             // epilogue slices per stage
+  static_assert(NS >= 2 && NS <= 4, "2..4 stages");
   static_assert(AB % 1024 == 0 && BB % 1024 == 0 && NI % NW == 0, "stage / wave mismatch");
-  static_assert((NW / 2) * WROWS * EPI_LDS * 4 <= SB, "epilogue slices must fit half the waves per stage");
+  static_assert(WPS * NS >= NW, "epilogue slices must fit the stages");
+  static_assert(SLAB % (F8 ? 64 : 32) == 0, "slab holds whole MFMA K steps");
+  static_assert(ROWB % 32 == 16, "row pitch: an odd number of 16-byte chunks");
   __shared__ __attribute__((aligned(1024))) char st0[SB];
   __shared__ __attribute__((aligned(1024))) char st1[SB];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? SB : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? SB : 16];
+  auto stage = [&](int s) -> char* {
+    return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3;
+  };
 
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
@@ -404,7 +423,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     const bool isb = (wave * IPW + j) * 1024 >= AB;
     const int o2 = isb ? off - AB : off;
     const int row = o2 / ROWB;
-    const int slot = min((o2 - row * ROWB) >> 4, 7);
+    const int slot = min((o2 - row * ROWB) >> 4, CPR - 2);
     voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw * ES + slot * 16
                   : min(m0 + row, g.M - 1) * g.lda * ES + slot * 16;
   }
@@ -417,53 +436,51 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = g.K / (GEMM_BK * 2 / ES);          // 128-byte K slabs
+  const int nk = g.K * ES / SLAB;                   // K slabs
   const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
   const int wrow = wm * WROWS;
   const int wcol = wn * (BN / WN);
 
-#define GEMM_DMA(stage, kt)                                                              \
+#define GEMM_DMA(stg, kt)                                                                \
   {                                                                                      \
-    const int ko_ = (kt) * 128;                                                          \
+    const int ko_ = (kt) * SLAB;                                                         \
     _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                   \
       const char* b_ = ((wave * IPW + j) * 1024 >= AB) ? wbase : abase;                  \
       __builtin_amdgcn_global_load_lds((const void*)(b_ + voff[j] + ko_),            \
-                                       (void*)((stage) + (wave * IPW + j) * 1024), 16, 0, 0); \
+                                       (void*)((stg) + (wave * IPW + j) * 1024), 16, 0, 0); \
     }                                                                                    \
   }
-  // fragments of K-chunk kk+1 are read while the MFMAs of chunk kk run
-#define GEMM_COMPUTE(stage)                                                              \
+  // bf16: 16-deep K steps (32 bytes of a row); the fragments of step kk+1 are
+  // read while the MFMAs of step kk run
+#define GEMM_COMPUTE(stg)                                                                \
   {                                                                                      \
-    const bf16_t* a_s = (const bf16_t*)(stage);                                          \
-    const bf16_t* b_s = (const bf16_t*)((stage) + AB);                                   \
+    const char* a_s = (const char*)(stg) + (lane >> 5) * 16;                             \
+    const char* b_s = (const char*)(stg) + AB + (lane >> 5) * 16;                        \
+    constexpr int KS = SLAB / 32;                                                        \
     bf16x8 af[2][TM], bw[2][TN];                                                         \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
-        af[0][i] = *(const bf16x8*)&a_s[(wrow + i * 32 + frow) * GEMM_LDS + fk];         \
+        af[0][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB);                \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
-        bw[0][j] = *(const bf16x8*)&b_s[(wcol + j * 32 + frow) * GEMM_LDS + fk];         \
-    _Pragma("unroll") for (int kk = 0; kk < GEMM_BK / 16; ++kk) {                       \
+        bw[0][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB);                \
+    _Pragma("unroll") for (int kk = 0; kk < KS; ++kk) {                                 \
       const int cb = kk & 1, nb = cb ^ 1;                                                \
-      if (kk + 1 < GEMM_BK / 16) {                                                       \
+      if (kk + 1 < KS) {                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
-            af[nb][i] = *(const bf16x8*)&a_s[(wrow + i * 32 + frow) * GEMM_LDS + (kk + 1) * 16 + fk]; \
+            af[nb][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB + (kk + 1) * 32); \
         _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
-            bw[nb][j] = *(const bf16x8*)&b_s[(wcol + j * 32 + frow) * GEMM_LDS + (kk + 1) * 16 + fk]; \
+            bw[nb][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB + (kk + 1) * 32); \
       }                                                                                  \
       _Pragma("unroll") for (int i = 0; i < TM; ++i)                                     \
           _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bw[cb][j], acc[i][j], 0, 0, 0); \
     }                                                                                    \
   }
-  // vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
-#define GEMM_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x0F70)
-
-  // fp8: two 64-deep MFMAs per slab, 32 bytes of K per lane (two 16-byte reads)
-#define GEMM_COMPUTE_F8(stage)                                                           \
+  // fp8: 64-deep K steps, 32 bytes of K per lane (two 16-byte reads)
+#define GEMM_COMPUTE_F8(stg)                                                             \
   {                                                                                      \
-    const char* a_s = (const char*)(stage);                                              \
-    const char* b_s = (const char*)(stage) + AB;                                         \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                  \
+    const char* a_s = (const char*)(stg);                                                \
+    const char* b_s = (const char*)(stg) + AB;                                           \
+    _Pragma("unroll") for (int kk = 0; kk < SLAB / 64; ++kk) {                          \
       i32x8 af[TM], bw[TN];                                                              \
       _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                   \
         const char* q_ = a_s + (wrow + i * 32 + frow) * ROWB + kk * 64 + (lane >> 5) * 32; \
@@ -482,25 +499,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     }                                                                                    \
   }
 
-  GEMM_DMA(st0, 0);
-  GEMM_WAIT_DMA();
+  // prologue: slabs 0 .. NS-2 in flight, wait for slab 0
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) GEMM_DMA(stage(s), s);
+  if (nk >= NS - 1) wait_vmcnt<(NS - 2) * IPW>();
+  else wait_vmcnt<0>();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = (kt & 1) ? st1 : st0;
-    char* nxt = (kt & 1) ? st0 : st1;
-    if (kt + 1 < nk) GEMM_DMA(nxt, kt + 1);
+    // the stage refilled here was consumed in iteration kt - 1 (before its barrier)
+    const bool refill = kt + NS - 1 < nk;
+    if (refill) GEMM_DMA(stage((kt + NS - 1) % NS), kt + NS - 1);
+    char* cur = stage(kt % NS);
     if constexpr (F8) GEMM_COMPUTE_F8(cur)
     else GEMM_COMPUTE(cur)
-    GEMM_WAIT_DMA();
+    // slab kt + 1 has landed once at most the later slabs' loads are outstanding
+    if (refill) wait_vmcnt<(NS - 2) * IPW>();
+    else wait_vmcnt<0>();
     __syncthreads();
   }
 #undef GEMM_DMA
 #undef GEMM_COMPUTE
 #undef GEMM_COMPUTE_F8
-#undef GEMM_WAIT_DMA
 
   const Epi epi = g1 ? p.e[1] : p.e[0];
-  float* slice = (float*)(wave < NW / 2 ? st0 : st1) + (wave % (NW / 2)) * WROWS * EPI_LDS;
+  float* slice = (float*)(stage(wave / WPS) + (wave % WPS) * SLICE);
   const bool cmaj = epi.colmajor(n0, BN);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -554,10 +577,189 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   }
 }
 
+// ---------------------------------------------------------------- fp32 path
+// Reference-precision blocks (fp32 weights and activations) for small models:
+// a plain LDS-tiled VALU GEMM (64 x 64 outputs, 256 threads of 4 x 4) with the
+// same epilogue interface, writing fp32.
+
+struct EpiSiluF32 {
+  float* out; int ldo;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    f32x4 o;
+    for (int i = 0; i < 4; ++i) o[i] = silu_f(v[i]);
+    *(f32x4*)(out + (size_t)r * ldo + c) = o;
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+struct EpiGeluF32 {
+  float* out; int ldo; int col_off;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    f32x4 o;
+    for (int i = 0; i < 4; ++i) o[i] = gelu_tanh_f(v[i]);
+    *(f32x4*)(out + (size_t)r * ldo + col_off + c) = o;
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+// Q, K (rotated) [B, H, L, d] and V^T [B, H, d, L], all fp32.
+struct EpiQKV32 {
+  float* q; float* k; float* vt; const float* rope;
+  int D, H, d; RowMap map;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    const int which = c / D;
+    const int cc = c - which * D;
+    const int h = cc / d;
+    const int dd = cc - h * d;
+    int b, t; map.token(r, b, t);
+    const size_t bh = (size_t)b * H + h;
+    if (which < 2) {
+      const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+      f32x4 o;
+      o[0] = v[0] * cs[0] - v[1] * cs[1];
+      o[1] = v[0] * cs[1] + v[1] * cs[0];
+      o[2] = v[2] * cs[2] - v[3] * cs[3];
+      o[3] = v[2] * cs[3] + v[3] * cs[2];
+      *(f32x4*)((which == 0 ? q : k) + (bh * map.L + t) * d + dd) = o;
+    } else {
+      float* dst = vt + (bh * d + dd) * map.L + t;
+      for (int i = 0; i < 4; ++i) dst[(size_t)i * map.L] = v[i];
+    }
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+struct EpiLinear1F32 {
+  EpiQKV32 qkv; EpiGeluF32 gelu; int n_qkv;
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
+  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+    if (c < n_qkv) qkv.row4(r, c, v);
+    else gelu.row4(r, c - n_qkv, v);
+  }
+  __device__ __forceinline__ void col4(int, int, f32x4) const {}
+};
+
+constexpr int G32_T = 64;    // output tile edge
+constexpr int G32_K = 16;    // K chunk
+
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams<Epi> p) {
+  __shared__ float sA[G32_K][G32_T + 4];   // k-major
+  __shared__ float sB[G32_K][G32_T + 4];
+  int lid = blockIdx.x;
+  const bool g1 = p.ngroups > 1 && lid >= p.tiles[0];
+  if (g1) lid -= p.tiles[0];
+  const GemmProblem g = g1 ? p.g[1] : p.g[0];
+  const int tiles_n = g1 ? p.tiles_n[1] : p.tiles_n[0];
+  const int m0 = (lid / tiles_n) * G32_T;
+  const int n0 = (lid % tiles_n) * G32_T;
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;
+  const int lrow = tid >> 2, lk = (tid & 3) * 4;   // loader: row of the tile, 4 K values
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += G32_K) {
+    const int kk = k0 + lk;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+    if (m0 + lrow < g.M && kk < g.K) a = *(const f32x4*)(g.A32 + (size_t)(m0 + lrow) * g.lda + kk);
+    if (n0 + lrow < g.N && kk < g.K) w = *(const f32x4*)(g.W32 + (size_t)(n0 + lrow) * g.ldw + kk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sA[lk + i][lrow] = a[i];
+      sB[lk + i][lrow] = w[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < G32_K; ++k) {
+      const f32x4 av = *(const f32x4*)&sA[k][ty * 4];
+      const f32x4 bv = *(const f32x4*)&sB[k][tx * 4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const Epi epi = g1 ? p.e[1] : p.e[0];
+  const int col = n0 + tx * 4;
+  if (col >= g.N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= g.M) break;
+    f32x4 v = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    if (g.bias) v += *(const f32x4*)(g.bias + col);
+    epi.row4(row, col, v);
+  }
+}
+
+template <class Epi>
+static hipError_t launch32(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st, int site) {
+  KTimerScope timer(site, st);
+  GemmParams<Epi> p{};
+  int total = 0;
+  p.ngroups = ng;
+  for (int i = 0; i < ng; ++i) {
+    if (gp[i].K % 4 || gp[i].N % 4 || gp[i].lda % 4 || gp[i].ldw % 4) return hipErrorInvalidValue;
+    p.g[i] = gp[i];
+    p.e[i] = ep[i];
+    p.tiles_n[i] = (gp[i].N + G32_T - 1) / G32_T;
+    p.tiles[i] = ((gp[i].M + G32_T - 1) / G32_T) * p.tiles_n[i];
+    total += p.tiles[i];
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel<Epi>, dim3(total), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t gemm32_store(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
+  EpiStoreF32 e{out, ldo};
+  return launch32(&g, &e, 1, st, KS_GEMM_F32);
+}
+
+hipError_t gemm32_silu(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
+  EpiSiluF32 e{out, ldo};
+  return launch32(&g, &e, 1, st, KS_GEMM_SILU);
+}
+
+hipError_t gemm32_gelu(const GemmProblem* g, int ng, float* const* out, const int* ldo,
+                       hipStream_t st) {
+  EpiGeluF32 e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiGeluF32{out[i], ldo[i], 0};
+  return launch32(g, e, ng, st, KS_GEMM_GELU);
+}
+
+hipError_t gemm32_gated_residual(const GemmProblem* g, int ng, float* x, int D,
+                                 const float* const* gate, int gate_bstride, const RowMap* map,
+                                 hipStream_t st) {
+  EpiGatedResidual<float> e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiGatedResidual<float>{x, D, gate[i], gate_bstride, map[i]};
+  return launch32(g, e, ng, st, KS_GEMM_RESID);
+}
+
+hipError_t gemm32_qkv(const GemmProblem* g, int ng, const QKVOut32& o, const RowMap* map,
+                      hipStream_t st) {
+  EpiQKV32 e[2];
+  for (int i = 0; i < ng; ++i) e[i] = EpiQKV32{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i]};
+  return launch32(g, e, ng, st, KS_GEMM_QKV);
+}
+
+hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap& map, float* cat,
+                          int ldcat, hipStream_t st) {
+  EpiLinear1F32 e;
+  e.qkv = EpiQKV32{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map};
+  e.gelu = EpiGeluF32{cat, ldcat, o.D};
+  e.n_qkv = 3 * o.D;
+  return launch32(&g, &e, 1, st, KS_GEMM_LIN1);
+}
+
 // ---------------------------------------------------------------- launch
 
-// KV: 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS bf16 kernel, 0 = register-staged bf16 kernel
-template <int BM, int BN, int WM, int WN, int KV, class Epi>
+// KV: 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS bf16 kernel, 0 = register-staged
+// bf16 kernel; NS stages of SLAB bytes per row for the direct-to-LDS kernels
+template <int BM, int BN, int WM, int WN, int KV, int NS = 2, int SLAB = 128, class Epi>
 static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
   GemmParams<Epi> p{};
   int total = 0;
@@ -571,8 +773,8 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
   }
   if (total == 0) return hipSuccess;
   void (*kern)(GemmParams<Epi>);
-  if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, true, Epi>;
-  else if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, false, Epi>;
+  if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, true, NS, SLAB, Epi>;
+  else if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, false, NS, SLAB, Epi>;
   else kern = &gemm_bf16_kernel<BM, BN, WM, WN, Epi>;
   hipLaunchKernelGGL(kern, dim3(total), dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
@@ -583,10 +785,15 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   KTimerScope timer(site, st);
   int maxM = 0, minN = 1 << 30;
   for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
-  if (gp[0].A8) return launch_cfg<256, 256, 2, 4, 2>(gp, ep, ng, st);   // fp8: one config
+#ifndef GEMM_NS
+#define GEMM_NS 2
+#define GEMM_SLAB 128
+#endif
+  if (gp[0].A8) return launch_cfg<256, 256, 2, 4, 2, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   if (maxM <= 64) return launch_cfg<32, 256, 1, 4, 0>(gp, ep, ng, st);
   // large problems: 256x256 tiles, 8 waves, fed by direct global->LDS loads
-  if (maxM >= 1024 && minN >= 1024) return launch_cfg<256, 256, 2, 4, 1>(gp, ep, ng, st);
+  if (maxM >= 1024 && minN >= 1024)
+    return launch_cfg<256, 256, 2, 4, 1, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
 }
 

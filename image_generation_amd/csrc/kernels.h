@@ -34,6 +34,9 @@ struct GemmProblem {
   const fp8_t* W8 = nullptr;
   const float* sa = nullptr;
   const float* sw = nullptr;
+  // fp32 (reference-precision blocks): A32 [M, K], W32 [N, K]; K % 4 == 0
+  const float* A32 = nullptr;
+  const float* W32 = nullptr;
 };
 
 // Destinations of the fused QKV epilogue.
@@ -59,17 +62,40 @@ hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap*
 hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
                         bf16_t* cat, int ldcat, hipStream_t st);
 
+// fp32 GEMMs (VALU, 64 x 64 tiles) with the same fused epilogues writing fp32:
+// Q, K, V^T [B, H, L, d] / [B, H, d, L], GELU hidden, gated residual, plain stores.
+struct QKVOut32 {
+  float* q; float* k; float* vt; const float* rope; int D, H, d;
+};
+hipError_t gemm32_store(const GemmProblem& g, float* out, int ldo, hipStream_t st);
+hipError_t gemm32_silu(const GemmProblem& g, float* out, int ldo, hipStream_t st);
+hipError_t gemm32_gelu(const GemmProblem* g, int ng, float* const* out, const int* ldo,
+                       hipStream_t st);
+hipError_t gemm32_gated_residual(const GemmProblem* g, int ng, float* x, int D,
+                                 const float* const* gate, int gate_bstride, const RowMap* map,
+                                 hipStream_t st);
+hipError_t gemm32_qkv(const GemmProblem* g, int ng, const QKVOut32& o, const RowMap* map,
+                      hipStream_t st);
+hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap& map, float* cat,
+                          int ldcat, hipStream_t st);
+
+// fp32 attention, head dim 32 or 64: q, k [B, H, L, d], vt [B, H, d, L], o fp32.
+hipError_t attention_f32(const float* q, const float* k, const float* vt, float* o, int ldo,
+                         const RowMap& map, int B, int H, int L, int d, float softmax_scale,
+                         hipStream_t st);
+
 // Flash attention: q, k bf16 [B, H, L, d], vt fp16 [B, H, d, L]; output (bf16) of
 // token (b, t), head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
 hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st);
 
-// LayerNorm (eps 1e-6, no affine) + modulate: out[r] = LN(x[map(r)]) * (1 + scale) + shift.
+// LayerNorm (eps 1e-6, no affine) + modulate: out[r] = LN(x[map(r)]) * (1 + scale) + shift
+// (OT = bf16_t or float).
 // Rows r < n_img take the image vectors, the rest the text vectors; per batch b
 // the vectors sit at mod + b * mod_bstride.
-template <class XT>
-hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& map,
+template <class XT, class OT>
+hipError_t ln_modulate(const XT* x, OT* out, int rows, int D, const RowMap& map,
                        int n_img_rows, const float* shift_img, const float* scale_img,
                        const float* shift_txt, const float* scale_txt, int mod_bstride,
                        hipStream_t st);

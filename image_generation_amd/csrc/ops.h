@@ -14,14 +14,17 @@ struct FbcResult {
 
 constexpr int FBC_PARTS = 1024;   // blocks of the first reduction pass
 
-hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, float* x,
+// WT, TT, OT: bf16_t or float
+template <class WT>
+hipError_t embed_latents(const float* lat, const WT* W, const float* bias, float* x,
                          float* before, int B, int Lt, int Li, int D, int Cin, hipStream_t st);
-hipError_t text_to_stream(const bf16_t* txt, float* x, int B, int Lt, int L, int D,
-                          hipStream_t st);
+template <class TT>
+hipError_t text_to_stream(const TT* txt, float* x, int B, int Lt, int L, int D, hipStream_t st);
 constexpr int SIG_CHUNK = 64;
 struct SigChunk { double s[SIG_CHUNK]; };
 // Timestep embedding of host sigmas (passed through kernel arguments).
-hipError_t sinusoid_host(const double* sig_host, bf16_t* e, int M, int half, hipStream_t st);
+template <class OT>
+hipError_t sinusoid_host(const double* sig_host, OT* e, int M, int half, hipStream_t st);
 hipError_t rope_table(float* tab, int grid_w, int Lt, int L, int d, double theta, hipStream_t st);
 hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, float* staging,
                       double* part, int nparts, FbcResult* res, int B, int Lt, int Li, int D,

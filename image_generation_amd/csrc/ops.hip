@@ -33,10 +33,11 @@ __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
   return v;
 }
 
-template <class XT, bool F8>
+// OUT: 0 = bf16, 1 = e4m3 + per-row scale, 2 = fp32
+template <class XT, int OUT>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(
-    const XT* __restrict__ x, bf16_t* __restrict__ out, fp8_t* __restrict__ out8,
-    float* __restrict__ oscale, int rows, int D, RowMap map, int n_img,
+    const XT* __restrict__ x, void* __restrict__ out_, float* __restrict__ oscale, int rows, int D,
+    RowMap map, int n_img,
     const float* __restrict__ sh_i, const float* __restrict__ sc_i,
     const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride) {
   const int lane = threadIdx.x & 63;
@@ -77,13 +78,18 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
       const f32x4 a = *(const f32x4*)(sc + col);
       const f32x4 z = *(const f32x4*)(sh + col);
       v[c] = v[c] * rstd * (1.0f + a) + z;
-      if constexpr (F8)
+      if constexpr (OUT == 1)
         amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])),
                                  fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
     }
   }
-  if constexpr (!F8) {
-    bf16_t* orow = out + (size_t)r * D;
+  if constexpr (OUT == 2) {
+    float* orow = (float*)out_ + (size_t)r * D;
+#pragma unroll
+    for (int c = 0; c < LN_MAXCH; ++c)
+      if (c < nch) *(f32x4*)(orow + c * 256 + lane * 4) = v[c];
+  } else if constexpr (OUT == 0) {
+    bf16_t* orow = (bf16_t*)out_ + (size_t)r * D;
 #pragma unroll
     for (int c = 0; c < LN_MAXCH; ++c) {
       if (c < nch) {
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
       scl = amax / 448.0f;
       inv = 448.0f / amax;
     }
-    fp8_t* orow = out8 + (size_t)r * D;
+    fp8_t* orow = (fp8_t*)out_ + (size_t)r * D;
 #pragma unroll
     for (int c = 0; c < LN_MAXCH; ++c) {
       if (c < nch) {
@@ -114,22 +120,26 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
   }
 }
 
-template <class XT>
-hipError_t ln_modulate(const XT* x, bf16_t* out, int rows, int D, const RowMap& map,
+template <class XT, class OT>
+hipError_t ln_modulate(const XT* x, OT* out, int rows, int D, const RowMap& map,
                        int n_img_rows, const float* shift_img, const float* scale_img,
                        const float* shift_txt, const float* scale_txt, int mod_bstride,
                        hipStream_t st) {
   if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   KTimerScope timer(KS_LN, st);
-  hipLaunchKernelGGL((ln_modulate_kernel<XT, false>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
-                     out, nullptr, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
+  constexpr int mode = sizeof(OT) == 4 ? 2 : 0;
+  hipLaunchKernelGGL((ln_modulate_kernel<XT, mode>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
+                     (void*)out, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
                      shift_txt, scale_txt, mod_bstride);
   return hipGetLastError();
 }
-template hipError_t ln_modulate<float>(const float*, bf16_t*, int, int, const RowMap&, int,
-                                       const float*, const float*, const float*, const float*, int,
-                                       hipStream_t);
+template hipError_t ln_modulate<float, bf16_t>(const float*, bf16_t*, int, int, const RowMap&, int,
+                                               const float*, const float*, const float*,
+                                               const float*, int, hipStream_t);
+template hipError_t ln_modulate<float, float>(const float*, float*, int, int, const RowMap&, int,
+                                              const float*, const float*, const float*,
+                                              const float*, int, hipStream_t);
 
 hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, int D,
                            const RowMap& map, int n_img_rows, const float* shift_img,
@@ -138,8 +148,8 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
   if (D % 256 != 0 || D > 256 * LN_MAXCH) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   KTimerScope timer(KS_LN, st);
-  hipLaunchKernelGGL((ln_modulate_kernel<float, true>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
-                     nullptr, out8, scale, rows, D, map, n_img_rows, shift_img, scale_img,
+  hipLaunchKernelGGL((ln_modulate_kernel<float, 1>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
+                     (void*)out8, scale, rows, D, map, n_img_rows, shift_img, scale_img,
                      shift_txt, scale_txt, mod_bstride);
   return hipGetLastError();
 }
@@ -148,8 +158,9 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
 
 // Image tokens: x[b, Lt + i, :] = before[b, i, :] = lat[i] W_in^T + b_in for every
 // batch row b (a CFG pair shares its latents).  16 tokens x 256 columns per block.
+template <class WT>
 __global__ __launch_bounds__(256) void embed_latents_kernel(
-    const float* __restrict__ lat, const bf16_t* __restrict__ W, const float* __restrict__ bias,
+    const float* __restrict__ lat, const WT* __restrict__ W, const float* __restrict__ bias,
     float* __restrict__ x, float* __restrict__ before, int B, int Lt, int Li, int L, int D,
     int Cin) {
   __shared__ float sl[16][64];
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(256) void embed_latents_kernel(
   if (n >= D) return;
   float w[64];
 #pragma unroll
-  for (int k = 0; k < 64; ++k) w[k] = k < Cin ? bf2f(W[(size_t)n * Cin + k]) : 0.f;
+  for (int k = 0; k < 64; ++k) w[k] = k < Cin ? to_f32(W[(size_t)n * Cin + k]) : 0.f;
   const float bn = bias[n];
   for (int i = 0; i < 16 && i0 + i < Li; ++i) {
     float acc = 0.f;
@@ -178,29 +189,31 @@ __global__ __launch_bounds__(256) void embed_latents_kernel(
   }
 }
 
-// Text tokens: x[b, t, :] = txt[b, t, :] (bf16 -> fp32 residual stream).
+// Text tokens: x[b, t, :] = txt[b, t, :] (bf16 or fp32 -> fp32 residual stream).
+template <class TT>
 __global__ __launch_bounds__(256) void text_to_stream_kernel(
-    const bf16_t* __restrict__ txt, float* __restrict__ x, int B, int Lt, int L, int D) {
+    const TT* __restrict__ txt, float* __restrict__ x, int B, int Lt, int L, int D) {
   const size_t n4 = (size_t)B * Lt * D / 4;
   for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
     const size_t e = j * 4;
     const size_t row = e / D;
     const int c = (int)(e - row * D);
     const int b = (int)(row / Lt), t = (int)(row - (size_t)b * Lt);
-    *(f32x4*)(x + ((size_t)b * L + t) * D + c) = load4<bf16_t>(txt + e);
+    *(f32x4*)(x + ((size_t)b * L + t) * D + c) = load4<TT>(txt + e);
   }
 }
 
 // Sinusoidal timestep embedding of t = sigma_m, in fp64: [cos(1000 t w_k), sin(1000 t w_k)],
-// w_k = 10000^(-k/half); bf16 out [M, 2*half].  Sigmas travel in the kernel
-// arguments, up to SIG_CHUNK per launch.
-__global__ void sinusoid_kernel(SigChunk sig, bf16_t* __restrict__ e, int half) {
+// w_k = 10000^(-k/half); out [M, 2*half] (bf16 or fp32).  Sigmas travel in the
+// kernel arguments, up to SIG_CHUNK per launch.
+template <class OT>
+__global__ void sinusoid_kernel(SigChunk sig, OT* __restrict__ e, int half) {
   const int m = blockIdx.x;
   for (int k = threadIdx.x; k < half; k += blockDim.x) {
     const double w = exp(-log(10000.0) * (double)k / (double)half);
     const double a = 1000.0 * sig.s[m] * w;
-    e[(size_t)m * 2 * half + k] = f2bf((float)cos(a));
-    e[(size_t)m * 2 * half + half + k] = f2bf((float)sin(a));
+    e[(size_t)m * 2 * half + k] = from_f32<OT>((float)cos(a));
+    e[(size_t)m * 2 * half + half + k] = from_f32<OT>((float)sin(a));
   }
 }
 
@@ -395,36 +408,46 @@ hipError_t narrow_f32(const float* a, bf16_t* b, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t embed_latents(const float* lat, const bf16_t* W, const float* bias, float* x,
+template <class WT>
+hipError_t embed_latents(const float* lat, const WT* W, const float* bias, float* x,
                          float* before, int B, int Lt, int Li, int D, int Cin, hipStream_t st) {
   KTimerScope timer(KS_OTHER, st);
   if (Cin > 64) return hipErrorInvalidValue;
   dim3 grid((Li + 15) / 16, (D + 255) / 256);
-  hipLaunchKernelGGL(embed_latents_kernel, grid, dim3(256), 0, st, lat, W, bias, x, before, B, Lt,
-                     Li, Lt + Li, D, Cin);
+  hipLaunchKernelGGL(embed_latents_kernel<WT>, grid, dim3(256), 0, st, lat, W, bias, x, before, B,
+                     Lt, Li, Lt + Li, D, Cin);
   return hipGetLastError();
 }
+template hipError_t embed_latents<bf16_t>(const float*, const bf16_t*, const float*, float*,
+                                          float*, int, int, int, int, int, hipStream_t);
+template hipError_t embed_latents<float>(const float*, const float*, const float*, float*, float*,
+                                         int, int, int, int, int, hipStream_t);
 
-hipError_t text_to_stream(const bf16_t* txt, float* x, int B, int Lt, int L, int D,
-                          hipStream_t st) {
+template <class TT>
+hipError_t text_to_stream(const TT* txt, float* x, int B, int Lt, int L, int D, hipStream_t st) {
   KTimerScope timer(KS_OTHER, st);
-  hipLaunchKernelGGL(text_to_stream_kernel, dim3(grid_for((size_t)B * Lt * D / 4)), dim3(256), 0,
-                     st, txt, x, B, Lt, L, D);
+  hipLaunchKernelGGL(text_to_stream_kernel<TT>, dim3(grid_for((size_t)B * Lt * D / 4)), dim3(256),
+                     0, st, txt, x, B, Lt, L, D);
   return hipGetLastError();
 }
+template hipError_t text_to_stream<bf16_t>(const bf16_t*, float*, int, int, int, int, hipStream_t);
+template hipError_t text_to_stream<float>(const float*, float*, int, int, int, int, hipStream_t);
 
-hipError_t sinusoid_host(const double* sig_host, bf16_t* e, int M, int half, hipStream_t st) {
+template <class OT>
+hipError_t sinusoid_host(const double* sig_host, OT* e, int M, int half, hipStream_t st) {
   for (int m0 = 0; m0 < M; m0 += SIG_CHUNK) {
     SigChunk c;
     const int n = M - m0 < SIG_CHUNK ? M - m0 : SIG_CHUNK;
     for (int i = 0; i < SIG_CHUNK; ++i) c.s[i] = i < n ? sig_host[m0 + i] : 0.0;
-    hipLaunchKernelGGL(sinusoid_kernel, dim3(n), dim3(128), 0, st, c, e + (size_t)m0 * 2 * half,
-                       half);
+    hipLaunchKernelGGL(sinusoid_kernel<OT>, dim3(n), dim3(128), 0, st, c,
+                       e + (size_t)m0 * 2 * half, half);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
+template hipError_t sinusoid_host<bf16_t>(const double*, bf16_t*, int, int, hipStream_t);
+template hipError_t sinusoid_host<float>(const double*, float*, int, int, hipStream_t);
 
 hipError_t rope_table(float* tab, int grid_w, int Lt, int L, int d, double theta, hipStream_t st) {
   KTimerScope timer(KS_OTHER, st);

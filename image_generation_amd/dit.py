@@ -185,12 +185,19 @@ def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.T
                   softmax_scale: Optional[float] = None, q_scale: Optional[torch.Tensor] = None,
                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
-    """bf16: q, k [B, H, L, d] bf16, vt [B, H, d, L] fp16.
-    fp8: q, k, vt e4m3 codes of the same shapes, scales fp32 [B, H].
-    o [B, L, H*d] bf16 (written)."""
+    """bf16: q, k [B, H, L, 128] bf16, vt [B, H, 128, L] fp16, o bf16.
+    fp8: q, k, vt e4m3 codes of the same shapes, scales fp32 [B, H], o bf16.
+    fp32: q, k [B, H, L, d] fp32 (d 32 or 64), vt [B, H, d, L] fp32, o fp32.
+    o [B, L, H*d] (written)."""
     B, H, L, d = q.shape
     fp8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
-    if fp8:
+    f32 = q.dtype == torch.float32
+    if f32:
+        _need(q, torch.float32, (B, H, L, d), "q")
+        _need(k, torch.float32, (B, H, L, d), "k")
+        _need(vt, torch.float32, (B, H, d, L), "vt")
+        _need(o, torch.float32, (B, L, H * d), "o")
+    elif fp8:
         _codes(q, (B, H, L, d), "q")
         _codes(k, (B, H, L, d), "k")
         _codes(vt, (B, H, d, L), "vt")
@@ -202,11 +209,13 @@ def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.T
         _need(q, torch.bfloat16, (B, H, L, d), "q")
         _need(k, torch.bfloat16, (B, H, L, d), "k")
         _need(vt, torch.float16, (B, H, d, L), "vt")
-    _need(o, torch.bfloat16, (B, L, H * d), "o")
+    if not f32:
+        _need(o, torch.bfloat16, (B, L, H * d), "o")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(q_scale), _ptr(k_scale),
-                             _ptr(v_scale), B, H, L, d, DIT_FP8 if fp8 else DIT_BF16,
+                             _ptr(v_scale), B, H, L, d,
+                             DIT_F32 if f32 else DIT_FP8 if fp8 else DIT_BF16,
                              float(softmax_scale), _stream(stream)))
     return o
 
@@ -246,8 +255,8 @@ def _lin(w: torch.Tensor, b: torch.Tensor, w_scale: Optional[torch.Tensor] = Non
     if b.dtype != torch.float32 or not (w.is_cuda and b.is_cuda):
         raise ValueError("linear: bias fp32, tensors on the GPU")
     if w_scale is None:
-        if w.dtype != torch.bfloat16:
-            raise ValueError("linear: bf16 weight expected")
+        if w.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("linear: bf16 (or fp32) weight expected")
     elif w.dtype not in (torch.uint8, torch.float8_e4m3fn) or w_scale.dtype != torch.float32 \
             or tuple(w_scale.shape) != (w.shape[0],):
         raise ValueError("linear: fp8 layer needs e4m3 codes and an fp32 scale per output")
@@ -344,20 +353,21 @@ class GPUModel:
         D = dims.D
         self.n_double, self.n_single = dims.n_double, dims.n_single
         self.t = {}
+        wdt = torch.float32 if dtype == DIT_F32 else torch.bfloat16
         for name, t in params.items():
             if name.rsplit(".", 1)[-1].startswith("b"):      # b, b1, b2: biases
                 self.t[name] = t.to(device=device, dtype=torch.float32).contiguous()
             elif name.endswith(".mod.w"):
                 continue
             else:
-                self.t[name] = t.to(device=device, dtype=torch.bfloat16).contiguous()
+                self.t[name] = t.to(device=device, dtype=wdt).contiguous()
         # stacked modulation weights in the order the library expects
         order = []
         for j in range(self.n_double):
             order += [f"double{j}.img.mod", f"double{j}.txt.mod"]
         order += [f"single{j}.mod" for j in range(self.n_single)]
         order += ["final.mod"]
-        self.mod_w = torch.cat([params[n + ".w"].to(device=device, dtype=torch.bfloat16)
+        self.mod_w = torch.cat([params[n + ".w"].to(device=device, dtype=wdt)
                                 for n in order]).contiguous()
         self.mod_b = torch.cat([self.t[n + ".b"] for n in order]).contiguous()
         self.n_mod = self.mod_w.shape[0]
@@ -371,7 +381,7 @@ class GPUModel:
                                                 if n.startswith(pre)}, pre))
             for n, t in q.items():
                 self.t[n] = t
-        elif dtype != DIT_BF16:
+        elif dtype not in (DIT_BF16, DIT_F32):
             raise ValueError(f"model dtype {dtype}")
         self.dtype = dtype
         blocks = [make_double_block(self.t, f"double{j}.") for j in range(self.n_double)]
@@ -423,11 +433,13 @@ class FBCache:
 def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,
                      latents: torch.Tensor, sigma: float, sigma_next: float,
                      cache: Optional[FBCache], ws: torch.Tensor, stream=None):
-    """One Euler step in place on latents [Li, C_in] fp32.  -> (rel, skipped)."""
+    """One Euler step in place on latents [Li, C_in] fp32; txt bf16 (fp32 for an fp32
+    model).  -> (rel, skipped)."""
     dm = gm.model.dims
     Li = dm.grid_h * dm.grid_w
     _need(mod_step, torch.float32, (gm.n_mod,), "mod_step")
-    _need(txt, torch.bfloat16, (dm.B, dm.Lt, dm.D), "txt")
+    _need(txt, torch.float32 if gm.dtype == DIT_F32 else torch.bfloat16, (dm.B, dm.Lt, dm.D),
+          "txt")
     _need(latents, torch.float32, (Li, gm.model.C_in), "latents")
     info = DitStepInfo()
     cp = ctypes.byref(cache.c) if cache is not None else None

@@ -95,7 +95,8 @@ typedef struct dit_dims {
  *   bf16 layers: w bf16, w_scale NULL.
  *   fp8 layers (DIT_FP8 blocks): w OCP e4m3 and w_scale fp32 [out], the
  *   per-output-channel scale (weight = code * w_scale[n]), as produced by
- *   dit_quantize_rows() on the bf16 weight. */
+ *   dit_quantize_rows() on the bf16 weight.
+ *   fp32 layers (DIT_F32 models and blocks): w fp32, w_scale NULL. */
 typedef struct dit_linear {
   const void* w;
   const float* b;
@@ -130,10 +131,11 @@ typedef struct dit_model {
   dit_linear mod;        /* [N_mod, D] */
   int C_in;              /* patch features, <= 64 */
   float guidance;        /* CFG scale (B == 2) */
-  int dtype;             /* DIT_BF16, or DIT_FP8: the blocks' linears and attention run
-                            in e4m3 with dynamic per-token activation scales; the
+  int dtype;             /* DIT_BF16; DIT_FP8: the blocks' linears and attention run
+                            in e4m3 with dynamic per-token activation scales, the
                             modulation, embedders, timestep MLP and velocity head stay
-                            bf16 */
+                            bf16; DIT_F32: every weight and activation fp32 (head dim
+                            32 or 64; reference precision for small models) */
 } dit_model;
 
 /* Caller-held First-Block-Cache state; resuming a loop = passing it back. */
@@ -216,11 +218,13 @@ DIT_API int dit_linear_forward(const void* x, int M, int K, const dit_linear* li
  *   dtype DIT_BF16: q, k device bf16 [B, H, L, 128]; vt device fp16
  *     [B, H, 128, L] (V transposed per head, fp16: the P V product runs on fp16
  *     MFMAs); scales NULL; L % 8 == 0, L >= 8.
+ *   dtype DIT_F32: q, k fp32 [B, H, L, d], vt fp32 [B, H, d, L], o fp32, head_dim
+ *     32 or 64, any L >= 1.
  *   dtype DIT_FP8: q, k e4m3 [B, H, L, 128], vt e4m3 [B, H, 128, L], each with
  *     one fp32 scale per (b, h) in q_scale / k_scale / v_scale [B * H] (value =
  *     code * scale); P is quantised as e4m3(448 P) against the exact running
  *     max, the row sum uses the unquantised P; L % 16 == 0, L >= 16.
- *   o: device bf16 [B, L, H * 128] (token-major).  Softmax statistics and both
+ *   o: device [B, L, H * head_dim] (token-major), bf16 (fp32 for DIT_F32).  Softmax statistics and both
  *   products accumulate in fp32.  Workspace: none. */
 DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
                           const float* q_scale, const float* k_scale, const float* v_scale,
@@ -246,8 +250,9 @@ DIT_API int dit_quantize_rows(const void* src, int src_dtype, int src_ld, int ro
  *        (mod_bstride = 0 shares them): double block 12 D-vectors (image
  *        shift1, scale1, gate1, shift2, scale2, gate2, then text), single 3.
  *   rope: device table from dit_rope_table() for these dims.
- *   dtype: DIT_BF16, or DIT_FP8 (e4m3 linears with w_scale set, per-token
- *   activation scales, e4m3 attention with per-(b, h) scales).
+ *   dtype: DIT_BF16; DIT_FP8 (e4m3 linears with w_scale set, per-token
+ *   activation scales, e4m3 attention with per-(b, h) scales); DIT_F32 (fp32
+ *   weights, head dim 32 or 64).
  *   workspace >= DIT_WS_BLOCK bytes. */
 DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,
@@ -282,7 +287,8 @@ DIT_API int fbcache_should_skip(const float* x_after, const float* x_before, con
  *   latents <- latents + (sigma_next - sigma) v,  v the velocity of the model at
  *   t = sigma (CFG pair: v = v_neg + guidance (v_pos - v_neg)).
  *   mod_step: device fp32 [N_mod], this sigma's row of dit_modulation().
- *   txt: device bf16 [B, Lt, D]; latents: device fp32 [Li, C_in], in place
+ *   txt: device [B, Lt, D], bf16 (fp32 for a DIT_F32 model); latents: device fp32
+ *   [Li, C_in], in place
  *   (shared by a CFG pair).  cache: NULL or a dit_fbcache (state updated).
  *   info_out: optional host pointer.  workspace >= DIT_WS_STEP bytes. */
 DIT_API int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt, float* latents,
