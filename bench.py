@@ -41,6 +41,32 @@ ALL_SITES = ["attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1", "g
              "gemm_silu", "ln", "fbc", "other", "quant"]
 BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 
+# HBM bytes per launch at the 1024px step from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (KiB per dispatch, scaled by a 1 GiB device copy: FETCH_SIZE reads 0.5 of the copied
+# bytes, WRITE_SIZE 1.0).  Valid only for the kernel source they were taken on: the
+# SHA-1 of that source file is checked at run time and traffic is reported as null
+# once it differs.
+TRAFFIC_1024 = {
+    "gemm_lin1": {"bytes": 1207256 * 1024 + 232461 * 1024,
+                  "source": "image_generation_amd/csrc/gemm.hip",
+                  "sha1": "ed503be76bb3b623f962ff0fb70d2ba88d105796"},
+    "attention": {"bytes": 101506 * 1024 + 27691 * 1024,
+                  "source": "image_generation_amd/csrc/attention.hip",
+                  "sha1": "3ab66887ffa2b827d3a12bd6fc3a1233870b626d"},
+}
+
+
+def measured_traffic(kernel):
+    """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    t = TRAFFIC_1024.get(kernel)
+    if t is None:
+        return None
+    with open(os.path.join(ROOT, t["source"]), "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != t["sha1"]:
+            return None
+    return t["bytes"]
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -236,6 +262,9 @@ def main():
     ap.add_argument("--fp8-steps", type=int, default=3)
     ap.add_argument("--only-2048", action="store_true",
                     help="run only the 2048px block and fp8 loop (profiling runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES of device memory 3 times (calibrates the HBM "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -243,6 +272,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
     import dit_inputs as DI
     from image_generation_amd import dit
 
@@ -307,7 +344,8 @@ def main():
     achieved = dom_flops / dom_avg / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom) if w.name == "flux_1024_28step" else None,
                 "flops_per_launch": dom_flops, "avg_launch_us": round(dom_avg * 1e6, 2)}
 
     out = {
