@@ -37,6 +37,24 @@ template <> struct Load8<f16_t> {
   }
 };
 
+// 16 raw bytes (8 elements) -> f32
+template <class T>
+__device__ __forceinline__ void decode8(const i32x4 u, float* v);
+template <>
+__device__ __forceinline__ void decode8<bf16_t>(const i32x4 u, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float((uint32_t)u[i] << 16);
+    v[2 * i + 1] = __uint_as_float((uint32_t)u[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void decode8<f16_t>(const i32x4 u, float* v) {
+  const f16x8 h = __builtin_bit_cast(f16x8, u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+}
+
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
@@ -84,6 +102,46 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ s
     float v[8];
     Load8<T>::get(s + c, v);
     store_fp8x8(d + c, v, inv);
+  }
+  if (lane == 0) scale[r] = sc;
+}
+
+// One wave per row with the row held in registers (NCH x 512 elements at most):
+// one read of the source instead of two.
+template <class T, int NCH>
+__global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T* __restrict__ src, int lds,
+                                                             fp8_t* __restrict__ dst, int ldd,
+                                                             float* __restrict__ scale, int rows,
+                                                             int width) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* s = src + (size_t)r * lds;
+  i32x4 raw[NCH];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = i * 512 + lane * 8;
+    if (c < width) {
+      raw[i] = *(const i32x4*)(s + c);
+      float v[8];
+      decode8<T>(raw[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+  }
+  amax = wave_max(amax);
+  float sc, inv;
+  scale_of(amax, sc, inv);
+  fp8_t* d = dst + (size_t)r * ldd;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = i * 512 + lane * 8;
+    if (c < width) {
+      float v[8];
+      decode8<T>(raw[i], v);
+      store_fp8x8(d + c, v, inv);
+    }
   }
   if (lane == 0) scale[r] = sc;
 }
@@ -140,8 +198,16 @@ hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, 
   if (width % 8 || lds % 8 || ldd % 8) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   KTimerScope timer(KS_QUANT, st);
-  hipLaunchKernelGGL(quant_rows_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, st, src, lds, dst,
-                     ldd, scale, rows, width);
+  const dim3 grid((rows + 3) / 4);
+  if (width <= 8 * 512)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8>), grid, dim3(256), 0, st, src, lds, dst, ldd,
+                       scale, rows, width);
+  else if (width <= 32 * 512)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<T, 32>), grid, dim3(256), 0, st, src, lds, dst, ldd,
+                       scale, rows, width);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<T>, grid, dim3(256), 0, st, src, lds, dst, ldd, scale,
+                       rows, width);
   return hipGetLastError();
 }
 template hipError_t quant_rows<bf16_t>(const bf16_t*, int, fp8_t*, int, float*, int, int, hipStream_t);

@@ -58,7 +58,7 @@ def _decode(codes: torch.Tensor) -> np.ndarray:
 
 # ---------------------------------------------------------------- quantisation
 
-@pytest.mark.parametrize("rows,width", [(1, 8), (37, 520), (300, 3072), (4, 589824)])
+@pytest.mark.parametrize("rows,width", [(1, 8), (37, 520), (300, 3072), (9, 4104), (64, 15360), (4, 589824)])
 def test_quantize_rows_bit_exact(dit, rows, width):
     _say(f"quantize rows={rows} width={width}")
     x = _bf16((rows, width), 41, 3.0)
