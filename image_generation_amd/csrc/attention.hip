@@ -262,8 +262,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 // moves by k, O and the row sum scale by exactly 2^-k, and the e4m3 rounding of
 // 448 P is the same for every integer r (down to e4m3's subnormals): the result
 // matches quantising against the final row max rounded the same way.  The row
-// sum adds the quantised P (decoded back from the codes), so the weights that
-// multiply V sum to one.
+// sum is that of the quantised P, taken by one more MFMA of the P codes against
+// an all-ones operand, so the weights that multiply V sum to one.
 constexpr int AF8_BN = 64;
 constexpr int AF8_KRB = 144;                      // K row: 128 B + 16 pad (9 chunks)
 constexpr int AF8_VRB = 80;                       // V^T row: 64 B + 16 pad (5 chunks)
@@ -321,7 +321,13 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float mref = -INFINITY;    // integer-valued reference, exp2 units
-  float lsum = 0.f;          // sum of 448 * quantised P, relative to mref
+  // row sums of the quantised 448 P, accumulated by one more MFMA against an
+  // all-ones e4m3 operand (every row of the result is the column's sum)
+  f32x16 lacc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                           0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
   // per-lane load offsets (bytes inside a tile): K chunk c -> row c/9, slot c%9;
   // V^T chunk c2 -> row c2/5, slot c2%5 (the last slot of a row is padding)
@@ -413,12 +419,14 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
       // 2^(mref - mnew): an exact power of two (0 before the first tile)
       const float alpha = mref == -INFINITY ? 0.f : ldexpf(1.0f, (int)(mref - mnew));
       mref = mnew;
-      lsum *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int db = 0; db < ATT_D / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
+    // 448 P = 2^(t - mref + log2 448): the factor rides in the exponent
+    const float moff = mref - 8.807354922057604f;
     int pw[8];   // 32 e4m3 codes of P * 448, keys g*32 + 0..31
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -427,13 +435,9 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p[e] = fast_exp2(fmaf(sacc[kb][w4 * 4 + e], cs, -mref)) * 448.f;
+          p[e] = fast_exp2(fmaf(sacc[kb][w4 * 4 + e], cs, -moff));
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
-        pw[kb * 4 + w4] = w;
-        const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        lsum += (d0.x + d0.y) + (d1.x + d1.y);
+        pw[kb * 4 + w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
       }
     const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
@@ -444,12 +448,12 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[db], 0, 0, 0, 127,
                                                                  0, 127);
     }
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 127, 0, 127);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
-  const float lt = lsum + __shfl_xor(lsum, 32);
-  const float inv = sv[bh] / lt;
+  const float inv = sv[bh] / lacc[0];
   const int t = q0 + l32;
   if (t < L) {
     bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * ATT_D;
