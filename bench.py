@@ -43,16 +43,20 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 
 # HBM bytes per launch at the 1024px step from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch, scaled by a 1 GiB device copy: FETCH_SIZE reads 0.5 of the copied
-# bytes, WRITE_SIZE 1.0).  Valid only for the kernel source they were taken on: the
-# SHA-1 of that source file is checked at run time and traffic is reported as null
-# once it differs.
+# bytes, WRITE_SIZE 1.0).  Valid only for the device code they were taken on: the SHA-1
+# of that code's source region (from the `begin` marker up to the `end` marker) is
+# checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
     "gemm_lin1": {"bytes": 1207256 * 1024 + 232461 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
-                  "sha1": "ed503be76bb3b623f962ff0fb70d2ba88d105796"},
+                  "begin": "// ---------------------------------------------------------------- epilogues",
+                  "end": "// ---------------------------------------------------------------- fp32 path",
+                  "sha1": "b54f59566986567c413642bee78427579bfa585c"},
     "attention": {"bytes": 101506 * 1024 + 27691 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
-                  "sha1": "3ab66887ffa2b827d3a12bd6fc3a1233870b626d"},
+                  "begin": "constexpr int ATT_D = 128;",
+                  "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
+                  "sha1": "9f33d97ad07418f52f8e49547fc8777681459d72"},
 }
 
 
@@ -62,9 +66,11 @@ def measured_traffic(kernel):
     t = TRAFFIC_1024.get(kernel)
     if t is None:
         return None
-    with open(os.path.join(ROOT, t["source"]), "rb") as f:
-        if hashlib.sha1(f.read()).hexdigest() != t["sha1"]:
-            return None
+    with open(os.path.join(ROOT, t["source"])) as f:
+        src = f.read()
+    a, b = src.find(t["begin"]), src.find(t["end"])
+    if a < 0 or b < a or hashlib.sha1(src[a:b].encode()).hexdigest() != t["sha1"]:
+        return None
     return t["bytes"]
 
 

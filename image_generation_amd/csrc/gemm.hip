@@ -784,7 +784,16 @@ template <class Epi>
 static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st, int site) {
   KTimerScope timer(site, st);
   int maxM = 0, minN = 1 << 30;
-  for (int i = 0; i < ng; ++i) { maxM = max(maxM, gp[i].M); minN = min(minN, gp[i].N); }
+  // the direct-to-LDS kernel keeps per-lane byte offsets in 32 bits
+  bool offsets32 = true;
+  for (int i = 0; i < ng; ++i) {
+    maxM = max(maxM, gp[i].M);
+    minN = min(minN, gp[i].N);
+    const long long es = gp[i].A8 ? 1 : 2;
+    offsets32 = offsets32 && (long long)gp[i].M * gp[i].lda * es < (1LL << 31) &&
+                (long long)gp[i].N * gp[i].ldw * es < (1LL << 31);
+  }
+  if (gp[0].A8 && !offsets32) return hipErrorInvalidValue;
 #ifndef GEMM_NS
 #define GEMM_NS 2
 #define GEMM_SLAB 128
@@ -792,7 +801,7 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   if (gp[0].A8) return launch_cfg<256, 256, 2, 4, 2, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   if (maxM <= 64) return launch_cfg<32, 256, 1, 4, 0>(gp, ep, ng, st);
   // large problems: 256x256 tiles, 8 waves, fed by direct global->LDS loads
-  if (maxM >= 1024 && minN >= 1024)
+  if (maxM >= 1024 && minN >= 1024 && offsets32)
     return launch_cfg<256, 256, 2, 4, 1, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
 }
