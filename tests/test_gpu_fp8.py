@@ -168,6 +168,7 @@ FP8_BLOCK_CASES = [
     (3072, 24, 12288, 2, 16, 8, 10, "double", torch.bfloat16),
     (256, 2, 512, 2, 16, 6, 8, "single", torch.float32),
     (3072, 24, 12288, 1, 32, 12, 20, "single", torch.float32),
+    (256, 2, 512, 2, 0, 4, 8, "double", torch.float32),     # image tokens only
 ]
 
 

@@ -145,6 +145,9 @@ BLOCK_CASES = [
     (3072, 24, 12288, 2, 16, 8, 10, "double", torch.bfloat16),
     (256, 2, 512, 2, 24, 6, 8, "single", torch.float32),
     (3072, 24, 12288, 1, 40, 12, 20, "single", torch.float32),
+    # image tokens only (no text stream)
+    (256, 2, 512, 2, 0, 6, 8, "double", torch.float32),
+    (256, 2, 512, 1, 0, 5, 8, "single", torch.bfloat16),
 ]
 
 
