@@ -134,7 +134,7 @@ struct BlockWS {
   fp8_t* cat8;  // [B*L, D + F], scales s_att (attention part or whole row), s_hid
   float *su, *s_att, *s_hid;
   float* s_qkv;          // [3, B*H]: q, k, v scales per (b, h)
-  unsigned int* amax;    // [B*H] reduction scratch
+  unsigned int* amax;    // [3, B*H]: largest stored |q|, |k|, |v| per (b, h) (fp32 bits)
   // fp32 blocks (overlaying the buffers above): LN out, Q, K, V^T, attention | MLP
   float *u32, *q32, *k32, *vt32, *cat32;
 };
@@ -160,7 +160,7 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.s_att = c.take<float>(rows);
   w.s_hid = c.take<float>(rows);
   w.s_qkv = c.take<float>(3 * bh);
-  w.amax = c.take<unsigned int>(bh);
+  w.amax = c.take<unsigned int>(3 * bh);
   w.u32 = c32.take<float>(n);
   w.q32 = c32.take<float>(n);
   w.k32 = c32.take<float>(n);
@@ -341,14 +341,15 @@ hipError_t block_f32(const Dims& dm, const dit_block& blk, float* x, const float
   return gemm32_gated_residual(&g2, 1, x, D, gate, bs, &jm, st);
 }
 
-// per-(b, h) e4m3 copies of the QKV epilogue's Q, K (bf16) and V^T (fp16)
+// per-(b, h) e4m3 copies of the QKV epilogue's Q, K (bf16) and V^T (fp16); their
+// per-head amax was gathered by that epilogue into w.amax
 hipError_t quant_qkv(const Dims& dm, const BlockWS& w, hipStream_t st) {
   const size_t n = (size_t)dm.L * dm.d;
   const int bh = dm.B * dm.H;
   hipError_t e;
   if ((e = quant_slices<bf16_t>(w.q, n, bh, w.amax, w.q8, w.s_qkv, st))) return e;
-  if ((e = quant_slices<bf16_t>(w.k, n, bh, w.amax, w.k8, w.s_qkv + bh, st))) return e;
-  return quant_slices<f16_t>(w.vt, n, bh, w.amax, w.v8, w.s_qkv + 2 * bh, st);
+  if ((e = quant_slices<bf16_t>(w.k, n, bh, w.amax + bh, w.k8, w.s_qkv + bh, st))) return e;
+  return quant_slices<f16_t>(w.vt, n, bh, w.amax + 2 * bh, w.v8, w.s_qkv + 2 * bh, st);
 }
 
 // fp8 block (x fp32): e4m3 GEMM operands with per-token activation scales, e4m3
@@ -357,7 +358,8 @@ hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float
                      const float* rope, const BlockWS& w, hipStream_t st) {
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F, H = dm.H;
   const int DF = D + F, BH = B * H;
-  const QKVOut qo{w.q, w.k, w.vt, rope, D, H, dm.d};
+  QKVOut qo{w.q, w.k, w.vt, rope, D, H, dm.d};
+  qo.amax = w.amax;
   const float scale = 1.0f / sqrtf((float)dm.d);
   const float *sq = w.s_qkv, *sk = w.s_qkv + BH, *sv = w.s_qkv + 2 * BH;
   hipError_t e;
@@ -375,6 +377,7 @@ hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float
       return e;
     GemmProblem g[2] = {gp8(w.u8, D, w.su, blk.qkv[0], D, B * Li, 3 * D),
                         gp8(w.u8 + ti * D, D, w.su + ti, blk.qkv[1], D, B * Lt, 3 * D)};
+    if ((e = zero_u32(w.amax, 3 * BH, st))) return e;
     if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
     if ((e = quant_qkv(dm, w, st))) return e;
     if ((e = attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, sm, B, H, L, dm.d, scale, st)))
@@ -402,6 +405,7 @@ hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float
   if ((e = ln_modulate_fp8(x, w.u8, w.su, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st)))
     return e;
   const GemmProblem g1 = gp8(w.u8, D, w.su, blk.lin1, D, B * L, 3 * D + F);
+  if ((e = zero_u32(w.amax, 3 * BH, st))) return e;
   if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
   if ((e = quant_qkv(dm, w, st))) return e;
   if ((e = attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, jm, B, H, L, dm.d, scale, st)))

@@ -13,6 +13,8 @@
 // lane: coalesced stores, RoPE pairs in-register) or column-wise (4 consecutive
 // rows of one column per lane: the transposed V store), then calls the fused
 // epilogue functor.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -94,14 +96,65 @@ struct EpiGatedResidual {
   __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
+// Epilogues that also report the largest magnitude they stored, per slot
+// (kTrackAmax): row4 / col4 return the largest |value| before the store's rounding,
+// slot(r, c) names the slot of an output (-1: not tracked) and stored(slot, m)
+// applies that slot's rounding (round-to-nearest is monotonic, so rounding the
+// largest magnitude gives the largest stored magnitude).  The kernel folds these
+// into amax[slot] with an atomic max of the fp32 bit patterns (non-negative values
+// order like their bits).
+template <class E, class = void> struct TracksAmax : std::false_type {};
+template <class E>
+struct TracksAmax<E, std::void_t<decltype(E::kTrackAmax)>> : std::bool_constant<E::kTrackAmax> {};
+
+template <class E>
+__device__ __forceinline__ unsigned int* amax_of(const E& e) {
+  if constexpr (TracksAmax<E>::value) return e.amax_ptr();
+  else return nullptr;
+}
+
+// One output's magnitude m straight into amax[sl] (tiles whose wave spans slots).
+template <class Epi>
+__device__ __forceinline__ void track_amax(const Epi& epi, int sl, float m, unsigned int* amax) {
+  if (sl >= 0 && amax) atomicMax(amax + sl, __float_as_uint(epi.stored(sl, m)));
+}
+
+__device__ __forceinline__ float amax4(float a, float b, float c, float d) {
+  return fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d)));
+}
+
 // Split the fused projection into head-major Q, K (bf16, rotated) and V^T (fp16).
-struct EpiQKV {
+// AMAX: the largest stored magnitude of every (tensor, b, h) is gathered too into
+// amax [3, B, H] (q, k, v: the per-head e4m3 scales of the fp8 path).
+template <bool AMAX>
+struct EpiQKVT {
+  static constexpr bool kTrackAmax = AMAX;
   bf16_t* q; bf16_t* k; f16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
   int D, H, d; RowMap map;
+  unsigned int* amax;
+  __device__ __forceinline__ unsigned int* amax_ptr() const { return amax; }
   __device__ __forceinline__ bool colmajor(int n0, int bn) const {
     return n0 >= 2 * D && n0 + bn <= 3 * D;
   }
-  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+  __device__ __forceinline__ int slot(int r, int c) const {
+    const int which = c / D;
+    const int h = (c - which * D) / d;
+    int b, t; map.token(r, b, t);
+    return (which * map.B + b) * H + h;
+  }
+  // The slot shared by rows [r0, r1] at column c, or -2 when they span several.
+  // Within the image rows and within the text rows the batch index never
+  // decreases, so equal end slots on one side of that split cover the range.
+  __device__ __forceinline__ int slot_span(int r0, int r1, int c) const {
+    const int s0 = slot(r0, c);
+    if (s0 != slot(r1, c)) return -2;
+    if (map.stream_major) {
+      const int ni = map.B * map.Li;
+      if ((r0 + map.base < ni) != (r1 + map.base < ni)) return -2;
+    }
+    return s0;
+  }
+  __device__ __forceinline__ float row4(int r, int c, f32x4 v) const {
     const int which = c / D;
     const int cc = c - which * D;
     const int h = cc / d;
@@ -117,38 +170,58 @@ struct EpiQKV {
       float o3 = v[2] * cs[3] + v[3] * cs[2];
       bf16_t* dst = which == 0 ? q : k;
       store_bf16x4(dst + (bh * map.L + t) * d + dd, o0, o1, o2, o3);
-    } else {
-      uint16_t* dst = (uint16_t*)vt + (bh * d + dd) * map.L + t;
-      const size_t L = map.L;
-      dst[0] = f2h(v[0]);
-      dst[L] = f2h(v[1]);
-      dst[2 * L] = f2h(v[2]);
-      dst[3 * L] = f2h(v[3]);
+      return amax4(o0, o1, o2, o3);
     }
+    uint16_t* dst = (uint16_t*)vt + (bh * d + dd) * map.L + t;
+    const size_t L = map.L;
+    const f16_t h0 = (f16_t)v[0], h1 = (f16_t)v[1], h2 = (f16_t)v[2], h3 = (f16_t)v[3];
+    dst[0] = __builtin_bit_cast(uint16_t, h0);
+    dst[L] = __builtin_bit_cast(uint16_t, h1);
+    dst[2 * L] = __builtin_bit_cast(uint16_t, h2);
+    dst[3 * L] = __builtin_bit_cast(uint16_t, h3);
+    return amax4(v[0], v[1], v[2], v[3]);
+  }
+  // Q, K slots store bf16, V slots fp16
+  __device__ __forceinline__ float stored(int slot, float m) const {
+    return slot < 2 * map.B * H ? bf2f(f2bf(m)) : (float)(f16_t)m;
   }
   // V columns, 4 consecutive rows (tokens t..t+3 of one batch row), fp16
-  __device__ __forceinline__ void col4(int r, int c, f32x4 v) const {
+  __device__ __forceinline__ float col4(int r, int c, f32x4 v) const {
     const int cc = c - 2 * D;
     const int h = cc / d;
     const int dd = cc - h * d;
     int b, t; map.token(r, b, t);
+    const f16_t h0 = (f16_t)v[0], h1 = (f16_t)v[1], h2 = (f16_t)v[2], h3 = (f16_t)v[3];
     uint2 u;
-    u.x = pack_f16x2(v[0], v[1]);
-    u.y = pack_f16x2(v[2], v[3]);
+    u.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    u.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
     *(uint2*)(vt + (((size_t)b * H + h) * d + dd) * map.L + t) = u;
+    return amax4(v[0], v[1], v[2], v[3]);
   }
 };
 
+using EpiQKV = EpiQKVT<false>;
+
 // Single-stream linear1: columns [0, 3D) are Q/K/V, the rest the GELU MLP branch.
-struct EpiLinear1 {
-  EpiQKV qkv; EpiGeluBf16 gelu; int n_qkv;
+template <bool AMAX>
+struct EpiLinear1T {
+  static constexpr bool kTrackAmax = AMAX;
+  EpiQKVT<AMAX> qkv; EpiGeluBf16 gelu; int n_qkv;
+  __device__ __forceinline__ unsigned int* amax_ptr() const { return qkv.amax; }
   __device__ __forceinline__ bool colmajor(int n0, int bn) const { return qkv.colmajor(n0, bn); }
-  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
-    if (c < n_qkv) qkv.row4(r, c, v);
-    else gelu.row4(r, c - n_qkv, v);
+  __device__ __forceinline__ int slot(int r, int c) const { return c < n_qkv ? qkv.slot(r, c) : -1; }
+  __device__ __forceinline__ int slot_span(int r0, int r1, int c) const {
+    return c < n_qkv ? qkv.slot_span(r0, r1, c) : -1;
   }
-  __device__ __forceinline__ void col4(int r, int c, f32x4 v) const { qkv.col4(r, c, v); }
+  __device__ __forceinline__ float row4(int r, int c, f32x4 v) const {
+    if (c < n_qkv) return qkv.row4(r, c, v);
+    gelu.row4(r, c - n_qkv, v);
+    return 0.f;
+  }
+  __device__ __forceinline__ float col4(int r, int c, f32x4 v) const { return qkv.col4(r, c, v); }
+  __device__ __forceinline__ float stored(int slot, float m) const { return qkv.stored(slot, m); }
 };
+using EpiLinear1 = EpiLinear1T<false>;
 
 // ---------------------------------------------------------------- kernel
 
@@ -525,7 +598,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   const Epi epi = g1 ? p.e[1] : p.e[0];
   float* slice = (float*)(stage(wave / WPS) + (wave % WPS) * SLICE);
   const bool cmaj = epi.colmajor(n0, BN);
-#pragma unroll
+  constexpr bool kAmax = TracksAmax<Epi>::value;
+  unsigned int* const amax_p = amax_of(epi);
+  // A wave's BN / WN = 64 columns start on a multiple of 64, so with head size and
+  // tensor widths multiples of 64 they lie in one tracked tensor and head (or in
+  // none); its rows usually lie in one batch row.  Then one slot covers the wave's
+  // whole tile and the lanes only keep a running max; otherwise every output goes
+  // to memory at once.
+  float am = 0.f;
+  int aslot = -1;
+  bool one_slot = false;
+  if constexpr (kAmax) {
+    static_assert(BN / WN == 64, "amax tracking assumes 64-column wave tiles");
+    const int r_lo = min(m0 + wrow, g.M - 1), r_hi = min(m0 + wrow + WROWS - 1, g.M - 1);
+    aslot = epi.slot_span(r_lo, r_hi, min(n0 + wcol, g.N - 1));
+    one_slot = aslot != -2;
+  }
+#pragma clang loop unroll(full)
   for (int j = 0; j < TN; ++j) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -548,7 +637,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
           f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
           if constexpr (F8) v *= *(const f32x4*)(g.sw + col) * g.sa[row];
           if (g.bias) v += *(const f32x4*)(g.bias + col);
-          epi.row4(row, col, v);
+          if constexpr (kAmax) {
+            const float m = epi.row4(row, col, v);
+            if (one_slot) am = fmaxf(am, m);
+            else track_amax(epi, epi.slot(row, col), m, amax_p);
+          } else {
+            epi.row4(row, col, v);
+          }
         }
       }
     } else {
@@ -567,13 +662,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
           v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
           if constexpr (F8) v *= *(const f32x4*)(g.sa + row) * g.sw[col];
           if (g.bias) v += g.bias[col];
-          epi.col4(row, col, v);
+          if constexpr (kAmax) {
+            const float m = epi.col4(row, col, v);
+            if (one_slot) am = fmaxf(am, m);
+            else track_amax(epi, epi.slot(row, col), m, amax_p);
+          } else {
+            epi.col4(row, col, v);
+          }
         }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if constexpr (kAmax) {
+    if (amax_p && one_slot && aslot >= 0) {   // one atomic per wave
+      float m = am;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane == 0) atomicMax(amax_p + aslot, __float_as_uint(epi.stored(aslot, m)));
+    }
   }
 }
 
@@ -841,15 +950,29 @@ template hipError_t gemm_gated_residual<float>(const GemmProblem*, int, float*, 
 
 hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap* map,
                     hipStream_t st) {
+  if (o.amax) {
+    EpiQKVT<true> e[2];
+    for (int i = 0; i < ng; ++i)
+      e[i] = EpiQKVT<true>{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i], o.amax};
+    return launch(g, e, ng, st, KS_GEMM_QKV);
+  }
   EpiQKV e[2];
-  for (int i = 0; i < ng; ++i) e[i] = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i]};
+  for (int i = 0; i < ng; ++i)
+    e[i] = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i], nullptr};
   return launch(g, e, ng, st, KS_GEMM_QKV);
 }
 
 hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map,
                         bf16_t* cat, int ldcat, hipStream_t st) {
+  if (o.amax) {
+    EpiLinear1T<true> e;
+    e.qkv = EpiQKVT<true>{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map, o.amax};
+    e.gelu = EpiGeluBf16{cat, ldcat, o.D};
+    e.n_qkv = 3 * o.D;
+    return launch(&g, &e, 1, st, KS_GEMM_LIN1);
+  }
   EpiLinear1 e;
-  e.qkv = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map};
+  e.qkv = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map, nullptr};
   e.gelu = EpiGeluBf16{cat, ldcat, o.D};
   e.n_qkv = 3 * o.D;
   return launch(&g, &e, 1, st, KS_GEMM_LIN1);

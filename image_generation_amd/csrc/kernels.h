@@ -46,6 +46,9 @@ struct QKVOut {
   f16_t* vt;          // [B, H, d, L] fp16
   const float* rope;  // [L, d/2, 2] (cos, sin)
   int D, H, d;
+  // optional [3, B, H]: largest stored |q|, |k|, |v| per (b, h) as fp32 bits,
+  // accumulated with atomic max (zero it before the GEMM); direct-to-LDS kernel only
+  unsigned int* amax = nullptr;
 };
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st);
@@ -111,10 +114,12 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
 template <class T>
 hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, int rows, int width,
                       hipStream_t st);
-// One scale per contiguous slice of n elements (nslices slices); amax_tmp [nslices].
+// One scale per contiguous slice of n elements (nslices slices), from each slice's
+// largest magnitude given as fp32 bits in amax[nslices] (the QKV epilogues gather it).
 template <class T>
-hipError_t quant_slices(const T* src, size_t n, int nslices, unsigned int* amax_tmp, fp8_t* dst,
-                        float* scale, hipStream_t st);
+hipError_t quant_slices(const T* src, size_t n, int nslices, const unsigned int* amax,
+                        fp8_t* dst, float* scale, hipStream_t st);
+hipError_t zero_u32(unsigned int* p, int n, hipStream_t st);
 
 // fp8 attention: q8, k8 e4m3 [B, H, L, d], vt8 e4m3 [B, H, d, L], one fp32 scale per
 // (b, h) for each of q, k, v; output bf16 as attention_bf16.

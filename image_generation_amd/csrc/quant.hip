@@ -146,30 +146,8 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T* __restrict
   if (lane == 0) scale[r] = sc;
 }
 
-// amax of each contiguous slice of n elements (one slice per blockIdx.y); the
-// float bit pattern of a non-negative value orders like the value, so an
-// integer atomic max combines the blocks.  amax must be zeroed beforehand.
-template <class T>
-__global__ __launch_bounds__(256) void amax_slices_kernel(const T* __restrict__ src, size_t n,
-                                                          unsigned int* __restrict__ amax) {
-  const T* s = src + (size_t)blockIdx.y * n;
-  float m = 0.f;
-  for (size_t c = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; c < n; c += (size_t)gridDim.x * 2048) {
-    float v[8];
-    Load8<T>::get(s + c, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  }
-  m = wave_max(m);
-  __shared__ float sm[4];
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float b = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    atomicMax(amax + blockIdx.y, __float_as_uint(b));
-  }
-}
-
+// e4m3 codes of one contiguous slice per blockIdx.y, scaled by that slice's given
+// amax (fp32 bits; a non-negative float's bits order like its value).
 template <class T>
 __global__ __launch_bounds__(256) void quant_slices_kernel(const T* __restrict__ src, size_t n,
                                                            const unsigned int* __restrict__ amax,
@@ -214,23 +192,26 @@ template hipError_t quant_rows<bf16_t>(const bf16_t*, int, fp8_t*, int, float*, 
 template hipError_t quant_rows<f16_t>(const f16_t*, int, fp8_t*, int, float*, int, int, hipStream_t);
 
 template <class T>
-hipError_t quant_slices(const T* src, size_t n, int nslices, unsigned int* amax_tmp, fp8_t* dst,
-                        float* scale, hipStream_t st) {
+hipError_t quant_slices(const T* src, size_t n, int nslices, const unsigned int* amax,
+                        fp8_t* dst, float* scale, hipStream_t st) {
   if (n % 8) return hipErrorInvalidValue;
   if (nslices == 0 || n == 0) return hipSuccess;
   KTimerScope timer(KS_QUANT, st);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((nslices + 255) / 256), dim3(256), 0, st, amax_tmp,
-                     nslices);
   size_t blocks = (n / 8 + 255) / 256;
   const int bx = (int)(blocks < 64 ? blocks : 64);
-  hipLaunchKernelGGL(amax_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax_tmp);
-  hipLaunchKernelGGL(quant_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax_tmp,
+  hipLaunchKernelGGL(quant_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax,
                      dst, scale);
   return hipGetLastError();
 }
-template hipError_t quant_slices<bf16_t>(const bf16_t*, size_t, int, unsigned int*, fp8_t*, float*,
-                                         hipStream_t);
-template hipError_t quant_slices<f16_t>(const f16_t*, size_t, int, unsigned int*, fp8_t*, float*,
-                                           hipStream_t);
+template hipError_t quant_slices<bf16_t>(const bf16_t*, size_t, int, const unsigned int*, fp8_t*,
+                                         float*, hipStream_t);
+template hipError_t quant_slices<f16_t>(const f16_t*, size_t, int, const unsigned int*, fp8_t*,
+                                        float*, hipStream_t);
+
+hipError_t zero_u32(unsigned int* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 }  // namespace dit

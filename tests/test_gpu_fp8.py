@@ -169,6 +169,9 @@ FP8_BLOCK_CASES = [
     (256, 2, 512, 2, 16, 6, 8, "single", torch.float32),
     (3072, 24, 12288, 1, 32, 12, 20, "single", torch.float32),
     (256, 2, 512, 2, 0, 4, 8, "double", torch.float32),     # image tokens only
+    # one 128-row GEMM wave tile runs from batch 1's image rows through batch 0's
+    # text rows into batch 1's text rows (Li = 112, Lt = 16, B = 2)
+    (256, 2, 512, 2, 16, 8, 14, "double", torch.float32),
 ]
 
 
