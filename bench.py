@@ -47,11 +47,11 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1203183 * 1024 + 232516 * 1024,
+    "gemm_lin1": {"bytes": 1134678 * 1024 + 230553 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "f23d54df5aa6de72fcdef19a67f978138cdd9c51"},
+                  "sha1": "cf1d8715d45fac840729630163064785fca6ee75"},
     "attention": {"bytes": 101506 * 1024 + 27691 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",

@@ -416,10 +416,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
 }
 
 // Variant fed by gfx950's direct global->LDS loads (global_load_lds_dwordx4): each
-// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so padded
-// rows are filled by giving every lane the global chunk that belongs at its LDS
-// slot (the last 16 B of a row is padding: it re-reads the row's last chunk).
-// No staging registers, no LDS store instructions.
+// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so a
+// permuted (or padded) row layout is built by giving every lane the global chunk
+// that belongs at its LDS slot: 8 lanes still cover one 128-byte row segment.
+// (Padded rows re-read the row's last chunk into the pad.)  No staging
+// registers, no LDS store instructions.
 //
 // Pipeline: NS stages, each holding a K slab of SLAB bytes per row for the A and
 // the W tile (SLAB / 2 bf16 or SLAB e4m3 values), so NS - 1 slabs are in flight
@@ -435,24 +436,134 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt at max
 }
 
+// Epilogue of the direct-to-LDS kernels: a wave parks its accumulators, 32
+// columns by PR = WROWS / EH rows at a time, in its LDS slice, then hands row- or
+// column-contiguous quads to the epilogue functor (dequantised first for e4m3).
+// Accumulator element e of block (i, j) is row i*32 + (e/4)*8 + (lane/32)*4 + e%4,
+// column j*32 + lane%32 of the wave's tile.
+template <int BN, int WN, int TM, int TN, int WROWS, int EH, bool F8, class Epi>
+__device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& epi,
+                                             f32x16 (&acc)[TM][TN], float* slice, int m0, int n0,
+                                             int wrow, int wcol, int lane) {
+  constexpr int PR = WROWS / EH;
+  const bool cmaj = epi.colmajor(n0, BN);
+  constexpr bool kAmax = TracksAmax<Epi>::value;
+  unsigned int* const amax_p = amax_of(epi);
+  // A wave's BN / WN = 64 columns start on a multiple of 64, so with head size and
+  // tensor widths multiples of 64 they lie in one tracked tensor and head (or in
+  // none); its rows usually lie in one batch row.  Then one slot covers the wave's
+  // whole tile and the lanes only keep a running max; otherwise every output goes
+  // to memory at once.
+  float am = 0.f;
+  int aslot = -1;
+  bool one_slot = false;
+  if constexpr (kAmax) {
+    static_assert(BN / WN == 64, "amax tracking assumes 64-column wave tiles");
+    const int r_lo = min(m0 + wrow, g.M - 1), r_hi = min(m0 + wrow + WROWS - 1, g.M - 1);
+    aslot = epi.slot_span(r_lo, r_hi, min(n0 + wcol, g.N - 1));
+    one_slot = aslot != -2;
+  }
+#pragma clang loop unroll(full)
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int h = 0; h < EH; ++h) {
+#pragma unroll
+      for (int i = 0; i < TM / EH; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          slice[(i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * EPI_LDS + (lane & 31)] =
+              acc[h * (TM / EH) + i][j][e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int cbase = n0 + wcol + j * 32;
+      const int rbase = m0 + wrow + h * PR;
+      if (!cmaj) {
+#pragma unroll
+        for (int ps = 0; ps < PR / 8; ++ps) {
+          const int rl = ps * 8 + (lane >> 3);
+          const int cl = (lane & 7) * 4;
+          const int row = rbase + rl;
+          const int col = cbase + cl;
+          if (row < g.M && col < g.N) {
+            f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
+            if constexpr (F8) v *= *(const f32x4*)(g.sw + col) * g.sa[row];
+            if (g.bias) v += *(const f32x4*)(g.bias + col);
+            if constexpr (kAmax) {
+              const float m = epi.row4(row, col, v);
+              if (one_slot) am = fmaxf(am, m);
+              else track_amax(epi, epi.slot(row, col), m, amax_p);
+            } else {
+              epi.row4(row, col, v);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ps = 0; ps < PR / 4 * 32 / 64; ++ps) {
+          const int idx = ps * 64 + lane;
+          const int rq = idx % (PR / 4);
+          const int cl = idx / (PR / 4);
+          const int row = rbase + rq * 4;
+          const int col = cbase + cl;
+          if (row + 3 < g.M && col < g.N) {
+            f32x4 v;
+            v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
+            v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
+            v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
+            v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
+            if constexpr (F8) v *= *(const f32x4*)(g.sa + row) * g.sw[col];
+            if (g.bias) v += g.bias[col];
+            if constexpr (kAmax) {
+              const float m = epi.col4(row, col, v);
+              if (one_slot) am = fmaxf(am, m);
+              else track_amax(epi, epi.slot(row, col), m, amax_p);
+            } else {
+              epi.col4(row, col, v);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  if constexpr (kAmax) {
+    if (amax_p && one_slot && aslot >= 0) {   // one atomic per wave
+      float m = am;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane == 0) atomicMax(amax_p + aslot, __float_as_uint(epi.stored(aslot, m)));
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, bool F8, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
   constexpr int WROWS = BM / WM;
-  constexpr int ROWB = SLAB + 16;             // padded LDS row (bytes)
+  // 128-byte slabs: unpadded rows whose 16-byte chunks are permuted by
+  // chunk ^ ((row >> 1) & 7), so the 16 consecutive rows that one LDS read cycle
+  // serves at one chunk hit 16 distinct bank groups; other slab widths pad each
+  // row by 16 bytes for the same effect
+  constexpr bool SWZ = SLAB == 128;
+  constexpr int ROWB = SWZ ? SLAB : SLAB + 16;  // LDS row pitch (bytes)
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per LDS row
   constexpr int AB = BM * ROWB, BB = BN * ROWB, SB = AB + BB;
   constexpr int NI = SB / 1024;               // 1-KB load instructions per stage
   constexpr int IPW = NI / NW;
-  constexpr int SLICE = WROWS * EPI_LDS * 4;  // bytes of one wave's parked epilogue slice
+  constexpr int EH = SWZ ? 2 : 1;             // epilogue passes over a wave's rows
+  constexpr int PR = WROWS / EH;              // rows parked per pass
+  constexpr int SLICE = PR * EPI_LDS * 4;     // bytes of one wave's parked epilogue slice
   constexpr int WPS = SB / SLICE;             // epilogue slices per stage
   static_assert(NS >= 2 && NS <= 4, "2..4 stages");
   static_assert(AB % 1024 == 0 && BB % 1024 == 0 && NI % NW == 0, "stage / wave mismatch");
   static_assert(WPS * NS >= NW, "epilogue slices must fit the stages");
   static_assert(SLAB % (F8 ? 64 : 32) == 0, "slab holds whole MFMA K steps");
-  static_assert(ROWB % 32 == 16, "row pitch: an odd number of 16-byte chunks");
+  static_assert(SWZ || ROWB % 32 == 16, "row pitch: an odd number of 16-byte chunks");
   __shared__ __attribute__((aligned(1024))) char st0[SB];
   __shared__ __attribute__((aligned(1024))) char st1[SB];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? SB : 16];
@@ -496,7 +607,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     const bool isb = (wave * IPW + j) * 1024 >= AB;
     const int o2 = isb ? off - AB : off;
     const int row = o2 / ROWB;
-    const int slot = min((o2 - row * ROWB) >> 4, CPR - 2);
+    const int slot = SWZ ? ((o2 - row * ROWB) >> 4) ^ ((row >> 1) & 7)
+                         : min((o2 - row * ROWB) >> 4, CPR - 2);
     voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw * ES + slot * 16
                   : min(m0 + row, g.M - 1) * g.lda * ES + slot * 16;
   }
@@ -513,6 +625,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   const int frow = lane & 31;
   const int wrow = wm * WROWS;
   const int wcol = wn * (BN / WN);
+  // byte offset within an LDS row of the 16-byte chunk c of a fragment row: bf16
+  // lanes 32..63 take the row's next chunk (K 8..15 of a 16-deep step), fp8 lanes
+  // the next pair of chunks (K 32..63 of a 64-deep step); the fragment rows of a
+  // lane are frow + multiples of 32, so their swizzle is (frow >> 1) & 7
+  const int hi = lane >> 5, swz = SWZ ? (frow >> 1) & 7 : 0;
+  auto xo = [&](int c) { return ((c + hi) ^ swz) << 4; };
+  auto xo8 = [&](int c) { return ((c + 2 * hi) ^ swz) << 4; };
 
 #define GEMM_DMA(stg, kt)                                                                \
   {                                                                                      \
@@ -527,21 +646,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   // read while the MFMAs of step kk run
 #define GEMM_COMPUTE(stg)                                                                \
   {                                                                                      \
-    const char* a_s = (const char*)(stg) + (lane >> 5) * 16;                             \
-    const char* b_s = (const char*)(stg) + AB + (lane >> 5) * 16;                        \
+    const char* a_s = (const char*)(stg);                                                \
+    const char* b_s = (const char*)(stg) + AB;                                           \
     constexpr int KS = SLAB / 32;                                                        \
     bf16x8 af[2][TM], bw[2][TN];                                                         \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
-        af[0][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB);                \
+        af[0][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB + xo(0));        \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
-        bw[0][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB);                \
+        bw[0][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB + xo(0));        \
     _Pragma("unroll") for (int kk = 0; kk < KS; ++kk) {                                 \
       const int cb = kk & 1, nb = cb ^ 1;                                                \
       if (kk + 1 < KS) {                                                                 \
         _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
-            af[nb][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB + (kk + 1) * 32); \
+            af[nb][i] = *(const bf16x8*)(a_s + (wrow + i * 32 + frow) * ROWB + xo(2 * kk + 2)); \
         _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
-            bw[nb][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB + (kk + 1) * 32); \
+            bw[nb][j] = *(const bf16x8*)(b_s + (wcol + j * 32 + frow) * ROWB + xo(2 * kk + 2)); \
       }                                                                                  \
       _Pragma("unroll") for (int i = 0; i < TM; ++i)                                     \
           _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
@@ -556,13 +675,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     _Pragma("unroll") for (int kk = 0; kk < SLAB / 64; ++kk) {                          \
       i32x8 af[TM], bw[TN];                                                              \
       _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                   \
-        const char* q_ = a_s + (wrow + i * 32 + frow) * ROWB + kk * 64 + (lane >> 5) * 32; \
-        const i32x4 lo_ = *(const i32x4*)q_, hi_ = *(const i32x4*)(q_ + 16);             \
+        const char* q_ = a_s + (wrow + i * 32 + frow) * ROWB;                            \
+        const i32x4 lo_ = *(const i32x4*)(q_ + xo8(4 * kk)),                             \
+                    hi_ = *(const i32x4*)(q_ + xo8(4 * kk + 1));                         \
         af[i] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};     \
       }                                                                                  \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                   \
-        const char* q_ = b_s + (wcol + j * 32 + frow) * ROWB + kk * 64 + (lane >> 5) * 32; \
-        const i32x4 lo_ = *(const i32x4*)q_, hi_ = *(const i32x4*)(q_ + 16);             \
+        const char* q_ = b_s + (wcol + j * 32 + frow) * ROWB;                            \
+        const i32x4 lo_ = *(const i32x4*)(q_ + xo8(4 * kk)),                             \
+                    hi_ = *(const i32x4*)(q_ + xo8(4 * kk + 1));                         \
         bw[j] = i32x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};     \
       }                                                                                  \
       _Pragma("unroll") for (int i = 0; i < TM; ++i)                                     \
@@ -596,94 +717,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 #undef GEMM_COMPUTE_F8
 
   const Epi epi = g1 ? p.e[1] : p.e[0];
-  float* slice = (float*)(stage(wave / WPS) + (wave % WPS) * SLICE);
-  const bool cmaj = epi.colmajor(n0, BN);
-  constexpr bool kAmax = TracksAmax<Epi>::value;
-  unsigned int* const amax_p = amax_of(epi);
-  // A wave's BN / WN = 64 columns start on a multiple of 64, so with head size and
-  // tensor widths multiples of 64 they lie in one tracked tensor and head (or in
-  // none); its rows usually lie in one batch row.  Then one slot covers the wave's
-  // whole tile and the lanes only keep a running max; otherwise every output goes
-  // to memory at once.
-  float am = 0.f;
-  int aslot = -1;
-  bool one_slot = false;
-  if constexpr (kAmax) {
-    static_assert(BN / WN == 64, "amax tracking assumes 64-column wave tiles");
-    const int r_lo = min(m0 + wrow, g.M - 1), r_hi = min(m0 + wrow + WROWS - 1, g.M - 1);
-    aslot = epi.slot_span(r_lo, r_hi, min(n0 + wcol, g.N - 1));
-    one_slot = aslot != -2;
-  }
-#pragma clang loop unroll(full)
-  for (int j = 0; j < TN; ++j) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        slice[(i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * EPI_LDS + (lane & 31)] =
-            acc[i][j][e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int cbase = n0 + wcol + j * 32;
-    if (!cmaj) {
-#pragma unroll
-      for (int ps = 0; ps < WROWS / 8; ++ps) {
-        const int rl = ps * 8 + (lane >> 3);
-        const int cl = (lane & 7) * 4;
-        const int row = m0 + wrow + rl;
-        const int col = cbase + cl;
-        if (row < g.M && col < g.N) {
-          f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
-          if constexpr (F8) v *= *(const f32x4*)(g.sw + col) * g.sa[row];
-          if (g.bias) v += *(const f32x4*)(g.bias + col);
-          if constexpr (kAmax) {
-            const float m = epi.row4(row, col, v);
-            if (one_slot) am = fmaxf(am, m);
-            else track_amax(epi, epi.slot(row, col), m, amax_p);
-          } else {
-            epi.row4(row, col, v);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ps = 0; ps < WROWS / 4 * 32 / 64; ++ps) {
-        const int idx = ps * 64 + lane;
-        const int rq = idx % (WROWS / 4);
-        const int cl = idx / (WROWS / 4);
-        const int row = m0 + wrow + rq * 4;
-        const int col = cbase + cl;
-        if (row + 3 < g.M && col < g.N) {
-          f32x4 v;
-          v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
-          v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
-          v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
-          v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
-          if constexpr (F8) v *= *(const f32x4*)(g.sa + row) * g.sw[col];
-          if (g.bias) v += g.bias[col];
-          if constexpr (kAmax) {
-            const float m = epi.col4(row, col, v);
-            if (one_slot) am = fmaxf(am, m);
-            else track_amax(epi, epi.slot(row, col), m, amax_p);
-          } else {
-            epi.col4(row, col, v);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-  if constexpr (kAmax) {
-    if (amax_p && one_slot && aslot >= 0) {   // one atomic per wave
-      float m = am;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      if (lane == 0) atomicMax(amax_p + aslot, __float_as_uint(epi.stored(aslot, m)));
-    }
-  }
+  dma_epilogue<BN, WN, TM, TN, WROWS, EH, F8>(
+      g, epi, acc, (float*)(stage(wave / WPS) + (wave % WPS) * SLICE), m0, n0, wrow, wcol, lane);
 }
 
 // ---------------------------------------------------------------- fp32 path
