@@ -782,6 +782,9 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
       return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: cache buffers NULL or misaligned");
     if (std::isnan(cache->threshold))
       return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: NaN threshold");
+    if (cache->warmup_steps < 0 || cache->max_skips < 0 || cache->steps_done < 0 ||
+        cache->skip_run < 0)
+      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: negative cache policy field");
   }
   const size_t need = ws_size(dm, DIT_WS_STEP, 0);
   if (ws_bytes < need)
@@ -816,7 +819,11 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
     DIT_CHECK_HIP(hipStreamSynchronize(st));
     if (h.nonfinite) return fail(DIT_ERR_NONFINITE, "dit_denoise_step: non-finite residual");
     rel = h.rel;
-    skip = h.skip;
+    // the rel test, then the policy: no skip during warm-up nor past max_skips in a row
+    skip = h.skip && cache->steps_done >= cache->warmup_steps &&
+           (cache->max_skips == 0 || cache->skip_run < cache->max_skips);
+    cache->steps_done += 1;
+    cache->skip_run = skip ? cache->skip_run + 1 : 0;
   }
   if (skip) {
     DIT_CHECK_HIP(fbc_apply(w.x, cache->cached, B, Lt, Li, D, st));

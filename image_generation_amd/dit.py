@@ -53,7 +53,8 @@ class DitModel(Structure):
 
 class DitFBCache(Structure):
     _fields_ = [("enabled", c_int), ("threshold", c_float), ("has_anchor", c_int),
-                ("anchor", c_void_p), ("cached", c_void_p)]
+                ("anchor", c_void_p), ("cached", c_void_p), ("warmup_steps", c_int),
+                ("max_skips", c_int), ("steps_done", c_int), ("skip_run", c_int)]
 
 
 class DitStepInfo(Structure):
@@ -420,14 +421,23 @@ class FBCache:
     """Caller-held First-Block-Cache state (device buffers + the ctypes struct)."""
 
     def __init__(self, B: int, Li: int, D: int, threshold: float, enabled: bool = True,
-                 device="cuda"):
+                 device="cuda", warmup_steps: int = 0, max_skips: int = 0):
         self.anchor = torch.zeros((B, Li, D), dtype=torch.float32, device=device)
         self.cached = torch.zeros((B, Li, D), dtype=torch.float32, device=device)
-        self.c = DitFBCache(int(enabled), float(threshold), 0, _ptr(self.anchor), _ptr(self.cached))
+        self.c = DitFBCache(int(enabled), float(threshold), 0, _ptr(self.anchor), _ptr(self.cached),
+                            int(warmup_steps), int(max_skips), 0, 0)
 
     @property
     def has_anchor(self) -> bool:
         return bool(self.c.has_anchor)
+
+    @property
+    def steps_done(self) -> int:
+        return int(self.c.steps_done)
+
+    @property
+    def skip_run(self) -> int:
+        return int(self.c.skip_run)
 
 
 def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,

@@ -148,6 +148,16 @@ typedef struct dit_fbcache {
                      /* last fully computed step                                */
   float* cached;     /* device fp32 [B, Li, D]: image hidden after the last     */
                      /* block minus image hidden after block 0, same step       */
+  /* Skip policy on top of the rel test (>= 0 each; zero-initialised = plain test).
+   * Warm-up and the cache's threshold as the tuning levers: "Optimization ledger",
+   * the optimisation table (warm-up of a step cache); the VisualGen article on
+   * FLUX Klein, Cache-DiT paragraph (residual-difference threshold). */
+  int warmup_steps;  /* the first warmup_steps steps taken with the cache enabled  */
+                     /* compute in full whatever rel is                         */
+  int max_skips;     /* after max_skips consecutive skipped steps the next step  */
+                     /* computes in full; 0: no limit                           */
+  int steps_done;    /* in/out: steps taken with the cache enabled              */
+  int skip_run;      /* in/out: consecutive skipped steps ending at the last one */
 } dit_fbcache;
 
 typedef struct dit_step_info {

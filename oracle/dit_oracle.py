@@ -44,7 +44,7 @@ __all__ = [
     "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
     "linear", "rope_table", "apply_rope", "attention", "attention_naive",
     "double_block", "single_block", "final_layer", "fbcache_rel",
-    "fbcache_decide", "euler_update", "cfg_combine", "time_embed",
+    "fbcache_decide", "fbcache_policy", "euler_update", "cfg_combine", "time_embed",
     "modulation_vectors", "denoise_step", "FBCacheState", "to64",
     "linear_fp8", "attention_fp8", "image_positions",
 ]
@@ -373,6 +373,20 @@ def fbcache_decide(rel: float, threshold: float) -> bool:
     return bool(rel < threshold)
 
 
+def fbcache_policy(test_skips: bool, steps_done: int, warmup_steps: int, skip_run: int,
+                   max_skips: int) -> bool:
+    """Skip policy on top of the rel test (R34, R35): a step whose test says skip
+    still computes in full while it is one of the first ``warmup_steps`` steps taken
+    with the cache, or when ``max_skips`` (> 0) steps in a row were just skipped."""
+    if not test_skips:
+        return False
+    if steps_done < warmup_steps:
+        return False
+    if max_skips > 0 and skip_run >= max_skips:
+        return False
+    return True
+
+
 def euler_update(x, v, sigma_i, sigma_next):
     """x <- x + (sigma_{i+1} - sigma_i) v, integrating sigma from 1 to 0 (R16)."""
     return x + (sigma_next - sigma_i) * v
@@ -384,14 +398,20 @@ def cfg_combine(v_pos, v_neg, g):
 
 
 class FBCacheState:
-    """Caller-held First-Block-Cache state (anchor residual + cached tail residual)."""
+    """Caller-held First-Block-Cache state (anchor residual + cached tail residual,
+    and the skip policy's counters)."""
 
-    def __init__(self, enabled: bool, threshold: float):
+    def __init__(self, enabled: bool, threshold: float, warmup_steps: int = 0,
+                 max_skips: int = 0):
         self.enabled = enabled
         self.threshold = threshold
         self.has_anchor = False
         self.anchor = None     # first block's residual at the last full step
         self.cached = None     # final image hidden - image hidden after block 0
+        self.warmup_steps = warmup_steps
+        self.max_skips = max_skips
+        self.steps_done = 0    # steps taken with the cache enabled
+        self.skip_run = 0      # consecutive skipped steps ending at the last one
 
 
 def _block_params(P, prefix):
@@ -430,10 +450,13 @@ def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = N
         if j == 0 and cache is not None and cache.enabled:
             r = x_img - before
             rel = fbcache_rel(r, cache.anchor) if cache.has_anchor else math.inf
-            skip = fbcache_decide(rel, cache.threshold)
+            skip = fbcache_policy(fbcache_decide(rel, cache.threshold), cache.steps_done,
+                                  cache.warmup_steps, cache.skip_run, cache.max_skips)
             if force_skip is not None:
                 skip = bool(force_skip)
             info["rel"], info["skip"] = rel, skip
+            cache.steps_done += 1
+            cache.skip_run = cache.skip_run + 1 if skip else 0
             after0 = x_img.copy()
             if skip:
                 break

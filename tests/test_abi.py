@@ -131,3 +131,36 @@ def test_invalid_arguments_rejected_before_launch():
     # token counts that are not multiples of 8
     d = dit.dims_of(1, 7, 2, 4, 256, 2, 512)
     assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every ctypes mirror in the binding has the size and field offsets that a C
+    compiler gives the header's struct (compiled here with gcc)."""
+    import shutil
+    import subprocess
+    from image_generation_amd import dit
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    mirrors = {"dit_dims": dit.DitDims, "dit_linear": dit.DitLinear, "dit_block": dit.DitBlock,
+               "dit_model": dit.DitModel, "dit_fbcache": dit.DitFBCache,
+               "dit_step_info": dit.DitStepInfo, "dit_kernel_timer": dit.DitKernelTimer}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dit.h"', "int main(void) {"]
+    for cname, py in mirrors.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, py in mirrors.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

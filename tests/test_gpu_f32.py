@@ -155,6 +155,41 @@ def test_tiny_fp32_loop_free_running(dit):
     assert e2e <= TOL_F32
 
 
+@pytest.mark.parametrize("warmup,max_skips,want", [(3, 2, "FFFSSFSS"), (0, 1, "FSFSFSFS")])
+def test_tiny_fp32_loop_skip_policy(dit, warmup, max_skips, want):
+    # tau = +inf: the pattern of skips is the policy's (warm-up, at most max_skips in
+    # a row); each step is compared with the oracle step from the same latents
+    import dataclasses
+    w = dataclasses.replace(DI.WORKLOADS["tiny_fp32"], steps=8)
+    dims = w.dims
+    params = dict(DI.iter_params(dims, "f32"))
+    gm = dit.GPUModel(dims, w.B, w.Lt, w.grid_h, w.grid_w, params, dtype=dit.DIT_F32)
+    P = {k: O.to64(v) for k, v in params.items()}
+    sig = dit.dit_sigmas(w.steps, w.shift)
+    mods = dit.dit_modulation(gm, sig[:-1])
+    ws = dit.workspace(gm.model.dims, dit.DIT_WS_STEP)
+    lat_g = DI.latents(w)[0].clone().cuda()
+    txt = DI.text_tokens(w)
+    cache = dit.FBCache(w.B, w.Li, dims.D, math.inf, True, warmup_steps=warmup,
+                        max_skips=max_skips)
+    ocache = O.FBCacheState(True, math.inf, warmup_steps=warmup, max_skips=max_skips)
+    got, errs = [], []
+    for i in range(w.steps):
+        x_in = lat_g.double().cpu().numpy()[None]
+        _, skip = dit.dit_denoise_step(gm, mods[i], txt.cuda(), lat_g, sig[i], sig[i + 1],
+                                       cache, ws)
+        torch.cuda.synchronize()
+        ref, info = O.denoise_step(P, dims, w, x_in, O.to64(txt), i, np.array(sig), ocache)
+        assert skip == info["skip"], (i, skip, info["skip"])
+        got.append("S" if skip else "F")
+        errs.append(parity_err(lat_g.double().cpu().numpy()[None] - x_in, ref - x_in))
+    _say(f"skip policy warmup={warmup} max={max_skips}: {''.join(got)} errs "
+         f"{['%.1e' % e for e in errs]}")
+    assert "".join(got) == want
+    assert cache.steps_done == w.steps and cache.skip_run == ocache.skip_run
+    assert max(errs) <= TOL_F32
+
+
 def test_tiny_fp32_modulation(dit):
     w = DI.WORKLOADS["tiny_fp32"]
     params = dict(DI.iter_params(w.dims, "f32"))

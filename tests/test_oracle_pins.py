@@ -414,6 +414,21 @@ def test_fbcache_rel_vs_python_loop():
     assert not O.fbcache_decide(math.inf, math.inf)
 
 
+def test_fbcache_policy_cases():
+    # (test says skip, steps done, warm-up steps, skips in a row, max skips) -> skip
+    cases = [
+        (False, 10, 0, 0, 0, False),   # the rel test decides first
+        (True, 0, 0, 0, 0, True),      # no policy: the test alone
+        (True, 2, 3, 0, 0, False),     # third step of a 3-step warm-up
+        (True, 3, 3, 0, 0, True),      # first step after it
+        (True, 9, 3, 1, 2, True),      # one skipped, two allowed
+        (True, 9, 3, 2, 2, False),     # two skipped in a row: compute
+        (True, 9, 0, 50, 0, True),     # max_skips 0: no limit
+    ]
+    for test, done, warm, run, mx, want in cases:
+        assert O.fbcache_policy(test, done, warm, run, mx) == want, (test, done, warm, run, mx)
+
+
 # ---------------------------------------------------------------- number formats
 
 def _e4m3_table():

@@ -67,6 +67,32 @@ def test_fbcache_threshold_inf_skips_every_step_after_first(model):
     assert skips == [False] + [True] * (W.steps - 1)
 
 
+def _policy_loop(P, lat, txt, steps, warmup, max_skips):
+    import dataclasses
+    w = dataclasses.replace(W, steps=steps)
+    sg = O.sigmas(steps, w.shift)
+    cache = O.FBCacheState(True, math.inf, warmup_steps=warmup, max_skips=max_skips)
+    skips, x = [], lat
+    for i in range(steps):
+        x, info = O.denoise_step(P, w.dims, w, x, txt, i, sg, cache)
+        skips.append(info["skip"])
+    return skips, cache
+
+
+@pytest.mark.parametrize("warmup,max_skips,want", [
+    # tau = +inf: every step with an anchor passes the rel test, so the pattern is the
+    # policy's: step 0 has no anchor; warm-up steps compute; at most max_skips in a row
+    (3, 2, "FFFSSFSS"),
+    (0, 1, "FSFSFSFS"),
+    (2, 0, "FFSSSSSS"),
+])
+def test_fbcache_policy_pattern(model, warmup, max_skips, want):
+    P, lat, txt = model
+    skips, cache = _policy_loop(P, lat, txt, 8, warmup, max_skips)
+    assert "".join("S" if s else "F" for s in skips) == want
+    assert cache.steps_done == 8 and cache.skip_run == len(want) - len(want.rstrip("S"))
+
+
 def test_fbcache_identity_tail_skip_equals_full(model):
     # blocks after the first are identity: the cached residual is 0 and the
     # skip path must give exactly the full path's latents
