@@ -38,7 +38,7 @@ from typing import Dict, Optional
 import numpy as np
 
 from .numerics import (quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX, round_bf16,
-                       round_fp16, e4m3_tie_mask)
+                       round_fp16, e4m3_tie_mask, quantize_mxfp4, dequantize_mxfp4)
 
 __all__ = [
     "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
@@ -46,7 +46,7 @@ __all__ = [
     "double_block", "single_block", "final_layer", "fbcache_rel",
     "fbcache_decide", "fbcache_policy", "euler_update", "cfg_combine", "time_embed",
     "modulation_vectors", "denoise_step", "FBCacheState", "to64",
-    "linear_fp8", "attention_fp8", "image_positions",
+    "linear_fp8", "linear_mxfp4", "attention_fp8", "image_positions",
 ]
 
 LN_EPS = 1e-6
@@ -216,6 +216,19 @@ def _merge(x):
 # --------------------------------------------------------------------------
 # fp8 W8A8 (R24-R28)
 # --------------------------------------------------------------------------
+
+def linear_mxfp4(x, w, b):
+    """W4A4 linear with MXFP4 operands (see ``numerics``): activations x [..., K]
+    and weights w [N, K] are both quantised along K in blocks of 32 with a shared
+    power-of-two scale each; the product of the dequantised operands is taken in
+    fp64, plus the bias."""
+    shp = x.shape
+    x2 = np.asarray(x).reshape(-1, shp[-1])
+    qx, ex = quantize_mxfp4(x2)
+    qw, ew = quantize_mxfp4(np.asarray(w))
+    y = dequantize_mxfp4(qx, ex) @ dequantize_mxfp4(qw, ew).T + b
+    return y.reshape(shp[:-1] + (w.shape[0],))
+
 
 def linear_fp8(x, w, b):
     """fp8 linear: per-token e4m3 activations x per-channel e4m3 weights (R25, R26).

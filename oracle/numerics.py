@@ -8,17 +8,31 @@ Formats (from their public definitions, not from any page):
     bits, no infinities, the all-ones code S.1111.111 is NaN; largest finite
     magnitude 1.75 * 2^8 = 448, smallest normal 2^-6, smallest subnormal 2^-9.
 
+  * OCP FP4 E2M1: 1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (no infinities or NaN).
+  * OCP MX block scaling (MXFP4): 32 consecutive elements share one E8M0 scale
+    2^e (an 8-bit biased exponent, bias 127); the shared exponent is
+    floor(log2(amax)) - 2, 2 being E2M1's largest exponent, and each element is
+    x / 2^e rounded to E2M1, values beyond 6 saturating.
+
 The fp8 W8A8 recipe the pages name ("FP8 W8A8 dynamic precision" in the
 runinfra.ai image-generation runbook, Optimization stack table) fixes no
 rounding rule; the reading used here is round-to-nearest-even with saturation
-to +-448 and a scale of amax/448 (amax = 0 gives scale 1).
+to +-448 and a scale of amax/448 (amax = 0 gives scale 1).  The 4-bit variant
+(the pages compare NVFP4 checkpoints with BF16 in the VisualGen article on FLUX
+Klein, and list FP4 among the optimisations in the runbook) is taken as MXFP4,
+gfx950's block-scaled FP4, with round-to-nearest-even.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["round_bf16", "round_fp16", "e4m3_tie_mask", "round_e4m3", "E4M3_MAX", "quant_scale_f32",
-           "quantize_rows_e4m3", "quantize_cols_e4m3"]
+           "quantize_rows_e4m3", "quantize_cols_e4m3", "round_e2m1", "E2M1_MAX", "MX_BLOCK",
+           "mx_block_exponent", "quantize_mxfp4", "dequantize_mxfp4"]
+
+E2M1_MAX = 6.0
+MX_BLOCK = 32
 
 E4M3_MAX = 448.0
 
@@ -110,3 +124,48 @@ def quantize_rows_e4m3(x: np.ndarray):
 def quantize_cols_e4m3(w: np.ndarray):
     """Per-output-channel quantisation of a weight [out, in] (one scale per row)."""
     return quantize_rows_e4m3(w)
+
+
+def round_e2m1(x) -> np.ndarray:
+    """fp64 -> nearest OCP E2M1 (FP4) value (as fp64), ties to even, saturating at +-6.
+
+    Two significant bits, smallest normal exponent 0 (spacing 0.5 below 2): the
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = _round_sig(x, 2, 0)
+    return np.clip(out, -E2M1_MAX, E2M1_MAX)
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """Shared MX exponent of a block: floor(log2(amax)) - 2, clamped to the E8M0
+    range [-127, 127]; an all-zero block takes exponent 0."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, k = np.frexp(np.where(a > 0, a, 1.0))       # a = m * 2^k, m in [0.5, 1)
+    e = np.where(a > 0, k - 1 - 2, 0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_mxfp4(x: np.ndarray):
+    """MXFP4 quantisation along the last axis (a multiple of 32 long).
+
+    Returns (q, e): q the E2M1 values (fp64, same shape as x) and e the shared
+    exponent of each 32-element block ([..., K/32] int64); x ~ q * 2^e.  The
+    value rounded is fp32(x) / 2^e, exact in fp32 as in a kernel.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    K = x.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("MXFP4: last axis must be a multiple of 32")
+    xb = x.reshape(x.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    e = mx_block_exponent(np.max(np.abs(xb), axis=-1))
+    q = round_e2m1(np.ldexp(xb, -e[..., None]))
+    return q.reshape(x.shape), e
+
+
+def dequantize_mxfp4(q: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """q * 2^e with each block's exponent broadcast over its 32 elements."""
+    K = q.shape[-1]
+    qb = np.asarray(q, dtype=np.float64).reshape(q.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return np.ldexp(qb, np.asarray(e)[..., None]).reshape(q.shape)
+

@@ -598,3 +598,62 @@ def test_attention_fp8_close_to_exact():
     ex = O.attention(q, k, v)
     wabs = O.attention(q, k, np.abs(v))
     assert np.max(np.abs(O.attention_fp8(q, k, v) - ex) / wabs) < 0.3
+
+
+# ---------------------------------------------------------------- MXFP4 (W4A4 variant)
+
+def test_e2m1_rounding_cases():
+    # (input, nearest E2M1 value; ties to the even mantissa; beyond 6 saturates)
+    cases = [(0.0, 0.0), (0.25, 0.0), (0.26, 0.5), (0.75, 1.0), (1.25, 1.0), (1.3, 1.5),
+             (1.75, 2.0), (2.5, 2.0), (2.51, 3.0), (3.5, 4.0), (5.0, 4.0), (5.01, 6.0),
+             (6.0, 6.0), (7.0, 6.0), (1e9, 6.0), (-0.74, -0.5), (-5.5, -6.0)]
+    got = O.round_e2m1(np.array([c[0] for c in cases]))
+    np.testing.assert_array_equal(got, np.array([c[1] for c in cases]))
+
+
+def test_e2m1_value_set():
+    x = np.linspace(-10, 10, 200001)
+    vals = set(np.unique(O.round_e2m1(x)).tolist())
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert vals == set(mags) | set(-m for m in mags)
+
+
+def test_mx_block_exponent_cases():
+    # floor(log2 amax) - 2: a block maximum in [4, 8) * 2^e
+    amax = np.array([6.0, 7.99, 8.0, 0.5, 1.0, 3.0, 0.0, 2.0 ** -200])
+    np.testing.assert_array_equal(O.mx_block_exponent(amax), [0, 0, 1, -3, -2, -1, 0, -127])
+
+
+def test_mxfp4_reproduces_representable_blocks():
+    # every 32-block holds E2M1 values times one power of two, with a +-4 or +-6
+    # in it: quantisation returns the input and the W4A4 linear is the exact product
+    rng = np.random.default_rng(5)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+    def make(rows, K):
+        q = rng.choice(mags, size=(rows, K)) * rng.choice([-1.0, 1.0], size=(rows, K))
+        q[:, ::32] = rng.choice([-6.0, -4.0, 4.0, 6.0], size=(rows, K // 32))
+        e = rng.integers(-6, 6, size=(rows, K // 32))
+        return O.dequantize_mxfp4(q, e), q, e
+
+    x, qx, ex = make(5, 96)
+    w, _, _ = make(7, 96)
+    q2, e2 = O.quantize_mxfp4(x)
+    np.testing.assert_array_equal(q2, qx)
+    np.testing.assert_array_equal(e2, ex)
+    b = rng.standard_normal(7)
+    np.testing.assert_array_equal(O.linear_mxfp4(x, w, b), x @ w.T + b)
+
+
+def test_mxfp4_error_bound():
+    x = np.random.default_rng(6).standard_normal((64, 256)) * 3.0
+    q, e = O.quantize_mxfp4(x)
+    d = O.dequantize_mxfp4(q, e)
+    scale = np.repeat(np.ldexp(1.0, e), 32, axis=-1)
+    err = np.abs(x - d)
+    assert np.all(err <= 2.0 * scale)                        # saturation above 6 * 2^e
+    inside = np.abs(x) <= 6.0 * scale
+    assert np.all(err[inside] <= 1.0 * scale[inside])        # half the top binade's spacing
+    blk_max = np.abs(x).reshape(64, 8, 32).max(-1)
+    s = np.ldexp(1.0, e)
+    assert np.all((blk_max >= 4 * s) & (blk_max < 8 * s))
