@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X published dense fp8 MFMA peak
+PEAK_FP4_TFLOPS = 10100.0   # MI355X published dense fp4 (and fp6) MFMA peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "DiT denoise steps/s at 1024px & 2048px; attention+GEMM TFLOP/s, % MFMA peak"
 ALL_SITES = ["attention", "gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1", "gemm_f32",
@@ -47,11 +48,11 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1134678 * 1024 + 230553 * 1024,
+    "gemm_lin1": {"bytes": 1138710 * 1024 + 230339 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "cf1d8715d45fac840729630163064785fca6ee75"},
+                  "sha1": "043831c2989c1af8728c27964c901b6f037608b1"},
     "attention": {"bytes": 101506 * 1024 + 27691 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",
@@ -164,6 +165,44 @@ def block_2048_bf16(dit, DI, device, reps=3):
             "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
             "gemm_frac_peak": round(gemm_f / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "kernels": kernel_table(by)}
+
+
+def mxfp4_gemms(dit, device, reps=10):
+    """W4A4 (MXFP4) GEMMs at the block shapes of the 1024px model and the 2048px CFG
+    pair's linear1: quantisation of both operands once (weights are quantised
+    offline; the activation pass is timed separately), then the block-scaled GEMM
+    alone, against the 10.1 PFLOP/s dense fp4 peak."""
+    import torch
+    shapes = [("qkv", 4608, 9216, 3072), ("linear1", 4608, 21504, 3072),
+              ("linear2", 4608, 3072, 15360), ("linear1_2048px_cfg", 33792, 21504, 3072)]
+    g = torch.Generator(device="cpu").manual_seed(11)
+    out = {}
+    for name, M, N, K in shapes:
+        x = torch.randn((M, K), generator=g).to(device=device, dtype=torch.bfloat16)
+        w = (torch.randn((N, K), generator=g) * 0.02).to(device=device, dtype=torch.bfloat16)
+        b = torch.zeros(N, device=device)
+        xq, wq = dit.dit_quantize_mxfp4(x), dit.dit_quantize_mxfp4(w)
+        y = torch.empty((M, N), device=device, dtype=torch.bfloat16)
+        dit.dit_linear_mxfp4(xq, wq, b, y)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            dit.dit_linear_mxfp4(xq, wq, b, y)
+        ev[1].record()
+        for _ in range(reps):
+            dit.dit_quantize_mxfp4(x)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) / reps * 1e-3
+        tq = ev[1].elapsed_time(ev[2]) / reps * 1e-3
+        fl = 2.0 * M * N * K
+        out[name] = {"M": M, "N": N, "K": K, "gemm_us": round(t * 1e6, 1),
+                     "tflops": round(fl / t / 1e12, 1),
+                     "frac_fp4_peak": round(fl / t / 1e12 / PEAK_FP4_TFLOPS, 4),
+                     "activation_quant_us": round(tq * 1e6, 1)}
+        del x, w, xq, wq, y
+    return out
 
 
 def loop_2048_fp8(dit, DI, device, K, warmup):
@@ -301,6 +340,8 @@ def main():
         out = {"block_2048px_bf16": block_2048_bf16(dit, DI, device)}
         torch.cuda.empty_cache()
         out["loop_2048px_fp8"] = loop_2048_fp8(dit, DI, device, args.fp8_steps, 1)
+        torch.cuda.empty_cache()
+        out["mxfp4_gemm"] = mxfp4_gemms(dit, device)
         print(json.dumps(out), flush=True)
         return
 
@@ -395,6 +436,9 @@ def main():
         out["block_2048px_bf16"] = block_2048_bf16(dit, DI, device)
         torch.cuda.empty_cache()
         out["loop_2048px_fp8"] = loop_2048_fp8(dit, DI, device, args.fp8_steps, 1)
+        torch.cuda.empty_cache()
+        log("[bench] MXFP4 (W4A4) GEMMs")
+        out["mxfp4_gemm"] = mxfp4_gemms(dit, device)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(DI, w)

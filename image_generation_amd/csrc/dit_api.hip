@@ -631,6 +631,72 @@ int dit_quantize_rows(const void* src, int src_dtype, int src_ld, int rows, int 
   return DIT_OK;
 }
 
+int dit_mx_rows(int rows) { return rows <= 0 ? 0 : (rows + 255) / 256 * 256; }
+
+int dit_quantize_mxfp4(const void* src, int src_dtype, int src_ld, int rows, int width,
+                       void* codes, unsigned char* scales, void* stream) {
+  if (!src || !codes || !scales)
+    return fail(DIT_ERR_INVALID_ARG, "dit_quantize_mxfp4: NULL pointer");
+  if (!aligned16(src) || !aligned16(codes) || !aligned16(scales))
+    return fail(DIT_ERR_INVALID_ARG, "dit_quantize_mxfp4: pointers must be 16-byte aligned");
+  if (src_dtype != DIT_BF16 && src_dtype != DIT_F32)
+    return fail(DIT_ERR_UNSUPPORTED, "dit_quantize_mxfp4: src_dtype %d (DIT_BF16, DIT_F32)",
+                src_dtype);
+  if (rows < 0 || width < 256 || width % 256 || src_ld < width || src_ld % 8)
+    return fail(DIT_ERR_INVALID_ARG,
+                "dit_quantize_mxfp4: width a multiple of 256, src_ld >= width, src_ld % 8 == 0");
+  if ((long long)rows * src_ld > (1LL << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "dit_quantize_mxfp4: problem too large");
+  int rc = check_device();
+  if (rc) return rc;
+  const int pad = dit_mx_rows(rows);
+  if (src_dtype == DIT_BF16)
+    DIT_CHECK_HIP(quant_mxfp4<bf16_t>((const bf16_t*)src, src_ld, rows, width, (uint8_t*)codes,
+                                      scales, pad, (hipStream_t)stream));
+  else
+    DIT_CHECK_HIP(quant_mxfp4<float>((const float*)src, src_ld, rows, width, (uint8_t*)codes,
+                                     scales, pad, (hipStream_t)stream));
+  return DIT_OK;
+}
+
+int dit_linear_mxfp4(const void* x_codes, const unsigned char* x_scales, int M, int K,
+                     const void* w_codes, const unsigned char* w_scales, const float* b, int N,
+                     void* y, int y_dtype, void* stream) {
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y)
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_mxfp4: NULL pointer");
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y) || (b && !aligned16(b)))
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_mxfp4: pointers must be 16-byte aligned");
+  if (M < 1 || K < 256 || K % 256 || N < 4 || N % 4)
+    return fail(DIT_ERR_INVALID_ARG,
+                "dit_linear_mxfp4: M >= 1, K a multiple of 256, N a multiple of 4");
+  if ((long long)M * (K / 2) >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31) ||
+      (long long)M * N > (1LL << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "dit_linear_mxfp4: problem too large");
+  if (y_dtype != DIT_F32 && y_dtype != DIT_BF16)
+    return fail(DIT_ERR_INVALID_ARG, "dit_linear_mxfp4: y_dtype %d", y_dtype);
+  int rc = check_device();
+  if (rc) return rc;
+  GemmProblem g{};
+  g.lda = K;
+  g.ldw = K;
+  g.bias = b;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A4 = (const uint8_t*)x_codes;
+  g.W4 = (const uint8_t*)w_codes;
+  g.xa = x_scales;
+  g.xw = w_scales;
+  g.pad_m = dit_mx_rows(M);
+  g.pad_n = dit_mx_rows(N);
+  if (y_dtype == DIT_F32)
+    DIT_CHECK_HIP(gemm_mx4_store_f32(g, (float*)y, N, (hipStream_t)stream));
+  else
+    DIT_CHECK_HIP(gemm_mx4_store_bf16(g, (bf16_t*)y, N, (hipStream_t)stream));
+  return DIT_OK;
+}
+
 int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,
                       size_t ws_bytes, void* stream) {

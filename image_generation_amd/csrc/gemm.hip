@@ -427,9 +427,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
 // while one is consumed; every stage is its own LDS object so the loads into
 // one never order the reads of another.
 //
-// F8: operands are OCP e4m3 with per-row (A) and per-column (W) scales;
+// FMT 1 (e4m3): operands are OCP e4m3 with per-row (A) and per-column (W) scales;
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) takes 32 bytes of K per
 // lane; the epilogue dequantises with sa[row] * sw[col].
+// FMT 2 (MXFP4): operands are E2M1 codes with an E8M0 scale per 32 K values; a
+// 128-byte slab is 256 K values, and the slab's scales (8 bytes per row) travel
+// with it into a 4-KB tail of the stage.  The same MFMA with E2M1 operands takes
+// 16 bytes (32 K values, one block) per lane and the lane's block scale, picked by
+// the opsel byte index from a word holding its 4 blocks of the slab.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -539,8 +544,14 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool F8, int NS, int SLAB, class Epi>
+template <int KK>
+__device__ __forceinline__ f32x16 mfma_mx4(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, KK, sa, KK, sb);
+}
+
+template <int BM, int BN, int WM, int WN, int FMT, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
+  constexpr bool F8 = FMT == 1, F4 = FMT == 2;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
@@ -553,6 +564,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   constexpr int ROWB = SWZ ? SLAB : SLAB + 16;  // LDS row pitch (bytes)
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per LDS row
   constexpr int AB = BM * ROWB, BB = BN * ROWB, SB = AB + BB;
+  constexpr int SXB = F4 ? (BM + BN) * 8 : 0; // MX block scales of a slab
   constexpr int NI = SB / 1024;               // 1-KB load instructions per stage
   constexpr int IPW = NI / NW;
   constexpr int EH = SWZ ? 2 : 1;             // epilogue passes over a wave's rows
@@ -563,9 +575,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   static_assert(AB % 1024 == 0 && BB % 1024 == 0 && NI % NW == 0, "stage / wave mismatch");
   static_assert(WPS * NS >= NW, "epilogue slices must fit the stages");
   static_assert(SLAB % (F8 ? 64 : 32) == 0, "slab holds whole MFMA K steps");
+  static_assert(!F4 || (SLAB == 128 && NS == 2 && BM == 256 && BN == 256 && NW >= 4),
+                "MX operands: 128-byte slabs, two stages, 256 x 256 tiles");
   static_assert(SWZ || ROWB % 32 == 16, "row pitch: an odd number of 16-byte chunks");
-  __shared__ __attribute__((aligned(1024))) char st0[SB];
-  __shared__ __attribute__((aligned(1024))) char st1[SB];
+  __shared__ __attribute__((aligned(1024))) char st0[SB + SXB];
+  __shared__ __attribute__((aligned(1024))) char st1[SB + SXB];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? SB : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? SB : 16];
   auto stage = [&](int s) -> char* {
@@ -597,9 +611,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 
   // byte offset of every lane's source chunk for each of this wave's load
   // instructions (an instruction lies wholly in the A or the B part of a stage)
-  constexpr int ES = F8 ? 1 : 2;                    // element bytes
-  const char* abase = F8 ? (const char*)g.A8 : (const char*)g.A;
-  const char* wbase = F8 ? (const char*)g.W8 : (const char*)g.W;
+  constexpr int ES = F8 ? 1 : 2;                    // element bytes (e4m3, bf16)
+  const char* abase = F4 ? (const char*)g.A4 : F8 ? (const char*)g.A8 : (const char*)g.A;
+  const char* wbase = F4 ? (const char*)g.W4 : F8 ? (const char*)g.W8 : (const char*)g.W;
+  const int apitch = F4 ? g.lda / 2 : g.lda * ES;   // row pitch in bytes
+  const int wpitch = F4 ? g.ldw / 2 : g.ldw * ES;
   int voff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
@@ -609,8 +625,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     const int row = o2 / ROWB;
     const int slot = SWZ ? ((o2 - row * ROWB) >> 4) ^ ((row >> 1) & 7)
                          : min((o2 - row * ROWB) >> 4, CPR - 2);
-    voff[j] = isb ? min(n0 + row, g.N - 1) * g.ldw * ES + slot * 16
-                  : min(m0 + row, g.M - 1) * g.lda * ES + slot * 16;
+    voff[j] = isb ? min(n0 + row, g.N - 1) * wpitch + slot * 16
+                  : min(m0 + row, g.M - 1) * apitch + slot * 16;
+  }
+  // MX scales: waves 0, 1 load the A tile's 256 rows x 8 bytes of a slab, waves 2, 3
+  // the W tile's, 1 KB each (the scale arrays are padded to 256-row multiples)
+  const uint8_t* xsrc = nullptr;
+  if constexpr (F4) {
+    if (wave < 4)
+      xsrc = wave < 2 ? g.xa + ((size_t)m0 + wave * 128) * 8 + lane * 16
+                      : g.xw + ((size_t)n0 + (wave - 2) * 128) * 8 + lane * 16;
   }
 
   f32x16 acc[TM][TN];
@@ -621,7 +645,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = g.K * ES / SLAB;                   // K slabs
+  const int nk = F4 ? g.K / 256 : g.K * ES / SLAB;  // K slabs
+  const int xstride = (wave < 2 ? g.pad_m : g.pad_n) * 8;   // bytes of MX scales per slab
   const int frow = lane & 31;
   const int wrow = wm * WROWS;
   const int wcol = wn * (BN / WN);
@@ -640,6 +665,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
       const char* b_ = ((wave * IPW + j) * 1024 >= AB) ? wbase : abase;                  \
       __builtin_amdgcn_global_load_lds((const void*)(b_ + voff[j] + ko_),            \
                                        (void*)((stg) + (wave * IPW + j) * 1024), 16, 0, 0); \
+    }                                                                                    \
+    if constexpr (F4) {                                                                  \
+      if (wave < 4)                                                                      \
+        __builtin_amdgcn_global_load_lds((const void*)(xsrc + (size_t)(kt) * xstride),   \
+                                         (void*)((stg) + SB + wave * 1024), 16, 0, 0);   \
     }                                                                                    \
   }
   // bf16: 16-deep K steps (32 bytes of a row); the fragments of step kk+1 are
@@ -693,6 +723,36 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     }                                                                                    \
   }
 
+  // MXFP4: four 64-deep K steps per slab, 16 bytes (one 32-value block) per lane;
+  // the lane's scale word holds its blocks 2 kk + hi for kk = 0..3, byte kk
+#define GEMM_MX4_STEP(KK)                                                                \
+  {                                                                                      \
+    i32x8 af[TM], bw[TN];                                                                \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                     \
+      const i32x4 v_ = *(const i32x4*)(a_s + (wrow + i * 32 + frow) * ROWB + xo(2 * KK)); \
+      af[i] = i32x8{v_[0], v_[1], v_[2], v_[3], 0, 0, 0, 0};                               \
+    }                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                     \
+      const i32x4 v_ = *(const i32x4*)(b_s + (wcol + j * 32 + frow) * ROWB + xo(2 * KK)); \
+      bw[j] = i32x8{v_[0], v_[1], v_[2], v_[3], 0, 0, 0, 0};                               \
+    }                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+            acc[i][j] = mfma_mx4<KK>(af[i], bw[j], acc[i][j], sa_[i], sb_[j]);            \
+  }
+#define GEMM_COMPUTE_F4(stg)                                                             \
+  {                                                                                      \
+    const char* a_s = (const char*)(stg);                                                \
+    const char* b_s = (const char*)(stg) + AB;                                           \
+    const char* x_s = (const char*)(stg) + SB;                                           \
+    int sa_[TM], sb_[TN];                                                                \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+        sa_[i] = *(const int*)(x_s + (wrow + i * 32 + frow) * 8 + hi * 4);               \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
+        sb_[j] = *(const int*)(x_s + BM * 8 + (wcol + j * 32 + frow) * 8 + hi * 4);      \
+    GEMM_MX4_STEP(0) GEMM_MX4_STEP(1) GEMM_MX4_STEP(2) GEMM_MX4_STEP(3)                  \
+  }
+
   // prologue: slabs 0 .. NS-2 in flight, wait for slab 0
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
@@ -705,7 +765,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     const bool refill = kt + NS - 1 < nk;
     if (refill) GEMM_DMA(stage((kt + NS - 1) % NS), kt + NS - 1);
     char* cur = stage(kt % NS);
-    if constexpr (F8) GEMM_COMPUTE_F8(cur)
+    if constexpr (F4) GEMM_COMPUTE_F4(cur)
+    else if constexpr (F8) GEMM_COMPUTE_F8(cur)
     else GEMM_COMPUTE(cur)
     // slab kt + 1 has landed once at most the later slabs' loads are outstanding
     if (refill) wait_vmcnt<(NS - 2) * IPW>();
@@ -715,6 +776,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 #undef GEMM_DMA
 #undef GEMM_COMPUTE
 #undef GEMM_COMPUTE_F8
+#undef GEMM_COMPUTE_F4
+#undef GEMM_MX4_STEP
 
   const Epi epi = g1 ? p.e[1] : p.e[0];
   dma_epilogue<BN, WN, TM, TN, WROWS, EH, F8>(
@@ -901,7 +964,8 @@ hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap&
 
 // ---------------------------------------------------------------- launch
 
-// KV: 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS bf16 kernel, 0 = register-staged
+// KV: 4 = direct-to-LDS MXFP4 kernel, 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS
+// bf16 kernel, 0 = register-staged
 // bf16 kernel; NS stages of SLAB bytes per row for the direct-to-LDS kernels
 template <int BM, int BN, int WM, int WN, int KV, int NS = 2, int SLAB = 128, class Epi>
 static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
@@ -917,8 +981,9 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
   }
   if (total == 0) return hipSuccess;
   void (*kern)(GemmParams<Epi>);
-  if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, true, NS, SLAB, Epi>;
-  else if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, false, NS, SLAB, Epi>;
+  if constexpr (KV == 4) kern = &gemm_dma_kernel<BM, BN, WM, WN, 2, NS, SLAB, Epi>;
+  else if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, 1, NS, SLAB, Epi>;
+  else if constexpr (KV == 1) kern = &gemm_dma_kernel<BM, BN, WM, WN, 0, NS, SLAB, Epi>;
   else kern = &gemm_bf16_kernel<BM, BN, WM, WN, Epi>;
   hipLaunchKernelGGL(kern, dim3(total), dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
@@ -948,6 +1013,23 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   if (maxM >= 1024 && minN >= 1024 && offsets32)
     return launch_cfg<256, 256, 2, 4, 1, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
+}
+
+// MXFP4 operands: the direct-to-LDS kernel only (256 x 256 tiles, any M, N).
+template <class Epi>
+static hipError_t launch_mx4(const GemmProblem& g, const Epi& e, hipStream_t st) {
+  KTimerScope timer(KS_GEMM_F32, st);
+  if ((long long)g.M * (g.lda / 2) >= (1LL << 31) || (long long)g.N * (g.ldw / 2) >= (1LL << 31))
+    return hipErrorInvalidValue;   // byte offsets are kept in 32 bits
+  return launch_cfg<256, 256, 2, 4, 4, 2, 128>(&g, &e, 1, st);
+}
+
+hipError_t gemm_mx4_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st) {
+  return launch_mx4(g, EpiStoreF32{out, ldo}, st);
+}
+
+hipError_t gemm_mx4_store_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st) {
+  return launch_mx4(g, EpiStoreBf16{out, ldo}, st);
 }
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st) {

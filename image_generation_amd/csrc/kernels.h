@@ -37,6 +37,15 @@ struct GemmProblem {
   // fp32 (reference-precision blocks): A32 [M, K], W32 [N, K]; K % 4 == 0
   const float* A32 = nullptr;
   const float* W32 = nullptr;
+  // MXFP4 (W4A4): E2M1 codes A4 [M, lda / 2 bytes], W4 [N, ldw / 2 bytes] (lda, ldw in
+  // elements) and E8M0 block scales xa [K / 256][pad_m][8], xw [K / 256][pad_n][8]
+  // (pad_m, pad_n multiples of 256; a row's 8 scales of a 256-wide K slab are
+  // stored as blocks 0, 2, 4, 6, 1, 3, 5, 7); K % 256 == 0
+  const uint8_t* A4 = nullptr;
+  const uint8_t* W4 = nullptr;
+  const uint8_t* xa = nullptr;
+  const uint8_t* xw = nullptr;
+  int pad_m = 0, pad_n = 0;
 };
 
 // Destinations of the fused QKV epilogue.
@@ -53,6 +62,9 @@ struct QKVOut {
 
 hipError_t gemm_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st);
 hipError_t gemm_store_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
+// MXFP4 (W4A4) GEMM, out = A W^T + bias, A4 / W4 / xa / xw set in g.
+hipError_t gemm_mx4_store_f32(const GemmProblem& g, float* out, int ldo, hipStream_t st);
+hipError_t gemm_mx4_store_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
 hipError_t gemm_silu_bf16(const GemmProblem& g, bf16_t* out, int ldo, hipStream_t st);
 hipError_t gemm_gelu_bf16(const GemmProblem* g, int ng, bf16_t* const* out, const int* ldo,
                           hipStream_t st);
@@ -120,6 +132,11 @@ template <class T>
 hipError_t quant_slices(const T* src, size_t n, int nslices, const unsigned int* amax,
                         fp8_t* dst, float* scale, hipStream_t st);
 hipError_t zero_u32(unsigned int* p, int n, hipStream_t st);
+// MXFP4 quantisation of rows (see GemmProblem for the code and scale layouts);
+// width % 256 == 0, pad_rows = rows rounded up to 256 (pad rows get scale 2^0).
+template <class T>
+hipError_t quant_mxfp4(const T* src, int lds, int rows, int width, uint8_t* codes, uint8_t* scales,
+                       int pad_rows, hipStream_t st);
 
 // fp8 attention: q8, k8 e4m3 [B, H, L, d], vt8 e4m3 [B, H, d, L], one fp32 scale per
 // (b, h) for each of q, k, v; output bf16 as attention_bf16.

@@ -29,6 +29,16 @@ template <> struct Load8<bf16_t> {
     }
   }
 };
+template <> struct Load8<float> {
+  static __device__ __forceinline__ void get(const float* p, float* v) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+};
 template <> struct Load8<f16_t> {
   static __device__ __forceinline__ void get(const f16_t* p, float* v) {
     const f16x8 h = *(const f16x8*)p;
@@ -207,6 +217,78 @@ template hipError_t quant_slices<bf16_t>(const bf16_t*, size_t, int, const unsig
                                          float*, hipStream_t);
 template hipError_t quant_slices<f16_t>(const f16_t*, size_t, int, const unsigned int*, fp8_t*,
                                         float*, hipStream_t);
+
+// ---------------------------------------------------------------- MXFP4
+// One lane per block of 32 consecutive elements of a row: e = floor(log2 amax) - 2
+// (clamped to the E8M0 range; 0 for an all-zero block), each element x / 2^e
+// (exact in fp32) rounded to E2M1 by counting the midpoints it passes, ties going
+// to the even mantissa (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4) and values beyond 6 saturating.  16 code bytes per block,
+// element 2j in the low nibble of byte j; the scale byte goes to the GEMM order
+// [slab][pad_rows][8] with a row's 8 slab blocks stored as 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | (__float_as_uint(v) >> 31 << 3);
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const T* __restrict__ src, int lds,
+                                                          int rows, int width, int pad_rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int nb = width >> 5;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)pad_rows * nb) return;
+  const int r = (int)(idx / nb), b = (int)(idx - (long long)r * nb);
+  const int j = b & 7;
+  uint8_t* sp = scales + (((size_t)(b >> 3) * pad_rows + r) << 3) + ((j & 1) ? 4 + (j >> 1) : j >> 1);
+  if (r >= rows) {   // padding rows of the scale array
+    *sp = 127;
+    return;
+  }
+  float v[32];
+  const T* p = src + (size_t)r * lds + (b << 5);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Load8<T>::get(p + q * 8, v + q * 8);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = 0;
+  if (amax > 0.f) {
+    int k;
+    frexpf(amax, &k);                    // amax = m 2^k, m in [0.5, 1)
+    e = min(max(k - 3, -127), 127);
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u |= e2m1_code(ldexpf(v[q * 8 + i], -e)) << (4 * i);
+    w[q] = u;
+  }
+  *(uint4*)(codes + (size_t)r * (width >> 1) + (b << 4)) = make_uint4(w[0], w[1], w[2], w[3]);
+  *sp = (uint8_t)(e + 127);
+}
+
+template <class T>
+hipError_t quant_mxfp4(const T* src, int lds, int rows, int width, uint8_t* codes, uint8_t* scales,
+                       int pad_rows, hipStream_t st) {
+  if (width % 256 || lds % 8 || pad_rows < rows || pad_rows % 256) return hipErrorInvalidValue;
+  if (pad_rows == 0) return hipSuccess;
+  KTimerScope timer(KS_QUANT, st);
+  const long long n = (long long)pad_rows * (width >> 5);
+  hipLaunchKernelGGL(quant_mxfp4_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     src, lds, rows, width, pad_rows, codes, scales);
+  return hipGetLastError();
+}
+template hipError_t quant_mxfp4<bf16_t>(const bf16_t*, int, int, int, uint8_t*, uint8_t*, int,
+                                        hipStream_t);
+template hipError_t quant_mxfp4<float>(const float*, int, int, int, uint8_t*, uint8_t*, int,
+                                       hipStream_t);
 
 hipError_t zero_u32(unsigned int* p, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;

@@ -101,6 +101,9 @@ def _load() -> ctypes.CDLL:
                                      POINTER(DitFBCache), P, c_size_t, P, POINTER(DitStepInfo)]),
         "dit_set_kernel_timer": (c_int, [POINTER(DitKernelTimer)]),
         "dit_linear_forward": (c_int, [P, c_int, c_int, POINTER(DitLinear), c_int, P, c_int, P]),
+        "dit_quantize_mxfp4": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P]),
+        "dit_mx_rows": (c_int, [c_int]),
+        "dit_linear_mxfp4": (c_int, [P, P, c_int, c_int, P, P, P, c_int, P, c_int, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -113,7 +116,7 @@ LIB = _load()
 EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
             "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
             "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward",
-            "dit_quantize_rows")
+            "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4")
 
 
 def _check(rc: int) -> None:
@@ -231,6 +234,41 @@ def dit_quantize_rows(src: torch.Tensor, stream=None):
     _check(LIB.dit_quantize_rows(_ptr(src), DIT_BF16, width, rows, width, _ptr(codes), width,
                                  _ptr(scale), _stream(stream)))
     return codes, scale
+
+
+def dit_quantize_mxfp4(src: torch.Tensor, stream=None):
+    """MXFP4 quantisation of a bf16 or fp32 [rows, width] tensor along its rows ->
+    (codes uint8 [rows, width / 2], scales uint8 [width / 256, dit_mx_rows(rows), 8])."""
+    if src.dim() != 2 or src.dtype not in (torch.bfloat16, torch.float32) or not src.is_cuda:
+        raise ValueError("src: bf16 or fp32 [rows, width] on the GPU")
+    if not src.is_contiguous():
+        raise ValueError("src: contiguous")
+    rows, width = src.shape
+    codes = torch.empty((rows, width // 2), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((width // 256, LIB.dit_mx_rows(rows), 8), dtype=torch.uint8,
+                         device=src.device)
+    dt = DIT_BF16 if src.dtype == torch.bfloat16 else DIT_F32
+    _check(LIB.dit_quantize_mxfp4(_ptr(src), dt, width, rows, width, _ptr(codes), _ptr(scales),
+                                  _stream(stream)))
+    return codes, scales
+
+
+def dit_linear_mxfp4(xq, w_q, b: Optional[torch.Tensor], out: torch.Tensor, stream=None):
+    """W4A4 y = x W^T + b; xq, w_q: (codes, scales) pairs from dit_quantize_mxfp4;
+    out fp32 or bf16 [M, N]."""
+    xc, xs = xq
+    wc, ws = w_q
+    M, N, K = xc.shape[0], wc.shape[0], xc.shape[1] * 2
+    if wc.shape[1] * 2 != K or tuple(out.shape) != (M, N):
+        raise ValueError("dit_linear_mxfp4: shape mismatch")
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out: fp32 or bf16")
+    if b is not None:
+        _need(b, torch.float32, (N,), "b")
+    yd = DIT_F32 if out.dtype == torch.float32 else DIT_BF16
+    _check(LIB.dit_linear_mxfp4(_ptr(xc), _ptr(xs), M, K, _ptr(wc), _ptr(ws), _ptr(b), N,
+                                _ptr(out), yd, _stream(stream)))
+    return out
 
 
 def dit_linear_forward(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor,

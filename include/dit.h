@@ -232,8 +232,9 @@ DIT_API int dit_linear_forward(const void* x, int M, int K, const dit_linear* li
  *     32 or 64, any L >= 1.
  *   dtype DIT_FP8: q, k e4m3 [B, H, L, 128], vt e4m3 [B, H, 128, L], each with
  *     one fp32 scale per (b, h) in q_scale / k_scale / v_scale [B * H] (value =
- *     code * scale); P is quantised as e4m3(448 P) against the exact running
- *     max, the row sum uses the unquantised P; L % 16 == 0, L >= 16.
+ *     code * scale); with t the scores in exp2 units and r the row maximum of t
+ *     rounded up to an integer, P = 2^(t - r) enters P V as e4m3(448 P) / 448 and
+ *     the normaliser is the sum of those quantised P; L % 16 == 0, L >= 16.
  *   o: device [B, L, H * head_dim] (token-major), bf16 (fp32 for DIT_F32).  Softmax statistics and both
  *   products accumulate in fp32.  Workspace: none. */
 DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
@@ -251,6 +252,39 @@ DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
  *   scale per output channel) and by the fp8 blocks for their activations. */
 DIT_API int dit_quantize_rows(const void* src, int src_dtype, int src_ld, int rows, int width,
                               void* dst, int dst_ld, float* scale, void* stream);
+
+/* MXFP4 block-scaled 4-bit quantisation of rows (the W4A4 variant next to the
+ * fp8 path; OCP microscaling: E2M1 elements sharing one E8M0 scale per 32
+ * consecutive elements of a row).  For each row r and block of 32:
+ *   e = floor(log2(amax)) - 2, clamped to [-127, 127] (0 for an all-zero block);
+ *   each element x / 2^e is rounded to the nearest E2M1 value (0, 0.5, 1, 1.5, 2,
+ *   3, 4, 6 and negatives), ties to the even mantissa, beyond 6 saturating.
+ *   src: device bf16 (src_dtype DIT_BF16) or fp32 (DIT_F32) [rows, src_ld];
+ *   width % 256 == 0, src_ld >= width, src_ld % 8 == 0;
+ *   codes: device [rows, width / 2] bytes, element 2j of a row in the low nibble
+ *     of byte j;
+ *   scales: device E8M0 bytes (2^(byte - 127)) in the GEMM's order
+ *     [width / 256][dit_mx_rows(rows)][8]: the 8 block scales of one row in one
+ *     256-wide slab, stored as blocks 0, 2, 4, 6, 1, 3, 5, 7; the padding rows
+ *     are written as 127 (2^0).
+ * Weights (offline) and activations use the same routine.  Workspace: none.
+ * Reading of the pages: their 4-bit format is NVFP4 (VisualGen article on FLUX
+ * Klein, checkpoint and speed tables; the diffusion-backend commit, precision per
+ * GPU generation: nvfp4 / fp8 / mxfp8); gfx950's block-scaled FP4 MFMA takes OCP
+ * MX scales, so that is the format here. */
+DIT_API int dit_quantize_mxfp4(const void* src, int src_dtype, int src_ld, int rows, int width,
+                               void* codes, unsigned char* scales, void* stream);
+/* Rows of an MXFP4 scale array for `rows` rows: rows rounded up to 256. */
+DIT_API int dit_mx_rows(int rows);
+
+/* W4A4 linear y = x W^T + b on MXFP4 operands, both as written by
+ * dit_quantize_mxfp4 (x [M, K], W [N, K]): block-scaled MFMAs
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands, each lane's E8M0 block
+ * scale), fp32 accumulation; b fp32 [N] or NULL; y device [M, N], DIT_F32 or
+ * DIT_BF16.  K % 256 == 0, N % 4 == 0.  Workspace: none. */
+DIT_API int dit_linear_mxfp4(const void* x_codes, const unsigned char* x_scales, int M, int K,
+                             const void* w_codes, const unsigned char* w_scales, const float* b,
+                             int N, void* y, int y_dtype, void* stream);
 
 /* One transformer block, in place on the joint residual stream.
  *   x: device [B, Lt + Li, D], dtype x_dtype (DIT_F32 or DIT_BF16), updated;

@@ -20,8 +20,9 @@ runinfra.ai image-generation runbook, Optimization stack table) fixes no
 rounding rule; the reading used here is round-to-nearest-even with saturation
 to +-448 and a scale of amax/448 (amax = 0 gives scale 1).  The 4-bit variant
 (the pages compare NVFP4 checkpoints with BF16 in the VisualGen article on FLUX
-Klein, and list FP4 among the optimisations in the runbook) is taken as MXFP4,
-gfx950's block-scaled FP4, with round-to-nearest-even.
+Klein, and the diffusion-backend commit picks nvfp4 / fp8 / mxfp8 by GPU
+generation) is taken as MXFP4, gfx950's block-scaled FP4, with
+round-to-nearest-even.
 """
 from __future__ import annotations
 
