@@ -43,7 +43,7 @@ from .numerics import (quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX
 __all__ = [
     "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
     "linear", "rope_table", "apply_rope", "attention", "attention_naive",
-    "double_block", "single_block", "final_layer", "fbcache_rel",
+    "double_block", "double_block_rows", "single_block", "final_layer", "fbcache_rel",
     "fbcache_decide", "fbcache_policy", "euler_update", "cfg_combine", "time_embed",
     "modulation_vectors", "denoise_step", "FBCacheState", "to64",
     "linear_fp8", "linear_mxfp4", "attention_fp8", "image_positions",
@@ -341,6 +341,50 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
         x = x + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
         out[s] = x
     return out["txt"], out["img"]
+
+
+def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False):
+    """The double block's output for the joint token rows ``rows`` only (text rows
+    first, 0 <= row < Lt + Li) -> [B, len(rows), D].
+
+    Every token's Q, K, V is computed (attention needs all keys and values, and
+    fp8 scales span whole heads); attention, projection and MLP then run for the
+    selected query rows alone: each row's update depends on its own row and the
+    keys and values only, so the result equals ``double_block`` at those rows.
+    """
+    attn_fn = attention_fp8 if fp8 else attention
+    Lt = x_txt.shape[1]
+    D = x_img.shape[-1]
+    rows = np.asarray(rows)
+    streams = {"txt": (x_txt, mod_txt), "img": (x_img, mod_img)}
+    qkv = {}
+    for s, (x, m) in streams.items():
+        u = modulate(x, m[:, 0:1], m[:, 1:2])
+        qkv[s] = _lin(u, P, f"{s}.qkv", fp8)
+    q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
+    k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
+    v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
+    q = _held(apply_rope(_heads(q, H), ang), fp8)
+    k = _held(apply_rope(_heads(k, H), ang), fp8)
+    vh = _held(_heads(v, H), fp8, round_fp16)
+    if fp8:
+        a = attn_fn(q, k, vh, rows=rows)
+    else:
+        a = attn_fn(q[:, :, rows], k, vh)
+    a = _held(_merge(a), fp8)                                  # [B, R, D]
+    B = x_img.shape[0]
+    out = np.empty((B, len(rows), D))
+    for s, (x, m) in streams.items():
+        sel = np.nonzero(rows < Lt)[0] if s == "txt" else np.nonzero(rows >= Lt)[0]
+        if len(sel) == 0:
+            continue
+        tok = rows[sel] if s == "txt" else rows[sel] - Lt
+        xs = x[:, tok]
+        xs = xs + m[:, 2:3] * _lin(a[:, sel], P, f"{s}.proj", fp8)
+        u = modulate(xs, m[:, 3:4], m[:, 4:5])
+        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8)), fp8)
+        out[:, sel] = xs + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
+    return out
 
 
 def single_block(x, mod, P, ang, H, fp8=False):

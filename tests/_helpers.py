@@ -27,3 +27,13 @@ def parity_err_bf16_stored(got, ref):
     half_ulp = np.ldexp(1.0, e - 9)
     excess = np.maximum(np.abs(g - r) - half_ulp, 0.0)
     return float(np.max(excess) / np.sqrt(np.mean(r * r)))
+
+
+def sampled_block_rows(Lt, L, n, seed):
+    """Sorted joint-token rows (text first): n random text and n random image rows
+    plus both streams' ends, the first image rows and tile edges after them."""
+    g = np.random.default_rng(seed)
+    fixed = [0, Lt - 1, Lt, Lt + 1, L - 1, L - 2, Lt + 127, Lt + 128, Lt + 255, Lt + 256]
+    picks = np.concatenate([g.choice(Lt, n, replace=False), Lt + g.choice(L - Lt, n, replace=False),
+                            [r for r in fixed if 0 <= r < L]])
+    return np.unique(picks).astype(np.int64)

@@ -14,7 +14,7 @@ import torch
 import dit_inputs as DI
 import oracle as O
 from oracle.numerics import quantize_rows_e4m3
-from _helpers import parity_err, parity_err_bf16_stored
+from _helpers import parity_err, parity_err_bf16_stored, sampled_block_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -244,6 +244,36 @@ def test_block_forward_fp8_flux_1024(dit):
     ref = _oracle_block_fp8(params, inp, w, dims, "double")
     err = parity_err(got, ref)
     _say(f"  err {err:.3e}")
+    assert err <= TOL_FP8
+
+
+
+@pytest.mark.timeout(300)        # the fp64 oracle's share takes ~1 min on 8 cores
+def test_block_forward_fp8_2048_cfg_sampled(dit):
+    """The fp8 double block at the 2048px CFG-pair shape of the fp8 model step
+    (2 x (16384 image + 512 text) tokens, D 3072, fp32 residual stream, per-batch
+    modulation), run whole on the GPU and compared on ~80 sampled rows per batch
+    element.  Activation scales are per token and attention scales per (batch,
+    head) over all rows, so the oracle's sampled rows equal its full block there."""
+    dims = DI.Dims(D=3072, H=24, F=12288, n_double=1, n_single=0)
+    w = DI.Workload("t", dims, B=2, grid_h=128, grid_w=128, Lt=512, dtype="fp8")
+    _say(f"fp8 block double sampled 2048px B={w.B} L={w.L}")
+    params, dev8, inp, blk, dd, rope, ws, x = _block_fp8_setup(dit, dims, w, "double",
+                                                               torch.float32)
+    dit.dit_block_forward(dd, blk, x, inp["mod"].cuda(), rope, ws, dtype=dit.DIT_FP8)
+    torch.cuda.synchronize()
+    rows = sampled_block_rows(w.Lt, w.L, 32, 2049)
+    got = x[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    del dev8, ws, x
+    P = {k: O.to64(v) for k, v in params.items()}
+    x64 = O.to64(inp["x"])
+    m64 = O.to64(inp["mod"])
+    ang = O.rope_table(O.image_positions(w.grid_h, w.grid_w, w.Lt), dims.d)
+    ref = O.double_block_rows(x64[:, :w.Lt], x64[:, w.Lt:], m64[:, :6], m64[:, 6:], P, ang,
+                              dims.H, rows, fp8=True)
+    err = parity_err(got, ref)
+    derr = parity_err(got - x64[:, rows], ref - x64[:, rows])
+    _say(f"  rows {len(rows)} x_out err {err:.3e} branch err {derr:.3e}")
     assert err <= TOL_FP8
 
 

@@ -14,7 +14,7 @@ import torch
 
 import dit_inputs as DI
 import oracle as O
-from _helpers import parity_err, parity_err_bf16_stored
+from _helpers import parity_err, parity_err_bf16_stored, sampled_block_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -185,6 +185,44 @@ def test_block_forward_flux_1024(dit):
     err = parity_err_bf16_stored(got, ref)
     _say(f"  err {err:.3e}")
     assert err <= TOL_BF16
+
+
+
+@pytest.mark.timeout(300)        # the fp64 oracle's share takes ~1 min on 8 cores
+def test_block_forward_2048_cfg_sampled(dit):
+    """The double block at the 2048px CFG-pair shape, in the launch configuration
+    the benchmark times (fp32 residual stream, per-batch modulation): 2 x (16384
+    image + 512 text) tokens, D 3072.  The GPU runs the whole block; the oracle
+    computes every token's Q, K, V and the complete output of ~80 sampled rows
+    per batch element, which is exactly what the full block gives at those rows."""
+    w = DI.WORKLOADS["block_2048_cfg"]
+    dims = w.dims
+    _say(f"block double sampled 2048px B={w.B} L={w.L} D={dims.D}")
+    params = DI.block_params(dims, "bf16", "double")
+    dev = {n: (t.cuda() if n.endswith(".w") else t.float().cuda()) for n, t in params.items()}
+    blk = dit.make_double_block(dev)
+    dd = dit.dims_of(w.B, w.Lt, w.grid_h, w.grid_w, dims.D, dims.H, dims.F)
+    rope = dit.dit_rope_table(w.grid_h, w.grid_w, w.Lt, dims.d)
+    ws = dit.workspace(dd, dit.DIT_WS_BLOCK)
+    x_in = DI.randn((w.B, w.L, dims.D), DI.SEED_ACT, 1.0, "f32")
+    mod = DI.randn((w.B, 12, dims.D), DI.SEED_MOD, DI.MOD_STD, "f32")
+    x = x_in.cuda()
+    dit.dit_block_forward(dd, blk, x, mod.cuda(), rope, ws)
+    torch.cuda.synchronize()
+    rows = sampled_block_rows(w.Lt, w.L, 32, 2048)
+    got = x[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    del dev, ws, x
+    P = {k: O.to64(v) for k, v in params.items()}
+    x64 = O.to64(x_in)
+    m64 = O.to64(mod)
+    ang = O.rope_table(O.image_positions(w.grid_h, w.grid_w, w.Lt), dims.d)
+    ref = O.double_block_rows(x64[:, :w.Lt], x64[:, w.Lt:], m64[:, :6], m64[:, 6:], P, ang,
+                              dims.H, rows)
+    err = parity_err(got, ref)
+    derr = parity_err(got - x64[:, rows], ref - x64[:, rows])
+    _say(f"  rows {len(rows)} x_out err {err:.3e} branch err {derr:.3e}")
+    assert err <= TOL_BF16
+    assert derr <= TOL_BRANCH
 
 
 # ---------------------------------------------------------------- First-Block-Cache

@@ -309,6 +309,19 @@ def test_double_block_stream_isolation():
     assert np.max(np.abs(oi - xi)) > 1e-3
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_double_block_rows_equals_full_block(fp8):
+    # the row-sampled block is the full block restricted to the sampled rows (text,
+    # image and boundary rows, out of order); fp8 included (its scales span heads)
+    rng = np.random.default_rng(15)
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng, D=64, H=2, F=256, Lt=5, gh=4, gw=4, B=2)
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H, fp8=fp8)
+    full = np.concatenate([ot, oi], axis=1)
+    rows = np.array([20, 0, 4, 5, 13, 2])
+    got = O.double_block_rows(xt, xi, mi, mt, P, ang, H, rows, fp8=fp8)
+    np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
+
+
 def test_double_block_brute_force_small():
     # the joint attention written out token by token, no reshapes, no rope
     # helpers: catches a transposed head split or a swapped stream order
