@@ -8,11 +8,14 @@ synthetic inputs: latents, text tokens and N(0, 0.02) weights drawn by torch's
 device generator (seeded per tensor), all resident in HBM before timing.
 
 Timed region: the modulation precompute for the K steps' sigmas (one skinny
-GEMM over all stacked modulation weights) + K calls of dit_denoise_step with
-the First-Block-Cache test evaluated every step.  ``value`` uses threshold 0,
-so no step skips work; the run at the workload's own threshold is reported
-beside it under ``fbcache``.  Per-kernel durations come from HIP events the
-library records around its own launches on the launch stream.
+GEMM over all stacked modulation weights) + K replays of the captured step graph
+(dit_loop_graph_run: step index, sigma and the First-Block-Cache decision read
+on the device, no host sync between steps) with the cache test evaluated every
+step.  ``value`` uses threshold 0, so no step skips work; the same K steps
+through the eager entry point (dit_denoise_step, one host sync per step) are
+reported under ``eager_loop``, and both loops at the workload's own threshold
+under ``fbcache``.  Per-kernel durations come from a separate eager pass with
+HIP events the library records around its own launches on the launch stream.
 
 Beside the 1024px line the same JSON carries the 2048px figures: one bf16
 double block of the 2048px CFG-pair shape (16384 + 512 tokens, batch 2:
@@ -48,16 +51,16 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1138710 * 1024 + 230339 * 1024,
+    "gemm_lin1": {"bytes": 1155664 * 1024 + 230383 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "043831c2989c1af8728c27964c901b6f037608b1"},
-    "attention": {"bytes": 101506 * 1024 + 27691 * 1024,
+                  "sha1": "f4dd20cfbc8cfe03ba6a3634bf6db2dca2da625b"},
+    "attention": {"bytes": 101508 * 1024 + 27693 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",
                   "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
-                  "sha1": "9f33d97ad07418f52f8e49547fc8777681459d72"},
+                  "sha1": "2c713befa949038ff16ffa14885b8ede97e74b2f"},
 }
 
 
@@ -267,6 +270,60 @@ def run_loop(dit, gm, sig, txt, lat0, ws, threshold, K, timer=None):
     return t1 - t0, skipped, rels
 
 
+def run_replayed(dit, gm, sig, txt, lat0, threshold, K):
+    """K Euler steps through the captured step graph (FBC decision on the device),
+    fresh cache; the graph is built and warmed once outside the timed region, as a
+    server would for a resolution.  Returns (seconds, skipped, rels)."""
+    import torch
+    D = gm.model.dims.D
+    Li = gm.model.dims.grid_h * gm.model.dims.grid_w
+    cache = dit.FBCache(gm.model.dims.B, Li, D, threshold, enabled=True)
+    lat = lat0.clone()
+    mods = dit.dit_modulation(gm, sig[:K])
+    g = dit.LoopGraph(gm, mods, txt, lat, sig[:K + 1], cache)
+    g.run(min(K, 2))                       # first replays upload the graph
+    g.sync()
+    lat.copy_(lat0)
+    cache.c.has_anchor, cache.c.steps_done, cache.c.skip_run = 0, 0, 0
+    g.reset(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dit.dit_modulation(gm, sig[:K], out=mods)
+    g.run(K)
+    done, info = g.sync()
+    t1 = time.perf_counter()
+    g.close()
+    assert done == K
+    return t1 - t0, sum(int(s_) for _, s_ in info), [r for r, _ in info]
+
+
+def tiny_loop_latency(dit, DI, device, reps=20):
+    """Latency of the whole 4-step loop of the tiny fp32 model (2 double blocks,
+    hidden 256, 16 x 16 + 32 tokens): eager steps vs the replayed step graph, FBC
+    on at threshold 0 (the test runs, nothing skips)."""
+    import torch
+    w = DI.WORKLOADS["tiny_fp32"]
+    params = dict(DI.iter_params(w.dims, "f32"))
+    gm = dit.GPUModel(w.dims, w.B, w.Lt, w.grid_h, w.grid_w, params, dtype=dit.DIT_F32)
+    sig = dit.dit_sigmas(w.steps, w.shift)
+    txt = DI.text_tokens(w).float().to(device)
+    lat0 = DI.latents(w)[0].to(device)
+    ws = dit.workspace(gm.model.dims, dit.DIT_WS_STEP)
+    K = w.steps
+    eager = []
+    for _ in range(reps):
+        secs, _, _ = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K)
+        eager.append(secs)
+    replayed = []
+    for _ in range(reps):
+        secs, _, _ = run_replayed(dit, gm, sig, txt, lat0, 0.0, K)
+        replayed.append(secs)
+    med = lambda v: sorted(v)[len(v) // 2]
+    return {"workload": w.name, "steps": K, "eager_loop_ms": round(1e3 * med(eager), 3),
+            "replayed_loop_ms": round(1e3 * med(replayed), 3),
+            "speedup": round(med(eager) / med(replayed), 3), "reps": reps, "stat": "median"}
+
+
 def cpu_baseline(DI, w):
     """The fp64 oracle on the host: one double-stream block of the workload's
     shape, extrapolated to a whole step.  Both block kinds carry the same
@@ -304,6 +361,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fbcache-run", action="store_true")
     ap.add_argument("--no-2048", action="store_true", help="skip the 2048px block and fp8 loop")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the tiny-model loop latency (eager vs replayed step graph)")
     ap.add_argument("--fp8-steps", type=int, default=3)
     ap.add_argument("--only-2048", action="store_true",
                     help="run only the 2048px block and fp8 loop (profiling runs)")
@@ -358,13 +417,22 @@ def main():
     if args.warmup > 0:
         run_loop(dit, gm, sig, txt, lat0, ws, 0.0, min(args.warmup, w.steps))
 
-    # timed region: K steps, threshold 0 (every block runs), kernel timers on
+    # timed region: K steps through the replayed step graph, FBC test on at
+    # threshold 0 (the test runs every step, every block runs)
     K = args.steps
+    log(f"[bench] timed: {K} steps, replayed step graph, FBC threshold 0")
+    secs, skipped, _ = run_replayed(dit, gm, sig, txt, lat0, 0.0, K)
+    assert skipped == 0
+    # the same K steps eagerly (one host-driven call per step, a host sync per step)
+    log(f"[bench] eager: {K} steps, FBC threshold 0")
+    secs_e, skipped_e, _ = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K)
+    assert skipped_e == 0
+    # per-kernel durations: an eager pass with HIP events around every launch (the
+    # events cost ~2% of the step, so this pass is not the timed one)
     per_step_sites = 8 * (dims.n_double + dims.n_single) + 16
     timer = dit.KernelTimer(ALL_SITES, capacity=per_step_sites * K + 64)
-    log(f"[bench] timed: {K} steps, FBC threshold 0")
-    secs, skipped, rels = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
-    assert skipped == 0
+    log(f"[bench] instrumented eager pass: {K} steps")
+    run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
     by_site = site_totals(timer.durations_ms())
     timer.close()
 
@@ -411,7 +479,10 @@ def main():
         "config": {"workload": w.name, "image_px": w.image_px, "tokens": [w.Lt, Li],
                    "blocks": [dims.n_double, dims.n_single], "D": dims.D, "heads": dims.H,
                    "mlp": dims.F, "batch": B, "euler_steps": w.steps, "shift": w.shift,
-                   "fbcache_threshold_timed": 0.0, "residual_stream": "f32"},
+                   "fbcache_threshold_timed": 0.0, "residual_stream": "f32",
+                   "loop": "replayed step graph"},
+        "eager_loop": {"steps_per_s": round(K / secs_e, 4),
+                       "ms_per_step": round(1e3 * secs_e / K, 3)},
         "attention_tflops": round(attn_tflops, 1) if attn_tflops else None,
         "attention_frac_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
         "block_gemm_tflops": round(block_gemm_tflops, 1) if block_gemm_tflops else None,
@@ -423,14 +494,19 @@ def main():
     }
 
     if not args.no_fbcache_run:
-        log(f"[bench] FBC run: threshold {w.threshold}")
-        secs_c, skipped_c, rels_c = run_loop(dit, gm, sig, txt, lat0, ws, w.threshold, K)
+        log(f"[bench] FBC runs: threshold {w.threshold}, replayed and eager")
+        secs_c, skipped_c, rels_c = run_replayed(dit, gm, sig, txt, lat0, w.threshold, K)
+        secs_ce, skipped_ce, _ = run_loop(dit, gm, sig, txt, lat0, ws, w.threshold, K)
         out["fbcache"] = {"threshold": w.threshold, "steps_per_s": round(K / secs_c, 4),
-                          "skipped_steps": skipped_c,
+                          "eager_steps_per_s": round(K / secs_ce, 4),
+                          "skipped_steps": skipped_c, "eager_skipped_steps": skipped_ce,
                           "rel_l1": [None if not math.isfinite(r) else round(r, 5)
                                      for r in rels_c]}
     del gm, ws
     torch.cuda.empty_cache()
+    if not args.no_tiny:
+        log("[bench] tiny fp32 loop latency, eager vs replayed")
+        out["tiny_loop_latency"] = tiny_loop_latency(dit, DI, device)
     if not args.no_2048:
         log("[bench] 2048px bf16 block")
         out["block_2048px_bf16"] = block_2048_bf16(dit, DI, device)

@@ -50,7 +50,9 @@ __device__ __forceinline__ int swap23(int r) {
 
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const f16_t* __restrict__ VT,
-    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
+    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
+    const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   __shared__ __attribute__((aligned(1024))) char st0[ATT_SB];
   __shared__ __attribute__((aligned(1024))) char st1[ATT_SB];
 
@@ -277,7 +279,9 @@ static_assert(AF8_KB % 1024 == 0 && AF8_VB % 1024 == 0, "whole 1-KB loads");
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
     const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ VT,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
-    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
+    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
+    const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   __shared__ __attribute__((aligned(1024))) char st0[AF8_SB];
   __shared__ __attribute__((aligned(1024))) char st1[AF8_SB];
 
@@ -478,7 +482,9 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
 template <int HD>
 __global__ __launch_bounds__(64) void attention_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ VT,
-    float* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2) {
+    float* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
+    const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   __shared__ float sK[64][HD];
   __shared__ float sV[HD][65];
   const int lane = threadIdx.x;
@@ -549,10 +555,10 @@ hipError_t attention_f32(const float* q, const float* k, const float* vt, float*
   const dim3 grid((L + 63) / 64, B * H);
   if (d == 64)
     hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
-                       L, scale_log2);
+                       L, scale_log2, launch_gate());
   else
     hipLaunchKernelGGL(attention_f32_kernel<32>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
-                       L, scale_log2);
+                       L, scale_log2, launch_gate());
   return hipGetLastError();
 }
 
@@ -566,7 +572,7 @@ hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, con
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   KTimerScope timer(KS_ATTENTION, st);
   hipLaunchKernelGGL(attention_fp8_kernel, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q8, k8, vt8,
-                     sq, sk, sv, o, ldo, map, H, L, scale_log2);
+                     sq, sk, sv, o, ldo, map, H, L, scale_log2, launch_gate());
   return hipGetLastError();
 }
 
@@ -580,7 +586,7 @@ hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf1
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   KTimerScope timer(KS_ATTENTION, st);
   hipLaunchKernelGGL(attention_bf16_kernel, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q, k, vt, o,
-                     ldo, map, H, L, scale_log2);
+                     ldo, map, H, L, scale_log2, launch_gate());
   return hipGetLastError();
 }
 

@@ -65,6 +65,12 @@ __device__ __forceinline__ float gelu_tanh_f(float x) {
   return x * fast_rcp(1.0f + fast_exp2(-2.0f * 1.4426950408889634f * u));
 }
 
+// A set launch gate holding a non-zero value: the kernel returns before any work.
+// Every thread reads the same word, so the exit is uniform.
+__device__ __forceinline__ bool gate_closed(const int* gate) {
+  return gate != nullptr && *gate != 0;
+}
+
 template <typename T> struct XIO;
 template <> struct XIO<float> {
   static __device__ __forceinline__ float ld(const float* p) { return *p; }

@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
+#include <new>
 
 #include "../../include/dit.h"
 #include "common.h"
@@ -21,6 +23,7 @@ namespace {
 
 thread_local std::string g_last_error;
 thread_local dit_kernel_timer* g_timer = nullptr;
+thread_local const int* g_gate = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -206,6 +209,27 @@ ModWS carve_mod(Carver& c, const Dims& dm, int n) {
   w.h = c.take<float>((size_t)n * dm.D);
   w.cs = c.take<float>((size_t)n * dm.D);
   return w;
+}
+
+// Caller memory of a graph-replayed loop (dit_loop_state_bytes).
+struct LoopBufs {
+  LoopState* state;
+  double* sig;       // [n + 1]
+  LoopLog* log;      // [n]
+  float* mod_cur;    // [N_mod]: the running step's modulation vectors
+};
+
+size_t n_mod_of(const dit_model* m) {
+  return (12 * (size_t)m->n_double + 3 * (size_t)m->n_single + 2) * (size_t)m->dims.D;
+}
+
+LoopBufs carve_loop(Carver& c, size_t n_mod, int n) {
+  LoopBufs b;
+  b.state = c.take<LoopState>(1);
+  b.sig = c.take<double>((size_t)n + 1);
+  b.log = c.take<LoopLog>((size_t)n);
+  b.mod_cur = c.take<float>(n_mod);
+  return b;
 }
 
 size_t ws_size(const Dims& dm, int purpose, int n) {
@@ -479,7 +503,136 @@ hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, 
   return block_impl<float>(dm, blk, x, mod, bs, rope, w, st);
 }
 
+// ---- the pieces of one denoise step, shared by the eager and the replayed loop
+
+// Model checks common to the step entry points.
+int check_model(const dit_model* m, Dims* dm, const char* fn) {
+  int rc;
+  if ((rc = make_dims(&m->dims, dm))) return rc;
+  if ((rc = check_block_dims(*dm, m->dtype))) return rc;
+  if (m->n_double < 1 || m->n_single < 0 || !m->blocks)
+    return fail(DIT_ERR_INVALID_ARG, "%s: needs >= 1 double block", fn);
+  for (int j = 0; j < m->n_double + m->n_single; ++j) {
+    if ((rc = check_block(&m->blocks[j], m->dtype == DIT_FP8))) return rc;
+    const int want = j < m->n_double ? DIT_BLOCK_DOUBLE : DIT_BLOCK_SINGLE;
+    if (m->blocks[j].kind != want)
+      return fail(DIT_ERR_INVALID_ARG, "%s: block %d has the wrong kind", fn, j);
+  }
+  if ((rc = check_linear(m->img_in, "img_in")) || (rc = check_linear(m->final_out, "final_out")))
+    return rc;
+  if (m->C_in < 4 || m->C_in > 64 || m->C_in % 4)
+    return fail(DIT_ERR_UNSUPPORTED, "%s: C_in %d (4..64, multiple of 4)", fn, m->C_in);
+  if (dm->B > 2) return fail(DIT_ERR_UNSUPPORTED, "%s: B must be 1 or 2", fn);
+  if (dm->B == 2 && !std::isfinite(m->guidance))
+    return fail(DIT_ERR_INVALID_ARG, "%s: non-finite guidance", fn);
+  return DIT_OK;
+}
+
+int check_cache(const dit_fbcache* cache, const char* fn) {
+  if (!cache || !cache->enabled) return DIT_OK;
+  if (!cache->anchor || !cache->cached || !aligned16(cache->anchor) || !aligned16(cache->cached))
+    return fail(DIT_ERR_INVALID_ARG, "%s: cache buffers NULL or misaligned", fn);
+  if (std::isnan(cache->threshold)) return fail(DIT_ERR_INVALID_ARG, "%s: NaN threshold", fn);
+  if (cache->warmup_steps < 0 || cache->max_skips < 0 || cache->steps_done < 0 ||
+      cache->skip_run < 0)
+    return fail(DIT_ERR_INVALID_ARG, "%s: negative cache policy field", fn);
+  return DIT_OK;
+}
+
+// RoPE table, text tokens and embedded latents into the joint stream; the image
+// hidden before block 0 into w.before.
+hipError_t step_embed(const dit_model* m, const Dims& dm, const void* txt, const float* latents,
+                      const StepWS& w, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, D = dm.D;
+  hipError_t e;
+  if ((e = rope_table(w.rope, dm.gw, Lt, dm.L, dm.d, 10000.0, st))) return e;
+  if (m->dtype == DIT_F32) {
+    if (Lt > 0 && (e = text_to_stream((const float*)txt, w.x, B, Lt, dm.L, D, st))) return e;
+    return embed_latents(latents, (const float*)m->img_in.w, m->img_in.b, w.x, w.before, B, Lt, Li,
+                         D, m->C_in, st);
+  }
+  if (Lt > 0 && (e = text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st))) return e;
+  return embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before, B, Lt, Li,
+                       D, m->C_in, st);
+}
+
+// Blocks 1.. (all but the first).
+hipError_t step_rest(const dit_model* m, const Dims& dm, const float* mod_step, const StepWS& w,
+                     hipStream_t st) {
+  const size_t D12 = 12 * (size_t)dm.D, D3 = 3 * (size_t)dm.D;
+  hipError_t e;
+  for (int j = 1; j < m->n_double; ++j)
+    if ((e = run_block(dm, m->dtype, m->blocks[j], w.x, mod_step + j * D12, 0, w.rope, w.blk, st)))
+      return e;
+  const float* ms = mod_step + m->n_double * D12;
+  for (int j = 0; j < m->n_single; ++j)
+    if ((e = run_block(dm, m->dtype, m->blocks[m->n_double + j], w.x, ms + j * D3, 0, w.rope, w.blk,
+                       st)))
+      return e;
+  return hipSuccess;
+}
+
+// Velocity head on the image rows into w.v [B * Li, C_in].
+hipError_t step_velocity(const dit_model* m, const Dims& dm, const float* mod_step,
+                         const StepWS& w, hipStream_t st) {
+  const int B = dm.B, Li = dm.Li, D = dm.D;
+  const float* mf = mod_step + m->n_double * 12 * (size_t)D + m->n_single * 3 * (size_t)D;
+  const RowMap sm{B, dm.Lt, Li, dm.L, 1, 0};
+  hipError_t e;
+  if (m->dtype == DIT_F32) {
+    if ((e = ln_modulate<float>(w.x, w.blk.u32, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D, 0,
+                                st)))
+      return e;
+    return gemm32_store(gp32(w.blk.u32, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in, st);
+  }
+  if ((e = ln_modulate<float>(w.x, w.blk.u, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D, 0, st)))
+    return e;
+  return gemm_store_f32(gp(w.blk.u, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in, st);
+}
+
+// One step of a replayed loop, every per-step value read from the loop state.
+hipError_t enqueue_loop_step(const dit_model* m, const Dims& dm, const float* mod_all,
+                             const void* txt, float* latents, float* anchor, float* cached,
+                             bool cache_on, const StepWS& w, const LoopBufs& lb, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, D = dm.D;
+  hipError_t e;
+  if ((e = loop_begin(lb.state, mod_all, n_mod_of(m), lb.sig, lb.mod_cur, lb.log, st))) return e;
+  if ((e = step_embed(m, dm, txt, latents, w, st))) return e;
+  if ((e = run_block(dm, m->dtype, m->blocks[0], w.x, lb.mod_cur, 0, w.rope, w.blk, st))) return e;
+  if (cache_on) {
+    int* skip = &lb.state->skip;
+    if ((e = fbc_reduce_loop(w.x, w.before, anchor, w.staging, w.part, FBC_PARTS, lb.state, lb.log,
+                             B, Lt, Li, D, st)))
+      return e;
+    {
+      GateScope gate(skip);
+      if ((e = step_rest(m, dm, lb.mod_cur, w, st))) return e;
+    }
+    if ((e = fbc_apply(w.x, cached, B, Lt, Li, D, st, skip, 1))) return e;
+    if ((e = fbc_commit(w.x, w.before, w.staging, cached, anchor, B, Lt, Li, D, st, skip, 0,
+                        &lb.state->has_anchor)))
+      return e;
+  } else if ((e = step_rest(m, dm, lb.mod_cur, w, st))) {
+    return e;
+  }
+  if ((e = step_velocity(m, dm, lb.mod_cur, w, st))) return e;
+  return euler_update_loop(latents, w.v, Li * m->C_in, B == 2 ? 1 : 0, m->guidance, lb.state, st);
+}
+
 }  // namespace
+
+// Host handle of a captured step graph.
+struct dit_loop_graph {
+  hipGraphExec_t exec;
+  int device;
+  int n_steps;
+  int launched;        // replays enqueued since create / reset
+  int cache_on;
+  float* anchor;       // the cache buffers baked into the graph
+  float* cached;
+  LoopState* state;
+  LoopLog* log;
+};
 
 namespace dit {
 void ktimer_start(int site, hipStream_t st) {
@@ -488,6 +641,9 @@ void ktimer_start(int site, hipStream_t st) {
   t->sites[t->count] = site;
   (void)hipEventRecord((hipEvent_t)t->start[t->count], st);
 }
+const int* launch_gate() { return g_gate; }
+GateScope::GateScope(const int* g) : prev(g_gate) { g_gate = g; }
+GateScope::~GateScope() { g_gate = prev; }
 void ktimer_stop(int site, hipStream_t st) {
   dit_kernel_timer* t = g_timer;
   if (!t || !((t->site_mask >> site) & 1u) || t->count >= t->capacity) return;
@@ -820,38 +976,14 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
     return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: NULL pointer");
   Dims dm;
   int rc;
-  if ((rc = make_dims(&m->dims, &dm))) return rc;
-  if ((rc = check_block_dims(dm, m->dtype))) return rc;
-  const int dt = m->dtype;
-  if (m->n_double < 1 || m->n_single < 0 || !m->blocks)
-    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: needs >= 1 double block");
-  for (int j = 0; j < m->n_double + m->n_single; ++j) {
-    if ((rc = check_block(&m->blocks[j], dt == DIT_FP8))) return rc;
-    const int want = j < m->n_double ? DIT_BLOCK_DOUBLE : DIT_BLOCK_SINGLE;
-    if (m->blocks[j].kind != want)
-      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: block %d has the wrong kind", j);
-  }
-  if ((rc = check_linear(m->img_in, "img_in")) || (rc = check_linear(m->final_out, "final_out")))
-    return rc;
-  if (m->C_in < 4 || m->C_in > 64 || m->C_in % 4)
-    return fail(DIT_ERR_UNSUPPORTED, "dit_denoise_step: C_in %d (4..64, multiple of 4)", m->C_in);
-  if (dm.B > 2) return fail(DIT_ERR_UNSUPPORTED, "dit_denoise_step: B must be 1 or 2");
-  if (!std::isfinite(sigma) || !std::isfinite(sigma_next) ||
-      (dm.B == 2 && !std::isfinite(m->guidance)))
-    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: non-finite sigma or guidance");
+  if ((rc = check_model(m, &dm, "dit_denoise_step"))) return rc;
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: non-finite sigma");
   if (!aligned16(mod_step) || !aligned16(latents) || !aligned16(workspace) ||
       (txt && !aligned16(txt)))
     return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: pointers must be 16-byte aligned");
   const bool use_cache = cache && cache->enabled;
-  if (use_cache) {
-    if (!cache->anchor || !cache->cached || !aligned16(cache->anchor) || !aligned16(cache->cached))
-      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: cache buffers NULL or misaligned");
-    if (std::isnan(cache->threshold))
-      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: NaN threshold");
-    if (cache->warmup_steps < 0 || cache->max_skips < 0 || cache->steps_done < 0 ||
-        cache->skip_run < 0)
-      return fail(DIT_ERR_INVALID_ARG, "dit_denoise_step: negative cache policy field");
-  }
+  if ((rc = check_cache(cache, "dit_denoise_step"))) return rc;
   const size_t need = ws_size(dm, DIT_WS_STEP, 0);
   if (ws_bytes < need)
     return fail(DIT_ERR_WORKSPACE, "dit_denoise_step: workspace %zu < %zu bytes", ws_bytes, need);
@@ -861,19 +993,9 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   Carver c{(char*)workspace, 0};
   const StepWS w = carve_step(c, dm);
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, D = dm.D;
-  const size_t D12 = 12 * (size_t)D, D3 = 3 * (size_t)D;
 
-  DIT_CHECK_HIP(rope_table(w.rope, dm.gw, Lt, dm.L, dm.d, 10000.0, st));
-  if (dt == DIT_F32) {
-    if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const float*)txt, w.x, B, Lt, dm.L, D, st));
-    DIT_CHECK_HIP(embed_latents(latents, (const float*)m->img_in.w, m->img_in.b, w.x, w.before,
-                                B, Lt, Li, D, m->C_in, st));
-  } else {
-    if (Lt > 0) DIT_CHECK_HIP(text_to_stream((const bf16_t*)txt, w.x, B, Lt, dm.L, D, st));
-    DIT_CHECK_HIP(embed_latents(latents, (const bf16_t*)m->img_in.w, m->img_in.b, w.x, w.before,
-                                B, Lt, Li, D, m->C_in, st));
-  }
-  DIT_CHECK_HIP(run_block(dm, dt, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
+  DIT_CHECK_HIP(step_embed(m, dm, txt, latents, w, st));
+  DIT_CHECK_HIP(run_block(dm, m->dtype, m->blocks[0], w.x, mod_step, 0, w.rope, w.blk, st));
 
   double rel = INFINITY;
   int skip = 0;
@@ -894,12 +1016,7 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   if (skip) {
     DIT_CHECK_HIP(fbc_apply(w.x, cache->cached, B, Lt, Li, D, st));
   } else {
-    for (int j = 1; j < m->n_double; ++j)
-      DIT_CHECK_HIP(run_block(dm, dt, m->blocks[j], w.x, mod_step + j * D12, 0, w.rope, w.blk, st));
-    const float* ms = mod_step + m->n_double * D12;
-    for (int j = 0; j < m->n_single; ++j)
-      DIT_CHECK_HIP(run_block(dm, dt, m->blocks[m->n_double + j], w.x, ms + j * D3, 0, w.rope,
-                              w.blk, st));
+    DIT_CHECK_HIP(step_rest(m, dm, mod_step, w, st));
     if (use_cache) {
       DIT_CHECK_HIP(fbc_commit(w.x, w.before, w.staging, cache->cached, cache->anchor, B, Lt, Li, D,
                                st));
@@ -907,25 +1024,196 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
     }
   }
   // velocity head on the image rows, then the Euler (+CFG) update
-  const float* mf = mod_step + m->n_double * D12 + m->n_single * D3;
-  const RowMap sm{B, Lt, Li, dm.L, 1, 0};
-  if (dt == DIT_F32) {
-    DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u32, B * Li, D, sm, B * Li, mf, mf + D, mf,
-                                     mf + D, 0, st));
-    DIT_CHECK_HIP(gemm32_store(gp32(w.blk.u32, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in,
-                               st));
-  } else {
-    DIT_CHECK_HIP(ln_modulate<float>(w.x, w.blk.u, B * Li, D, sm, B * Li, mf, mf + D, mf, mf + D,
-                                     0, st));
-    DIT_CHECK_HIP(gemm_store_f32(gp(w.blk.u, D, m->final_out, D, B * Li, m->C_in), w.v, m->C_in,
-                                 st));
-  }
+  DIT_CHECK_HIP(step_velocity(m, dm, mod_step, w, st));
   DIT_CHECK_HIP(euler_update(latents, w.v, Li * m->C_in, B == 2 ? 1 : 0, m->guidance,
                              (float)(sigma_next - sigma), st));
   if (info_out) {
     info_out->rel = rel;
     info_out->skipped = skip;
   }
+  return DIT_OK;
+}
+
+size_t dit_loop_state_bytes(const dit_model* m, int n_steps) {
+  if (!m || n_steps < 1 || m->n_double < 0 || m->n_single < 0 || m->dims.D <= 0) return 0;
+  Carver c{nullptr, 0};
+  carve_loop(c, n_mod_of(m), n_steps);
+  return (c.off + 255) & ~(size_t)255;
+}
+
+// Initial device state of a replayed loop from the caller's cache state.
+static int write_loop_state(LoopState* dst, int n_steps, int first_step, const dit_fbcache* cache,
+                            hipStream_t st) {
+  LoopState h{};
+  h.next = first_step;
+  h.cur = first_step;
+  h.n_steps = n_steps;
+  if (cache && cache->enabled) {
+    h.cache_on = 1;
+    h.has_anchor = cache->has_anchor ? 1 : 0;
+    h.steps_done = cache->steps_done;
+    h.skip_run = cache->skip_run;
+    h.warmup_steps = cache->warmup_steps;
+    h.max_skips = cache->max_skips;
+    h.threshold = cache->threshold;
+  }
+  DIT_CHECK_HIP(hipMemcpyAsync(dst, &h, sizeof(h), hipMemcpyHostToDevice, st));
+  DIT_CHECK_HIP(hipStreamSynchronize(st));
+  return DIT_OK;
+}
+
+int dit_loop_graph_create(const dit_model* m, const float* mod_all, const void* txt,
+                          float* latents, const double* sigmas_host, int n_steps,
+                          const dit_fbcache* cache, void* workspace, size_t ws_bytes,
+                          void* loop_state, size_t state_bytes, void* stream,
+                          dit_loop_graph** out) {
+  const char* fn = "dit_loop_graph_create";
+  if (!out) return fail(DIT_ERR_INVALID_ARG, "%s: NULL out", fn);
+  *out = nullptr;
+  if (!m || !mod_all || !latents || !sigmas_host || !workspace || !loop_state ||
+      (m->dims.Lt > 0 && !txt))
+    return fail(DIT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (n_steps < 1) return fail(DIT_ERR_INVALID_ARG, "%s: n_steps %d < 1", fn, n_steps);
+  Dims dm;
+  int rc;
+  if ((rc = check_model(m, &dm, fn))) return rc;
+  for (int i = 0; i <= n_steps; ++i)
+    if (!std::isfinite(sigmas_host[i])) return fail(DIT_ERR_INVALID_ARG, "%s: non-finite sigma", fn);
+  if (!aligned16(mod_all) || !aligned16(latents) || !aligned16(workspace) ||
+      !aligned16(loop_state) || (txt && !aligned16(txt)))
+    return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  if ((rc = check_cache(cache, fn))) return rc;
+  const size_t need = ws_size(dm, DIT_WS_STEP, 0);
+  if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  const size_t need_state = dit_loop_state_bytes(m, n_steps);
+  if (state_bytes < need_state)
+    return fail(DIT_ERR_WORKSPACE, "%s: loop state %zu < %zu bytes", fn, state_bytes, need_state);
+  if ((rc = check_device())) return rc;
+  int dev = 0;
+  DIT_CHECK_HIP(hipGetDevice(&dev));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carver c{(char*)workspace, 0};
+  const StepWS w = carve_step(c, dm);
+  Carver cl{(char*)loop_state, 0};
+  const LoopBufs lb = carve_loop(cl, n_mod_of(m), n_steps);
+  const bool cache_on = cache && cache->enabled;
+  DIT_CHECK_HIP(hipMemcpyAsync(lb.sig, sigmas_host, sizeof(double) * (n_steps + 1),
+                               hipMemcpyHostToDevice, st));
+  if ((rc = write_loop_state(lb.state, n_steps, 0, cache, st))) return rc;
+
+  // capture one step on a private stream; nothing runs until the graph is launched
+  hipStream_t cs = nullptr;
+  DIT_CHECK_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) {
+    dit_kernel_timer* timer = g_timer;   // event records stay out of the graph
+    g_timer = nullptr;
+    e = enqueue_loop_step(m, dm, mod_all, txt, latents, cache_on ? cache->anchor : nullptr,
+                          cache_on ? cache->cached : nullptr, cache_on, w, lb, cs);
+    g_timer = timer;
+    const hipError_t e2 = hipStreamEndCapture(cs, &graph);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(cs);
+  if (e != hipSuccess)
+    return fail(DIT_ERR_HIP, "%s: step capture failed: %s", fn, hipGetErrorString(e));
+  dit_loop_graph* g = new (std::nothrow) dit_loop_graph;
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    return fail(DIT_ERR_INVALID_ARG, "%s: out of host memory", fn);
+  }
+  g->exec = exec;
+  g->device = dev;
+  g->n_steps = n_steps;
+  g->launched = 0;
+  g->cache_on = cache_on ? 1 : 0;
+  g->anchor = cache_on ? cache->anchor : nullptr;
+  g->cached = cache_on ? cache->cached : nullptr;
+  g->state = lb.state;
+  g->log = lb.log;
+  *out = g;
+  return DIT_OK;
+}
+
+int dit_loop_graph_run(dit_loop_graph* g, int n, void* stream) {
+  if (!g || n < 0) return fail(DIT_ERR_INVALID_ARG, "dit_loop_graph_run: NULL graph or n < 0");
+  if (g->launched + n > g->n_steps)
+    return fail(DIT_ERR_INVALID_ARG, "dit_loop_graph_run: %d + %d replays exceed the %d steps",
+                g->launched, n, g->n_steps);
+  int dev = 0;
+  DIT_CHECK_HIP(hipGetDevice(&dev));
+  if (dev != g->device)
+    return fail(DIT_ERR_INVALID_ARG, "dit_loop_graph_run: graph of device %d, current %d",
+                g->device, dev);
+  for (int i = 0; i < n; ++i) {
+    DIT_CHECK_HIP(hipGraphLaunch(g->exec, (hipStream_t)stream));
+    g->launched += 1;
+  }
+  return DIT_OK;
+}
+
+int dit_loop_graph_sync(dit_loop_graph* g, dit_fbcache* cache, dit_step_info* info, int n_info,
+                        void* stream, int* steps_run) {
+  if (!g || n_info < 0 || (n_info > 0 && !info))
+    return fail(DIT_ERR_INVALID_ARG, "dit_loop_graph_sync: NULL graph or info");
+  if (cache && (cache->enabled ? 1 : 0) != g->cache_on)
+    return fail(DIT_ERR_INVALID_ARG, "dit_loop_graph_sync: cache enabled flag differs from create");
+  hipStream_t st = (hipStream_t)stream;
+  LoopState h;
+  std::vector<LoopLog> log((size_t)g->n_steps);
+  DIT_CHECK_HIP(hipMemcpyAsync(&h, g->state, sizeof(h), hipMemcpyDeviceToHost, st));
+  DIT_CHECK_HIP(hipMemcpyAsync(log.data(), g->log, sizeof(LoopLog) * log.size(),
+                               hipMemcpyDeviceToHost, st));
+  DIT_CHECK_HIP(hipStreamSynchronize(st));
+  const int done = h.next < g->n_steps ? h.next : g->n_steps;
+  int nonfinite = 0;
+  for (int i = 0; i < g->n_steps; ++i) {
+    if (i < n_info) {
+      info[i].rel = log[i].rel;
+      info[i].skipped = log[i].skip;
+    }
+    if (i < done && log[i].nonfinite) nonfinite = 1;
+  }
+  if (steps_run) *steps_run = done;
+  if (cache && g->cache_on) {
+    cache->has_anchor = h.has_anchor;
+    cache->steps_done = h.steps_done;
+    cache->skip_run = h.skip_run;
+  }
+  if (nonfinite)
+    return fail(DIT_ERR_NONFINITE, "dit_loop_graph_sync: a step met a non-finite residual");
+  return DIT_OK;
+}
+
+int dit_loop_graph_reset(dit_loop_graph* g, const dit_fbcache* cache, int first_step,
+                         void* stream) {
+  const char* fn = "dit_loop_graph_reset";
+  if (!g) return fail(DIT_ERR_INVALID_ARG, "%s: NULL graph", fn);
+  if (first_step < 0 || first_step > g->n_steps)
+    return fail(DIT_ERR_INVALID_ARG, "%s: first_step %d outside [0, %d]", fn, first_step,
+                g->n_steps);
+  const int on = cache && cache->enabled ? 1 : 0;
+  if (on != g->cache_on || (on && (cache->anchor != g->anchor || cache->cached != g->cached)))
+    return fail(DIT_ERR_INVALID_ARG, "%s: the cache must be the one the graph was created with", fn);
+  int rc;
+  if ((rc = check_cache(cache, fn))) return rc;
+  if ((rc = write_loop_state(g->state, g->n_steps, first_step, cache, (hipStream_t)stream)))
+    return rc;
+  g->launched = first_step;
+  return DIT_OK;
+}
+
+int dit_loop_graph_destroy(dit_loop_graph* g) {
+  if (!g) return DIT_OK;
+  const hipError_t e = hipGraphExecDestroy(g->exec);
+  delete g;
+  if (e != hipSuccess)
+    return fail(DIT_ERR_HIP, "dit_loop_graph_destroy: %s", hipGetErrorString(e));
   return DIT_OK;
 }
 

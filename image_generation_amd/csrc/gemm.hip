@@ -232,10 +232,12 @@ struct GemmParams {
   int ngroups;
   int tiles[2];     // tiles per group
   int tiles_n[2];   // n-tiles per group
+  const int* gate;  // launch gate (nullptr: always run)
 };
 
 template <int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi> p) {
+  if (gate_closed(p.gate)) return;
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
@@ -551,6 +553,7 @@ __device__ __forceinline__ f32x16 mfma_mx4(i32x8 a, i32x8 b, f32x16 c, int sa, i
 
 template <int BM, int BN, int WM, int WN, int FMT, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
+  if (gate_closed(p.gate)) return;
   constexpr bool F8 = FMT == 1, F4 = FMT == 2;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
@@ -854,6 +857,7 @@ constexpr int G32_K = 16;    // K chunk
 
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams<Epi> p) {
+  if (gate_closed(p.gate)) return;
   __shared__ float sA[G32_K][G32_T + 4];   // k-major
   __shared__ float sB[G32_K][G32_T + 4];
   int lid = blockIdx.x;
@@ -908,6 +912,7 @@ static hipError_t launch32(const GemmProblem* gp, const Epi* ep, int ng, hipStre
   GemmParams<Epi> p{};
   int total = 0;
   p.ngroups = ng;
+  p.gate = launch_gate();
   for (int i = 0; i < ng; ++i) {
     if (gp[i].K % 4 || gp[i].N % 4 || gp[i].lda % 4 || gp[i].ldw % 4) return hipErrorInvalidValue;
     p.g[i] = gp[i];
@@ -972,6 +977,7 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
   GemmParams<Epi> p{};
   int total = 0;
   p.ngroups = ng;
+  p.gate = launch_gate();
   for (int i = 0; i < ng; ++i) {
     p.g[i] = gp[i];
     p.e[i] = ep[i];

@@ -20,6 +20,17 @@ struct KTimerScope {
   ~KTimerScope() { ktimer_stop(site, st); }
 };
 
+// Gate of the launches made while a GateScope is alive on the calling thread: a
+// device int that each gated kernel reads on entry, returning at once unless it
+// holds 0 (a graph-replayed loop keeps the First-Block-Cache decision there).
+// nullptr, the default: kernels run unconditionally.
+const int* launch_gate();
+struct GateScope {
+  const int* prev;
+  explicit GateScope(const int* g);
+  ~GateScope();
+};
+
 // One GEMM problem: C[M, N] = A[M, K] W[N, K]^T + bias.
 //   bf16: A, W; K % 64 == 0.
 //   fp8 (e4m3): A8, W8 with per-row scales sa[M] and per-output-channel scales

@@ -39,7 +39,9 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
     const XT* __restrict__ x, void* __restrict__ out_, float* __restrict__ oscale, int rows, int D,
     RowMap map, int n_img,
     const float* __restrict__ sh_i, const float* __restrict__ sc_i,
-    const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride) {
+    const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride,
+    const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -131,7 +133,7 @@ hipError_t ln_modulate(const XT* x, OT* out, int rows, int D, const RowMap& map,
   constexpr int mode = sizeof(OT) == 4 ? 2 : 0;
   hipLaunchKernelGGL((ln_modulate_kernel<XT, mode>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
                      (void*)out, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
-                     shift_txt, scale_txt, mod_bstride);
+                     shift_txt, scale_txt, mod_bstride, launch_gate());
   return hipGetLastError();
 }
 template hipError_t ln_modulate<float, bf16_t>(const float*, bf16_t*, int, int, const RowMap&, int,
@@ -150,7 +152,7 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
   KTimerScope timer(KS_LN, st);
   hipLaunchKernelGGL((ln_modulate_kernel<float, 1>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
                      (void*)out8, scale, rows, D, map, n_img_rows, shift_img, scale_img,
-                     shift_txt, scale_txt, mod_bstride);
+                     shift_txt, scale_txt, mod_bstride, launch_gate());
   return hipGetLastError();
 }
 
@@ -286,11 +288,11 @@ __global__ __launch_bounds__(256) void fbc_partial_kernel(
   }
 }
 
-// Pass 2 (one block): fixed-order fp64 sum of the partials and the decision
-// skip = has_anchor && rel < threshold (strict; NaN and a zero denominator never skip).
-__global__ __launch_bounds__(256) void fbc_final_kernel(const double* __restrict__ part, int nparts,
-                                                        int has_anchor, double threshold,
-                                                        FbcResult* __restrict__ res) {
+// Pass 2 (one block): fixed-order fp64 sum of the partials; the result is valid
+// in thread 0.  rel = num / den (+inf without an anchor or with a zero
+// denominator, NaN for 0/0 of NaN sums); nonfinite flags a NaN / Inf in the sums.
+__device__ void fbc_final_sums(const double* __restrict__ part, int nparts, int has_anchor,
+                               double* rel_out, int* nonfinite_out) {
   __shared__ double sn[256], sd[256];
   double a = 0.0, c = 0.0;
   for (int i = threadIdx.x; i < nparts; i += 256) {
@@ -317,9 +319,49 @@ __global__ __launch_bounds__(256) void fbc_final_kernel(const double* __restrict
       nonfinite = !(isfinite(num) && isfinite(den));
       rel = den > 0.0 ? num / den : (num == num ? INFINITY : NAN);
     }
+    *rel_out = rel;
+    *nonfinite_out = nonfinite;
+  }
+}
+
+// The decision skip = has_anchor && rel < threshold (strict; NaN and a zero
+// denominator never skip).
+__global__ __launch_bounds__(256) void fbc_final_kernel(const double* __restrict__ part, int nparts,
+                                                        int has_anchor, double threshold,
+                                                        FbcResult* __restrict__ res) {
+  double rel;
+  int nonfinite;
+  fbc_final_sums(part, nparts, has_anchor, &rel, &nonfinite);
+  if (threadIdx.x == 0) {
     res->rel = rel;
     res->skip = (has_anchor && !nonfinite && rel < threshold) ? 1 : 0;
     res->nonfinite = nonfinite;
+  }
+}
+
+// Loop form: the same test with the anchor flag and threshold of the loop state,
+// then the skip policy (no skip during the warm-up steps nor past max_skips
+// consecutive skips) and its counters, all on the device.  A NaN / Inf in the sums
+// never skips and is recorded in the step's log entry.
+__global__ __launch_bounds__(256) void fbc_final_loop_kernel(const double* __restrict__ part,
+                                                             int nparts, LoopState* __restrict__ s,
+                                                             LoopLog* __restrict__ log) {
+  const int has_anchor = s->has_anchor;
+  double rel;
+  int nonfinite;
+  fbc_final_sums(part, nparts, has_anchor, &rel, &nonfinite);
+  if (threadIdx.x == 0) {
+    const int test = (has_anchor && !nonfinite && rel < (double)s->threshold) ? 1 : 0;
+    const int skip = test && s->steps_done >= s->warmup_steps &&
+                     (s->max_skips == 0 || s->skip_run < s->max_skips);
+    s->steps_done += 1;
+    s->skip_run = skip ? s->skip_run + 1 : 0;
+    s->skip = skip;
+    if (s->cur < s->n_steps) {
+      log[s->cur].rel = rel;
+      log[s->cur].skip = skip;
+      log[s->cur].nonfinite = nonfinite;
+    }
   }
 }
 
@@ -327,7 +369,10 @@ __global__ __launch_bounds__(256) void fbc_final_kernel(const double* __restrict
 __global__ __launch_bounds__(256) void fbc_commit_kernel(
     const float* __restrict__ x, const float* __restrict__ before,
     const float* __restrict__ staging, float* __restrict__ cached, float* __restrict__ anchor,
-    int B, int Lt, int Li, int L, int D) {
+    int B, int Lt, int Li, int L, int D, const int* __restrict__ skip, int run_if,
+    int* __restrict__ has_anchor_out) {
+  if (skip != nullptr && (*skip != 0) != run_if) return;
+  if (has_anchor_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *has_anchor_out = 1;
   const size_t n4 = (size_t)B * Li * D / 4;
   for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
     const size_t e = j * 4;
@@ -344,7 +389,9 @@ __global__ __launch_bounds__(256) void fbc_commit_kernel(
 // Skipped step: x_img += cached.
 __global__ __launch_bounds__(256) void fbc_apply_kernel(float* __restrict__ x,
                                                         const float* __restrict__ cached, int B,
-                                                        int Lt, int Li, int L, int D) {
+                                                        int Lt, int Li, int L, int D,
+                                                        const int* __restrict__ skip, int run_if) {
+  if (skip != nullptr && (*skip != 0) != run_if) return;
   const size_t n4 = (size_t)B * Li * D / 4;
   for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n4; j += (size_t)gridDim.x * 256) {
     const size_t e = j * 4;
@@ -358,9 +405,14 @@ __global__ __launch_bounds__(256) void fbc_apply_kernel(float* __restrict__ x,
 
 // ---------------------------------------------------------------- Euler + CFG
 // lat += dt * v, with v = v_neg + g (v_pos - v_neg) for a CFG pair (pos = batch row 0).
+// With a loop state s, dt comes from it and the step counter advances.
 __global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ lat,
                                                     const float* __restrict__ v, int n, int cfg,
-                                                    float g, float dt) {
+                                                    float g, float dt, LoopState* __restrict__ s) {
+  if (s != nullptr) {
+    dt = s->dt;
+    if (blockIdx.x == 0 && threadIdx.x == 0) s->next = s->next + 1;
+  }
   for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) {
     float vv = v[j];
     if (cfg) {
@@ -368,6 +420,37 @@ __global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ lat,
       vv = vn + g * (vv - vn);
     }
     lat[j] += dt * vv;
+  }
+}
+
+// Start of a replayed step (see loop_begin).  A replay past the last step copies
+// nothing and sets dt = 0, so it leaves the latents as they are.
+__global__ __launch_bounds__(256) void loop_begin_kernel(LoopState* __restrict__ s,
+                                                         const float* __restrict__ mod_all,
+                                                         size_t n_mod, const double* __restrict__ sig,
+                                                         float* __restrict__ mod_cur,
+                                                         LoopLog* __restrict__ log) {
+  const int i = s->next;
+  const int n = s->n_steps;
+  if (i < n) {
+    const f32x4* src = (const f32x4*)(mod_all + (size_t)i * n_mod);
+    f32x4* dst = (f32x4*)mod_cur;
+    for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n_mod / 4;
+         j += (size_t)gridDim.x * 256)
+      dst[j] = src[j];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    s->cur = i;
+    s->skip = 0;
+    if (i < n) {
+      s->dt = (float)(sig[i + 1] - sig[i]);
+      log[i].rel = INFINITY;
+      log[i].skip = 0;
+      log[i].nonfinite = 0;
+    } else {
+      s->dt = 0.0f;
+      s->overrun = 1;
+    }
   }
 }
 
@@ -467,17 +550,40 @@ hipError_t fbc_reduce(const float* x, const float* before, const float* anchor, 
 }
 
 hipError_t fbc_commit(const float* x, const float* before, const float* staging, float* cached,
-                      float* anchor, int B, int Lt, int Li, int D, hipStream_t st) {
+                      float* anchor, int B, int Lt, int Li, int D, hipStream_t st,
+                      const int* skip, int run_if, int* has_anchor_out) {
   KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(fbc_commit_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
-                     x, before, staging, cached, anchor, B, Lt, Li, Lt + Li, D);
+                     x, before, staging, cached, anchor, B, Lt, Li, Lt + Li, D, skip, run_if,
+                     has_anchor_out);
   return hipGetLastError();
 }
 
-hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D, hipStream_t st) {
+hipError_t fbc_apply(float* x, const float* cached, int B, int Lt, int Li, int D, hipStream_t st,
+                     const int* skip, int run_if) {
   KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(fbc_apply_kernel, dim3(grid_for((size_t)B * Li * D / 4)), dim3(256), 0, st,
-                     x, cached, B, Lt, Li, Lt + Li, D);
+                     x, cached, B, Lt, Li, Lt + Li, D, skip, run_if);
+  return hipGetLastError();
+}
+
+hipError_t fbc_reduce_loop(const float* x, const float* before, const float* anchor,
+                           float* staging, double* part, int nparts, LoopState* s, LoopLog* log,
+                           int B, int Lt, int Li, int D, hipStream_t st) {
+  KTimerScope timer(KS_FBC, st);
+  // the sums are always taken; without an anchor the final pass ignores them
+  hipLaunchKernelGGL(fbc_partial_kernel, dim3(nparts), dim3(256), 0, st, x, before, anchor, staging,
+                     part, B, Lt, Li, Lt + Li, D, 1);
+  hipLaunchKernelGGL(fbc_final_loop_kernel, dim3(1), dim3(256), 0, st, part, nparts, s, log);
+  return hipGetLastError();
+}
+
+hipError_t loop_begin(LoopState* s, const float* mod_all, size_t n_mod, const double* sig,
+                      float* mod_cur, LoopLog* log, hipStream_t st) {
+  if (n_mod % 4) return hipErrorInvalidValue;
+  KTimerScope timer(KS_OTHER, st);
+  hipLaunchKernelGGL(loop_begin_kernel, dim3(grid_for(n_mod / 4 + 1)), dim3(256), 0, st, s,
+                     mod_all, n_mod, sig, mod_cur, log);
   return hipGetLastError();
 }
 
@@ -485,7 +591,15 @@ hipError_t euler_update(float* lat, const float* v, int n, int cfg, float g, flo
                         hipStream_t st) {
   KTimerScope timer(KS_OTHER, st);
   hipLaunchKernelGGL(euler_kernel, dim3(grid_for((size_t)n / 4 + 1)), dim3(256), 0, st, lat, v, n,
-                     cfg, g, dt);
+                     cfg, g, dt, (LoopState*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t euler_update_loop(float* lat, const float* v, int n, int cfg, float g, LoopState* s,
+                             hipStream_t st) {
+  KTimerScope timer(KS_OTHER, st);
+  hipLaunchKernelGGL(euler_kernel, dim3(grid_for((size_t)n / 4 + 1)), dim3(256), 0, st, lat, v, n,
+                     cfg, g, 0.0f, s);
   return hipGetLastError();
 }
 

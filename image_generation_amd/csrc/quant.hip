@@ -92,7 +92,8 @@ template <class T>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ src, int lds,
                                                          fp8_t* __restrict__ dst, int ldd,
                                                          float* __restrict__ scale, int rows,
-                                                         int width) {
+                                                         int width, const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -122,7 +123,9 @@ template <class T, int NCH>
 __global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T* __restrict__ src, int lds,
                                                              fp8_t* __restrict__ dst, int ldd,
                                                              float* __restrict__ scale, int rows,
-                                                             int width) {
+                                                             int width,
+                                                             const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -162,7 +165,9 @@ template <class T>
 __global__ __launch_bounds__(256) void quant_slices_kernel(const T* __restrict__ src, size_t n,
                                                            const unsigned int* __restrict__ amax,
                                                            fp8_t* __restrict__ dst,
-                                                           float* __restrict__ scale) {
+                                                           float* __restrict__ scale,
+                                                           const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   float sc, inv;
   scale_of(__uint_as_float(amax[blockIdx.y]), sc, inv);
   const T* s = src + (size_t)blockIdx.y * n;
@@ -175,7 +180,8 @@ __global__ __launch_bounds__(256) void quant_slices_kernel(const T* __restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[blockIdx.y] = sc;
 }
 
-__global__ void zero_u32_kernel(unsigned int* p, int n) {
+__global__ void zero_u32_kernel(unsigned int* p, int n, const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
@@ -189,13 +195,13 @@ hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, 
   const dim3 grid((rows + 3) / 4);
   if (width <= 8 * 512)
     hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8>), grid, dim3(256), 0, st, src, lds, dst, ldd,
-                       scale, rows, width);
+                       scale, rows, width, launch_gate());
   else if (width <= 32 * 512)
     hipLaunchKernelGGL((quant_rows_reg_kernel<T, 32>), grid, dim3(256), 0, st, src, lds, dst, ldd,
-                       scale, rows, width);
+                       scale, rows, width, launch_gate());
   else
     hipLaunchKernelGGL(quant_rows_kernel<T>, grid, dim3(256), 0, st, src, lds, dst, ldd, scale,
-                       rows, width);
+                       rows, width, launch_gate());
   return hipGetLastError();
 }
 template hipError_t quant_rows<bf16_t>(const bf16_t*, int, fp8_t*, int, float*, int, int, hipStream_t);
@@ -210,7 +216,7 @@ hipError_t quant_slices(const T* src, size_t n, int nslices, const unsigned int*
   size_t blocks = (n / 8 + 255) / 256;
   const int bx = (int)(blocks < 64 ? blocks : 64);
   hipLaunchKernelGGL(quant_slices_kernel<T>, dim3(bx, nslices), dim3(256), 0, st, src, n, amax,
-                     dst, scale);
+                     dst, scale, launch_gate());
   return hipGetLastError();
 }
 template hipError_t quant_slices<bf16_t>(const bf16_t*, size_t, int, const unsigned int*, fp8_t*,
@@ -292,7 +298,7 @@ template hipError_t quant_mxfp4<float>(const float*, int, int, int, uint8_t*, ui
 
 hipError_t zero_u32(unsigned int* p, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, launch_gate());
   return hipGetLastError();
 }
 

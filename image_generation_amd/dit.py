@@ -104,6 +104,15 @@ def _load() -> ctypes.CDLL:
         "dit_quantize_mxfp4": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P]),
         "dit_mx_rows": (c_int, [c_int]),
         "dit_linear_mxfp4": (c_int, [P, P, c_int, c_int, P, P, P, c_int, P, c_int, P]),
+        "dit_loop_state_bytes": (c_size_t, [POINTER(DitModel), c_int]),
+        "dit_loop_graph_create": (c_int, [POINTER(DitModel), P, P, P, POINTER(c_double), c_int,
+                                          POINTER(DitFBCache), P, c_size_t, P, c_size_t, P,
+                                          POINTER(P)]),
+        "dit_loop_graph_run": (c_int, [P, c_int, P]),
+        "dit_loop_graph_sync": (c_int, [P, POINTER(DitFBCache), POINTER(DitStepInfo), c_int, P,
+                                        POINTER(c_int)]),
+        "dit_loop_graph_reset": (c_int, [P, POINTER(DitFBCache), c_int, P]),
+        "dit_loop_graph_destroy": (c_int, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -116,7 +125,9 @@ LIB = _load()
 EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_sigmas",
             "dit_rope_table", "dit_attention", "dit_block_forward", "dit_modulation",
             "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward",
-            "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4")
+            "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4",
+            "dit_loop_state_bytes", "dit_loop_graph_create", "dit_loop_graph_run",
+            "dit_loop_graph_sync", "dit_loop_graph_reset", "dit_loop_graph_destroy")
 
 
 def _check(rc: int) -> None:
@@ -495,6 +506,79 @@ def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,
                                 float(sigma), float(sigma_next), cp, _ptr(ws), ws.numel(),
                                 _stream(stream), ctypes.byref(info)))
     return info.rel, bool(info.skipped)
+
+
+class LoopGraph:
+    """A denoise loop captured as one HIP graph per step and replayed with the
+    First-Block-Cache decision kept on the device (dit_loop_graph_*).
+
+    mod_all [n_steps, N_mod] fp32 (dit_modulation over sigmas[:-1]); sigmas: the
+    n_steps + 1 schedule; txt, latents as for dit_denoise_step; cache: FBCache or
+    None.  The workspace and loop state are allocated here and kept with the
+    graph, as are references to every tensor it points into."""
+
+    def __init__(self, gm: GPUModel, mod_all: torch.Tensor, txt: torch.Tensor,
+                 latents: torch.Tensor, sigmas: Sequence[float], cache: Optional[FBCache] = None,
+                 stream=None):
+        n = len(sigmas) - 1
+        dm = gm.model.dims
+        Li = dm.grid_h * dm.grid_w
+        _need(mod_all, torch.float32, (n, gm.n_mod), "mod_all")
+        _need(txt, torch.float32 if gm.dtype == DIT_F32 else torch.bfloat16, (dm.B, dm.Lt, dm.D),
+              "txt")
+        _need(latents, torch.float32, (Li, gm.model.C_in), "latents")
+        self.n_steps = n
+        self.ws = workspace(dm, DIT_WS_STEP)
+        nb = LIB.dit_loop_state_bytes(ctypes.byref(gm.model), n)
+        if nb == 0:
+            raise ValueError("dit_loop_state_bytes rejected the model or step count")
+        self.state = torch.empty(nb, dtype=torch.uint8, device=latents.device)
+        self._keep = (gm, mod_all, txt, latents, cache)
+        self.cache = cache
+        sig = (c_double * (n + 1))(*[float(x) for x in sigmas])
+        h = c_void_p()
+        cp = ctypes.byref(cache.c) if cache is not None else None
+        _check(LIB.dit_loop_graph_create(ctypes.byref(gm.model), _ptr(mod_all), _ptr(txt),
+                                         _ptr(latents), sig, n, cp, _ptr(self.ws), self.ws.numel(),
+                                         _ptr(self.state), self.state.numel(), _stream(stream),
+                                         ctypes.byref(h)))
+        self.h = h
+        self.launched = 0
+
+    def run(self, n: Optional[int] = None, stream=None) -> None:
+        """Enqueue n replays (default: the rest of the loop); returns at once."""
+        if n is None:
+            n = self.n_steps - self.launched
+        _check(LIB.dit_loop_graph_run(self.h, int(n), _stream(stream)))
+        self.launched += int(n)
+
+    def sync(self, stream=None):
+        """Wait for the replays; -> (steps completed, [(rel, skipped)] per step).
+        The FBCache's counters are updated."""
+        n = self.n_steps
+        info = (DitStepInfo * n)()
+        done = c_int(0)
+        cp = ctypes.byref(self.cache.c) if self.cache is not None else None
+        _check(LIB.dit_loop_graph_sync(self.h, cp, info, n, _stream(stream), ctypes.byref(done)))
+        return int(done.value), [(info[i].rel, bool(info[i].skipped)) for i in range(n)]
+
+    def reset(self, first_step: int = 0, stream=None) -> None:
+        """Restart at first_step with the FBCache's current counters."""
+        cp = ctypes.byref(self.cache.c) if self.cache is not None else None
+        _check(LIB.dit_loop_graph_reset(self.h, cp, int(first_step), _stream(stream)))
+        self.launched = int(first_step)
+
+    def close(self) -> None:
+        if getattr(self, "h", None) is not None and self.h.value is not None:
+            torch.cuda.synchronize()
+            _check(LIB.dit_loop_graph_destroy(self.h))
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------ launch timing

@@ -29,11 +29,13 @@
  *     pointers (e.g. torch tensor data_ptr()), 16-byte aligned, contiguous,
  *     row-major.  The library allocates nothing and keeps no state between
  *     calls; scratch comes from a caller workspace sized by
- *     dit_workspace_bytes().
+ *     dit_workspace_bytes().  (One exception: the handle of a replayed loop,
+ *     dit_loop_graph_create() to dit_loop_graph_destroy().)
  *   - stream: a hipStream_t (NULL = default stream).  Work is enqueued
  *     asynchronously; only fbcache_should_skip() and dit_denoise_step() with an
  *     enabled cache synchronise that stream, to hand the skip decision to the
- *     host.
+ *     host, and the replayed loop's create / sync / reset calls, which move its
+ *     state between host and device.
  *   - Return value: DIT_OK (0) or a negative DIT_ERR_* code.  All arguments are
  *     validated before anything is enqueued; on an error nothing has been
  *     launched (except DIT_ERR_HIP, raised by the runtime mid-way, and
@@ -338,6 +340,65 @@ DIT_API int fbcache_should_skip(const float* x_after, const float* x_before, con
 DIT_API int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt, float* latents,
                      double sigma, double sigma_next, dit_fbcache* cache, void* workspace,
                      size_t ws_bytes, void* stream, dit_step_info* info_out);
+
+/* ------------------------------------------------------------------ replayed loop
+ *
+ * The denoise loop as one captured HIP graph per step, replayed with no host
+ * synchronisation: the step index, the sigma step, the modulation row and the
+ * First-Block-Cache decision (with its warm-up / max-skips policy) live in
+ * device memory, and every kernel of blocks 1.. reads the decision on entry and
+ * returns at once on a skipped step (HIP graphs have no conditional nodes here,
+ * so the skip is a gate inside the kernels).  The per-step host sync of
+ * dit_denoise_step() and its per-launch host work go away.  Sources: recording
+ * and replaying the step's kernel launches more than halved the 8-GPU denoise
+ * time once per-GPU work had shrunk (VisualGen article on FLUX Klein, section on
+ * why the speed-ups differ); the First-Block-Cache commit notes that the cache's
+ * per-step decision breaks a whole-step compiled graph, which a decision kept on
+ * the device avoids.
+ *
+ * Results equal the eager loop's bit for bit (same kernels, same inputs).  One
+ * difference: a NaN / Inf in the cache test does not stop the loop; that step
+ * computes in full and dit_loop_graph_sync() reports DIT_ERR_NONFINITE.
+ *
+ * Memory: the caller owns the workspace (DIT_WS_STEP bytes) and the loop state
+ * (dit_loop_state_bytes()); the graph keeps their addresses and those of
+ * mod_all, txt, latents and the cache buffers, which must stay valid and must not
+ * be used by other work while replays are pending.  The handle itself (the
+ * instantiated graph) is host memory the library allocates at create and frees
+ * at destroy: the one exception to "allocates nothing". */
+typedef struct dit_loop_graph dit_loop_graph;
+
+/* Device bytes of a loop's own state for n_steps steps (state, sigma table,
+ * per-step log, the running step's modulation row).  0 for bad arguments. */
+DIT_API size_t dit_loop_state_bytes(const dit_model* m, int n_steps);
+
+/* Capture one step of m into a graph.  mod_all: device fp32 [n_steps, N_mod],
+ * row i from dit_modulation() at sigmas_host[i]; sigmas_host: n_steps + 1 host
+ * values (copied); txt, latents as for dit_denoise_step(); cache: NULL or an
+ * enabled / disabled state, whose policy fields and counters seed the device
+ * state (its anchor / cached buffers are baked in).  The device state is set to
+ * step 0 (stream is synchronised).  *out receives the handle. */
+DIT_API int dit_loop_graph_create(const dit_model* m, const float* mod_all, const void* txt,
+                                  float* latents, const double* sigmas_host, int n_steps,
+                                  const dit_fbcache* cache, void* workspace, size_t ws_bytes,
+                                  void* loop_state, size_t state_bytes, void* stream,
+                                  dit_loop_graph** out);
+/* Enqueue n replays (n steps, from the device's next step) on stream; no sync.
+ * DIT_ERR_INVALID_ARG if the loop would pass n_steps or the current device is
+ * not the one the graph was created on. */
+DIT_API int dit_loop_graph_run(dit_loop_graph* g, int n, void* stream);
+/* Synchronise stream and read back: info[i] (i < n_info) = step i's rel and skip
+ * (steps not run hold earlier contents); cache (optional, the create-time one)
+ * gets has_anchor / steps_done / skip_run; *steps_run (optional) = steps
+ * completed.  DIT_ERR_NONFINITE if a completed step met a NaN / Inf in the test. */
+DIT_API int dit_loop_graph_sync(dit_loop_graph* g, dit_fbcache* cache, dit_step_info* info,
+                                int n_info, void* stream, int* steps_run);
+/* Restart at first_step (0..n_steps) with the counters of cache (same buffers and
+ * enabled flag as at create; threshold and policy may change).  Synchronises. */
+DIT_API int dit_loop_graph_reset(dit_loop_graph* g, const dit_fbcache* cache, int first_step,
+                                 void* stream);
+/* Free the handle (NULL is a no-op).  Replays must have finished. */
+DIT_API int dit_loop_graph_destroy(dit_loop_graph* g);
 
 #ifdef __cplusplus
 }

@@ -133,6 +133,39 @@ def test_invalid_arguments_rejected_before_launch():
     assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
 
 
+def test_loop_graph_arguments_rejected_on_the_host():
+    """The replayed-loop entry points refuse bad handles and arguments before
+    touching the device."""
+    from image_generation_amd import dit
+    L = dit.LIB
+    N = None
+    assert L.dit_loop_state_bytes(N, 4) == 0
+    m = dit.DitModel()
+    m.dims = dit.dims_of(1, 8, 2, 4, 256, 2, 512)
+    m.n_double, m.n_single = 2, 1
+    assert L.dit_loop_state_bytes(ctypes.byref(m), 0) == 0
+    nb = L.dit_loop_state_bytes(ctypes.byref(m), 4)
+    # state (one 256-byte slot), 5 sigmas, 4 log entries, N_mod = (24 + 3 + 2) * 256 floats
+    assert nb >= 256 + 5 * 8 + 4 * 16 + (24 + 3 + 2) * 256 * 4
+    assert nb % 256 == 0
+    out = ctypes.c_void_p()
+    sig = (ctypes.c_double * 5)(1.0, 0.75, 0.5, 0.25, 0.0)
+    rc = L.dit_loop_graph_create(ctypes.byref(m), N, N, N, sig, 4, N, N, 0, N, 0, N,
+                                 ctypes.byref(out))
+    assert rc == dit.DIT_ERR_INVALID_ARG and out.value is None
+    fake = ctypes.c_void_p(4096)
+    rc = L.dit_loop_graph_create(ctypes.byref(m), fake, fake, fake, sig, 0, N, fake, 1 << 30, fake,
+                                 1 << 30, N, ctypes.byref(out))
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_loop_graph_create(ctypes.byref(m), fake, fake, fake, sig, 4, N, fake, 1 << 30, fake,
+                                 1 << 30, N, None)
+    assert rc == dit.DIT_ERR_INVALID_ARG
+    assert L.dit_loop_graph_run(N, 1, N) == dit.DIT_ERR_INVALID_ARG
+    assert L.dit_loop_graph_sync(N, N, N, 0, N, N) == dit.DIT_ERR_INVALID_ARG
+    assert L.dit_loop_graph_reset(N, N, 0, N) == dit.DIT_ERR_INVALID_ARG
+    assert L.dit_loop_graph_destroy(N) == dit.DIT_OK
+
+
 def test_struct_layouts_match_the_header(tmp_path):
     """Every ctypes mirror in the binding has the size and field offsets that a C
     compiler gives the header's struct (compiled here with gcc)."""
