@@ -246,6 +246,44 @@ def loop_2048_fp8(dit, DI, device, K, warmup):
             "kernels": kernel_table(by)}
 
 
+def loop_1024_mxfp4(dit, DI, device, K, warmup, bf16_steps_per_s=None):
+    """K steps of the 19 + 38 block model at 1024px with every block linear W4A4 in
+    MXFP4 (attention bf16), timed like the headline: replayed step graph, FBC test
+    at threshold 0; kernel shares from a separate instrumented eager pass."""
+    import torch
+    w = DI.WORKLOADS["flux_1024_28step"]
+    dims = w.dims
+    log(f"[bench] building {w.name} (MXFP4 W4A4 block linears)")
+    gm = build_model(dit, DI, w, device, dit.DIT_MXFP4)
+    txt = DI.device_randn((w.B, w.Lt, dims.D), DI.SEED_TEXT, 1.0, device)
+    lat0 = DI.device_randn((w.Li, dims.C_in), DI.SEED_LATENTS, 1.0, device, torch.float32)
+    sig = dit.dit_sigmas(w.steps, w.shift)
+    ws = dit.workspace(gm.model.dims, dit.DIT_WS_STEP)
+    if warmup:
+        run_loop(dit, gm, sig, txt, lat0, ws, 0.0, warmup)
+    log(f"[bench] MXFP4 timed: {K} steps")
+    secs, skipped, _ = run_replayed(dit, gm, sig, txt, lat0, 0.0, K)
+    timer = dit.KernelTimer(ALL_SITES, capacity=40 * (dims.n_double + dims.n_single) * K + 256)
+    run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
+    by = site_totals(timer.durations_ms())
+    timer.close()
+    del gm, ws
+    torch.cuda.empty_cache()
+    B, L, Li = w.B, w.L, w.Li
+    gemm_f = (gemm_flops_per_step(dims, B, w.Lt, Li, dims.C_in) - 2.0 * B * Li * dims.D * dims.C_in) * K
+    gemm_ms = sum(by.get(s_, [0, 0.0])[1] for s_ in BLOCK_GEMM_SITES)
+    gemm_tf = gemm_f / (gemm_ms * 1e-3) / 1e12
+    sps = K / secs
+    return {"workload": w.name, "image_px": w.image_px, "tokens": [w.Lt, Li], "batch": B,
+            "dtype": "MXFP4 W4A4 block linears, bf16 attention", "steps": K, "warmup": warmup,
+            "steps_per_s": round(sps, 4), "ms_per_step": round(1e3 * secs / K, 2),
+            "vs_bf16": round(sps / bf16_steps_per_s, 3) if bf16_steps_per_s else None,
+            "block_gemm_tflops": round(gemm_tf, 1),
+            "block_gemm_frac_fp4_peak": round(gemm_tf / PEAK_FP4_TFLOPS, 4),
+            "quant_ms_per_step": round(by.get("quant", [0, 0.0])[1] / K, 3),
+            "kernels": kernel_table(by)}
+
+
 def run_loop(dit, gm, sig, txt, lat0, ws, threshold, K, timer=None):
     """K Euler steps from a fresh cache; returns (seconds, skipped, rels)."""
     import torch
@@ -361,6 +399,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fbcache-run", action="store_true")
     ap.add_argument("--no-2048", action="store_true", help="skip the 2048px block and fp8 loop")
+    ap.add_argument("--no-mxfp4-loop", action="store_true",
+                    help="skip the 1024px loop with MXFP4 block linears")
     ap.add_argument("--no-tiny", action="store_true",
                     help="skip the tiny-model loop latency (eager vs replayed step graph)")
     ap.add_argument("--fp8-steps", type=int, default=3)
@@ -504,6 +544,9 @@ def main():
                                      for r in rels_c]}
     del gm, ws
     torch.cuda.empty_cache()
+    if not args.no_mxfp4_loop:
+        out["loop_1024px_mxfp4"] = loop_1024_mxfp4(dit, DI, device, K, 1, K / secs)
+        torch.cuda.empty_cache()
     if not args.no_tiny:
         log("[bench] tiny fp32 loop latency, eager vs replayed")
         out["tiny_loop_latency"] = tiny_loop_latency(dit, DI, device)

@@ -89,7 +89,7 @@ int make_dims(const dit_dims* in, Dims* o) {
 }
 
 int check_block_dims(const Dims& dm, int dtype) {
-  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32)
+  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32 && dtype != DIT_MXFP4)
     return fail(DIT_ERR_UNSUPPORTED, "block dtype %d", dtype);
   if (dm.D % 256 || dm.D > 3072)
     return fail(DIT_ERR_UNSUPPORTED, "hidden size %d (needs a multiple of 256, <= 3072)", dm.D);
@@ -106,6 +106,8 @@ int check_block_dims(const Dims& dm, int dtype) {
     if (dm.F % 128) return fail(DIT_ERR_UNSUPPORTED, "fp8: MLP size %d (multiple of 128)", dm.F);
     if (dm.L % 16) return fail(DIT_ERR_UNSUPPORTED, "fp8: joint length %d (multiple of 16)", dm.L);
   }
+  if (dtype == DIT_MXFP4 && dm.F % 256)   // MX K slabs are 256 deep
+    return fail(DIT_ERR_UNSUPPORTED, "mxfp4: MLP size %d (multiple of 256)", dm.F);
   return DIT_OK;
 }
 
@@ -138,6 +140,12 @@ struct BlockWS {
   float *su, *s_att, *s_hid;
   float* s_qkv;          // [3, B*H]: q, k, v scales per (b, h)
   unsigned int* amax;    // [3, B*H]: largest stored |q|, |k|, |v| per (b, h) (fp32 bits)
+  // MXFP4 blocks: one linear input at a time as E2M1 codes [B*L, K/2] (over cat8)
+  // and E8M0 scales [K/256][mx_pad][8]
+  uint8_t* a4;
+  uint8_t* a4s;
+  int mx_pad;            // scale rows: B*L rounded up to 256, plus 256 so a GEMM group
+                         // starting inside the array reads whole 256-row tiles
   // fp32 blocks (overlaying the buffers above): LN out, Q, K, V^T, attention | MLP
   float *u32, *q32, *k32, *vt32, *cat32;
 };
@@ -164,6 +172,9 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.s_hid = c.take<float>(rows);
   w.s_qkv = c.take<float>(3 * bh);
   w.amax = c.take<unsigned int>(3 * bh);
+  w.a4 = (uint8_t*)w.cat8;
+  w.mx_pad = (int)((rows + 255) / 256 * 256 + 256);
+  w.a4s = c.take<uint8_t>(((size_t)(dm.D + dm.F) / 256 + 1) * w.mx_pad * 8);
   w.u32 = c32.take<float>(n);
   w.q32 = c32.take<float>(n);
   w.k32 = c32.take<float>(n);
@@ -248,29 +259,32 @@ size_t ws_size(const Dims& dm, int purpose, int n) {
   return (c.off + 255) & ~(size_t)255;
 }
 
-// fp8: the layer must carry its per-channel weight scales
-int check_linear(const dit_linear& l, const char* name, bool fp8 = false) {
+// fp8: the layer must carry its per-channel weight scales; MXFP4 its block scales
+int check_linear(const dit_linear& l, const char* name, int dtype = DIT_BF16) {
   if (!l.w || !l.b) return fail(DIT_ERR_INVALID_ARG, "%s: NULL weight or bias", name);
   if (!aligned16(l.w) || !aligned16(l.b))
     return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", name);
-  if (fp8 && (!l.w_scale || !aligned16(l.w_scale)))
+  if (dtype == DIT_FP8 && (!l.w_scale || !aligned16(l.w_scale)))
     return fail(DIT_ERR_INVALID_ARG, "%s: fp8 layer needs a 16-byte aligned w_scale", name);
+  if (dtype == DIT_MXFP4 && (!l.w_mx || !aligned16(l.w_mx)))
+    return fail(DIT_ERR_INVALID_ARG, "%s: mxfp4 layer needs 16-byte aligned w_mx scales", name);
   return DIT_OK;
 }
 
-int check_block(const dit_block* blk, bool fp8) {
+int check_block(const dit_block* blk, int dtype) {
   if (!blk) return fail(DIT_ERR_INVALID_ARG, "block is NULL");
   int rc;
   if (blk->kind == DIT_BLOCK_DOUBLE) {
     for (int s = 0; s < 2; ++s) {
-      if ((rc = check_linear(blk->qkv[s], "qkv", fp8)) ||
-          (rc = check_linear(blk->proj[s], "proj", fp8)) ||
-          (rc = check_linear(blk->mlp1[s], "mlp1", fp8)) ||
-          (rc = check_linear(blk->mlp2[s], "mlp2", fp8)))
+      if ((rc = check_linear(blk->qkv[s], "qkv", dtype)) ||
+          (rc = check_linear(blk->proj[s], "proj", dtype)) ||
+          (rc = check_linear(blk->mlp1[s], "mlp1", dtype)) ||
+          (rc = check_linear(blk->mlp2[s], "mlp2", dtype)))
         return rc;
     }
   } else if (blk->kind == DIT_BLOCK_SINGLE) {
-    if ((rc = check_linear(blk->lin1, "lin1", fp8)) || (rc = check_linear(blk->lin2, "lin2", fp8)))
+    if ((rc = check_linear(blk->lin1, "lin1", dtype)) ||
+        (rc = check_linear(blk->lin2, "lin2", dtype)))
       return rc;
   } else {
     return fail(DIT_ERR_INVALID_ARG, "unknown block kind %d", blk->kind);
@@ -444,6 +458,86 @@ hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float
 hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
                      int bs, const float* rope, const BlockWS& w, hipStream_t st);
 
+// MXFP4 problem: activation codes [M, K/2] and their E8M0 scales, both starting at
+// row r0 of the quantised activation (scale slab stride: pad rows); weight codes
+// l.w [N, K/2] with block scales l.w_mx
+GemmProblem gp4(const uint8_t* a4, const uint8_t* a4s, int r0, int pad, const dit_linear& l, int K,
+                int M, int N) {
+  GemmProblem g = gp(nullptr, K, l, K, M, N);
+  g.W = nullptr;
+  g.A4 = a4 + (size_t)r0 * (K / 2);
+  g.W4 = (const uint8_t*)l.w;
+  g.xa = a4s + (size_t)r0 * 8;
+  g.xw = l.w_mx;
+  g.pad_m = pad;
+  g.pad_n = (N + 255) / 256 * 256;
+  return g;
+}
+
+// MXFP4 (W4A4) block: the bf16 block's sequence with every linear's bf16 input
+// quantised to MXFP4 just before its GEMM (32-value blocks along K, E8M0 scales);
+// attention stays bf16
+hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float* mod, int bs,
+                     const float* rope, const BlockWS& w, hipStream_t st) {
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
+  const int DF = D + F;
+  const int P = w.mx_pad;
+  const QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  const float scale = 1.0f / sqrtf((float)dm.d);
+  hipError_t e;
+  if (blk.kind == DIT_BLOCK_DOUBLE) {
+    const RowMap sm{B, Lt, Li, L, 1, 0};
+    RowMap st_txt = sm;
+    st_txt.base = B * Li;
+    const RowMap maps[2] = {sm, st_txt};
+    const int ng = (B * Lt > 0) ? 2 : 1;
+    const float* mi = mod;
+    const float* mt = mod + 6 * (size_t)D;
+    const int ti = B * Li;   // first text row of the stream-major row space
+
+    if ((e = ln_modulate<float>(x, w.u, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs, st)))
+      return e;
+    if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
+    GemmProblem g[2] = {gp4(w.a4, w.a4s, 0, P, blk.qkv[0], D, B * Li, 3 * D),
+                        gp4(w.a4, w.a4s, ti, P, blk.qkv[1], D, B * Lt, 3 * D)};
+    if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
+    if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, sm, B, dm.H, L, dm.d, scale, st))) return e;
+    if ((e = quant_mxfp4<bf16_t>(w.cat, DF, B * L, D, w.a4, w.a4s, P, st))) return e;
+    g[0] = gp4(w.a4, w.a4s, 0, P, blk.proj[0], D, B * Li, D);
+    g[1] = gp4(w.a4, w.a4s, ti, P, blk.proj[1], D, B * Lt, D);
+    const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
+    if ((e = gemm_gated_residual<float>(g, ng, x, D, gate1, bs, maps, st))) return e;
+    if ((e = ln_modulate<float>(x, w.u, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D, mt + 3 * D,
+                                mt + 4 * D, bs, st)))
+      return e;
+    if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
+    g[0] = gp4(w.a4, w.a4s, 0, P, blk.mlp1[0], D, B * Li, F);
+    g[1] = gp4(w.a4, w.a4s, ti, P, blk.mlp1[1], D, B * Lt, F);
+    bf16_t* hid[2] = {w.cat + D, w.cat + (size_t)ti * DF + D};
+    const int ldh[2] = {DF, DF};
+    if ((e = gemm_gelu_bf16(g, ng, hid, ldh, st))) return e;
+    if ((e = quant_mxfp4<bf16_t>(w.cat + D, DF, B * L, F, w.a4, w.a4s, P, st))) return e;
+    g[0] = gp4(w.a4, w.a4s, 0, P, blk.mlp2[0], F, B * Li, D);
+    g[1] = gp4(w.a4, w.a4s, ti, P, blk.mlp2[1], F, B * Lt, D);
+    const float* gate2[2] = {mi + 5 * D, mt + 5 * D};
+    return gemm_gated_residual<float>(g, ng, x, D, gate2, bs, maps, st);
+  }
+  // single-stream block, joint row order
+  const RowMap jm{B, Lt, Li, L, 0, 0};
+  if ((e = ln_modulate<float>(x, w.u, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st)))
+    return e;
+  if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
+  const GemmProblem g1 = gp4(w.a4, w.a4s, 0, P, blk.lin1, D, B * L, 3 * D + F);
+  if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
+  if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, jm, B, dm.H, L, dm.d, scale, st))) return e;
+  // linear2 takes [attention | GELU] as one row
+  if ((e = quant_mxfp4<bf16_t>(w.cat, DF, B * L, DF, w.a4, w.a4s, P, st))) return e;
+  const GemmProblem g2 = gp4(w.a4, w.a4s, 0, P, blk.lin2, DF, B * L, D);
+  const float* gate[1] = {mod + 2 * D};
+  return gemm_gated_residual<float>(&g2, 1, x, D, gate, bs, &jm, st);
+}
+
+
 // ---- one block, already validated
 template <class XT>
 hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* mod, int bs,
@@ -499,6 +593,7 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
 hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
                      int bs, const float* rope, const BlockWS& w, hipStream_t st) {
   if (dtype == DIT_FP8) return block_fp8(dm, blk, x, mod, bs, rope, w, st);
+  if (dtype == DIT_MXFP4) return block_mx4(dm, blk, x, mod, bs, rope, w, st);
   if (dtype == DIT_F32) return block_f32(dm, blk, x, mod, bs, rope, w, st);
   return block_impl<float>(dm, blk, x, mod, bs, rope, w, st);
 }
@@ -513,7 +608,7 @@ int check_model(const dit_model* m, Dims* dm, const char* fn) {
   if (m->n_double < 1 || m->n_single < 0 || !m->blocks)
     return fail(DIT_ERR_INVALID_ARG, "%s: needs >= 1 double block", fn);
   for (int j = 0; j < m->n_double + m->n_single; ++j) {
-    if ((rc = check_block(&m->blocks[j], m->dtype == DIT_FP8))) return rc;
+    if ((rc = check_block(&m->blocks[j], m->dtype))) return rc;
     const int want = j < m->n_double ? DIT_BLOCK_DOUBLE : DIT_BLOCK_SINGLE;
     if (m->blocks[j].kind != want)
       return fail(DIT_ERR_INVALID_ARG, "%s: block %d has the wrong kind", fn, j);
@@ -860,7 +955,7 @@ int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, voi
   int rc;
   if ((rc = make_dims(dims, &dm))) return rc;
   if ((rc = check_block_dims(dm, dtype))) return rc;
-  if ((rc = check_block(blk, dtype == DIT_FP8))) return rc;
+  if ((rc = check_block(blk, dtype))) return rc;
   if (!x || !mod || !rope || !workspace)
     return fail(DIT_ERR_INVALID_ARG, "dit_block_forward: NULL pointer");
   if (!aligned16(x) || !aligned16(mod) || !aligned16(rope) || !aligned16(workspace))
@@ -911,7 +1006,8 @@ int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* 
     return fail(DIT_ERR_WORKSPACE, "dit_modulation: workspace %zu < %zu bytes", ws_bytes, need);
   const long long nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm.D;
   if (nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: too many vectors");
-  if (m->dtype != DIT_BF16 && m->dtype != DIT_FP8 && m->dtype != DIT_F32)
+  if (m->dtype != DIT_BF16 && m->dtype != DIT_FP8 && m->dtype != DIT_F32 &&
+      m->dtype != DIT_MXFP4)
     return fail(DIT_ERR_INVALID_ARG, "dit_modulation: model dtype %d", m->dtype);
   if ((rc = check_device())) return rc;
   hipStream_t st = (hipStream_t)stream;

@@ -1009,6 +1009,13 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
                 (long long)gp[i].N * gp[i].ldw * es < (1LL << 31);
   }
   if (gp[0].A8 && !offsets32) return hipErrorInvalidValue;
+  if (gp[0].A4) {   // MXFP4 operands: the direct-to-LDS kernel, byte offsets in 32 bits
+    for (int i = 0; i < ng; ++i)
+      if ((long long)gp[i].M * (gp[i].lda / 2) >= (1LL << 31) ||
+          (long long)gp[i].N * (gp[i].ldw / 2) >= (1LL << 31) || gp[i].K % 256)
+        return hipErrorInvalidValue;
+    return launch_cfg<256, 256, 2, 4, 4, 2, 128>(gp, ep, ng, st);
+  }
 #ifndef GEMM_NS
 #define GEMM_NS 2
 #define GEMM_SLAB 128

@@ -244,7 +244,9 @@ template <class T>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const T* __restrict__ src, int lds,
                                                           int rows, int width, int pad_rows,
                                                           uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales) {
+                                                          uint8_t* __restrict__ scales,
+                                                          const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
   const int nb = width >> 5;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)pad_rows * nb) return;
@@ -288,7 +290,7 @@ hipError_t quant_mxfp4(const T* src, int lds, int rows, int width, uint8_t* code
   KTimerScope timer(KS_QUANT, st);
   const long long n = (long long)pad_rows * (width >> 5);
   hipLaunchKernelGGL(quant_mxfp4_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     src, lds, rows, width, pad_rows, codes, scales);
+                     src, lds, rows, width, pad_rows, codes, scales, launch_gate());
   return hipGetLastError();
 }
 template hipError_t quant_mxfp4<bf16_t>(const bf16_t*, int, int, int, uint8_t*, uint8_t*, int,

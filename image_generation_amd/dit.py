@@ -24,7 +24,7 @@ DIT_ERR_WORKSPACE = -3
 DIT_ERR_HIP = -4
 DIT_ERR_NONFINITE = -5
 
-DIT_F32, DIT_BF16, DIT_FP8 = 0, 1, 2
+DIT_F32, DIT_BF16, DIT_FP8, DIT_MXFP4 = 0, 1, 2, 3
 DIT_BLOCK_DOUBLE, DIT_BLOCK_SINGLE = 0, 1
 DIT_WS_ATTENTION, DIT_WS_BLOCK, DIT_WS_STEP, DIT_WS_MODULATION, DIT_WS_FBCACHE = range(5)
 
@@ -35,7 +35,7 @@ class DitDims(Structure):
 
 
 class DitLinear(Structure):
-    _fields_ = [("w", c_void_p), ("b", c_void_p), ("w_scale", c_void_p)]
+    _fields_ = [("w", c_void_p), ("b", c_void_p), ("w_scale", c_void_p), ("w_mx", c_void_p)]
 
 
 class DitBlock(Structure):
@@ -300,21 +300,29 @@ def dit_linear_forward(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor,
     return out
 
 
-def _lin(w: torch.Tensor, b: torch.Tensor, w_scale: Optional[torch.Tensor] = None) -> DitLinear:
-    """bf16 layer (w_scale None) or e4m3 layer (w uint8 codes, w_scale fp32 [out])."""
+def _lin(w: torch.Tensor, b: torch.Tensor, w_scale: Optional[torch.Tensor] = None,
+         w_mx: Optional[torch.Tensor] = None) -> DitLinear:
+    """bf16 layer (w_scale None), e4m3 layer (w uint8 codes, w_scale fp32 [out]) or
+    MXFP4 layer (w uint8 E2M1 codes [out, in / 2], w_mx its E8M0 block scales)."""
     if b.dtype != torch.float32 or not (w.is_cuda and b.is_cuda):
         raise ValueError("linear: bias fp32, tensors on the GPU")
+    if w_mx is not None:
+        N, K2 = w.shape
+        if w.dtype != torch.uint8 or w_mx.dtype != torch.uint8 or \
+                tuple(w_mx.shape) != (2 * K2 // 256, LIB.dit_mx_rows(N), 8):
+            raise ValueError("linear: mxfp4 layer needs E2M1 codes and their block scales")
+        return DitLinear(_ptr(w), _ptr(b), None, _ptr(w_mx))
     if w_scale is None:
         if w.dtype not in (torch.bfloat16, torch.float32):
             raise ValueError("linear: bf16 (or fp32) weight expected")
     elif w.dtype not in (torch.uint8, torch.float8_e4m3fn) or w_scale.dtype != torch.float32 \
             or tuple(w_scale.shape) != (w.shape[0],):
         raise ValueError("linear: fp8 layer needs e4m3 codes and an fp32 scale per output")
-    return DitLinear(_ptr(w), _ptr(b), _ptr(w_scale))
+    return DitLinear(_ptr(w), _ptr(b), _ptr(w_scale), None)
 
 
 def _lin_of(p: dict, name: str) -> DitLinear:
-    return _lin(p[name + ".w"], p[name + ".b"], p.get(name + ".w_scale"))
+    return _lin(p[name + ".w"], p[name + ".b"], p.get(name + ".w_scale"), p.get(name + ".w_mx"))
 
 
 def make_double_block(p: dict, prefix: str = "") -> DitBlock:
@@ -348,6 +356,19 @@ def quantize_block_params(p: dict, prefix: str = "", stream=None) -> dict:
         codes, scale = dit_quantize_rows(p[name], stream)
         out[name] = codes
         out[name + "_scale"] = scale
+    return out
+
+
+def quantize_block_params_mx(p: dict, prefix: str = "", stream=None) -> dict:
+    """Copy of p with every block linear under prefix replaced by its MXFP4 (E2M1)
+    codes and E8M0 block scales '<name>.w_mx' (dit_quantize_mxfp4 on the GPU)."""
+    out = dict(p)
+    for name in list(p):
+        if not name.startswith(prefix) or not name.endswith(".w") or ".mod." in name:
+            continue
+        codes, scales = dit_quantize_mxfp4(p[name], stream)
+        out[name] = codes
+        out[name + "_mx"] = scales
     return out
 
 
@@ -429,6 +450,15 @@ class GPUModel:
                        [f"single{j}." for j in range(self.n_single)]:
                 q.update(quantize_block_params({n: t for n, t in self.t.items()
                                                 if n.startswith(pre)}, pre))
+            for n, t in q.items():
+                self.t[n] = t
+        elif dtype == DIT_MXFP4:
+            # block linears W4A4 in MXFP4; the rest stays bf16
+            q = {}
+            for pre in [f"double{j}." for j in range(self.n_double)] + \
+                       [f"single{j}." for j in range(self.n_single)]:
+                q.update(quantize_block_params_mx({n: t for n, t in self.t.items()
+                                                   if n.startswith(pre)}, pre))
             for n, t in q.items():
                 self.t[n] = t
         elif dtype not in (DIT_BF16, DIT_F32):

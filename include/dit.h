@@ -71,6 +71,7 @@ extern "C" {
 #define DIT_F32 0
 #define DIT_BF16 1
 #define DIT_FP8 2   /* OCP e4m3 ("e4m3fn") */
+#define DIT_MXFP4 3 /* OCP MXFP4: E2M1 elements, one E8M0 scale per 32 (blocks only) */
 
 #define DIT_BLOCK_DOUBLE 0
 #define DIT_BLOCK_SINGLE 1
@@ -98,11 +99,15 @@ typedef struct dit_dims {
  *   fp8 layers (DIT_FP8 blocks): w OCP e4m3 and w_scale fp32 [out], the
  *   per-output-channel scale (weight = code * w_scale[n]), as produced by
  *   dit_quantize_rows() on the bf16 weight.
- *   fp32 layers (DIT_F32 models and blocks): w fp32, w_scale NULL. */
+ *   fp32 layers (DIT_F32 models and blocks): w fp32, w_scale NULL.
+ *   MXFP4 layers (DIT_MXFP4 blocks): w E2M1 codes [out, in / 2] and w_mx their
+ *   E8M0 block scales [in / 256][dit_mx_rows(out)][8], both as produced by
+ *   dit_quantize_mxfp4() on the bf16 weight; in a multiple of 256. */
 typedef struct dit_linear {
   const void* w;
   const float* b;
   const float* w_scale;
+  const unsigned char* w_mx;
 } dit_linear;
 
 /* A transformer block.
@@ -136,7 +141,9 @@ typedef struct dit_model {
   int dtype;             /* DIT_BF16; DIT_FP8: the blocks' linears and attention run
                             in e4m3 with dynamic per-token activation scales, the
                             modulation, embedders, timestep MLP and velocity head stay
-                            bf16; DIT_F32: every weight and activation fp32 (head dim
+                            bf16; DIT_MXFP4: the blocks' linears W4A4 in MXFP4 (see
+                            dit_block_forward), the rest as for DIT_FP8;
+                            DIT_F32: every weight and activation fp32 (head dim
                             32 or 64; reference precision for small models) */
 } dit_model;
 
@@ -297,8 +304,10 @@ DIT_API int dit_linear_mxfp4(const void* x_codes, const unsigned char* x_scales,
  *        shift1, scale1, gate1, shift2, scale2, gate2, then text), single 3.
  *   rope: device table from dit_rope_table() for these dims.
  *   dtype: DIT_BF16; DIT_FP8 (e4m3 linears with w_scale set, per-token
- *   activation scales, e4m3 attention with per-(b, h) scales); DIT_F32 (fp32
- *   weights, head dim 32 or 64).
+ *   activation scales, e4m3 attention with per-(b, h) scales); DIT_MXFP4 (W4A4
+ *   linears with w_mx set: each linear's bf16 input is quantised to MXFP4 on the
+ *   fly, 32-value blocks along the input dimension; attention in bf16; D and F
+ *   multiples of 256); DIT_F32 (fp32 weights, head dim 32 or 64).
  *   workspace >= DIT_WS_BLOCK bytes. */
 DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,

@@ -305,13 +305,16 @@ def _held(x, fp8, rounding=round_bf16):
     return rounding(x) if fp8 else x
 
 
-def _lin(x, P, name, fp8):
+def _lin(x, P, name, fp8, mx4=False):
+    if mx4:
+        # MXFP4 blocks (R38): the input is stored bf16 before it is quantised
+        return linear_mxfp4(round_bf16(x), P[name + ".w"], P[name + ".b"])
     if fp8:
         return linear_fp8(x, P[name + ".w"], P[name + ".b"])
     return linear(x, P[name + ".w"], P[name + ".b"])
 
 
-def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
+def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False):
     """Double-stream block (R1, R2, R4, R8): separate weights per stream, joint attention.
 
     x_txt [B, Lt, D], x_img [B, Li, D]; mod_* [B or 1, 6, D] in the order
@@ -324,7 +327,7 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
     qkv = {}
     for s, (x, m) in streams.items():
         u = modulate(x, m[:, 0:1], m[:, 1:2])
-        qkv[s] = _lin(u, P, f"{s}.qkv", fp8)
+        qkv[s] = _lin(u, P, f"{s}.qkv", fp8, mx4)
     D = x_img.shape[-1]
     q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
     k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
@@ -335,15 +338,15 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False):
     out = {}
     for s, (x, m) in streams.items():
         a_s = a[:, :Lt] if s == "txt" else a[:, Lt:]
-        x = x + m[:, 2:3] * _lin(a_s, P, f"{s}.proj", fp8)
+        x = x + m[:, 2:3] * _lin(a_s, P, f"{s}.proj", fp8, mx4)
         u = modulate(x, m[:, 3:4], m[:, 4:5])
-        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8)), fp8)
-        x = x + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
+        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8, mx4)), fp8)
+        x = x + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8, mx4)
         out[s] = x
     return out["txt"], out["img"]
 
 
-def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False):
+def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False, mx4=False):
     """The double block's output for the joint token rows ``rows`` only (text rows
     first, 0 <= row < Lt + Li) -> [B, len(rows), D].
 
@@ -360,7 +363,7 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
     qkv = {}
     for s, (x, m) in streams.items():
         u = modulate(x, m[:, 0:1], m[:, 1:2])
-        qkv[s] = _lin(u, P, f"{s}.qkv", fp8)
+        qkv[s] = _lin(u, P, f"{s}.qkv", fp8, mx4)
     q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
     k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
@@ -380,14 +383,14 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
             continue
         tok = rows[sel] if s == "txt" else rows[sel] - Lt
         xs = x[:, tok]
-        xs = xs + m[:, 2:3] * _lin(a[:, sel], P, f"{s}.proj", fp8)
+        xs = xs + m[:, 2:3] * _lin(a[:, sel], P, f"{s}.proj", fp8, mx4)
         u = modulate(xs, m[:, 3:4], m[:, 4:5])
-        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8)), fp8)
-        out[:, sel] = xs + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8)
+        hdn = _held(gelu_tanh(_lin(u, P, f"{s}.mlp1", fp8, mx4)), fp8)
+        out[:, sel] = xs + m[:, 5:6] * _lin(hdn, P, f"{s}.mlp2", fp8, mx4)
     return out
 
 
-def single_block(x, mod, P, ang, H, fp8=False):
+def single_block(x, mod, P, ang, H, fp8=False, mx4=False):
     """Single-stream block (R10): one modulated LN feeding attention and MLP in parallel.
 
     x [B, L, D]; mod [B or 1, 3, D] = shift, scale, gate; P keys "lin1.w" ...
@@ -395,13 +398,13 @@ def single_block(x, mod, P, ang, H, fp8=False):
     attn_fn = attention_fp8 if fp8 else attention
     D = x.shape[-1]
     u = modulate(x, mod[:, 0:1], mod[:, 1:2])
-    h = _lin(u, P, "lin1", fp8)
+    h = _lin(u, P, "lin1", fp8, mx4)
     q = _held(apply_rope(_heads(h[..., :D], H), ang), fp8)
     k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), fp8)
     v = _held(_heads(h[..., 2 * D:3 * D], H), fp8, round_fp16)
     a = _merge(attn_fn(q, k, v))
     cat = _held(np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1), fp8)
-    return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8)
+    return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8, mx4)
 
 
 def final_layer(x_img, shift, scale, w, b):
@@ -477,7 +480,8 @@ def _block_params(P, prefix):
 
 
 def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = None,
-                 force_skip: Optional[bool] = None, fp8: bool = False):
+                 force_skip: Optional[bool] = None, fp8: bool = False,
+                 mx4: bool = False):
     """One flow-matching Euler step of the whole model (steps 1-11 of the oracle definition).
 
     P: parameters keyed as in ``dit_inputs.param_specs`` (fp64 arrays);
@@ -503,7 +507,7 @@ def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = N
         bp = _block_params(P, f"double{j}")
         m_img = mods(f"double{j}.img", 6)
         m_txt = mods(f"double{j}.txt", 6)
-        x_txt, x_img = double_block(x_txt, x_img, m_img, m_txt, bp, ang, H, fp8)
+        x_txt, x_img = double_block(x_txt, x_img, m_img, m_txt, bp, ang, H, fp8, mx4)
         if j == 0 and cache is not None and cache.enabled:
             r = x_img - before
             rel = fbcache_rel(r, cache.anchor) if cache.has_anchor else math.inf
@@ -524,7 +528,7 @@ def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = N
             x = np.concatenate([x_txt, x_img], axis=1)
             for j in range(dims.n_single):
                 x = single_block(x, mods(f"single{j}", 3), _block_params(P, f"single{j}"),
-                                 ang, H, fp8)
+                                 ang, H, fp8, mx4)
             x_img = x[:, w.Lt:]
         if cache is not None and cache.enabled:
             cache.cached = x_img - after0

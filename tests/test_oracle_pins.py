@@ -309,17 +309,65 @@ def test_double_block_stream_isolation():
     assert np.max(np.abs(oi - xi)) > 1e-3
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_double_block_rows_equals_full_block(fp8):
+@pytest.mark.parametrize("fp8,mx4", [(False, False), (True, False), (False, True)])
+def test_double_block_rows_equals_full_block(fp8, mx4):
     # the row-sampled block is the full block restricted to the sampled rows (text,
     # image and boundary rows, out of order); fp8 included (its scales span heads)
+    # and MXFP4 (its blocks lie along each row)
     rng = np.random.default_rng(15)
     P, xt, xi, mi, mt, ang, H = _tiny_double(rng, D=64, H=2, F=256, Lt=5, gh=4, gw=4, B=2)
-    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H, fp8=fp8)
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H, fp8=fp8, mx4=mx4)
     full = np.concatenate([ot, oi], axis=1)
     rows = np.array([20, 0, 4, 5, 13, 2])
-    got = O.double_block_rows(xt, xi, mi, mt, P, ang, H, rows, fp8=fp8)
+    got = O.double_block_rows(xt, xi, mi, mt, P, ang, H, rows, fp8=fp8, mx4=mx4)
     np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
+
+
+def test_mx4_blocks_route_every_linear_through_mxfp4(monkeypatch):
+    # every linear of an MXFP4 block (8 in a double block, 2 in a single one) goes
+    # through the W4A4 linear, on an input already rounded to bf16, with the
+    # expected (K, N); no full-precision or fp8 linear is left in the block
+    import oracle.dit_oracle as DO
+    calls = []
+    real = DO.linear_mxfp4
+
+    def rec(x, w, b):
+        assert np.array_equal(O.round_bf16(x), x), "MXFP4 input not bf16-held"
+        calls.append((w.shape[1], w.shape[0]))
+        return real(x, w, b)
+
+    def forbidden(*a, **k):
+        raise AssertionError("a block linear bypassed MXFP4")
+
+    monkeypatch.setattr(DO, "linear_mxfp4", rec)
+    monkeypatch.setattr(DO, "linear", forbidden)
+    monkeypatch.setattr(DO, "linear_fp8", forbidden)
+    rng = np.random.default_rng(17)
+    D, F = 64, 256
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng, D=D, H=2, F=F)
+    DO.double_block(xt, xi, mi, mt, P, ang, H, mx4=True)
+    assert sorted(calls) == sorted([(D, 3 * D), (D, D), (D, F), (F, D)] * 2)
+    calls.clear()
+    Ps = {"lin1.w": rng.standard_normal((3 * D + F, D)) * 0.05, "lin1.b": np.zeros(3 * D + F),
+          "lin2.w": rng.standard_normal((D, D + F)) * 0.05, "lin2.b": np.zeros(D)}
+    x = np.concatenate([xt, xi], axis=1)
+    DO.single_block(x, mi[:, :3], Ps, ang, H, mx4=True)
+    assert calls == [(D, 3 * D + F), (D + F, D)]
+
+
+def test_mx4_double_block_zero_weights_keeps_biases_exact():
+    # all weights zero: every MXFP4 linear returns its bias exactly (zero blocks
+    # quantise to zero), so the block adds gate1 * b_proj + gate2 * b_mlp2
+    rng = np.random.default_rng(18)
+    P, xt, xi, mi, mt, ang, H = _tiny_double(rng)
+    for k in P:
+        if k.endswith(".w"):
+            P[k] = np.zeros_like(P[k])
+    ot, oi = O.double_block(xt, xi, mi, mt, P, ang, H, mx4=True)
+    for got, x, m, s in ((oi, xi, mi, "img"), (ot, xt, mt, "txt")):
+        ref = x + m[:, 2:3] * P[f"{s}.proj.b"]
+        ref = ref + m[:, 5:6] * P[f"{s}.mlp2.b"]
+        np.testing.assert_array_equal(got, ref)
 
 
 def test_double_block_brute_force_small():
