@@ -51,11 +51,11 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1155664 * 1024 + 230383 * 1024,
+    "gemm_lin1": {"bytes": 1134784 * 1024 + 228601 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "f4dd20cfbc8cfe03ba6a3634bf6db2dca2da625b"},
+                  "sha1": "84b7d0efb79d6263fdebeba04609eacd733b0b53"},
     "attention": {"bytes": 101508 * 1024 + 27693 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",

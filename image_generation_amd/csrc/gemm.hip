@@ -417,12 +417,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
   }
 }
 
-// Variant fed by gfx950's direct global->LDS loads (global_load_lds_dwordx4): each
-// wave instruction writes 64 lanes x 16 B = 1 KB of LDS contiguously, so a
-// permuted (or padded) row layout is built by giving every lane the global chunk
-// that belongs at its LDS slot: 8 lanes still cover one 128-byte row segment.
-// (Padded rows re-read the row's last chunk into the pad.)  No staging
-// registers, no LDS store instructions.
+// Tiled kernel whose LDS image is written 1 KB per wave instruction: 64 lanes x
+// 16 B contiguously, so a permuted (or padded) row layout is built by giving every
+// lane the global chunk that belongs at its LDS slot: 8 lanes still cover one
+// 128-byte row segment.  (Padded rows re-read the row's last chunk into the pad.)
+// e4m3 and MXFP4 operands (and bf16 with more than two stages) use gfx950's direct
+// global->LDS loads (global_load_lds_dwordx4), with no staging registers; bf16 with
+// two stages loads the same chunks into registers (global_load_dwordx4) and writes
+// them with ds_write_b128, which lets the fragment reads run ahead of the MFMAs
+// with exact waits (measured 3-6% faster on the block shapes).
 //
 // Pipeline: NS stages, each holding a K slab of SLAB bytes per row for the A and
 // the W tile (SLAB / 2 bf16 or SLAB e4m3 values), so NS - 1 slabs are in flight
@@ -555,6 +558,9 @@ template <int BM, int BN, int WM, int WN, int FMT, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
   if (gate_closed(p.gate)) return;
   constexpr bool F8 = FMT == 1, F4 = FMT == 2;
+  // bf16 with two stages: global loads staged through registers and written to LDS
+  // by the waves (see below); e4m3 and MXFP4: direct-to-LDS loads
+  constexpr bool VS = FMT == 0 && NS == 2;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
@@ -699,6 +705,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
           _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bw[cb][j], acc[i][j], 0, 0, 0); \
     }                                                                                    \
+    /* keep the fragment reads of step kk + 1 interleaved with step kk's MFMAs */       \
+    if constexpr (VS) {                                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                          \
+      _Pragma("unroll") for (int kk = 0; kk < KS - 1; ++kk) {                           \
+        _Pragma("unroll") for (int r = 0; r < TM + TN; ++r) {                           \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            \
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            \
+        }                                                                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);             \
+      }                                                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);                          \
+    }                                                                                    \
   }
   // fp8: 64-deep K steps, 32 bytes of K per lane (two 16-byte reads)
 #define GEMM_COMPUTE_F8(stg)                                                             \
@@ -756,6 +774,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     GEMM_MX4_STEP(0) GEMM_MX4_STEP(1) GEMM_MX4_STEP(2) GEMM_MX4_STEP(3)                  \
   }
 
+  if constexpr (VS) {
+    // Register-staged pipeline: slab kt + 2 is loaded into registers while slab kt
+    // is computed, and written to LDS at the start of the next iteration.  (While
+    // a direct-to-LDS load is in flight the compiler can only wait for all LDS
+    // reads at once, lgkmcnt(0), so fragment reads could not run ahead of the
+    // MFMAs; with ordinary loads the waits are exact.)
+    i32x4 sreg[IPW];
+#define GEMM_LOADR(kt)                                                                    \
+  {                                                                                      \
+    const int ko_ = (kt) * SLAB;                                                         \
+    _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                   \
+      const char* b_ = ((wave * IPW + j) * 1024 >= AB) ? wbase : abase;                  \
+      sreg[j] = *(const i32x4*)(b_ + voff[j] + ko_);                                     \
+    }                                                                                    \
+  }
+#define GEMM_STORER(stg)                                                                  \
+  {                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < IPW; ++j)                                     \
+        *(i32x4*)((stg) + (wave * IPW + j) * 1024 + lane * 16) = sreg[j];                \
+  }
+    GEMM_LOADR(0)
+    GEMM_STORER(stage(0))
+    if (nk > 1) GEMM_LOADR(1)
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      // slab kt + 1 goes into the stage slab kt - 1 used (released by the last barrier)
+      if (kt + 1 < nk) {
+        GEMM_STORER(stage((kt + 1) & 1))
+        if (kt + 2 < nk) GEMM_LOADR(kt + 2)
+      }
+      GEMM_COMPUTE(stage(kt & 1))
+      __syncthreads();
+    }
+#undef GEMM_LOADR
+#undef GEMM_STORER
+  } else {
   // prologue: slabs 0 .. NS-2 in flight, wait for slab 0
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
@@ -775,6 +829,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     if (refill) wait_vmcnt<(NS - 2) * IPW>();
     else wait_vmcnt<0>();
     __syncthreads();
+  }
   }
 #undef GEMM_DMA
 #undef GEMM_COMPUTE
@@ -969,9 +1024,9 @@ hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap&
 
 // ---------------------------------------------------------------- launch
 
-// KV: 4 = direct-to-LDS MXFP4 kernel, 2 = direct-to-LDS fp8 kernel, 1 = direct-to-LDS
-// bf16 kernel, 0 = register-staged
-// bf16 kernel; NS stages of SLAB bytes per row for the direct-to-LDS kernels
+// KV: 4 = MXFP4 tiled kernel, 2 = fp8 tiled kernel, 1 = bf16 tiled kernel (256 x 256
+// tiles, see above), 0 = the 32 x 256 / 128 x 128 register-staged kernel; NS stages
+// of SLAB bytes per row for the tiled kernels
 template <int BM, int BN, int WM, int WN, int KV, int NS = 2, int SLAB = 128, class Epi>
 static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipStream_t st) {
   GemmParams<Epi> p{};
@@ -1022,7 +1077,7 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
 #endif
   if (gp[0].A8) return launch_cfg<256, 256, 2, 4, 2, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   if (maxM <= 64) return launch_cfg<32, 256, 1, 4, 0>(gp, ep, ng, st);
-  // large problems: 256x256 tiles, 8 waves, fed by direct global->LDS loads
+  // large problems: 256x256 tiles, 8 waves, 128-byte K slabs in two LDS stages
   if (maxM >= 1024 && minN >= 1024 && offsets32)
     return launch_cfg<256, 256, 2, 4, 1, GEMM_NS, GEMM_SLAB>(gp, ep, ng, st);
   return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
