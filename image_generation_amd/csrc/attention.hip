@@ -188,9 +188,11 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // move the reference only when some query of the wave would overflow 2^8
+    // move the reference only when some query of the wave would overflow 2^8; a
+    // lane's half of the keys decides that as well as the whole row does (the
+    // test is wave-wide), so the two halves exchange maxima only when it moves
     if (__any((mx - mref) * scale_log2 > ATT_RESCALE_LOG2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mref, mx);
       const float alpha = fast_exp2((mref - mnew) * scale_log2);
       mref = mnew;
@@ -416,9 +418,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxl = mx * cs;
-    if (__any(mxl > mref)) {
+    // as in the bf16 kernel: the halves exchange maxima only when the reference moves
+    if (__any(mx * cs > mref)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxl = mx * cs;
       const float mnew = fmaxf(mref, ceilf(mxl));
       // 2^(mref - mnew): an exact power of two (0 before the first tile)
       const float alpha = mref == -INFINITY ? 0.f : ldexpf(1.0f, (int)(mref - mnew));
