@@ -246,15 +246,17 @@ def loop_2048_fp8(dit, DI, device, K, warmup):
             "kernels": kernel_table(by)}
 
 
-def loop_1024_mxfp4(dit, DI, device, K, warmup, bf16_steps_per_s=None):
+def loop_1024_mxfp4(dit, DI, device, K, warmup, bf16_steps_per_s=None, fp8_attention=False):
     """K steps of the 19 + 38 block model at 1024px with every block linear W4A4 in
-    MXFP4 (attention bf16), timed like the headline: replayed step graph, FBC test
-    at threshold 0; kernel shares from a separate instrumented eager pass."""
+    MXFP4 (attention bf16, or e4m3 with fp8_attention), timed like the headline:
+    replayed step graph, FBC test at threshold 0; kernel shares from a separate
+    instrumented eager pass."""
     import torch
     w = DI.WORKLOADS["flux_1024_28step"]
     dims = w.dims
-    log(f"[bench] building {w.name} (MXFP4 W4A4 block linears)")
-    gm = build_model(dit, DI, w, device, dit.DIT_MXFP4)
+    log(f"[bench] building {w.name} (MXFP4 W4A4 block linears, fp8 attention {fp8_attention})")
+    gm = build_model(dit, DI, w, device,
+                     dit.DIT_MXFP4_FP8ATTN if fp8_attention else dit.DIT_MXFP4)
     txt = DI.device_randn((w.B, w.Lt, dims.D), DI.SEED_TEXT, 1.0, device)
     lat0 = DI.device_randn((w.Li, dims.C_in), DI.SEED_LATENTS, 1.0, device, torch.float32)
     sig = dit.dit_sigmas(w.steps, w.shift)
@@ -275,7 +277,8 @@ def loop_1024_mxfp4(dit, DI, device, K, warmup, bf16_steps_per_s=None):
     gemm_tf = gemm_f / (gemm_ms * 1e-3) / 1e12
     sps = K / secs
     return {"workload": w.name, "image_px": w.image_px, "tokens": [w.Lt, Li], "batch": B,
-            "dtype": "MXFP4 W4A4 block linears, bf16 attention", "steps": K, "warmup": warmup,
+            "dtype": "MXFP4 W4A4 block linears, " + ("e4m3" if fp8_attention else "bf16")
+                     + " attention", "steps": K, "warmup": warmup,
             "steps_per_s": round(sps, 4), "ms_per_step": round(1e3 * secs / K, 2),
             "vs_bf16": round(sps / bf16_steps_per_s, 3) if bf16_steps_per_s else None,
             "block_gemm_tflops": round(gemm_tf, 1),
@@ -546,6 +549,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_mxfp4_loop:
         out["loop_1024px_mxfp4"] = loop_1024_mxfp4(dit, DI, device, K, 1, K / secs)
+        torch.cuda.empty_cache()
+        out["loop_1024px_mxfp4_fp8attn"] = loop_1024_mxfp4(dit, DI, device, K, 1, K / secs, True)
         torch.cuda.empty_cache()
     if not args.no_tiny:
         log("[bench] tiny fp32 loop latency, eager vs replayed")

@@ -89,7 +89,8 @@ int make_dims(const dit_dims* in, Dims* o) {
 }
 
 int check_block_dims(const Dims& dm, int dtype) {
-  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32 && dtype != DIT_MXFP4)
+  if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32 && dtype != DIT_MXFP4 &&
+      dtype != DIT_MXFP4_FP8ATTN)
     return fail(DIT_ERR_UNSUPPORTED, "block dtype %d", dtype);
   if (dm.D % 256 || dm.D > 3072)
     return fail(DIT_ERR_UNSUPPORTED, "hidden size %d (needs a multiple of 256, <= 3072)", dm.D);
@@ -106,8 +107,10 @@ int check_block_dims(const Dims& dm, int dtype) {
     if (dm.F % 128) return fail(DIT_ERR_UNSUPPORTED, "fp8: MLP size %d (multiple of 128)", dm.F);
     if (dm.L % 16) return fail(DIT_ERR_UNSUPPORTED, "fp8: joint length %d (multiple of 16)", dm.L);
   }
-  if (dtype == DIT_MXFP4 && dm.F % 256)   // MX K slabs are 256 deep
+  if ((dtype == DIT_MXFP4 || dtype == DIT_MXFP4_FP8ATTN) && dm.F % 256)   // 256-deep MX slabs
     return fail(DIT_ERR_UNSUPPORTED, "mxfp4: MLP size %d (multiple of 256)", dm.F);
+  if (dtype == DIT_MXFP4_FP8ATTN && dm.L % 16)
+    return fail(DIT_ERR_UNSUPPORTED, "fp8 attention: joint length %d (multiple of 16)", dm.L);
   return DIT_OK;
 }
 
@@ -266,7 +269,7 @@ int check_linear(const dit_linear& l, const char* name, int dtype = DIT_BF16) {
     return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", name);
   if (dtype == DIT_FP8 && (!l.w_scale || !aligned16(l.w_scale)))
     return fail(DIT_ERR_INVALID_ARG, "%s: fp8 layer needs a 16-byte aligned w_scale", name);
-  if (dtype == DIT_MXFP4 && (!l.w_mx || !aligned16(l.w_mx)))
+  if ((dtype == DIT_MXFP4 || dtype == DIT_MXFP4_FP8ATTN) && (!l.w_mx || !aligned16(l.w_mx)))
     return fail(DIT_ERR_INVALID_ARG, "%s: mxfp4 layer needs 16-byte aligned w_mx scales", name);
   return DIT_OK;
 }
@@ -477,13 +480,25 @@ GemmProblem gp4(const uint8_t* a4, const uint8_t* a4s, int r0, int pad, const di
 // MXFP4 (W4A4) block: the bf16 block's sequence with every linear's bf16 input
 // quantised to MXFP4 just before its GEMM (32-value blocks along K, E8M0 scales);
 // attention stays bf16
+// A8: attention in e4m3 as in the fp8 block (per-(b, h) scales from the QKV
+// epilogue's amax), the linears still MXFP4
+template <bool A8>
 hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float* mod, int bs,
                      const float* rope, const BlockWS& w, hipStream_t st) {
-  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
-  const int DF = D + F;
+  const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F, H = dm.H;
+  const int DF = D + F, BH = B * H;
   const int P = w.mx_pad;
-  const QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  if (A8) qo.amax = w.amax;
   const float scale = 1.0f / sqrtf((float)dm.d);
+  const float *sq = w.s_qkv, *sk = w.s_qkv + BH, *sv = w.s_qkv + 2 * BH;
+  // joint attention into the first D columns of cat, in the given row map
+  auto attend = [&](const RowMap& map) -> hipError_t {
+    if (!A8) return attention_bf16(w.q, w.k, w.vt, w.cat, DF, map, B, H, L, dm.d, scale, st);
+    hipError_t e2;
+    if ((e2 = quant_qkv(dm, w, st))) return e2;
+    return attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, map, B, H, L, dm.d, scale, st);
+  };
   hipError_t e;
   if (blk.kind == DIT_BLOCK_DOUBLE) {
     const RowMap sm{B, Lt, Li, L, 1, 0};
@@ -500,8 +515,9 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
     if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
     GemmProblem g[2] = {gp4(w.a4, w.a4s, 0, P, blk.qkv[0], D, B * Li, 3 * D),
                         gp4(w.a4, w.a4s, ti, P, blk.qkv[1], D, B * Lt, 3 * D)};
+    if (A8 && (e = zero_u32(w.amax, 3 * BH, st))) return e;
     if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
-    if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, sm, B, dm.H, L, dm.d, scale, st))) return e;
+    if ((e = attend(sm))) return e;
     if ((e = quant_mxfp4<bf16_t>(w.cat, DF, B * L, D, w.a4, w.a4s, P, st))) return e;
     g[0] = gp4(w.a4, w.a4s, 0, P, blk.proj[0], D, B * Li, D);
     g[1] = gp4(w.a4, w.a4s, ti, P, blk.proj[1], D, B * Lt, D);
@@ -528,8 +544,9 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
     return e;
   if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
   const GemmProblem g1 = gp4(w.a4, w.a4s, 0, P, blk.lin1, D, B * L, 3 * D + F);
+  if (A8 && (e = zero_u32(w.amax, 3 * BH, st))) return e;
   if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
-  if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, jm, B, dm.H, L, dm.d, scale, st))) return e;
+  if ((e = attend(jm))) return e;
   // linear2 takes [attention | GELU] as one row
   if ((e = quant_mxfp4<bf16_t>(w.cat, DF, B * L, DF, w.a4, w.a4s, P, st))) return e;
   const GemmProblem g2 = gp4(w.a4, w.a4s, 0, P, blk.lin2, DF, B * L, D);
@@ -593,7 +610,8 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
 hipError_t run_block(const Dims& dm, int dtype, const dit_block& blk, float* x, const float* mod,
                      int bs, const float* rope, const BlockWS& w, hipStream_t st) {
   if (dtype == DIT_FP8) return block_fp8(dm, blk, x, mod, bs, rope, w, st);
-  if (dtype == DIT_MXFP4) return block_mx4(dm, blk, x, mod, bs, rope, w, st);
+  if (dtype == DIT_MXFP4) return block_mx4<false>(dm, blk, x, mod, bs, rope, w, st);
+  if (dtype == DIT_MXFP4_FP8ATTN) return block_mx4<true>(dm, blk, x, mod, bs, rope, w, st);
   if (dtype == DIT_F32) return block_f32(dm, blk, x, mod, bs, rope, w, st);
   return block_impl<float>(dm, blk, x, mod, bs, rope, w, st);
 }
@@ -1007,7 +1025,7 @@ int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* 
   const long long nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm.D;
   if (nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: too many vectors");
   if (m->dtype != DIT_BF16 && m->dtype != DIT_FP8 && m->dtype != DIT_F32 &&
-      m->dtype != DIT_MXFP4)
+      m->dtype != DIT_MXFP4 && m->dtype != DIT_MXFP4_FP8ATTN)
     return fail(DIT_ERR_INVALID_ARG, "dit_modulation: model dtype %d", m->dtype);
   if ((rc = check_device())) return rc;
   hipStream_t st = (hipStream_t)stream;

@@ -24,7 +24,7 @@ DIT_ERR_WORKSPACE = -3
 DIT_ERR_HIP = -4
 DIT_ERR_NONFINITE = -5
 
-DIT_F32, DIT_BF16, DIT_FP8, DIT_MXFP4 = 0, 1, 2, 3
+DIT_F32, DIT_BF16, DIT_FP8, DIT_MXFP4, DIT_MXFP4_FP8ATTN = 0, 1, 2, 3, 4
 DIT_BLOCK_DOUBLE, DIT_BLOCK_SINGLE = 0, 1
 DIT_WS_ATTENTION, DIT_WS_BLOCK, DIT_WS_STEP, DIT_WS_MODULATION, DIT_WS_FBCACHE = range(5)
 
@@ -376,7 +376,8 @@ def dit_block_forward(dims: DitDims, blk: DitBlock, x: torch.Tensor, mod: torch.
                       rope: torch.Tensor, ws: torch.Tensor, mod_bstride: Optional[int] = None,
                       dtype: int = DIT_BF16, stream=None) -> torch.Tensor:
     """x [B, L, D] (fp32 or bf16) updated in place; mod [B or 1, k, D] fp32.
-    dtype DIT_BF16, or DIT_FP8 for a block built from quantize_block_params()."""
+    dtype DIT_BF16; DIT_FP8 for a block built from quantize_block_params(); DIT_MXFP4 or
+    DIT_MXFP4_FP8ATTN (e4m3 attention) for one built from quantize_block_params_mx()."""
     L = dims.Lt + dims.grid_h * dims.grid_w
     if tuple(x.shape) != (dims.B, L, dims.D) or x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"x: expected fp32/bf16 {(dims.B, L, dims.D)}, got {x.dtype} {tuple(x.shape)}")
@@ -452,7 +453,7 @@ class GPUModel:
                                                 if n.startswith(pre)}, pre))
             for n, t in q.items():
                 self.t[n] = t
-        elif dtype == DIT_MXFP4:
+        elif dtype in (DIT_MXFP4, DIT_MXFP4_FP8ATTN):
             # block linears W4A4 in MXFP4; the rest stays bf16
             q = {}
             for pre in [f"double{j}." for j in range(self.n_double)] + \

@@ -72,6 +72,7 @@ extern "C" {
 #define DIT_BF16 1
 #define DIT_FP8 2   /* OCP e4m3 ("e4m3fn") */
 #define DIT_MXFP4 3 /* OCP MXFP4: E2M1 elements, one E8M0 scale per 32 (blocks only) */
+#define DIT_MXFP4_FP8ATTN 4 /* MXFP4 block linears with e4m3 attention (blocks only) */
 
 #define DIT_BLOCK_DOUBLE 0
 #define DIT_BLOCK_SINGLE 1
@@ -143,6 +144,7 @@ typedef struct dit_model {
                             modulation, embedders, timestep MLP and velocity head stay
                             bf16; DIT_MXFP4: the blocks' linears W4A4 in MXFP4 (see
                             dit_block_forward), the rest as for DIT_FP8;
+                            DIT_MXFP4_FP8ATTN: the same with e4m3 attention;
                             DIT_F32: every weight and activation fp32 (head dim
                             32 or 64; reference precision for small models) */
 } dit_model;
@@ -307,7 +309,9 @@ DIT_API int dit_linear_mxfp4(const void* x_codes, const unsigned char* x_scales,
  *   activation scales, e4m3 attention with per-(b, h) scales); DIT_MXFP4 (W4A4
  *   linears with w_mx set: each linear's bf16 input is quantised to MXFP4 on the
  *   fly, 32-value blocks along the input dimension; attention in bf16; D and F
- *   multiples of 256); DIT_F32 (fp32 weights, head dim 32 or 64).
+ *   multiples of 256); DIT_MXFP4_FP8ATTN (the same linears, attention in e4m3 as
+ *   for DIT_FP8; joint length a multiple of 16); DIT_F32 (fp32 weights, head dim
+ *   32 or 64).
  *   workspace >= DIT_WS_BLOCK bytes. */
 DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,

@@ -314,14 +314,16 @@ def _lin(x, P, name, fp8, mx4=False):
     return linear(x, P[name + ".w"], P[name + ".b"])
 
 
-def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False):
+def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False,
+                 attn8=False):
     """Double-stream block (R1, R2, R4, R8): separate weights per stream, joint attention.
 
     x_txt [B, Lt, D], x_img [B, Li, D]; mod_* [B or 1, 6, D] in the order
     shift1, scale1, gate1, shift2, scale2, gate2; P keys "img.qkv.w" etc.;
     ang: RoPE angles [Lt + Li, d/2].  Returns the updated (x_txt, x_img).
     """
-    attn_fn = attention_fp8 if fp8 else attention
+    a8 = fp8 or attn8        # e4m3 attention (R27), alone with MXFP4 linears (R40)
+    attn_fn = attention_fp8 if a8 else attention
     Lt = x_txt.shape[1]
     streams = {"txt": (x_txt, mod_txt), "img": (x_img, mod_img)}
     qkv = {}
@@ -332,9 +334,9 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False
     q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
     k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
-    q = _held(apply_rope(_heads(q, H), ang), fp8)
-    k = _held(apply_rope(_heads(k, H), ang), fp8)
-    a = _held(_merge(attn_fn(q, k, _held(_heads(v, H), fp8, round_fp16))), fp8)
+    q = _held(apply_rope(_heads(q, H), ang), a8)
+    k = _held(apply_rope(_heads(k, H), ang), a8)
+    a = _held(_merge(attn_fn(q, k, _held(_heads(v, H), a8, round_fp16))), a8)
     out = {}
     for s, (x, m) in streams.items():
         a_s = a[:, :Lt] if s == "txt" else a[:, Lt:]
@@ -346,7 +348,8 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False
     return out["txt"], out["img"]
 
 
-def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False, mx4=False):
+def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False, mx4=False,
+                      attn8=False):
     """The double block's output for the joint token rows ``rows`` only (text rows
     first, 0 <= row < Lt + Li) -> [B, len(rows), D].
 
@@ -355,7 +358,8 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
     selected query rows alone: each row's update depends on its own row and the
     keys and values only, so the result equals ``double_block`` at those rows.
     """
-    attn_fn = attention_fp8 if fp8 else attention
+    a8 = fp8 or attn8        # e4m3 attention (R27), alone with MXFP4 linears (R40)
+    attn_fn = attention_fp8 if a8 else attention
     Lt = x_txt.shape[1]
     D = x_img.shape[-1]
     rows = np.asarray(rows)
@@ -367,14 +371,14 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
     q = np.concatenate([qkv["txt"][..., :D], qkv["img"][..., :D]], axis=1)
     k = np.concatenate([qkv["txt"][..., D:2 * D], qkv["img"][..., D:2 * D]], axis=1)
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
-    q = _held(apply_rope(_heads(q, H), ang), fp8)
-    k = _held(apply_rope(_heads(k, H), ang), fp8)
-    vh = _held(_heads(v, H), fp8, round_fp16)
-    if fp8:
+    q = _held(apply_rope(_heads(q, H), ang), a8)
+    k = _held(apply_rope(_heads(k, H), ang), a8)
+    vh = _held(_heads(v, H), a8, round_fp16)
+    if a8:
         a = attn_fn(q, k, vh, rows=rows)
     else:
         a = attn_fn(q[:, :, rows], k, vh)
-    a = _held(_merge(a), fp8)                                  # [B, R, D]
+    a = _held(_merge(a), a8)                                  # [B, R, D]
     B = x_img.shape[0]
     out = np.empty((B, len(rows), D))
     for s, (x, m) in streams.items():
@@ -390,18 +394,19 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
     return out
 
 
-def single_block(x, mod, P, ang, H, fp8=False, mx4=False):
+def single_block(x, mod, P, ang, H, fp8=False, mx4=False, attn8=False):
     """Single-stream block (R10): one modulated LN feeding attention and MLP in parallel.
 
     x [B, L, D]; mod [B or 1, 3, D] = shift, scale, gate; P keys "lin1.w" ...
     """
-    attn_fn = attention_fp8 if fp8 else attention
+    a8 = fp8 or attn8        # e4m3 attention (R27), alone with MXFP4 linears (R40)
+    attn_fn = attention_fp8 if a8 else attention
     D = x.shape[-1]
     u = modulate(x, mod[:, 0:1], mod[:, 1:2])
     h = _lin(u, P, "lin1", fp8, mx4)
-    q = _held(apply_rope(_heads(h[..., :D], H), ang), fp8)
-    k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), fp8)
-    v = _held(_heads(h[..., 2 * D:3 * D], H), fp8, round_fp16)
+    q = _held(apply_rope(_heads(h[..., :D], H), ang), a8)
+    k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), a8)
+    v = _held(_heads(h[..., 2 * D:3 * D], H), a8, round_fp16)
     a = _merge(attn_fn(q, k, v))
     cat = _held(np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1), fp8)
     return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8, mx4)
@@ -481,7 +486,7 @@ def _block_params(P, prefix):
 
 def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = None,
                  force_skip: Optional[bool] = None, fp8: bool = False,
-                 mx4: bool = False):
+                 mx4: bool = False, attn8: bool = False):
     """One flow-matching Euler step of the whole model (steps 1-11 of the oracle definition).
 
     P: parameters keyed as in ``dit_inputs.param_specs`` (fp64 arrays);
@@ -507,7 +512,7 @@ def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = N
         bp = _block_params(P, f"double{j}")
         m_img = mods(f"double{j}.img", 6)
         m_txt = mods(f"double{j}.txt", 6)
-        x_txt, x_img = double_block(x_txt, x_img, m_img, m_txt, bp, ang, H, fp8, mx4)
+        x_txt, x_img = double_block(x_txt, x_img, m_img, m_txt, bp, ang, H, fp8, mx4, attn8)
         if j == 0 and cache is not None and cache.enabled:
             r = x_img - before
             rel = fbcache_rel(r, cache.anchor) if cache.has_anchor else math.inf
@@ -528,7 +533,7 @@ def denoise_step(P, dims, w, lat, txt, i, sig, cache: Optional[FBCacheState] = N
             x = np.concatenate([x_txt, x_img], axis=1)
             for j in range(dims.n_single):
                 x = single_block(x, mods(f"single{j}", 3), _block_params(P, f"single{j}"),
-                                 ang, H, fp8, mx4)
+                                 ang, H, fp8, mx4, attn8)
             x_img = x[:, w.Lt:]
         if cache is not None and cache.enabled:
             cache.cached = x_img - after0

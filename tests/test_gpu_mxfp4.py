@@ -142,8 +142,9 @@ def _rms_rel(a, b):
     return float(np.sqrt(np.mean((a - b) ** 2)) / np.sqrt(np.mean(b ** 2)))
 
 
-def _mx4_block(dit, dims, w, kind, zero_gates=()):
-    """Run the MXFP4 block on the GPU -> (gpu, oracle MXFP4, oracle unquantised, x_in)."""
+def _mx4_block(dit, dims, w, kind, zero_gates=(), attn8=False):
+    """Run the MXFP4 block on the GPU -> (gpu, oracle MXFP4, oracle unquantised, x_in);
+    attn8: e4m3 attention (DIT_MXFP4_FP8ATTN)."""
     params = DI.block_params(dims, "bf16", kind)
     dev = {n: (t.cuda() if n.endswith(".w") else t.float().cuda()) for n, t in params.items()}
     dev4 = dit.quantize_block_params_mx(dev)
@@ -155,7 +156,8 @@ def _mx4_block(dit, dims, w, kind, zero_gates=()):
     rope = dit.dit_rope_table(w.grid_h, w.grid_w, w.Lt, dims.d)
     ws = dit.workspace(dd, dit.DIT_WS_BLOCK)
     x = inp["x"].float().cuda()
-    dit.dit_block_forward(dd, blk, x, inp["mod"].cuda(), rope, ws, dtype=dit.DIT_MXFP4)
+    dit.dit_block_forward(dd, blk, x, inp["mod"].cuda(), rope, ws,
+                          dtype=dit.DIT_MXFP4_FP8ATTN if attn8 else dit.DIT_MXFP4)
     torch.cuda.synchronize()
     got = x.double().cpu().numpy()
     del dev, dev4, ws
@@ -167,9 +169,9 @@ def _mx4_block(dit, dims, w, kind, zero_gates=()):
     def oracle_block(mx4):
         if kind == "double":
             xt, xi = O.double_block(x0[:, :w.Lt], x0[:, w.Lt:], mod[:, :6], mod[:, 6:], P, ang,
-                                    dims.H, mx4=mx4)
+                                    dims.H, mx4=mx4, attn8=attn8 and mx4)
             return np.concatenate([xt, xi], axis=1)
-        return O.single_block(x0, mod, P, ang, dims.H, mx4=mx4)
+        return O.single_block(x0, mod, P, ang, dims.H, mx4=mx4, attn8=attn8 and mx4)
 
     return got, oracle_block(True), oracle_block(False), x0
 
@@ -186,12 +188,15 @@ def _check_mx4_property(got, ref4, exact, x0):
     assert e_go <= MX4_CLOSER * e_orc
 
 
+@pytest.mark.parametrize("attn8", [False, True])
 @pytest.mark.parametrize("D,H,F,B,Lt,gh,gw,kind", MX4_BLOCK_CASES)
-def test_block_forward_mxfp4(dit, D, H, F, B, Lt, gh, gw, kind):
-    _say(f"mxfp4 block {kind} D={D} B={B} Lt={Lt} grid={gh}x{gw}")
+def test_block_forward_mxfp4(dit, D, H, F, B, Lt, gh, gw, kind, attn8):
+    if attn8 and (Lt + gh * gw) % 16:
+        pytest.skip("e4m3 attention needs a joint length that is a multiple of 16")
+    _say(f"mxfp4 block {kind} D={D} B={B} Lt={Lt} grid={gh}x{gw} e4m3 attention={attn8}")
     dims = DI.Dims(D=D, H=H, F=F, n_double=1, n_single=0)
     w = DI.Workload("t", dims, B=B, grid_h=gh, grid_w=gw, Lt=Lt, dtype="bf16")
-    got, ref4, exact, x0 = _mx4_block(dit, dims, w, kind)
+    got, ref4, exact, x0 = _mx4_block(dit, dims, w, kind, attn8=attn8)
     _say(f"  x_out max err vs oracle {parity_err(got, ref4):.3e}")
     _check_mx4_property(got, ref4, exact, x0)
 
@@ -211,16 +216,17 @@ def test_block_forward_mxfp4_mlp_half(dit, D, H, F):
     assert derr <= TOL_MX4_HALF_BRANCH
 
 
-def test_block_forward_mxfp4_flux_1024(dit):
+@pytest.mark.parametrize("attn8", [False, True])
+def test_block_forward_mxfp4_flux_1024(dit, attn8):
     """The full MXFP4 double block at the 1024px shape (4096 image + 512 text tokens)."""
-    _say("mxfp4 block double full 1024px")
+    _say(f"mxfp4 block double full 1024px, e4m3 attention={attn8}")
     w = DI.WORKLOADS["block_1024"]
-    got, ref4, exact, x0 = _mx4_block(dit, w.dims, w, "double")
+    got, ref4, exact, x0 = _mx4_block(dit, w.dims, w, "double", attn8=attn8)
     _check_mx4_property(got, ref4, exact, x0)
 
 
-@pytest.mark.parametrize("B,guidance", [(1, 0.0), (2, 3.5)])
-def test_denoise_loop_mxfp4_teacher_forced(dit, B, guidance):
+@pytest.mark.parametrize("B,guidance,attn8", [(1, 0.0, False), (2, 3.5, False), (2, 3.5, True)])
+def test_denoise_loop_mxfp4_teacher_forced(dit, B, guidance, attn8):
     """Four Euler steps of a small MXFP4 model (2 double + 2 single blocks), alone and
     as a CFG pair.  At the step level the unquantised final layer carries most of
     the update, so the MXFP4 effect is small next to the bf16 storage noise that
@@ -233,14 +239,15 @@ def test_denoise_loop_mxfp4_teacher_forced(dit, B, guidance):
     small = DI.Dims(D=256, H=2, F=512, n_double=2, n_single=2)
     w = DI.Workload("m", small, B=B, grid_h=8, grid_w=8, Lt=32, dtype="bf16", steps=4, shift=3.0,
                     guidance=guidance)
-    _say(f"mxfp4 loop B={B} guidance={guidance}")
+    _say(f"mxfp4 loop B={B} guidance={guidance} e4m3 attention={attn8}")
     params = dict(DI.iter_params(small, "bf16"))
+    q4 = dit.DIT_MXFP4_FP8ATTN if attn8 else dit.DIT_MXFP4
     gms = {dt: dit.GPUModel(small, w.B, w.Lt, w.grid_h, w.grid_w, params, guidance=w.guidance,
-                            dtype=dt) for dt in (dit.DIT_BF16, dit.DIT_MXFP4)}
+                            dtype=dt) for dt in (dit.DIT_BF16, q4)}
     P = {k: O.to64(v) for k, v in params.items()}
     sig = dit.dit_sigmas(w.steps, w.shift)
     mods = {dt: dit.dit_modulation(gm, sig[:-1]) for dt, gm in gms.items()}
-    ws = dit.workspace(gms[dit.DIT_MXFP4].model.dims, dit.DIT_WS_STEP)
+    ws = dit.workspace(gms[q4].model.dims, dit.DIT_WS_STEP)
     lat = DI.latents(w)[0].clone().cuda()
     txt = DI.text_tokens(w)
     for i in range(w.steps):
@@ -251,9 +258,10 @@ def test_denoise_loop_mxfp4_teacher_forced(dit, B, guidance):
             dit.dit_denoise_step(gm, mods[dt][i], txt.cuda(), l2, sig[i], sig[i + 1], None, ws)
             torch.cuda.synchronize()
             out[dt] = l2
-        ref4, _ = O.denoise_step(P, small, w, x_in, O.to64(txt), i, np.array(sig), None, mx4=True)
+        ref4, _ = O.denoise_step(P, small, w, x_in, O.to64(txt), i, np.array(sig), None, mx4=True,
+                                 attn8=attn8)
         exact, _ = O.denoise_step(P, small, w, x_in, O.to64(txt), i, np.array(sig), None)
-        g4 = out[dit.DIT_MXFP4].double().cpu().numpy()[None]
+        g4 = out[q4].double().cpu().numpy()[None]
         g16 = out[dit.DIT_BF16].double().cpu().numpy()[None]
         n = np.sqrt(np.mean((exact - x_in) ** 2))
         e_b = np.sqrt(np.mean((g16 - exact) ** 2)) / n
@@ -265,4 +273,4 @@ def test_denoise_loop_mxfp4_teacher_forced(dit, B, guidance):
         assert np.isfinite(g4).all()
         assert e_go <= e_b + 0.5 * e_q
         assert e_ge <= e_b + 1.1 * e_q
-        lat = out[dit.DIT_MXFP4]
+        lat = out[q4]

@@ -323,13 +323,31 @@ def test_double_block_rows_equals_full_block(fp8, mx4):
     np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
 
 
-def test_mx4_blocks_route_every_linear_through_mxfp4(monkeypatch):
+@pytest.mark.parametrize("attn8", [False, True])
+def test_mx4_blocks_route_every_linear_through_mxfp4(monkeypatch, attn8):
     # every linear of an MXFP4 block (8 in a double block, 2 in a single one) goes
     # through the W4A4 linear, on an input already rounded to bf16, with the
-    # expected (K, N); no full-precision or fp8 linear is left in the block
+    # expected (K, N); no full-precision or fp8 linear is left in the block; the
+    # attention is the e4m3 one exactly when asked for, on Q, K held in bf16 and V
+    # in fp16
     import oracle.dit_oracle as DO
     calls = []
+    attn_calls = []
     real = DO.linear_mxfp4
+    real_a, real_a8 = DO.attention, DO.attention_fp8
+
+    def rec_a(q, k, v, *a, **kw):
+        attn_calls.append("bf16")
+        return real_a(q, k, v, *a, **kw)
+
+    def rec_a8(q, k, v, *a, **kw):
+        assert np.array_equal(O.round_bf16(q), q) and np.array_equal(O.round_bf16(k), k)
+        assert np.array_equal(O.round_fp16(v), v)
+        attn_calls.append("fp8")
+        return real_a8(q, k, v, *a, **kw)
+
+    monkeypatch.setattr(DO, "attention", rec_a)
+    monkeypatch.setattr(DO, "attention_fp8", rec_a8)
 
     def rec(x, w, b):
         assert np.array_equal(O.round_bf16(x), x), "MXFP4 input not bf16-held"
@@ -345,14 +363,17 @@ def test_mx4_blocks_route_every_linear_through_mxfp4(monkeypatch):
     rng = np.random.default_rng(17)
     D, F = 64, 256
     P, xt, xi, mi, mt, ang, H = _tiny_double(rng, D=D, H=2, F=F)
-    DO.double_block(xt, xi, mi, mt, P, ang, H, mx4=True)
+    DO.double_block(xt, xi, mi, mt, P, ang, H, mx4=True, attn8=attn8)
     assert sorted(calls) == sorted([(D, 3 * D), (D, D), (D, F), (F, D)] * 2)
+    assert attn_calls == ["fp8" if attn8 else "bf16"]
     calls.clear()
+    attn_calls.clear()
     Ps = {"lin1.w": rng.standard_normal((3 * D + F, D)) * 0.05, "lin1.b": np.zeros(3 * D + F),
           "lin2.w": rng.standard_normal((D, D + F)) * 0.05, "lin2.b": np.zeros(D)}
     x = np.concatenate([xt, xi], axis=1)
-    DO.single_block(x, mi[:, :3], Ps, ang, H, mx4=True)
+    DO.single_block(x, mi[:, :3], Ps, ang, H, mx4=True, attn8=attn8)
     assert calls == [(D, 3 * D + F), (D + F, D)]
+    assert attn_calls == ["fp8" if attn8 else "bf16"]
 
 
 def test_mx4_double_block_zero_weights_keeps_biases_exact():
