@@ -71,6 +71,28 @@ __device__ __forceinline__ bool gate_closed(const int* gate) {
   return gate != nullptr && *gate != 0;
 }
 
+// ---- MXFP4 (OCP E2M1 elements, E8M0 scale per 32 consecutive K values)
+// E2M1 code of x / 2^e (exact in fp32), rounded to nearest by counting the
+// midpoints it passes, ties to the even mantissa (0.25 -> 0, 0.75 -> 1,
+// 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), beyond 6 saturating.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | (__float_as_uint(v) >> 31 << 3);
+}
+// Block exponent: floor(log2 amax) - 2, clamped to the E8M0 range; 0 for amax 0.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  frexpf(amax, &k);                    // amax = m 2^k, m in [0.5, 1)
+  return min(max(k - 3, -127), 127);
+}
+// Byte of block j (0..7 within a 256-wide slab) in a row's 8 stored scales: the
+// GEMM reads them in the order 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ int mx_scale_pos(int j) { return (j & 1) ? 4 + (j >> 1) : j >> 1; }
+
 template <typename T> struct XIO;
 template <> struct XIO<float> {
   static __device__ __forceinline__ float ld(const float* p) { return *p; }

@@ -478,8 +478,8 @@ GemmProblem gp4(const uint8_t* a4, const uint8_t* a4s, int r0, int pad, const di
 }
 
 // MXFP4 (W4A4) block: the bf16 block's sequence with every linear's bf16 input
-// quantised to MXFP4 just before its GEMM (32-value blocks along K, E8M0 scales);
-// attention stays bf16
+// quantised to MXFP4 just before its GEMM (32-value blocks along K, E8M0 scales;
+// the LN outputs straight from the LN pass); attention stays bf16
 // A8: attention in e4m3 as in the fp8 block (per-(b, h) scales from the QKV
 // epilogue's amax), the linears still MXFP4
 template <bool A8>
@@ -510,9 +510,9 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
     const float* mt = mod + 6 * (size_t)D;
     const int ti = B * Li;   // first text row of the stream-major row space
 
-    if ((e = ln_modulate<float>(x, w.u, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs, st)))
+    if ((e = ln_modulate_mx4(x, w.a4, w.a4s, P, B * L, D, sm, B * Li, mi, mi + D, mt, mt + D, bs,
+                             st)))
       return e;
-    if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
     GemmProblem g[2] = {gp4(w.a4, w.a4s, 0, P, blk.qkv[0], D, B * Li, 3 * D),
                         gp4(w.a4, w.a4s, ti, P, blk.qkv[1], D, B * Lt, 3 * D)};
     if (A8 && (e = zero_u32(w.amax, 3 * BH, st))) return e;
@@ -523,10 +523,9 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
     g[1] = gp4(w.a4, w.a4s, ti, P, blk.proj[1], D, B * Lt, D);
     const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
     if ((e = gemm_gated_residual<float>(g, ng, x, D, gate1, bs, maps, st))) return e;
-    if ((e = ln_modulate<float>(x, w.u, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D, mt + 3 * D,
-                                mt + 4 * D, bs, st)))
+    if ((e = ln_modulate_mx4(x, w.a4, w.a4s, P, B * L, D, sm, B * Li, mi + 3 * D, mi + 4 * D,
+                             mt + 3 * D, mt + 4 * D, bs, st)))
       return e;
-    if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
     g[0] = gp4(w.a4, w.a4s, 0, P, blk.mlp1[0], D, B * Li, F);
     g[1] = gp4(w.a4, w.a4s, ti, P, blk.mlp1[1], D, B * Lt, F);
     bf16_t* hid[2] = {w.cat + D, w.cat + (size_t)ti * DF + D};
@@ -540,9 +539,9 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
   }
   // single-stream block, joint row order
   const RowMap jm{B, Lt, Li, L, 0, 0};
-  if ((e = ln_modulate<float>(x, w.u, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st)))
+  if ((e = ln_modulate_mx4(x, w.a4, w.a4s, P, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs,
+                           st)))
     return e;
-  if ((e = quant_mxfp4<bf16_t>(w.u, D, B * L, D, w.a4, w.a4s, P, st))) return e;
   const GemmProblem g1 = gp4(w.a4, w.a4s, 0, P, blk.lin1, D, B * L, 3 * D + F);
   if (A8 && (e = zero_u32(w.amax, 3 * BH, st))) return e;
   if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;

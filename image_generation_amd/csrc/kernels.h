@@ -131,6 +131,13 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
                            const RowMap& map, int n_img_rows, const float* shift_img,
                            const float* scale_img, const float* shift_txt, const float* scale_txt,
                            int mod_bstride, hipStream_t st);
+// LN + modulate straight to MXFP4 (codes [rows, D/2], scales [D/256][pad_rows][8])
+// of the bf16-rounded output: the same codes and scales as ln_modulate to bf16
+// followed by quant_mxfp4.
+hipError_t ln_modulate_mx4(const float* x, uint8_t* codes, uint8_t* scales, int pad_rows, int rows,
+                           int D, const RowMap& map, int n_img_rows, const float* shift_img,
+                           const float* scale_img, const float* shift_txt, const float* scale_txt,
+                           int mod_bstride, hipStream_t st);
 
 // Per-row dynamic quantisation: dst[r, :width] = e4m3(src[r, :width] * 448 / amax_r),
 // scale[r] = amax_r / 448.  T = bf16_t or f16_t.

@@ -33,18 +33,26 @@ __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
   return v;
 }
 
-// OUT: 0 = bf16, 1 = e4m3 + per-row scale, 2 = fp32
+// OUT: 0 = bf16, 1 = e4m3 + per-row scale, 2 = fp32, 3 = MXFP4 codes [rows, D/2] +
+// E8M0 block scales mxs [D/256][pad_rows][8] of the bf16-rounded output (the
+// values the separate quantiser would see; rows in [rows, pad_rows) get scale 2^0)
 template <class XT, int OUT>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(
     const XT* __restrict__ x, void* __restrict__ out_, float* __restrict__ oscale, int rows, int D,
     RowMap map, int n_img,
     const float* __restrict__ sh_i, const float* __restrict__ sc_i,
     const float* __restrict__ sh_t, const float* __restrict__ sc_t, int bstride,
-    const int* __restrict__ gate) {
+    const int* __restrict__ gate, uint8_t* __restrict__ mxs, int pad_rows) {
   if (gate_closed(gate)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  if (r >= rows) {
+    if constexpr (OUT == 3) {
+      if (r < pad_rows && lane < 8)
+        for (int c = 0; c < (D >> 8); ++c) mxs[((size_t)c * pad_rows + r) * 8 + lane] = 127;
+    }
+    return;
+  }
   int b, t;
   map.token(r, b, t);
   const XT* xr = x + ((size_t)b * map.L + t) * D;
@@ -85,7 +93,29 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(
                                  fmaxf(fabsf(v[c][2]), fabsf(v[c][3]))));
     }
   }
-  if constexpr (OUT == 2) {
+  if constexpr (OUT == 3) {
+    uint8_t* crow = (uint8_t*)out_ + (size_t)r * (D >> 1);
+#pragma unroll
+    for (int c = 0; c < LN_MAXCH; ++c) {
+      if (c < nch) {
+        // a 32-value block is 8 consecutive lanes' 4 values
+        f32x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = bf2f(f2bf(v[c][i]));
+        float m = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        const int e = mx_exponent(m);
+        uint32_t u = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u |= e2m1_code(ldexpf(h[i], -e)) << (4 * i);
+        *(uint16_t*)(crow + c * 128 + lane * 2) = (uint16_t)u;
+        if ((lane & 7) == 0)
+          mxs[((size_t)c * pad_rows + r) * 8 + mx_scale_pos(lane >> 3)] = (uint8_t)(e + 127);
+      }
+    }
+  } else if constexpr (OUT == 2) {
     float* orow = (float*)out_ + (size_t)r * D;
 #pragma unroll
     for (int c = 0; c < LN_MAXCH; ++c)
@@ -133,7 +163,7 @@ hipError_t ln_modulate(const XT* x, OT* out, int rows, int D, const RowMap& map,
   constexpr int mode = sizeof(OT) == 4 ? 2 : 0;
   hipLaunchKernelGGL((ln_modulate_kernel<XT, mode>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
                      (void*)out, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
-                     shift_txt, scale_txt, mod_bstride, launch_gate());
+                     shift_txt, scale_txt, mod_bstride, launch_gate(), (uint8_t*)nullptr, 0);
   return hipGetLastError();
 }
 template hipError_t ln_modulate<float, bf16_t>(const float*, bf16_t*, int, int, const RowMap&, int,
@@ -152,7 +182,21 @@ hipError_t ln_modulate_fp8(const float* x, fp8_t* out8, float* scale, int rows, 
   KTimerScope timer(KS_LN, st);
   hipLaunchKernelGGL((ln_modulate_kernel<float, 1>), dim3((rows + 3) / 4), dim3(256), 0, st, x,
                      (void*)out8, scale, rows, D, map, n_img_rows, shift_img, scale_img,
-                     shift_txt, scale_txt, mod_bstride, launch_gate());
+                     shift_txt, scale_txt, mod_bstride, launch_gate(), (uint8_t*)nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t ln_modulate_mx4(const float* x, uint8_t* codes, uint8_t* scales, int pad_rows, int rows,
+                           int D, const RowMap& map, int n_img_rows, const float* shift_img,
+                           const float* scale_img, const float* shift_txt, const float* scale_txt,
+                           int mod_bstride, hipStream_t st) {
+  if (D % 256 != 0 || D > 256 * LN_MAXCH || pad_rows < rows || pad_rows % 256)
+    return hipErrorInvalidValue;
+  if (pad_rows == 0) return hipSuccess;
+  KTimerScope timer(KS_LN, st);
+  hipLaunchKernelGGL((ln_modulate_kernel<float, 3>), dim3((pad_rows + 3) / 4), dim3(256), 0, st, x,
+                     (void*)codes, nullptr, rows, D, map, n_img_rows, shift_img, scale_img,
+                     shift_txt, scale_txt, mod_bstride, launch_gate(), scales, pad_rows);
   return hipGetLastError();
 }
 

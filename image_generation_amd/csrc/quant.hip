@@ -232,13 +232,8 @@ template hipError_t quant_slices<f16_t>(const f16_t*, size_t, int, const unsigne
 // 3.5 -> 4, 5 -> 4) and values beyond 6 saturating.  16 code bytes per block,
 // element 2j in the low nibble of byte j; the scale byte goes to the GEMM order
 // [slab][pad_rows][8] with a row's 8 slab blocks stored as 0, 2, 4, 6, 1, 3, 5, 7.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return c | (__float_as_uint(v) >> 31 << 3);
-}
+// (e2m1_code, mx_exponent and mx_scale_pos live in common.h: the fused LN pass
+// uses them too.)
 
 template <class T>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const T* __restrict__ src, int lds,
@@ -251,8 +246,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const T* __restrict__ 
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)pad_rows * nb) return;
   const int r = (int)(idx / nb), b = (int)(idx - (long long)r * nb);
-  const int j = b & 7;
-  uint8_t* sp = scales + (((size_t)(b >> 3) * pad_rows + r) << 3) + ((j & 1) ? 4 + (j >> 1) : j >> 1);
+  uint8_t* sp = scales + (((size_t)(b >> 3) * pad_rows + r) << 3) + mx_scale_pos(b & 7);
   if (r >= rows) {   // padding rows of the scale array
     *sp = 127;
     return;
@@ -264,12 +258,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const T* __restrict__ 
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int e = 0;
-  if (amax > 0.f) {
-    int k;
-    frexpf(amax, &k);                    // amax = m 2^k, m in [0.5, 1)
-    e = min(max(k - 3, -127), 127);
-  }
+  const int e = mx_exponent(amax);
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
