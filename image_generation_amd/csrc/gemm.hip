@@ -421,11 +421,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
 // 16 B contiguously, so a permuted (or padded) row layout is built by giving every
 // lane the global chunk that belongs at its LDS slot: 8 lanes still cover one
 // 128-byte row segment.  (Padded rows re-read the row's last chunk into the pad.)
-// e4m3 and MXFP4 operands (and bf16 with more than two stages) use gfx950's direct
-// global->LDS loads (global_load_lds_dwordx4), with no staging registers; bf16 with
-// two stages loads the same chunks into registers (global_load_dwordx4) and writes
-// them with ds_write_b128, which lets the fragment reads run ahead of the MFMAs
-// with exact waits (measured 3-6% faster on the block shapes).
+// e4m3 operands (and bf16 with more than two stages) use gfx950's direct
+// global->LDS loads (global_load_lds_dwordx4), with no staging registers; bf16 and
+// MXFP4 with two stages load the same chunks into registers (global_load_dwordx4)
+// and write them with ds_write_b128, which lets the fragment reads run ahead of
+// the MFMAs with exact waits (measured 3-6% faster on the bf16 block shapes and
+// 1.5-4.5% on the MXFP4 ones; for e4m3 it measured slower).
 //
 // Pipeline: NS stages, each holding a K slab of SLAB bytes per row for the A and
 // the W tile (SLAB / 2 bf16 or SLAB e4m3 values), so NS - 1 slabs are in flight
@@ -558,9 +559,9 @@ template <int BM, int BN, int WM, int WN, int FMT, int NS, int SLAB, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> p) {
   if (gate_closed(p.gate)) return;
   constexpr bool F8 = FMT == 1, F4 = FMT == 2;
-  // bf16 with two stages: global loads staged through registers and written to LDS
-  // by the waves (see below); e4m3 and MXFP4: direct-to-LDS loads
-  constexpr bool VS = FMT == 0 && NS == 2;
+  // bf16 and MXFP4 with two stages: global loads staged through registers and
+  // written to LDS by the waves (see below); e4m3: direct-to-LDS loads
+  constexpr bool VS = (FMT == 0 || FMT == 2) && NS == 2;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
@@ -772,6 +773,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
         sb_[j] = *(const int*)(x_s + BM * 8 + (wcol + j * 32 + frow) * 8 + hi * 4);      \
     GEMM_MX4_STEP(0) GEMM_MX4_STEP(1) GEMM_MX4_STEP(2) GEMM_MX4_STEP(3)                  \
+    /* register-staged: the reads of step kk + 1 go one per MFMA between those of kk */  \
+    if constexpr (VS) {                                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);                    \
+      _Pragma("unroll") for (int kk = 0; kk < 3; ++kk) {                                \
+        _Pragma("unroll") for (int r = 0; r < TM + TN; ++r) {                           \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            \
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            \
+        }                                                                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);             \
+      }                                                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);                          \
+    }                                                                                    \
   }
 
   if constexpr (VS) {
@@ -781,6 +794,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
     // reads at once, lgkmcnt(0), so fragment reads could not run ahead of the
     // MFMAs; with ordinary loads the waits are exact.)
     i32x4 sreg[IPW];
+    i32x4 xreg = {};   // MXFP4: this wave's 1 KB share of the slab's block scales
 #define GEMM_LOADR(kt)                                                                    \
   {                                                                                      \
     const int ko_ = (kt) * SLAB;                                                         \
@@ -788,11 +802,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
       const char* b_ = ((wave * IPW + j) * 1024 >= AB) ? wbase : abase;                  \
       sreg[j] = *(const i32x4*)(b_ + voff[j] + ko_);                                     \
     }                                                                                    \
+    if constexpr (F4) {                                                                  \
+      if (wave < 4) xreg = *(const i32x4*)(xsrc + (size_t)(kt) * xstride);               \
+    }                                                                                    \
   }
 #define GEMM_STORER(stg)                                                                  \
   {                                                                                      \
     _Pragma("unroll") for (int j = 0; j < IPW; ++j)                                     \
         *(i32x4*)((stg) + (wave * IPW + j) * 1024 + lane * 16) = sreg[j];                \
+    if constexpr (F4) {                                                                  \
+      if (wave < 4) *(i32x4*)((stg) + SB + wave * 1024 + lane * 16) = xreg;              \
+    }                                                                                    \
   }
     GEMM_LOADR(0)
     GEMM_STORER(stage(0))
@@ -804,7 +824,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
         GEMM_STORER(stage((kt + 1) & 1))
         if (kt + 2 < nk) GEMM_LOADR(kt + 2)
       }
-      GEMM_COMPUTE(stage(kt & 1))
+      if constexpr (F4) GEMM_COMPUTE_F4(stage(kt & 1))
+      else GEMM_COMPUTE(stage(kt & 1))
       __syncthreads();
     }
 #undef GEMM_LOADR
@@ -1064,7 +1085,7 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
                 (long long)gp[i].N * gp[i].ldw * es < (1LL << 31);
   }
   if (gp[0].A8 && !offsets32) return hipErrorInvalidValue;
-  if (gp[0].A4) {   // MXFP4 operands: the direct-to-LDS kernel, byte offsets in 32 bits
+  if (gp[0].A4) {   // MXFP4 operands: the tiled kernel, byte offsets in 32 bits
     for (int i = 0; i < ng; ++i)
       if ((long long)gp[i].M * (gp[i].lda / 2) >= (1LL << 31) ||
           (long long)gp[i].N * (gp[i].ldw / 2) >= (1LL << 31) || gp[i].K % 256)
@@ -1083,7 +1104,7 @@ static hipError_t launch(const GemmProblem* gp, const Epi* ep, int ng, hipStream
   return launch_cfg<128, 128, 2, 2, 0>(gp, ep, ng, st);
 }
 
-// MXFP4 operands: the direct-to-LDS kernel only (256 x 256 tiles, any M, N).
+// MXFP4 operands: the tiled kernel only (256 x 256 tiles, any M, N).
 template <class Epi>
 static hipError_t launch_mx4(const GemmProblem& g, const Epi& e, hipStream_t st) {
   KTimerScope timer(KS_GEMM_F32, st);
