@@ -51,16 +51,16 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1134784 * 1024 + 228601 * 1024,
+    "gemm_lin1": {"bytes": 1133381 * 1024 + 228260 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "84b7d0efb79d6263fdebeba04609eacd733b0b53"},
-    "attention": {"bytes": 101508 * 1024 + 27693 * 1024,
+                  "sha1": "397c0165415f20578684d12aa11b846dbd7a48da"},
+    "attention": {"bytes": 101508 * 1024 + 27688 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",
                   "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
-                  "sha1": "2c713befa949038ff16ffa14885b8ede97e74b2f"},
+                  "sha1": "d448700a0993f9c3df91abae76e9dc17cd5d50f2"},
 }
 
 
