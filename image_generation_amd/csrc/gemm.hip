@@ -28,6 +28,10 @@ constexpr int EPI_LDS = 36;             // padded fp32 row of a parked 32-column
 // row4(r, c, v): v = C[r, c..c+3] (bias added), c % 4 == 0
 // col4(r, c, v): v = C[r..r+3, c] (bias added), r % 4 == 0
 // colmajor(n0, BN): true if the tile starting at column n0 wants col4
+// rows<NR>(r0, rs, c, v) (optional): v[i] = C[r0 + i rs, c..c+3] for i < NR, every
+//   row in bounds and the calling wave's columns inside one tensor and head, so
+//   branches on c agree across the wave; the functor issues all its loads before
+//   its first store.  Returns the largest |stored value| (amax-tracking functors).
 
 struct EpiStoreF32 {
   float* out; int ldo;
@@ -93,6 +97,36 @@ struct EpiGatedResidual {
                    o3 + g[3] * v[3]);
     }
   }
+  template <int NR>
+  __device__ __forceinline__ float rows(int r0, int rs, int c, const f32x4 (&v)[NR]) const {
+    XT* p[NR];
+    f32x4 g[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int b, t; map.token(r0 + i * rs, b, t);
+      p[i] = x + ((size_t)b * map.L + t) * D + c;
+      g[i] = *(const f32x4*)(gate + (size_t)b * gate_bstride + c);
+    }
+    if constexpr (sizeof(XT) == 4) {
+      f32x4 o[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) o[i] = *(const f32x4*)p[i];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) *(f32x4*)p[i] = o[i] + g[i] * v[i];
+    } else {
+      uint2 u[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) u[i] = *(const uint2*)p[i];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float o0 = __uint_as_float(u[i].x << 16), o1 = __uint_as_float(u[i].x & 0xffff0000u);
+        const float o2 = __uint_as_float(u[i].y << 16), o3 = __uint_as_float(u[i].y & 0xffff0000u);
+        store_bf16x4((bf16_t*)p[i], o0 + g[i][0] * v[i][0], o1 + g[i][1] * v[i][1],
+                     o2 + g[i][2] * v[i][2], o3 + g[i][3] * v[i][3]);
+      }
+    }
+    return 0.f;
+  }
   __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
@@ -121,6 +155,27 @@ __device__ __forceinline__ void track_amax(const Epi& epi, int sl, float m, unsi
 
 __device__ __forceinline__ float amax4(float a, float b, float c, float d) {
   return fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d)));
+}
+
+template <class E, class = void> struct HasRows : std::false_type {};
+template <class E>
+struct HasRows<E, std::void_t<decltype(&E::template rows<1>)>> : std::true_type {};
+
+// NR in-bounds rows r0 + i rs through the functor's rows() if it has one, else row4
+// one row at a time; the largest |stored value| when the functor tracks it.
+template <int NR, class Epi>
+__device__ __forceinline__ float epi_rows(const Epi& e, int r0, int rs, int c, const f32x4 (&v)[NR]) {
+  if constexpr (HasRows<Epi>::value) {
+    return e.template rows<NR>(r0, rs, c, v);
+  } else {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if constexpr (TracksAmax<Epi>::value) m = fmaxf(m, e.row4(r0 + i * rs, c, v[i]));
+      else e.row4(r0 + i * rs, c, v[i]);
+    }
+    return m;
+  }
 }
 
 // Split the fused projection into head-major Q, K (bf16, rotated) and V^T (fp16).
@@ -181,6 +236,39 @@ struct EpiQKVT {
     dst[3 * L] = __builtin_bit_cast(uint16_t, h3);
     return amax4(v[0], v[1], v[2], v[3]);
   }
+  // Q, K columns: the rows' tokens and RoPE entries first, then the rotations and stores
+  template <int NR>
+  __device__ __forceinline__ float rows(int r0, int rs, int c, const f32x4 (&v)[NR]) const {
+    const int which = c / D;
+    if (which == 2) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) m = fmaxf(m, row4(r0 + i * rs, c, v[i]));
+      return m;
+    }
+    const int cc = c - which * D;
+    const int h = cc / d;
+    const int dd = cc - h * d;
+    bf16_t* dst[NR];
+    f32x4 cs[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int b, t; map.token(r0 + i * rs, b, t);
+      dst[i] = (which == 0 ? q : k) + (((size_t)b * H + h) * map.L + t) * d + dd;
+      cs[i] = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float o0 = v[i][0] * cs[i][0] - v[i][1] * cs[i][1];
+      const float o1 = v[i][0] * cs[i][1] + v[i][1] * cs[i][0];
+      const float o2 = v[i][2] * cs[i][2] - v[i][3] * cs[i][3];
+      const float o3 = v[i][2] * cs[i][3] + v[i][3] * cs[i][2];
+      store_bf16x4(dst[i], o0, o1, o2, o3);
+      m = fmaxf(m, amax4(o0, o1, o2, o3));
+    }
+    return m;
+  }
   // Q, K slots store bf16, V slots fp16
   __device__ __forceinline__ float stored(int slot, float m) const {
     return slot < 2 * map.B * H ? bf2f(f2bf(m)) : (float)(f16_t)m;
@@ -216,6 +304,13 @@ struct EpiLinear1T {
   __device__ __forceinline__ float row4(int r, int c, f32x4 v) const {
     if (c < n_qkv) return qkv.row4(r, c, v);
     gelu.row4(r, c - n_qkv, v);
+    return 0.f;
+  }
+  template <int NR>
+  __device__ __forceinline__ float rows(int r0, int rs, int c, const f32x4 (&v)[NR]) const {
+    if (c < n_qkv) return qkv.template rows<NR>(r0, rs, c, v);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) gelu.row4(r0 + i * rs, c - n_qkv, v[i]);
     return 0.f;
   }
   __device__ __forceinline__ float col4(int r, int c, f32x4 v) const { return qkv.col4(r, c, v); }
@@ -489,7 +584,36 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int cbase = n0 + wcol + j * 32;
       const int rbase = m0 + wrow + h * PR;
-      if (!cmaj) {
+      // every row and column of this pass in bounds (and one amax slot, if tracked):
+      // the functor gets all PR / 8 rows of a lane at once, with no branch between
+      // them, so their loads are issued together
+      const bool whole = rbase + PR <= g.M && cbase + 32 <= g.N && (!kAmax || one_slot);
+      if (!cmaj && whole) {
+        const int cl = (lane & 7) * 4;
+        const int col = cbase + cl;
+        const int row0 = rbase + (lane >> 3);
+        f32x4 v[PR / 8];
+#pragma unroll
+        for (int ps = 0; ps < PR / 8; ++ps) {
+          v[ps] = *(const f32x4*)&slice[(ps * 8 + (lane >> 3)) * EPI_LDS + cl];
+          if constexpr (F8) v[ps] *= *(const f32x4*)(g.sw + col) * g.sa[row0 + ps * 8];
+        }
+        if (g.bias) {
+          const f32x4 bv = *(const f32x4*)(g.bias + col);
+#pragma unroll
+          for (int ps = 0; ps < PR / 8; ++ps) v[ps] += bv;
+        }
+        // e4m3: two batches of rows (a single batch of 8 spills next to the 128 accumulators)
+        constexpr int NB = F8 ? 2 : 1, NRB = PR / 8 / NB;
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
+          f32x4 vb[NRB];
+#pragma unroll
+          for (int i = 0; i < NRB; ++i) vb[i] = v[bt * NRB + i];
+          const float m = epi_rows<NRB>(epi, row0 + bt * NRB * 8, 8, col, vb);
+          if constexpr (kAmax) am = fmaxf(am, m);
+        }
+      } else if (!cmaj) {
 #pragma unroll
         for (int ps = 0; ps < PR / 8; ++ps) {
           const int rl = ps * 8 + (lane >> 3);
