@@ -633,6 +633,33 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
             }
           }
         }
+      } else if (whole) {
+        // column quads, all in bounds: operands and bias first, then the stores
+        constexpr int NP = PR / 4 * 32 / 64;
+        f32x4 v[NP];
+#pragma unroll
+        for (int ps = 0; ps < NP; ++ps) {
+          const int idx = ps * 64 + lane;
+          const int rq = idx % (PR / 4);
+          const int cl = idx / (PR / 4);
+          v[ps][0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
+          v[ps][1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
+          v[ps][2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
+          v[ps][3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
+          if constexpr (F8) v[ps] *= *(const f32x4*)(g.sa + rbase + rq * 4) * g.sw[cbase + cl];
+        }
+        if (g.bias) {
+#pragma unroll
+          for (int ps = 0; ps < NP; ++ps) v[ps] += g.bias[cbase + (ps * 64 + lane) / (PR / 4)];
+        }
+#pragma unroll
+        for (int ps = 0; ps < NP; ++ps) {
+          const int idx = ps * 64 + lane;
+          const int row = rbase + (idx % (PR / 4)) * 4;
+          const int col = cbase + idx / (PR / 4);
+          if constexpr (kAmax) am = fmaxf(am, epi.col4(row, col, v[ps]));
+          else epi.col4(row, col, v[ps]);
+        }
       } else {
 #pragma unroll
         for (int ps = 0; ps < PR / 4 * 32 / 64; ++ps) {
