@@ -51,11 +51,11 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1133381 * 1024 + 228260 * 1024,
+    "gemm_lin1": {"bytes": 1070525 * 1024 + 241488 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "397c0165415f20578684d12aa11b846dbd7a48da"},
+                  "sha1": "c1da96acaf660510a751270e7e1aa35607be8801"},
     "attention": {"bytes": 101508 * 1024 + 27688 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_D = 128;",
