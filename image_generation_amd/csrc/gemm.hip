@@ -12,7 +12,9 @@
 // time and reads it back either row-wise (4 consecutive columns of one row per
 // lane: coalesced stores, RoPE pairs in-register) or column-wise (4 consecutive
 // rows of one column per lane: the transposed V store), then calls the fused
-// epilogue functor.
+// epilogue functor; a pass wholly in bounds hands the functor all of a lane's rows
+// at once, so the loads they need (RoPE entries, residual rows, gates) are in
+// flight together.
 #include <type_traits>
 
 #include "common.h"
