@@ -69,3 +69,26 @@ def test_linear_forward(dit, M, K, N, out_dtype):
     print(f"  err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= tol
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_linear_forward_epilogue_paths_agree(dit, out_dtype):
+    """The tiled kernel's epilogue stores a pass wholly inside the problem through its
+    batched path and a pass that crosses the last row one row at a time; both do the
+    same arithmetic, so a row must come out bit-identical either way.  Rows 1024..1063
+    of a 1064-row problem (per-row path: their pass runs to row 1087) are computed
+    again as rows 0..39 of a 1024-row problem (batched path)."""
+    print(f"linear epilogue paths out={out_dtype}", flush=True)
+    sys.stdout.flush()
+    K, N = 192, 1024
+    x = DI.randn((1064, K), 94, 1.0, "bf16").cuda()
+    w = DI.randn((N, K), 95, K ** -0.5, "bf16").cuda()
+    b = DI.randn((N,), 96, 0.1, "f32").cuda()
+    y_rag = torch.empty((1064, N), dtype=out_dtype, device="cuda")
+    dit.dit_linear_forward(x, w, b, y_rag)
+    x2 = torch.cat([x[1024:], x[:984]]).contiguous()
+    y_full = torch.empty((1024, N), dtype=out_dtype, device="cuda")
+    dit.dit_linear_forward(x2, w, b, y_full)
+    torch.cuda.synchronize()
+    assert torch.equal(y_rag[1024:], y_full[:40])
+    assert torch.equal(y_rag[:984], y_full[40:])
