@@ -29,6 +29,56 @@ carries its reading number (R1..R32) as listed in the design notes.
 
 Everything is fp64 numpy.  Parameters are ``dict[str, ndarray]`` with weights
 in ``torch.nn.Linear`` layout ``[out, in]``: ``y = x @ W.T + b``.
+
+Pins: each function, and the CPU test (``tests/test_oracle_pins.py`` unless
+another file is named) that fails on a plausible mistake in it -- a dropped
+term, a wrong sign or index, a transposed operand:
+
+  sigmas              test_sigmas_golden_shift3 (hand-derived values),
+                      test_sigmas_endpoints_monotone, test_sigmas_shift1_is_linear
+  timestep_sinusoid   test_timestep_sinusoid_t0, test_timestep_sinusoid_frequencies
+  silu, gelu_tanh     test_silu_vs_torch, test_gelu_tanh_vs_torch_and_erf
+  linear              test_linear_vs_triple_loop, test_linear_one_hot_weight_selects_column
+  time_embed          test_time_embed_hand_derived
+  modulation_vectors  test_modulation_vectors_hand_derived
+  layer_norm          test_layer_norm_vs_torch_and_moments
+  modulate            test_modulate_identity_and_affine, test_final_layer_hand_derived
+  image_positions,    test_rope_matches_complex_rotation_and_keeps_pair_norms,
+  rope_table,         test_rope_relative_position_per_axis, test_rope_axis_split
+  apply_rope
+  attention           test_attention_rows_are_a_distribution,
+                      test_attention_identical_keys_gives_mean_of_v,
+                      test_attention_dominant_key, test_attention_vs_naive_triple_loop,
+                      test_attention_vs_torch_sdpa
+  attention_naive     the textbook triple loop itself; agrees with torch's SDPA
+                      through test_attention_vs_torch_sdpa / _vs_naive_triple_loop
+  linear_fp8,         test_linear_fp8_exact_on_representable_inputs,
+  linear_fp8_codes    test_quantize_rows_scale_and_roundtrip
+  linear_mxfp4        test_mx4_blocks_route_every_linear_through_mxfp4,
+                      test_mx4_double_block_zero_weights_keeps_biases_exact,
+                      test_mxfp4_reproduces_representable_blocks
+  attention_fp8       test_attention_fp8_identical_keys_mean_of_v,
+                      test_attention_fp8_identical_values_returned_exactly,
+                      test_attention_fp8_exact_when_p_is_representable,
+                      test_attention_fp8_close_to_exact, test_attention_fp8_slack_grows_with_the_band
+  double_block        test_double_block_brute_force_small, test_double_block_zero_gates_is_identity,
+                      test_double_block_zero_value_weights, test_double_block_stream_isolation
+  double_block_rows   test_double_block_rows_equals_full_block
+  single_block        test_single_block_brute_force_small (with a planted q / k swap
+                      that the hand version rejects), test_single_block_zero_gate_and_wiring
+  single_block_rows   test_single_block_rows_equals_full_block
+  final_layer         test_final_layer_hand_derived
+  fbcache_rel         test_fbcache_rel_vs_python_loop;
+                      tests/test_oracle_step.py::test_fbcache_rel_is_direct_recomputation
+  fbcache_decide,     test_fbcache_policy_cases; tests/test_oracle_step.py (threshold 0
+  fbcache_policy,     never skips, +inf skips every step after the first, warm-up / cap
+  FBCacheState        patterns, identity tail: skip == full)
+  euler_update        test_euler_constant_velocity_total_displacement,
+                      test_euler_lands_on_target_for_exact_velocity
+  cfg_combine         test_cfg_combine_cases;
+                      tests/test_oracle_step.py::test_cfg_identical_prompts_equals_single
+  denoise_step        test_step_velocity_head_wiring_hand_derived; tests/test_oracle_step.py
+  to64                a cast (exact for bf16 and fp32 inputs)
 """
 from __future__ import annotations
 
@@ -38,15 +88,15 @@ from typing import Dict, Optional
 import numpy as np
 
 from .numerics import (quantize_rows_e4m3, round_e4m3, quant_scale_f32, E4M3_MAX, round_bf16,
-                       round_fp16, e4m3_tie_mask, quantize_mxfp4, dequantize_mxfp4)
+                       e4m3_tie_mask, quantize_mxfp4, dequantize_mxfp4)
 
 __all__ = [
     "sigmas", "timestep_sinusoid", "silu", "gelu_tanh", "layer_norm", "modulate",
     "linear", "rope_table", "apply_rope", "attention", "attention_naive",
-    "double_block", "double_block_rows", "single_block", "final_layer", "fbcache_rel",
+    "double_block", "double_block_rows", "single_block", "single_block_rows", "final_layer", "fbcache_rel",
     "fbcache_decide", "fbcache_policy", "euler_update", "cfg_combine", "time_embed",
     "modulation_vectors", "denoise_step", "FBCacheState", "to64",
-    "linear_fp8", "linear_mxfp4", "attention_fp8", "image_positions",
+    "linear_fp8", "linear_fp8_codes", "linear_mxfp4", "attention_fp8", "image_positions",
 ]
 
 LN_EPS = 1e-6
@@ -239,9 +289,17 @@ def linear_fp8(x, w, b):
     shp = x.shape
     x2 = x.reshape(-1, shp[-1])
     qx, sx = quantize_rows_e4m3(x2)
-    qw, sw = quantize_rows_e4m3(w)
-    y = (qx @ qw.T) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + b
+    y = linear_fp8_codes(qx, sx, w, b)
     return y.reshape(*shp[:-1], w.shape[0])
+
+
+def linear_fp8_codes(qx, sx, w, b):
+    """The product half of ``linear_fp8``: activations already quantised (e4m3
+    values qx [M, K] with row scales sx [M]) times the per-channel e4m3 weight,
+    dequantised, in fp64, plus the bias."""
+    qw, sw = quantize_rows_e4m3(w)
+    return (np.asarray(qx, np.float64) @ qw.T) * np.asarray(sx, np.float64)[:, None] \
+        * sw.astype(np.float64)[None, :] + b
 
 
 def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
@@ -298,11 +356,12 @@ def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
 # blocks
 # --------------------------------------------------------------------------
 
-def _held(x, fp8, rounding=round_bf16):
-    """fp8 blocks (R33): an activation that is quantised to e4m3 later is first
-    rounded to the 16-bit format it is stored in between the two steps (bf16;
-    fp16 for V), so each e4m3 code is decided on the stored value."""
-    return rounding(x) if fp8 else x
+def _held(x, fp8):
+    """fp8 blocks (R33): every activation between two steps of a bf16 model is
+    stored in bf16, so one that is quantised to e4m3 later (Q, K, V, attention
+    output, GELU output) is rounded to bf16 first and each e4m3 code is decided
+    on that stored value."""
+    return round_bf16(x) if fp8 else x
 
 
 def _lin(x, P, name, fp8, mx4=False):
@@ -336,7 +395,7 @@ def double_block(x_txt, x_img, mod_img, mod_txt, P, ang, H, fp8=False, mx4=False
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
     q = _held(apply_rope(_heads(q, H), ang), a8)
     k = _held(apply_rope(_heads(k, H), ang), a8)
-    a = _held(_merge(attn_fn(q, k, _held(_heads(v, H), a8, round_fp16))), a8)
+    a = _held(_merge(attn_fn(q, k, _held(_heads(v, H), a8))), a8)
     out = {}
     for s, (x, m) in streams.items():
         a_s = a[:, :Lt] if s == "txt" else a[:, Lt:]
@@ -373,7 +432,7 @@ def double_block_rows(x_txt, x_img, mod_img, mod_txt, P, ang, H, rows, fp8=False
     v = np.concatenate([qkv["txt"][..., 2 * D:], qkv["img"][..., 2 * D:]], axis=1)
     q = _held(apply_rope(_heads(q, H), ang), a8)
     k = _held(apply_rope(_heads(k, H), ang), a8)
-    vh = _held(_heads(v, H), a8, round_fp16)
+    vh = _held(_heads(v, H), a8)
     if a8:
         a = attn_fn(q, k, vh, rows=rows)
     else:
@@ -406,10 +465,34 @@ def single_block(x, mod, P, ang, H, fp8=False, mx4=False, attn8=False):
     h = _lin(u, P, "lin1", fp8, mx4)
     q = _held(apply_rope(_heads(h[..., :D], H), ang), a8)
     k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), a8)
-    v = _held(_heads(h[..., 2 * D:3 * D], H), a8, round_fp16)
+    v = _held(_heads(h[..., 2 * D:3 * D], H), a8)
     a = _merge(attn_fn(q, k, v))
     cat = _held(np.concatenate([a, gelu_tanh(h[..., 3 * D:])], axis=-1), fp8)
     return x + mod[:, 2:3] * _lin(cat, P, "lin2", fp8, mx4)
+
+
+def single_block_rows(x, mod, P, ang, H, rows, fp8=False, mx4=False, attn8=False):
+    """The single-stream block's output for the joint token rows ``rows`` only
+    -> [B, len(rows), D].
+
+    Every token's linear1 output is computed (attention needs all keys and
+    values, and fp8 Q / K / V scales span whole heads); attention, the GELU half
+    and linear2 then run for the selected rows alone.  A row's update depends on
+    its own row and on the keys and values only, so the result equals
+    ``single_block`` at those rows.
+    """
+    a8 = fp8 or attn8
+    attn_fn = attention_fp8 if a8 else attention
+    D = x.shape[-1]
+    rows = np.asarray(rows)
+    u = modulate(x, mod[:, 0:1], mod[:, 1:2])
+    h = _lin(u, P, "lin1", fp8, mx4)
+    q = _held(apply_rope(_heads(h[..., :D], H), ang), a8)
+    k = _held(apply_rope(_heads(h[..., D:2 * D], H), ang), a8)
+    v = _held(_heads(h[..., 2 * D:3 * D], H), a8)
+    a = attn_fn(q, k, v, rows=rows) if a8 else attn_fn(q[:, :, rows], k, v)
+    cat = _held(np.concatenate([_merge(a), gelu_tanh(h[:, rows, 3 * D:])], axis=-1), fp8)
+    return x[:, rows] + mod[:, 2:3] * _lin(cat, P, "lin2", fp8, mx4)
 
 
 def final_layer(x_img, shift, scale, w, b):

@@ -23,6 +23,21 @@ to +-448 and a scale of amax/448 (amax = 0 gives scale 1).  The 4-bit variant
 Klein, and the diffusion-backend commit picks nvfp4 / fp8 / mxfp8 by GPU
 generation) is taken as MXFP4, gfx950's block-scaled FP4, with
 round-to-nearest-even.
+
+Pins (tests/test_oracle_pins.py):
+  round_bf16          test_bf16_rounding_vs_torch_cast
+  round_fp16          test_fp16_rounding_vs_numpy_cast
+  round_e4m3          test_e4m3_code_table_bruteforce (all 256 codes),
+                      test_e4m3_golden_points (tests/golden/e4m3_points.txt),
+                      test_e4m3_representable_values_are_fixed_points
+  e4m3_tie_mask       test_e4m3_tie_mask_against_code_table
+  quant_scale_f32,    test_quantize_rows_scale_and_roundtrip
+  quantize_rows_e4m3,
+  quantize_cols_e4m3
+  round_e2m1          test_e2m1_rounding_cases, test_e2m1_value_set
+  mx_block_exponent   test_mx_block_exponent_cases
+  quantize_mxfp4,     test_mxfp4_reproduces_representable_blocks, test_mxfp4_error_bound
+  dequantize_mxfp4
 """
 from __future__ import annotations
 

@@ -475,6 +475,198 @@ def test_single_block_zero_gate_and_wiring():
                                x + mod[:, 2:3] * (mlp + P["lin2.b"]), atol=1e-13)
 
 
+
+def _single_block_by_hand(x, mod, P, H, pos, swap_qk=False):
+    """The single-stream block written out token by token (R10): lin1's output
+    columns are q | k | v | MLP-in, RoPE turns q and k only, lin2 reads
+    [attention out, GELU(MLP-in)].  swap_qk plants the q/k column mix-up."""
+    L, D = x.shape
+    d = D // H
+
+    def ln(u):
+        mu = sum(u) / len(u)
+        var = sum((t - mu) ** 2 for t in u) / len(u)
+        return [(t - mu) / math.sqrt(var + 1e-6) for t in u]
+
+    def lin(u, w, b):
+        return [sum(u[k] * w[n][k] for k in range(len(u))) + b[n] for n in range(len(b))]
+
+    def rot(vec, p):
+        out = list(vec)
+        for pr in range(d // 2):
+            ax = 0 if pr < d // 4 else 1
+            j = pr % (d // 4)
+            th = p[ax] * 10000.0 ** (-j / (d // 4))
+            a, b = vec[2 * pr], vec[2 * pr + 1]
+            out[2 * pr] = a * math.cos(th) - b * math.sin(th)
+            out[2 * pr + 1] = a * math.sin(th) + b * math.cos(th)
+        return out
+
+    gelu = lambda z: 0.5 * z * (1 + math.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+    qs, ks, vs, ms = [], [], [], []
+    for t in range(L):
+        u = [ln(list(x[t]))[c] * (1 + mod[1][c]) + mod[0][c] for c in range(D)]
+        h = lin(u, P["lin1.w"], P["lin1.b"])
+        q, k = (h[D:2 * D], h[:D]) if swap_qk else (h[:D], h[D:2 * D])
+        qs.append(q); ks.append(k); vs.append(h[2 * D:3 * D]); ms.append(h[3 * D:])
+    att = [[0.0] * D for _ in range(L)]
+    for hh in range(H):
+        sl = slice(hh * d, (hh + 1) * d)
+        qh = [rot(qs[t][sl], pos[t]) for t in range(L)]
+        kh = [rot(ks[t][sl], pos[t]) for t in range(L)]
+        for t in range(L):
+            s = [sum(a * b for a, b in zip(qh[t], kh[u])) / math.sqrt(d) for u in range(L)]
+            mx = max(s)
+            e = [math.exp(z - mx) for z in s]
+            z = sum(e)
+            for c in range(d):
+                att[t][hh * d + c] = sum(e[u] * vs[u][sl][c] for u in range(L)) / z
+    out = []
+    for t in range(L):
+        y = lin(att[t] + [gelu(z) for z in ms[t]], P["lin2.w"], P["lin2.b"])
+        out.append([x[t][c] + mod[2][c] * y[c] for c in range(D)])
+    return np.array(out)
+
+
+def test_single_block_brute_force_small():
+    # the single-stream block's attention half written out by hand: catches a
+    # q / k / v column mix-up in linear1, RoPE on v (or not on k), a wrong head
+    # split or a swapped [attention, GELU] order in linear2's input
+    rng = np.random.default_rng(16)
+    D, H, F, Lt, gh, gw = 8, 2, 16, 2, 2, 2
+    L = Lt + gh * gw
+    P = {"lin1.w": rng.standard_normal((3 * D + F, D)) * 0.4,
+         "lin1.b": rng.standard_normal(3 * D + F) * 0.1,
+         "lin2.w": rng.standard_normal((D, D + F)) * 0.3,
+         "lin2.b": rng.standard_normal(D) * 0.1}
+    x = rng.standard_normal((1, L, D))
+    mod = rng.standard_normal((1, 3, D)) * 0.3
+    pos = [(0, 0)] * Lt + [(r, c) for r in range(gh) for c in range(gw)]
+    ang = O.rope_table(O.image_positions(gh, gw, Lt), D // H)
+    got = O.single_block(x, mod, P, ang, H)[0]
+    ref = _single_block_by_hand(x[0], mod[0], P, H, pos)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    # the hand version is sensitive to the planted q / k swap
+    bad = _single_block_by_hand(x[0], mod[0], P, H, pos, swap_qk=True)
+    assert np.max(np.abs(bad - ref)) > 1e-3
+
+
+def test_time_embed_hand_derived():
+    # one-hot rows pick single sinusoid entries, so the timestep MLP reduces to
+    # closed forms: catches [sin, cos] order, a wrong frequency exponent or time
+    # scale, and SiLU misplaced (after the second linear, or missing)
+    D = 4
+    w1 = np.zeros((D, 256)); b1 = np.array([0.5, 0.0, -0.25, 0.1])
+    w1[0, 0] = 2.0        # cos, k = 0
+    w1[1, 128] = -3.0     # sin, k = 0
+    w1[2, 5] = 1.5        # cos, k = 5
+    w1[3, 255] = 4.0      # sin, k = 127
+    w2 = np.array([[0.0, 1.5, 0.0, 0.0],
+                   [1.0, 0.0, -1.0, 0.0],
+                   [0.0, 0.0, 0.0, 2.0],
+                   [0.5, 0.5, 0.5, 0.5]])
+    b2 = np.array([0.25, -0.5, 0.0, 1.0])
+    P = {"time.w1": w1, "time.b1": b1, "time.w2": w2, "time.b2": b2}
+    silu = lambda z: z / (1.0 + math.exp(-z))
+    for t in (0.0, 0.3, 1.0):
+        a0 = 1000.0 * t
+        a5 = 1000.0 * t * 10000.0 ** (-5 / 128)
+        a127 = 1000.0 * t * 10000.0 ** (-127 / 128)
+        h = [silu(2.0 * math.cos(a0) + 0.5), silu(-3.0 * math.sin(a0)),
+             silu(1.5 * math.cos(a5) - 0.25), silu(4.0 * math.sin(a127) + 0.1)]
+        want = [1.5 * h[1] + 0.25, h[0] - h[2] - 0.5, 2.0 * h[3], 0.5 * sum(h) + 1.0]
+        got = O.time_embed(P, np.array([t]))[0]
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_final_layer_hand_derived():
+    # rows with a known LayerNorm: [1,-1,1,-1] normalises to itself / sqrt(1 + eps),
+    # a constant row to zero.  One-hot output rows then read single modulated
+    # entries: catches shift / scale swapped, a missing (1 + scale) and the
+    # LN epsilon misplaced
+    x = np.array([[[1.0, -1.0, 1.0, -1.0], [2.0, 2.0, 2.0, 2.0]]])
+    shift = np.array([[[0.1, 0.2, 0.3, 0.4]]])
+    scale = np.array([[[1.0, 0.0, -1.0, 0.5]]])
+    w = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 1.0, 0.0], [0.0, 0.0, 0.0, -2.0]])
+    b = np.array([0.01, 0.02, 0.03])
+    n = 1.0 / math.sqrt(1.0 + 1e-6)
+    want = np.array([[[2.0 * n + 0.1 + 0.01, 0.0 * n + 0.3 + 0.02, -2.0 * (-1.0 * n * 1.5 + 0.4) + 0.03],
+                      [0.1 + 0.01, 0.3 + 0.02, -2.0 * 0.4 + 0.03]]])
+    got = O.final_layer(x, shift, scale, w, b)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_step_velocity_head_wiring_hand_derived():
+    # a whole oracle step whose blocks are identities (every gate 0) and whose
+    # final modulation is constant (weight 0, bias = [shift ; scale]): the
+    # velocity is then a closed form of the embedded latents, which pins the
+    # final layer's chunk order (shift first), its use of the image rows only
+    # and the Euler update's sign and step
+    import dit_inputs as DI
+    dims = DI.Dims(D=4, H=1, F=8, n_double=1, n_single=1, C_in=4)
+    w = DI.Workload("t", dims, B=1, grid_h=1, grid_w=2, Lt=2, dtype="f32", steps=2, shift=1.0)
+    rng = np.random.default_rng(17)
+    P = {}
+    for name, t in DI.iter_params(dims, "f32"):
+        P[name] = rng.standard_normal(tuple(t.shape)) * 0.1
+    for s in ("img", "txt"):
+        P[f"double0.{s}.mod.w"][:] = 0.0
+        P[f"double0.{s}.mod.b"][:] = 0.0       # gates 0: the double block is the identity
+    P["single0.mod.w"][:] = 0.0
+    P["single0.mod.b"][:] = 0.0                # gate 0: so is the single block
+    P["img_in.w"] = np.eye(4) * 2.0
+    P["img_in.b"] = np.zeros(4)
+    shift = np.array([0.1, 0.2, 0.3, 0.4]); scale = np.array([1.0, 0.0, -1.0, 0.5])
+    P["final.mod.w"][:] = 0.0
+    P["final.mod.b"] = np.concatenate([shift, scale])
+    P["final.out.w"] = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [0, 0, 1.0, 0], [0, 0, 0, 1.0]])
+    P["final.out.b"] = np.array([0.0, 0.5, 0.0, -0.5])
+    lat = np.array([[[0.5, -0.5, 0.5, -0.5], [1.0, 1.0, 1.0, 1.0]]])     # [1, Li = 2, C_in]
+    txt = rng.standard_normal((1, 2, 4))
+    sg = O.sigmas(2, 1.0)                                               # 1, 0.5, 0
+    new, info = O.denoise_step(P, dims, w, lat, txt, 0, sg)
+    n = 1.0 / math.sqrt(1.0 + 1e-6)
+    ln0 = np.array([n, -n, n, -n])                     # h = 2 lat = [1,-1,1,-1]
+    v0 = ln0 * (1.0 + scale) + shift + P["final.out.b"]
+    v1 = shift + P["final.out.b"]                       # constant row: LN = 0
+    np.testing.assert_allclose(info["v"][0], [v0, v1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(new[0], lat[0] - 0.5 * np.array([v0, v1]), rtol=0, atol=1e-14)
+
+
+
+@pytest.mark.parametrize("fp8,mx4", [(False, False), (True, False), (False, True)])
+def test_single_block_rows_equals_full_block(fp8, mx4):
+    rng = np.random.default_rng(18)
+    D, H, F, Lt, gh, gw, B = 64, 2, 256, 3, 4, 8, 2
+    L = Lt + gh * gw
+    P = {"lin1.w": rng.standard_normal((3 * D + F, D)) * 0.05,
+         "lin1.b": rng.standard_normal(3 * D + F) * 0.05,
+         "lin2.w": rng.standard_normal((D, D + F)) * 0.05,
+         "lin2.b": rng.standard_normal(D) * 0.05}
+    x = rng.standard_normal((B, L, D))
+    mod = rng.standard_normal((B, 3, D)) * 0.1
+    ang = O.rope_table(O.image_positions(gh, gw, Lt), D // H)
+    full = O.single_block(x, mod, P, ang, H, fp8=fp8, mx4=mx4)
+    rows = np.array([0, 2, Lt, Lt + 5, L - 1])
+    got = O.single_block_rows(x, mod, P, ang, H, rows, fp8=fp8, mx4=mx4)
+    np.testing.assert_allclose(got, full[:, rows], rtol=0, atol=1e-12)
+
+
+def test_modulation_vectors_hand_derived():
+    # SiLU is applied to c before the modulation linear, and the output is cut
+    # into D-wide chunks in order: catches a missing SiLU, SiLU after the linear
+    # and a transposed [chunk, D] split
+    D = 2
+    c = np.array([[1.0, -2.0]])
+    w = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 0.0], [0.0, -1.0], [1.0, 1.0], [0.0, 0.0]])
+    b = np.array([0.0, 0.0, 0.5, 0.0, 0.0, 0.25])
+    s1 = 1.0 / (1.0 + math.exp(-1.0))             # SiLU(1)
+    s2 = -2.0 / (1.0 + math.exp(2.0))             # SiLU(-2)
+    want = np.array([[[s1, s2], [2 * s1 + 0.5, -s2], [s1 + s2, 0.25]]])
+    got = O.modulation_vectors(c, w, b, D)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
 # ---------------------------------------------------------------- FBC
 
 def test_fbcache_rel_vs_python_loop():
