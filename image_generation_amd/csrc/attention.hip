@@ -1,6 +1,9 @@
-// Flash-style joint attention, bf16, for gfx950 (MFMA + LDS-staged K/V tiles).
+// Flash-style joint attention for gfx950 (MFMA + LDS-staged K/V tiles), bf16
+// and e4m3, head dim 64 or 128, any sequence length.
 //
 //   O[b, t, h*d + c] = sum_u softmax_u(Q[b,h,t] . K[b,h,u] * scale) V[b,h,u,c]
+//
+// Q, K and V arrive in the same layout, [B, H, L, d] row-major.
 //
 // Work split: one workgroup = 8 wave64s = 256 queries of one (b, h); each wave
 // owns 32 queries, two waves share a SIMD so one wave's softmax arithmetic runs
@@ -10,51 +13,135 @@
 // K rows are fed to the MFMA in the order (r with bits 2 and 3 swapped), which
 // makes the 8 score registers a lane holds per 16-key chunk correspond to 8
 // consecutive keys: exactly the B operand of the P V^T MFMA, so P never leaves
-// registers.  V arrives pre-transposed ([B, H, d, L], written that way by the
-// QKV projection epilogue), so its MFMA operand is a contiguous LDS read too.
-// The P V^T product runs in fp16 (V stored as fp16, P <= 2^8 converted to
-// fp16): the same MFMA rate as bf16 with three more mantissa bits on both
-// operands.
+// registers.
 //
-// Softmax reference max: exp2 is taken relative to a per-query reference m that
-// only moves when a tile's maximum exceeds it by more than 2^8 (in exp2 units);
-// otherwise P <= 256 and the rescale of O and of the row sum is skipped.  The
-// reference cancels exactly in O / l.
+// V^T operands without a transposed copy of V: a 64-key V tile sits in LDS row
+// by row (as loaded), and the A operand of O^T = V^T P^T is read with gfx950's
+// transposing LDS loads.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane
+// 4e + q of a group supplies 8 bytes (4 values) and lane 4q + r receives value r
+// of the lanes 4e + q, e = 0..3; so when lane 4e + q points at V[key0 + e]
+// [d0 + 4q .. + 3], lane j of the group receives keys key0 .. key0 + 3 of column
+// d0 + j, four consecutive K values of the MFMA operand row j.  The 8-bit form
+// does the same with 8 lanes' bytes: lane 2e + q supplies V[key0 + e][d0 + 8q ..
+// + 7] and lane 8q + r receives keys key0 .. key0 + 7 of column d0 + 8q + r.  (This
+// lane layout was measured on the GPU.)  The 16-byte chunks of each V row are
+// stored permuted by an XOR with a function of the key, chosen so that the 32
+// lanes one LDS cycle serves (4 keys x 64 bytes for bf16, 8 keys x 32 bytes for
+// e4m3) fall in 64 distinct banks.
+//
+// Softmax reference max (bf16): exp2 is taken relative to a per-query reference
+// m that only moves when a tile's maximum exceeds it by more than 2^8 (in exp2
+// units); otherwise P <= 256 and the rescale of O and of the row sum is
+// skipped.  The reference cancels exactly in O / l.  P enters P V^T as bf16.
 //
 // K/V tiles of 64 keys are double-buffered in LDS, filled by direct
-// global->LDS loads (each wave instruction writes 1 KB contiguously; padded rows
-// are filled by giving each lane the chunk that belongs at its slot).  Keys past
-// L are masked to -inf; queries past L are computed on clamped rows, not stored.
+// global->LDS loads (each wave instruction writes 1 KB contiguously; the padded
+// K rows and the permuted V rows are built by giving each lane the chunk that
+// belongs at its slot).  Keys past L load row L - 1 and are masked to -inf;
+// queries past L are computed on clamped rows and not stored.
 #include "common.h"
 #include "kernels.h"
 
 namespace dit {
 
-constexpr int ATT_D = 128;          // head dim handled by this kernel
 constexpr int ATT_BN = 64;          // keys per tile
 constexpr int ATT_QW = 32;          // queries per wave
 constexpr int ATT_WAVES = 8;
 constexpr int ATT_BM = ATT_QW * ATT_WAVES;
-constexpr int ATT_KS = ATT_D + 8;   // padded K row (bf16): 272 B = 17 chunks
-constexpr int ATT_VS = ATT_BN + 8;  // padded V^T row (fp16): 144 B = 9 chunks
-constexpr int ATT_KB = ATT_BN * ATT_KS * 2;     // K tile bytes (17 KB)
-constexpr int ATT_VB = ATT_D * ATT_VS * 2;      // V^T tile bytes (18 KB)
-constexpr int ATT_SB = ATT_KB + ATT_VB;         // stage bytes
-constexpr int ATT_NI = ATT_SB / 1024;           // 1-KB load instructions per stage
-static_assert(ATT_KB % 1024 == 0 && ATT_VB % 1024 == 0, "stage must be whole 1-KB loads");
 constexpr float ATT_RESCALE_LOG2 = 8.0f;        // P stays <= 2^8 between rescales
+
+typedef short s16x4v __attribute__((vector_size(8)));
+typedef int i32x2v __attribute__((vector_size(8)));
+typedef short s16x8v __attribute__((vector_size(16)));
+#define DIT_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Transposing LDS reads (see above); p is each lane's own 8-byte source.
+__device__ __forceinline__ s16x4v lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(DIT_LDS(s16x4v, (char*)p));
+}
+__device__ __forceinline__ i32x2v lds_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(DIT_LDS(i32x2v, (char*)p));
+}
 
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Tile geometry.  ES: element bytes (2 bf16, 1 e4m3).  K rows are padded by 16
+// bytes (an odd number of 16-byte chunks per 64 banks for the row-wise fragment
+// reads); V rows are unpadded with permuted chunks.
+template <int D, int ES>
+struct AttGeo {
+  static constexpr int KROW = D * ES + 16;
+  static constexpr int KC = KROW / 16;
+  static constexpr int VROW = D * ES;
+  static constexpr int VC = VROW / 16;
+  static constexpr int KB = ATT_BN * KROW;
+  static constexpr int VB = ATT_BN * VROW;
+  static constexpr int SB = KB + VB;
+  static constexpr int KI = KB / 1024;                     // K load instructions
+  static constexpr int NI = SB / 1024;                     // per stage
+  static constexpr int IPW = (NI + ATT_WAVES - 1) / ATT_WAVES;
+  static_assert(KB % 1024 == 0 && VB % 1024 == 0, "stage must be whole 1-KB loads");
+  // chunk permutation of V row `key` (XOR on the 16-byte chunk index)
+  static __device__ __forceinline__ int vswz(int key) {
+    if constexpr (ES == 2) return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+    else return D == 128 ? 2 * ((key >> 1) & 3) : 2 * ((key >> 2) & 1);
+  }
+};
+
+// Per-lane source offsets (elements) of a stage's direct-to-LDS loads: wave w issues
+// load instructions w, w + 8, ...; instruction i < KI fills K rows, the rest V rows.
+template <int D, int ES>
+struct AttLoads {
+  using G = AttGeo<D, ES>;
+  int doff[G::IPW];   // row * D + chunk * (16 / ES)
+  int dkv[G::IPW];    // key row inside the tile
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < G::IPW; ++j) {
+      const int inst = wave + j * ATT_WAVES;
+      const int c = inst * 64 + lane;
+      int row, chunk;
+      if (inst < G::KI) {
+        row = c / G::KC;
+        chunk = min(c - row * G::KC, G::VC - 1);   // the pad slot repeats the last chunk
+      } else {
+        const int c2 = c - G::KI * 64;
+        row = c2 / G::VC;
+        chunk = (c2 - row * G::VC) ^ G::vswz(row);
+      }
+      doff[j] = row * D + chunk * (16 / ES);
+      dkv[j] = row;
+    }
+  }
+  // K and V tile kt of one (b, h) into `stage`; rows past L load row L - 1
+  template <class T>
+  __device__ __forceinline__ void issue(char* stage, const T* Kb, const T* Vb, int kt, int L,
+                                        int wave) const {
+    const int kv0 = kt * ATT_BN;
+    const bool full = kv0 + ATT_BN <= L;
+#pragma unroll
+    for (int j = 0; j < G::IPW; ++j) {
+      const int inst = wave + j * ATT_WAVES;
+      if (inst >= G::NI) break;
+      const T* base = inst < G::KI ? Kb : Vb;
+      const T* src = base + (size_t)kv0 * D + doff[j];
+      if (!full && kv0 + dkv[j] > L - 1) src = base + (size_t)(L - 1) * D + (doff[j] - dkv[j] * D);
+      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(stage + inst * 1024), 16, 0, 0);
+    }
+  }
+};
+
+template <int D>
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const f16_t* __restrict__ VT,
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
     const int* __restrict__ gate) {
+  using G = AttGeo<D, 2>;
   if (gate_closed(gate)) return;
-  __shared__ __attribute__((aligned(1024))) char st0[ATT_SB];
-  __shared__ __attribute__((aligned(1024))) char st1[ATT_SB];
+  __shared__ __attribute__((aligned(1024))) char st0[G::SB];
+  __shared__ __attribute__((aligned(1024))) char st1[G::SB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,88 +160,53 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   const int b = bh / H;
   const int h = bh - b * H;
 
-  const bf16_t* Qb = Q + (size_t)bh * L * ATT_D;
-  const bf16_t* Kb = K + (size_t)bh * L * ATT_D;
-  const f16_t* Vb = VT + (size_t)bh * ATT_D * L;
+  const bf16_t* Qb = Q + (size_t)bh * L * D;
+  const bf16_t* Kb = K + (size_t)bh * L * D;
+  const bf16_t* Vb = V + (size_t)bh * L * D;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[q][c*16 + g*8 .. +8]
   const int q0 = qt * ATT_BM + wave * ATT_QW;
-  bf16x8 qf[ATT_D / 16];
+  bf16x8 qf[D / 16];
   {
     const int qr = min(q0 + l32, L - 1);
 #pragma unroll
-    for (int c = 0; c < ATT_D / 16; ++c)
-      qf[c] = *(const bf16x8*)(Qb + (size_t)qr * ATT_D + c * 16 + g * 8);
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = *(const bf16x8*)(Qb + (size_t)qr * D + c * 16 + g * 8);
   }
 
-  f32x16 oacc[ATT_D / 32];   // O^T blocks, one per 32 head channels
+  f32x16 oacc[D / 32];   // O^T blocks, one per 32 head channels
 #pragma unroll
-  for (int db = 0; db < ATT_D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float mref = -INFINITY;     // reference max (raw score units)
   float lsum = 0.f;           // this lane's partial row sum, relative to mref
 
-  // ---- direct-to-LDS loads of a K / V^T tile pair.  Chunk c of a stage: the
-  // first 64*17 chunks are K rows (16 data chunks + 1 pad) = load instructions
-  // 0..16, then 128*9 V^T rows = instructions 17..34.  Wave w issues
-  // instructions w, w+8, ...; each lane's source offset inside a tile is fixed,
-  // so it is computed once here.
-  constexpr int ATT_KI = ATT_BN * 17 / 64;        // K instructions (17)
-  constexpr int ATT_IPW = (ATT_NI + ATT_WAVES - 1) / ATT_WAVES;
-  static_assert(ATT_BN * 17 % 64 == 0, "K part must be whole instructions");
-  int doff[ATT_IPW];   // K: row*128 + slot*8 ; V^T: row*L + slot*8
-  int dkv[ATT_IPW];    // K: key row in tile ; V^T: first key of the chunk in tile
+  AttLoads<D, 2> ld;
+  ld.init(wave, lane);
+
+  // transposing V reads: lane 4e + q of its 16-lane group sources key
+  // (chunk base) + e, channels db*32 + (group & 1)*16 + 4q .. + 3
+  const int tg = lane >> 4, ts = lane & 15, te = ts >> 2, tq = ts & 3;
+  const int vsw = G::vswz(te);   // the rows a lane sources are all = te (mod 4)
+  int vbase[D / 32];
 #pragma unroll
-  for (int j = 0; j < ATT_IPW; ++j) {
-    const int inst = wave + j * ATT_WAVES;
-    const int c = inst * 64 + lane;
-    if (inst < ATT_KI) {
-      const int row = c / 17;
-      const int slot = min(c - row * 17, 15);
-      doff[j] = row * ATT_D + slot * 8;
-      dkv[j] = row;
-    } else {
-      const int c2 = c - ATT_BN * 17;
-      const int row = c2 / 9;
-      const int slot = min(c2 - row * 9, 7);
-      doff[j] = row * L + slot * 8;
-      dkv[j] = slot * 8;
-    }
-  }
-  auto issue_tile = [&](char* stage, int kt) {
-    const int kv0 = kt * ATT_BN;
-    const bool full = kv0 + ATT_BN <= L;
-#pragma unroll
-    for (int j = 0; j < ATT_IPW; ++j) {
-      const int inst = wave + j * ATT_WAVES;
-      if (inst >= ATT_NI) break;
-      const void* src;
-      if (inst < ATT_KI) {
-        src = Kb + (size_t)kv0 * ATT_D + doff[j];
-        if (!full && kv0 + dkv[j] > L - 1)   // tail tile: clamp the key row
-          src = Kb + (size_t)(L - 1) * ATT_D + (doff[j] - dkv[j] * ATT_D);
-      } else {
-        src = Vb + kv0 + doff[j];
-        if (!full && kv0 + dkv[j] > L - 8)   // tail tile: clamp the key chunk
-          src = Vb + (L - 8) + (doff[j] - dkv[j]);
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(stage + inst * 1024), 16, 0, 0);
-    }
-  };
+  for (int db = 0; db < D / 32; ++db)
+    vbase[db] = (g * 8 + te) * G::VROW +
+                (((4 * db + 2 * (tg & 1) + (tq >> 1)) ^ vsw) << 4) + 8 * (tq & 1);
 
   const int ntiles = (L + ATT_BN - 1) / ATT_BN;
   const int krow_perm = swap23(l32);
-  issue_tile(st0, 0);
+  ld.issue(st0, Kb, Vb, 0, L, wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     char* cur = (kt & 1) ? st1 : st0;
     char* nxt = (kt & 1) ? st0 : st1;
-    if (kt + 1 < ntiles) issue_tile(nxt, kt + 1);
-    const bf16_t* sK = (const bf16_t*)cur;
-    const f16_t* sV = (const f16_t*)(cur + ATT_KB);
+    if (kt + 1 < ntiles) ld.issue(nxt, Kb, Vb, kt + 1, L, wave);
+    const char* sK = cur;
+    const char* sV = cur + G::KB;
     const int kv0 = kt * ATT_BN;
 
     // S^T for 2 key blocks of 32
@@ -164,10 +216,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-    for (int c = 0; c < ATT_D / 16; ++c) {
+    for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)&sK[(kb * 32 + krow_perm) * ATT_KS + c * 16 + g * 8];
+        const bf16x8 kf = *(const bf16x8*)(sK + (kb * 32 + krow_perm) * G::KROW + c * 32 + g * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
       }
     }
@@ -198,33 +250,38 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
       mref = mnew;
       lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < ATT_D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
     const float moff = mref * scale_log2;
-    f16x8 pf[4];   // [16-key chunk]
+    bf16x8 pf[4];   // [16-key chunk]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        f16x8 t;
+        bf16x8 t;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pv = fast_exp2(fmaf(sacc[kb][ch * 8 + e], scale_log2, -moff));
           lsum += pv;
-          t[e] = (_Float16)pv;
+          t[e] = (__bf16)pv;
         }
         pf[kb * 2 + ch] = t;
       }
 
-    // O^T += V^T P^T over the 4 chunks of 16 keys
+    // O^T += V^T P^T over the 4 chunks of 16 keys; the V^T fragment of chunk ch
+    // (keys ch*16 + g*8 .. + 7 of channel db*32 + l32) is two transposing reads
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
-      for (int db = 0; db < ATT_D / 32; ++db) {
-        const f16x8 vf = *(const f16x8*)&sV[(db * 32 + l32) * ATT_VS + ch * 16 + g * 8];
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ch], oacc[db], 0, 0, 0);
+      for (int db = 0; db < D / 32; ++db) {
+        const char* vp = sV + vbase[db] + ch * 16 * G::VROW;
+        const s16x4v lo = lds_tr16(vp);
+        const s16x4v hi = lds_tr16(vp + 4 * G::VROW);
+        const s16x8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[ch],
+                                                           oacc[db], 0, 0, 0);
       }
     }
 
@@ -238,9 +295,9 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   const float inv = 1.0f / lt;
   const int t = q0 + l32;
   if (t < L) {
-    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * ATT_D;
+    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * D;
 #pragma unroll
-    for (int db = 0; db < ATT_D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int dd = db * 32 + e4 * 8 + g * 4;
@@ -253,13 +310,14 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 }
 
 // ---------------------------------------------------------------- fp8 (e4m3)
-// Same work split.  Q, K, V^T are e4m3 with one scale per (b, h) each, so the
+// Same work split.  Q, K, V are e4m3 with one scale per (b, h) each, so the
 // score scale sq * sk folds into the exp2 constant and sv into the final
 // normalisation.  S^T uses v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales):
 // for key block kb the MFMA row r is fed K row  g(r)*32 + kb*16 + i(r),
 // g(r) = (r/4)&1, i(r) = (r/8)*4 + r%4, so a lane's 32 score registers over the
 // 64-key tile are the 32 consecutive keys its lane group needs as the P operand
-// of the fp8 P V^T MFMA.
+// of the fp8 P V^T MFMA; that operand's V^T fragment (channel db*32 + l32, keys
+// g*32 .. + 31) is four 8-bit transposing reads.
 //
 // Softmax reference: in exp2 units the running row max is rounded up to an
 // integer r, so P = 2^(t - r) <= 1 and 448 P never saturates e4m3.  When r
@@ -268,24 +326,16 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 // matches quantising against the final row max rounded the same way.  The row
 // sum is that of the quantised P, taken by one more MFMA of the P codes against
 // an all-ones operand, so the weights that multiply V sum to one.
-constexpr int AF8_BN = 64;
-constexpr int AF8_KRB = 144;                      // K row: 128 B + 16 pad (9 chunks)
-constexpr int AF8_VRB = 80;                       // V^T row: 64 B + 16 pad (5 chunks)
-constexpr int AF8_KB = AF8_BN * AF8_KRB;          // 9 KB
-constexpr int AF8_VB = ATT_D * AF8_VRB;           // 10 KB
-constexpr int AF8_SB = AF8_KB + AF8_VB;
-constexpr int AF8_NI = AF8_SB / 1024;             // 19 load instructions per stage
-constexpr int AF8_KI = AF8_KB / 1024;             // 9 of them for K
-static_assert(AF8_KB % 1024 == 0 && AF8_VB % 1024 == 0, "whole 1-KB loads");
-
+template <int D>
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
-    const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ VT,
+    const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ V,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
     bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
     const int* __restrict__ gate) {
+  using G = AttGeo<D, 1>;
   if (gate_closed(gate)) return;
-  __shared__ __attribute__((aligned(1024))) char st0[AF8_SB];
-  __shared__ __attribute__((aligned(1024))) char st1[AF8_SB];
+  __shared__ __attribute__((aligned(1024))) char st0[G::SB];
+  __shared__ __attribute__((aligned(1024))) char st1[G::SB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -303,27 +353,27 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   const int b = bh / H;
   const int h = bh - b * H;
 
-  const fp8_t* Qb = Q + (size_t)bh * L * ATT_D;
-  const fp8_t* Kb = K + (size_t)bh * L * ATT_D;
-  const fp8_t* Vb = VT + (size_t)bh * ATT_D * L;
+  const fp8_t* Qb = Q + (size_t)bh * L * D;
+  const fp8_t* Kb = K + (size_t)bh * L * D;
+  const fp8_t* Vb = V + (size_t)bh * L * D;
   const float cs = scale_log2 * sq[bh] * sk[bh];   // raw score -> exp2 units
 
-  // Q fragments: lane holds Q[q][c*64 + g*32 .. +32], c = 0, 1
+  // Q fragments: lane holds Q[q][c*64 + g*32 .. +32]
   const int q0 = qt * ATT_BM + wave * ATT_QW;
-  i32x8 qf[2];
+  i32x8 qf[D / 64];
   {
     const int qr = min(q0 + l32, L - 1);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const i32x4 lo = *(const i32x4*)(Qb + (size_t)qr * ATT_D + c * 64 + g * 32);
-      const i32x4 hi = *(const i32x4*)(Qb + (size_t)qr * ATT_D + c * 64 + g * 32 + 16);
+    for (int c = 0; c < D / 64; ++c) {
+      const i32x4 lo = *(const i32x4*)(Qb + (size_t)qr * D + c * 64 + g * 32);
+      const i32x4 hi = *(const i32x4*)(Qb + (size_t)qr * D + c * 64 + g * 32 + 16);
       qf[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
 
-  f32x16 oacc[ATT_D / 32];
+  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int db = 0; db < ATT_D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float mref = -INFINITY;    // integer-valued reference, exp2 units
@@ -335,61 +385,32 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
                            0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
-  // per-lane load offsets (bytes inside a tile): K chunk c -> row c/9, slot c%9;
-  // V^T chunk c2 -> row c2/5, slot c2%5 (the last slot of a row is padding)
-  constexpr int IPW = (AF8_NI + ATT_WAVES - 1) / ATT_WAVES;
-  int doff[IPW], dkv[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int inst = wave + j * ATT_WAVES;
-    const int c = inst * 64 + lane;
-    if (inst < AF8_KI) {
-      const int row = c / 9;
-      const int slot = min(c - row * 9, 7);
-      doff[j] = row * ATT_D + slot * 16;
-      dkv[j] = row;
-    } else {
-      const int c2 = c - AF8_KI * 64;
-      const int row = c2 / 5;
-      const int slot = min(c2 - row * 5, 3);
-      doff[j] = row * L + slot * 16;
-      dkv[j] = slot * 16;
-    }
-  }
-  auto issue_tile = [&](char* stage, int kt) {
-    const int kv0 = kt * AF8_BN;
-    const bool full = kv0 + AF8_BN <= L;
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int inst = wave + j * ATT_WAVES;
-      if (inst >= AF8_NI) break;
-      const fp8_t* src;
-      if (inst < AF8_KI) {
-        src = Kb + (size_t)kv0 * ATT_D + doff[j];
-        if (!full && kv0 + dkv[j] > L - 1)
-          src = Kb + (size_t)(L - 1) * ATT_D + (doff[j] - dkv[j] * ATT_D);
-      } else {
-        src = Vb + kv0 + doff[j];
-        if (!full && kv0 + dkv[j] > L - 16) src = Vb + (L - 16) + (doff[j] - dkv[j]);
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(stage + inst * 1024), 16, 0, 0);
-    }
-  };
+  AttLoads<D, 1> ld;
+  ld.init(wave, lane);
 
-  const int ntiles = (L + AF8_BN - 1) / AF8_BN;
+  // transposing V reads: lane 2e + q of its 16-lane group sources key
+  // g*32 + 8t + e, channels db*32 + (group & 1)*16 + 8q .. + 7
+  const int tg = lane >> 4, ts = lane & 15, te = ts >> 1, tq = ts & 1;
+  const int vsw = G::vswz(te);   // the rows a lane sources are all = te (mod 8)
+  int vbase[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    vbase[db] = (g * 32 + te) * G::VROW + (((2 * db + (tg & 1)) ^ vsw) << 4) + 8 * tq;
+
+  const int ntiles = (L + ATT_BN - 1) / ATT_BN;
   // K row fed to MFMA row l32 of key block kb
   const int krow0 = ((l32 >> 2) & 1) * 32 + (l32 >> 3) * 4 + (l32 & 3);
-  issue_tile(st0, 0);
+  ld.issue(st0, Kb, Vb, 0, L, wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     char* cur = (kt & 1) ? st1 : st0;
     char* nxt = (kt & 1) ? st0 : st1;
-    if (kt + 1 < ntiles) issue_tile(nxt, kt + 1);
+    if (kt + 1 < ntiles) ld.issue(nxt, Kb, Vb, kt + 1, L, wave);
     const char* sK = cur;
-    const char* sV = cur + AF8_KB;
-    const int kv0 = kt * AF8_BN;
+    const char* sV = cur + G::KB;
+    const int kv0 = kt * ATT_BN;
 
     f32x16 sacc[2];
 #pragma unroll
@@ -397,8 +418,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const char* q_ = sK + (krow0 + kb * 16) * AF8_KRB + c * 64 + g * 32;
+      for (int c = 0; c < D / 64; ++c) {
+        const char* q_ = sK + (krow0 + kb * 16) * G::KROW + c * 64 + g * 32;
         const i32x4 lo = *(const i32x4*)q_, hi = *(const i32x4*)(q_ + 16);
         const i32x8 kf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[c], sacc[kb], 0, 0, 0,
@@ -406,7 +427,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
       }
     }
     // element e of sacc[kb] is key kv0 + g*32 + kb*16 + e of query column l32
-    if (kv0 + AF8_BN > L) {
+    if (kv0 + ATT_BN > L) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -428,7 +449,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
       mref = mnew;
       lacc *= alpha;
 #pragma unroll
-      for (int db = 0; db < ATT_D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
@@ -448,10 +469,11 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
       }
     const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
-    for (int db = 0; db < ATT_D / 32; ++db) {
-      const char* v_ = sV + (db * 32 + l32) * AF8_VRB + g * 32;
-      const i32x4 lo = *(const i32x4*)v_, hi = *(const i32x4*)(v_ + 16);
-      const i32x8 vf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int db = 0; db < D / 32; ++db) {
+      const char* vp = sV + vbase[db];
+      const i32x2v t0 = lds_tr8(vp), t1 = lds_tr8(vp + 8 * G::VROW);
+      const i32x2v t2 = lds_tr8(vp + 16 * G::VROW), t3 = lds_tr8(vp + 24 * G::VROW);
+      const i32x8 vf = i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[db], 0, 0, 0, 127,
                                                                  0, 127);
     }
@@ -463,9 +485,9 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   const float inv = sv[bh] / lacc[0];
   const int t = q0 + l32;
   if (t < L) {
-    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * ATT_D;
+    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * D;
 #pragma unroll
-    for (int db = 0; db < ATT_D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int dd = db * 32 + e4 * 8 + g * 4;
@@ -479,12 +501,13 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
 
 // ---------------------------------------------------------------- fp32
 // Reference-precision attention for small models (head dim 32 or 64): one wave
-// per 64 queries of one (b, h), one query per lane, 64-key K and V^T tiles in LDS
+// per 64 queries of one (b, h), one query per lane, 64-key K and V tiles in LDS
+// (V stored transposed there)
 // (every lane reads the same key, so the LDS reads broadcast); online softmax in
 // exp2 units with the scale folded into q.
 template <int HD>
 __global__ __launch_bounds__(64) void attention_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ VT,
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
     const int* __restrict__ gate) {
   if (gate_closed(gate)) return;
@@ -496,7 +519,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
   const int t = blockIdx.x * 64 + lane;
   const int tq = min(t, L - 1);
   const float* Kb = K + (size_t)bh * L * HD;
-  const float* Vb = VT + (size_t)bh * HD * L;
+  const float* Vb = V + (size_t)bh * L * HD;
   float q[HD], acc[HD];
 #pragma unroll
   for (int c = 0; c < HD; ++c) {
@@ -509,7 +532,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
 #pragma unroll
     for (int c = 0; c < HD; ++c) {
       sK[lane][c] = kr < L ? Kb[(size_t)kr * HD + c] : 0.f;
-      sV[c][lane] = kr < L ? Vb[(size_t)c * L + kr] : 0.f;
+      sV[c][lane] = kr < L ? Vb[(size_t)kr * HD + c] : 0.f;
     }
     __syncthreads();
     const int nk = min(64, L - k0);
@@ -548,7 +571,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
   }
 }
 
-hipError_t attention_f32(const float* q, const float* k, const float* vt, float* o, int ldo,
+hipError_t attention_f32(const float* q, const float* k, const float* v, float* o, int ldo,
                          const RowMap& map, int B, int H, int L, int d, float softmax_scale,
                          hipStream_t st) {
   if ((d != 32 && d != 64) || L < 1) return hipErrorInvalidValue;
@@ -557,39 +580,41 @@ hipError_t attention_f32(const float* q, const float* k, const float* vt, float*
   KTimerScope timer(KS_ATTENTION, st);
   const dim3 grid((L + 63) / 64, B * H);
   if (d == 64)
-    hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
+    hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(64), 0, st, q, k, v, o, ldo, map, H,
                        L, scale_log2, launch_gate());
   else
-    hipLaunchKernelGGL(attention_f32_kernel<32>, grid, dim3(64), 0, st, q, k, vt, o, ldo, map, H,
+    hipLaunchKernelGGL(attention_f32_kernel<32>, grid, dim3(64), 0, st, q, k, v, o, ldo, map, H,
                        L, scale_log2, launch_gate());
   return hipGetLastError();
 }
 
-hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, const float* sq,
+hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* v8, const float* sq,
                          const float* sk, const float* sv, bf16_t* o, int ldo, const RowMap& map,
                          int B, int H, int L, int d, float softmax_scale, hipStream_t st) {
-  if (d != ATT_D || L < 16 || L % 16) return hipErrorInvalidValue;
+  if ((d != 64 && d != 128) || L < 1) return hipErrorInvalidValue;
   const int nqt = (L + ATT_BM - 1) / ATT_BM;
   const int nblk = B * H * nqt;
   if (nblk == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   KTimerScope timer(KS_ATTENTION, st);
-  hipLaunchKernelGGL(attention_fp8_kernel, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q8, k8, vt8,
-                     sq, sk, sv, o, ldo, map, H, L, scale_log2, launch_gate());
+  auto kern = d == 128 ? attention_fp8_kernel<128> : attention_fp8_kernel<64>;
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q8, k8, v8, sq, sk, sv, o, ldo,
+                     map, H, L, scale_log2, launch_gate());
   return hipGetLastError();
 }
 
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf16_t* o,
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st) {
-  if (d != ATT_D || L < 8 || L % 8) return hipErrorInvalidValue;
+  if ((d != 64 && d != 128) || L < 1) return hipErrorInvalidValue;
   const int nqt = (L + ATT_BM - 1) / ATT_BM;
   const int nblk = B * H * nqt;
   if (nblk == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   KTimerScope timer(KS_ATTENTION, st);
-  hipLaunchKernelGGL(attention_bf16_kernel, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q, k, vt, o,
-                     ldo, map, H, L, scale_log2, launch_gate());
+  auto kern = d == 128 ? attention_bf16_kernel<128> : attention_bf16_kernel<64>;
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q, k, v, o, ldo, map, H, L,
+                     scale_log2, launch_gate());
   return hipGetLastError();
 }
 

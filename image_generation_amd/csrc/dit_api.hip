@@ -81,8 +81,6 @@ int make_dims(const dit_dims* in, Dims* o) {
   o->gw = in->grid_w;
   if (o->D % o->H) return fail(DIT_ERR_INVALID_ARG, "D %% H != 0");
   o->d = o->D / o->H;
-  if (o->Lt % 8 || o->Li % 8)
-    return fail(DIT_ERR_INVALID_ARG, "text and image token counts must be multiples of 8");
   if ((long long)o->B * o->L * (o->D + o->F) > (1LL << 31) - 1)
     return fail(DIT_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
   return DIT_OK;
@@ -100,17 +98,14 @@ int check_block_dims(const Dims& dm, int dtype) {
     if (dm.F % 4) return fail(DIT_ERR_UNSUPPORTED, "fp32 blocks: MLP size %d (multiple of 4)", dm.F);
     return DIT_OK;
   }
-  if (dm.d != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d (bf16/fp8 run 128)", dm.d);
+  if (dm.d != 64 && dm.d != 128)
+    return fail(DIT_ERR_UNSUPPORTED, "head dim %d (bf16/fp8 run 64 or 128)", dm.d);
   if (dm.F % 64) return fail(DIT_ERR_UNSUPPORTED, "MLP size %d (needs a multiple of 64)", dm.F);
-  if (dtype == DIT_FP8) {
-    // e4m3 K slabs are 128 deep; fp8 attention tiles keys by 16
-    if (dm.F % 128) return fail(DIT_ERR_UNSUPPORTED, "fp8: MLP size %d (multiple of 128)", dm.F);
-    if (dm.L % 16) return fail(DIT_ERR_UNSUPPORTED, "fp8: joint length %d (multiple of 16)", dm.L);
-  }
+  // e4m3 K slabs are 128 deep
+  if (dtype == DIT_FP8 && dm.F % 128)
+    return fail(DIT_ERR_UNSUPPORTED, "fp8: MLP size %d (multiple of 128)", dm.F);
   if ((dtype == DIT_MXFP4 || dtype == DIT_MXFP4_FP8ATTN) && dm.F % 256)   // 256-deep MX slabs
     return fail(DIT_ERR_UNSUPPORTED, "mxfp4: MLP size %d (multiple of 256)", dm.F);
-  if (dtype == DIT_MXFP4_FP8ATTN && dm.L % 16)
-    return fail(DIT_ERR_UNSUPPORTED, "fp8 attention: joint length %d (multiple of 16)", dm.L);
   return DIT_OK;
 }
 
@@ -130,15 +125,15 @@ struct Carver {
 struct BlockWS {
   float* xf;    // fp32 residual stream for a bf16-stored x [B, L, D]
   bf16_t* u;    // LN-modulate output [B*L, D] (row order of the block)
-  bf16_t* q;    // [B, H, L, d]
-  bf16_t* k;    // [B, H, L, d]
-  f16_t* vt;    // [B, H, d, L] fp16
+  bf16_t* q;    // [B, H, L, d] (rotated)
+  bf16_t* k;    // [B, H, L, d] (rotated)
+  bf16_t* v;    // [B, H, L, d]
   bf16_t* cat;  // [B*L, D + F]: attention output | MLP hidden
   // e4m3 operands of the fp8 blocks and their scales
   fp8_t* u8;    // [B*L, D], scale su [B*L]
   fp8_t* q8;    // [B, H, L, d]
   fp8_t* k8;    // [B, H, L, d]
-  fp8_t* v8;    // [B, H, d, L]
+  fp8_t* v8;    // [B, H, L, d]
   fp8_t* cat8;  // [B*L, D + F], scales s_att (attention part or whole row), s_hid
   float *su, *s_att, *s_hid;
   float* s_qkv;          // [3, B*H]: q, k, v scales per (b, h)
@@ -149,8 +144,8 @@ struct BlockWS {
   uint8_t* a4s;
   int mx_pad;            // scale rows: B*L rounded up to 256, plus 256 so a GEMM group
                          // starting inside the array reads whole 256-row tiles
-  // fp32 blocks (overlaying the buffers above): LN out, Q, K, V^T, attention | MLP
-  float *u32, *q32, *k32, *vt32, *cat32;
+  // fp32 blocks (overlaying the buffers above): LN out, Q, K, V, attention | MLP
+  float *u32, *q32, *k32, *v32, *cat32;
 };
 
 BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
@@ -163,7 +158,7 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.u = c.take<bf16_t>(n);
   w.q = c.take<bf16_t>(n);
   w.k = c.take<bf16_t>(n);
-  w.vt = c.take<f16_t>(n);
+  w.v = c.take<bf16_t>(n);
   w.cat = c.take<bf16_t>(rows * (dm.D + dm.F));
   w.u8 = c.take<fp8_t>(n);
   w.q8 = c.take<fp8_t>(n);
@@ -181,7 +176,7 @@ BlockWS carve_block(Carver& c, const Dims& dm, bool with_xf) {
   w.u32 = c32.take<float>(n);
   w.q32 = c32.take<float>(n);
   w.k32 = c32.take<float>(n);
-  w.vt32 = c32.take<float>(n);
+  w.v32 = c32.take<float>(n);
   w.cat32 = c32.take<float>(rows * (dm.D + dm.F));
   if (c32.off > c.off) c.off = c32.off;
   return w;
@@ -333,7 +328,7 @@ hipError_t block_f32(const Dims& dm, const dit_block& blk, float* x, const float
                      const float* rope, const BlockWS& w, hipStream_t st) {
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
   const int DF = D + F;
-  const QKVOut32 qo{w.q32, w.k32, w.vt32, rope, D, dm.H, dm.d};
+  const QKVOut32 qo{w.q32, w.k32, w.v32, rope, D, dm.H, dm.d};
   const float scale = 1.0f / sqrtf((float)dm.d);
   hipError_t e;
   if (blk.kind == DIT_BLOCK_DOUBLE) {
@@ -351,7 +346,7 @@ hipError_t block_f32(const Dims& dm, const dit_block& blk, float* x, const float
     GemmProblem g[2] = {gp32(u, D, blk.qkv[0], D, B * Li, 3 * D),
                         gp32(u + ti * D, D, blk.qkv[1], D, B * Lt, 3 * D)};
     if ((e = gemm32_qkv(g, ng, qo, maps, st))) return e;
-    if ((e = attention_f32(w.q32, w.k32, w.vt32, cat, DF, sm, B, dm.H, L, dm.d, scale, st)))
+    if ((e = attention_f32(w.q32, w.k32, w.v32, cat, DF, sm, B, dm.H, L, dm.d, scale, st)))
       return e;
     g[0] = gp32(cat, DF, blk.proj[0], D, B * Li, D);
     g[1] = gp32(cat + ti * DF, DF, blk.proj[1], D, B * Lt, D);
@@ -375,22 +370,22 @@ hipError_t block_f32(const Dims& dm, const dit_block& blk, float* x, const float
     return e;
   const GemmProblem g1 = gp32(w.u32, D, blk.lin1, D, B * L, 3 * D + F);
   if ((e = gemm32_linear1(g1, qo, jm, w.cat32, DF, st))) return e;
-  if ((e = attention_f32(w.q32, w.k32, w.vt32, w.cat32, DF, jm, B, dm.H, L, dm.d, scale, st)))
+  if ((e = attention_f32(w.q32, w.k32, w.v32, w.cat32, DF, jm, B, dm.H, L, dm.d, scale, st)))
     return e;
   const GemmProblem g2 = gp32(w.cat32, DF, blk.lin2, DF, B * L, D);
   const float* gate[1] = {mod + 2 * D};
   return gemm32_gated_residual(&g2, 1, x, D, gate, bs, &jm, st);
 }
 
-// per-(b, h) e4m3 copies of the QKV epilogue's Q, K (bf16) and V^T (fp16); their
-// per-head amax was gathered by that epilogue into w.amax
+// per-(b, h) e4m3 copies of the QKV epilogue's Q, K and V (bf16); their per-head
+// amax was gathered by that epilogue into w.amax
 hipError_t quant_qkv(const Dims& dm, const BlockWS& w, hipStream_t st) {
   const size_t n = (size_t)dm.L * dm.d;
   const int bh = dm.B * dm.H;
   hipError_t e;
   if ((e = quant_slices<bf16_t>(w.q, n, bh, w.amax, w.q8, w.s_qkv, st))) return e;
   if ((e = quant_slices<bf16_t>(w.k, n, bh, w.amax + bh, w.k8, w.s_qkv + bh, st))) return e;
-  return quant_slices<f16_t>(w.vt, n, bh, w.amax + 2 * bh, w.v8, w.s_qkv + 2 * bh, st);
+  return quant_slices<bf16_t>(w.v, n, bh, w.amax + 2 * bh, w.v8, w.s_qkv + 2 * bh, st);
 }
 
 // fp8 block (x fp32): e4m3 GEMM operands with per-token activation scales, e4m3
@@ -399,7 +394,7 @@ hipError_t block_fp8(const Dims& dm, const dit_block& blk, float* x, const float
                      const float* rope, const BlockWS& w, hipStream_t st) {
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F, H = dm.H;
   const int DF = D + F, BH = B * H;
-  QKVOut qo{w.q, w.k, w.vt, rope, D, H, dm.d};
+  QKVOut qo{w.q, w.k, w.v, rope, D, H, dm.d};
   qo.amax = w.amax;
   const float scale = 1.0f / sqrtf((float)dm.d);
   const float *sq = w.s_qkv, *sk = w.s_qkv + BH, *sv = w.s_qkv + 2 * BH;
@@ -488,13 +483,13 @@ hipError_t block_mx4(const Dims& dm, const dit_block& blk, float* x, const float
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F, H = dm.H;
   const int DF = D + F, BH = B * H;
   const int P = w.mx_pad;
-  QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  QKVOut qo{w.q, w.k, w.v, rope, D, dm.H, dm.d};
   if (A8) qo.amax = w.amax;
   const float scale = 1.0f / sqrtf((float)dm.d);
   const float *sq = w.s_qkv, *sk = w.s_qkv + BH, *sv = w.s_qkv + 2 * BH;
   // joint attention into the first D columns of cat, in the given row map
   auto attend = [&](const RowMap& map) -> hipError_t {
-    if (!A8) return attention_bf16(w.q, w.k, w.vt, w.cat, DF, map, B, H, L, dm.d, scale, st);
+    if (!A8) return attention_bf16(w.q, w.k, w.v, w.cat, DF, map, B, H, L, dm.d, scale, st);
     hipError_t e2;
     if ((e2 = quant_qkv(dm, w, st))) return e2;
     return attention_fp8(w.q8, w.k8, w.v8, sq, sk, sv, w.cat, DF, map, B, H, L, dm.d, scale, st);
@@ -560,7 +555,7 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
                       const float* rope, const BlockWS& w, hipStream_t st) {
   const int B = dm.B, Lt = dm.Lt, Li = dm.Li, L = dm.L, D = dm.D, F = dm.F;
   const int DF = D + F;
-  const QKVOut qo{w.q, w.k, w.vt, rope, D, dm.H, dm.d};
+  const QKVOut qo{w.q, w.k, w.v, rope, D, dm.H, dm.d};
   const float scale = 1.0f / sqrtf((float)dm.d);
   hipError_t e;
   if (blk.kind == DIT_BLOCK_DOUBLE) {
@@ -577,7 +572,7 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
     GemmProblem g[2] = {gp(w.u, D, blk.qkv[0], D, B * Li, 3 * D),
                         gp(w.u + ti * D, D, blk.qkv[1], D, B * Lt, 3 * D)};
     if ((e = gemm_qkv(g, ng, qo, maps, st))) return e;
-    if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, sm, B, dm.H, L, dm.d, scale, st))) return e;
+    if ((e = attention_bf16(w.q, w.k, w.v, w.cat, DF, sm, B, dm.H, L, dm.d, scale, st))) return e;
     g[0] = gp(w.cat, DF, blk.proj[0], D, B * Li, D);
     g[1] = gp(w.cat + ti * DF, DF, blk.proj[1], D, B * Lt, D);
     const float* gate1[2] = {mi + 2 * D, mt + 2 * D};
@@ -600,7 +595,7 @@ hipError_t block_impl(const Dims& dm, const dit_block& blk, XT* x, const float* 
   if ((e = ln_modulate<XT>(x, w.u, B * L, D, jm, B * L, mod, mod + D, mod, mod + D, bs, st))) return e;
   const GemmProblem g1 = gp(w.u, D, blk.lin1, D, B * L, 3 * D + F);
   if ((e = gemm_linear1(g1, qo, jm, w.cat, DF, st))) return e;
-  if ((e = attention_bf16(w.q, w.k, w.vt, w.cat, DF, jm, B, dm.H, L, dm.d, scale, st))) return e;
+  if ((e = attention_bf16(w.q, w.k, w.v, w.cat, DF, jm, B, dm.H, L, dm.d, scale, st))) return e;
   const GemmProblem g2 = gp(w.cat, DF, blk.lin2, DF, B * L, D);
   const float* gate[1] = {mod + 2 * D};
   return gemm_gated_residual<XT>(&g2, 1, x, D, gate, bs, &jm, st);
@@ -841,39 +836,66 @@ int dit_linear_forward(const void* x, int M, int K, const dit_linear* lin, int N
   return DIT_OK;
 }
 
-int dit_attention(const void* q, const void* k, const void* vt, void* o, const float* q_scale,
+int dit_block_views_of(const dit_dims* dims, void* workspace, size_t ws_bytes,
+                       dit_block_views* out) {
+  if (!workspace || !out) return fail(DIT_ERR_INVALID_ARG, "dit_block_views_of: NULL pointer");
+  Dims dm;
+  int rc;
+  if ((rc = make_dims(dims, &dm))) return rc;
+  const size_t need = ws_size(dm, DIT_WS_BLOCK, 0);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "dit_block_views_of: workspace %zu < %zu bytes", ws_bytes, need);
+  Carver c{(char*)workspace, 0};
+  const BlockWS w = carve_block(c, dm, true);
+  out->ln = w.u;
+  out->ln8 = w.u8;
+  out->ln_scale = w.su;
+  out->q = w.q;
+  out->k = w.k;
+  out->v = w.v;
+  out->q8 = w.q8;
+  out->k8 = w.k8;
+  out->v8 = w.v8;
+  out->qkv_scale = w.s_qkv;
+  out->cat = w.cat;
+  out->cat8 = w.cat8;
+  out->att_scale = w.s_att;
+  out->hid_scale = w.s_hid;
+  return DIT_OK;
+}
+
+int dit_attention(const void* q, const void* k, const void* v, void* o, const float* q_scale,
                   const float* k_scale, const float* v_scale, int B, int H, int L, int head_dim,
                   int dtype, float softmax_scale, void* stream) {
-  if (!q || !k || !vt || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+  if (!q || !k || !v || !o) return fail(DIT_ERR_INVALID_ARG, "dit_attention: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: pointers must be 16-byte aligned");
   if (dtype != DIT_BF16 && dtype != DIT_FP8 && dtype != DIT_F32)
     return fail(DIT_ERR_UNSUPPORTED, "dit_attention: dtype %d", dtype);
-  const int lmul = dtype == DIT_FP8 ? 16 : dtype == DIT_F32 ? 1 : 8;
-  if (B < 1 || H < 1 || L < lmul || L % lmul)
-    return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H >= 1 and L a positive multiple of %d",
-                lmul);
+  if (B < 1 || H < 1 || L < 1)
+    return fail(DIT_ERR_INVALID_ARG, "dit_attention: B, H and L must be >= 1");
   if (dtype == DIT_FP8 && (!q_scale || !k_scale || !v_scale))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: fp8 needs q, k and v scales");
-  if (dtype == DIT_F32 ? (head_dim != 32 && head_dim != 64) : head_dim != 128)
+  if (dtype == DIT_F32 ? (head_dim != 32 && head_dim != 64) : (head_dim != 64 && head_dim != 128))
     return fail(DIT_ERR_UNSUPPORTED, "dit_attention: head_dim %d for dtype %d", head_dim, dtype);
   if (!std::isfinite(softmax_scale))
     return fail(DIT_ERR_INVALID_ARG, "dit_attention: softmax_scale must be finite");
-  if ((long long)B * H * L * head_dim > (1LL << 40) || (long long)B * L > (1LL << 31) - 1)
+  if ((long long)B * H * L * head_dim > (1LL << 40) || (long long)B * L > (1LL << 31) - 1 ||
+      (long long)L * head_dim > (1LL << 31) - 1)
     return fail(DIT_ERR_UNSUPPORTED, "dit_attention: problem too large");
   int rc = check_device();
   if (rc) return rc;
   const RowMap jm{B, 0, L, L, 0, 0};
   if (dtype == DIT_F32)
-    DIT_CHECK_HIP(attention_f32((const float*)q, (const float*)k, (const float*)vt, (float*)o,
+    DIT_CHECK_HIP(attention_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
                                 H * head_dim, jm, B, H, L, head_dim, softmax_scale,
                                 (hipStream_t)stream));
   else if (dtype == DIT_FP8)
-    DIT_CHECK_HIP(attention_fp8((const fp8_t*)q, (const fp8_t*)k, (const fp8_t*)vt, q_scale,
+    DIT_CHECK_HIP(attention_fp8((const fp8_t*)q, (const fp8_t*)k, (const fp8_t*)v, q_scale,
                                 k_scale, v_scale, (bf16_t*)o, H * head_dim, jm, B, H, L, head_dim,
                                 softmax_scale, (hipStream_t)stream));
   else
-    DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const f16_t*)vt, (bf16_t*)o,
+    DIT_CHECK_HIP(attention_bf16((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)o,
                                  H * head_dim, jm, B, H, L, head_dim, softmax_scale,
                                  (hipStream_t)stream));
   return DIT_OK;

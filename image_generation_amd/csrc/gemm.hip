@@ -11,7 +11,7 @@
 // Epilogue: each wave parks one 32-column slice of its accumulators in LDS at a
 // time and reads it back either row-wise (4 consecutive columns of one row per
 // lane: coalesced stores, RoPE pairs in-register) or column-wise (4 consecutive
-// rows of one column per lane: the transposed V store), then calls the fused
+// rows of one column per lane), then calls the fused
 // epilogue functor; a pass wholly in bounds hands the functor all of a lane's rows
 // at once, so the loads they need (RoPE entries, residual rows, gates) are in
 // flight together.
@@ -180,19 +180,18 @@ __device__ __forceinline__ float epi_rows(const Epi& e, int r0, int rs, int c, c
   }
 }
 
-// Split the fused projection into head-major Q, K (bf16, rotated) and V^T (fp16).
-// AMAX: the largest stored magnitude of every (tensor, b, h) is gathered too into
-// amax [3, B, H] (q, k, v: the per-head e4m3 scales of the fp8 path).
+// Split the fused projection into head-major Q, K (rotated) and V, all bf16
+// [B, H, L, d].  AMAX: the largest stored magnitude of every (tensor, b, h) is
+// gathered too into amax [3, B, H] (q, k, v: the per-head e4m3 scales of the
+// fp8 path).
 template <bool AMAX>
 struct EpiQKVT {
   static constexpr bool kTrackAmax = AMAX;
-  bf16_t* q; bf16_t* k; f16_t* vt; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
+  bf16_t* q; bf16_t* k; bf16_t* v; const float* rope;  // rope: [L, d/2, 2] (cos, sin)
   int D, H, d; RowMap map;
   unsigned int* amax;
   __device__ __forceinline__ unsigned int* amax_ptr() const { return amax; }
-  __device__ __forceinline__ bool colmajor(int n0, int bn) const {
-    return n0 >= 2 * D && n0 + bn <= 3 * D;
-  }
+  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ int slot(int r, int c) const {
     const int which = c / D;
     const int h = (c - which * D) / d;
@@ -211,83 +210,70 @@ struct EpiQKVT {
     }
     return s0;
   }
-  __device__ __forceinline__ float row4(int r, int c, f32x4 v) const {
+  __device__ __forceinline__ float row4(int r, int c, f32x4 x) const {
     const int which = c / D;
     const int cc = c - which * D;
     const int h = cc / d;
     const int dd = cc - h * d;
     int b, t; map.token(r, b, t);
     const size_t bh = (size_t)b * H + h;
-    if (which < 2) {
-      // pairs (dd, dd+1) and (dd+2, dd+3): table entries p = dd/2 and dd/2 + 1
-      const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
-      float o0 = v[0] * cs[0] - v[1] * cs[1];
-      float o1 = v[0] * cs[1] + v[1] * cs[0];
-      float o2 = v[2] * cs[2] - v[3] * cs[3];
-      float o3 = v[2] * cs[3] + v[3] * cs[2];
-      bf16_t* dst = which == 0 ? q : k;
-      store_bf16x4(dst + (bh * map.L + t) * d + dd, o0, o1, o2, o3);
-      return amax4(o0, o1, o2, o3);
-    }
-    uint16_t* dst = (uint16_t*)vt + (bh * d + dd) * map.L + t;
-    const size_t L = map.L;
-    const f16_t h0 = (f16_t)v[0], h1 = (f16_t)v[1], h2 = (f16_t)v[2], h3 = (f16_t)v[3];
-    dst[0] = __builtin_bit_cast(uint16_t, h0);
-    dst[L] = __builtin_bit_cast(uint16_t, h1);
-    dst[2 * L] = __builtin_bit_cast(uint16_t, h2);
-    dst[3 * L] = __builtin_bit_cast(uint16_t, h3);
-    return amax4(v[0], v[1], v[2], v[3]);
-  }
-  // Q, K columns: the rows' tokens and RoPE entries first, then the rotations and stores
-  template <int NR>
-  __device__ __forceinline__ float rows(int r0, int rs, int c, const f32x4 (&v)[NR]) const {
-    const int which = c / D;
+    bf16_t* dst = (which == 0 ? q : which == 1 ? k : v) + (bh * map.L + t) * d + dd;
     if (which == 2) {
-      float m = 0.f;
-#pragma unroll
-      for (int i = 0; i < NR; ++i) m = fmaxf(m, row4(r0 + i * rs, c, v[i]));
-      return m;
+      store_bf16x4(dst, x[0], x[1], x[2], x[3]);
+      return amax4(x[0], x[1], x[2], x[3]);
     }
+    // pairs (dd, dd+1) and (dd+2, dd+3): table entries p = dd/2 and dd/2 + 1
+    const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+    const float o0 = x[0] * cs[0] - x[1] * cs[1];
+    const float o1 = x[0] * cs[1] + x[1] * cs[0];
+    const float o2 = x[2] * cs[2] - x[3] * cs[3];
+    const float o3 = x[2] * cs[3] + x[3] * cs[2];
+    store_bf16x4(dst, o0, o1, o2, o3);
+    return amax4(o0, o1, o2, o3);
+  }
+  // the rows' tokens (and RoPE entries for Q, K) first, then the stores
+  template <int NR>
+  __device__ __forceinline__ float rows(int r0, int rs, int c, const f32x4 (&x)[NR]) const {
+    const int which = c / D;
     const int cc = c - which * D;
     const int h = cc / d;
     const int dd = cc - h * d;
+    bf16_t* const base = which == 0 ? q : which == 1 ? k : v;
     bf16_t* dst[NR];
-    f32x4 cs[NR];
+    int tok[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       int b, t; map.token(r0 + i * rs, b, t);
-      dst[i] = (which == 0 ? q : k) + (((size_t)b * H + h) * map.L + t) * d + dd;
-      cs[i] = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+      dst[i] = base + (((size_t)b * H + h) * map.L + t) * d + dd;
+      tok[i] = t;
     }
     float m = 0.f;
+    if (which == 2) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        store_bf16x4(dst[i], x[i][0], x[i][1], x[i][2], x[i][3]);
+        m = fmaxf(m, amax4(x[i][0], x[i][1], x[i][2], x[i][3]));
+      }
+      return m;
+    }
+    f32x4 cs[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      cs[i] = *(const f32x4*)(rope + ((size_t)tok[i] * (d >> 1) + (dd >> 1)) * 2);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      const float o0 = v[i][0] * cs[i][0] - v[i][1] * cs[i][1];
-      const float o1 = v[i][0] * cs[i][1] + v[i][1] * cs[i][0];
-      const float o2 = v[i][2] * cs[i][2] - v[i][3] * cs[i][3];
-      const float o3 = v[i][2] * cs[i][3] + v[i][3] * cs[i][2];
+      const float o0 = x[i][0] * cs[i][0] - x[i][1] * cs[i][1];
+      const float o1 = x[i][0] * cs[i][1] + x[i][1] * cs[i][0];
+      const float o2 = x[i][2] * cs[i][2] - x[i][3] * cs[i][3];
+      const float o3 = x[i][2] * cs[i][3] + x[i][3] * cs[i][2];
       store_bf16x4(dst[i], o0, o1, o2, o3);
       m = fmaxf(m, amax4(o0, o1, o2, o3));
     }
     return m;
   }
-  // Q, K slots store bf16, V slots fp16
-  __device__ __forceinline__ float stored(int slot, float m) const {
-    return slot < 2 * map.B * H ? bf2f(f2bf(m)) : (float)(f16_t)m;
-  }
-  // V columns, 4 consecutive rows (tokens t..t+3 of one batch row), fp16
-  __device__ __forceinline__ float col4(int r, int c, f32x4 v) const {
-    const int cc = c - 2 * D;
-    const int h = cc / d;
-    const int dd = cc - h * d;
-    int b, t; map.token(r, b, t);
-    const f16_t h0 = (f16_t)v[0], h1 = (f16_t)v[1], h2 = (f16_t)v[2], h3 = (f16_t)v[3];
-    uint2 u;
-    u.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    u.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-    *(uint2*)(vt + (((size_t)b * H + h) * d + dd) * map.L + t) = u;
-    return amax4(v[0], v[1], v[2], v[3]);
-  }
+  // every slot stores bf16
+  __device__ __forceinline__ float stored(int, float m) const { return bf2f(f2bf(m)); }
+  __device__ __forceinline__ float col4(int, int, f32x4) const { return 0.f; }
 };
 
 using EpiQKV = EpiQKVT<false>;
@@ -1043,30 +1029,30 @@ struct EpiGeluF32 {
   __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
-// Q, K (rotated) [B, H, L, d] and V^T [B, H, d, L], all fp32.
+// Q, K (rotated) and V [B, H, L, d], all fp32.
 struct EpiQKV32 {
-  float* q; float* k; float* vt; const float* rope;
+  float* q; float* k; float* v; const float* rope;
   int D, H, d; RowMap map;
   __device__ __forceinline__ bool colmajor(int, int) const { return false; }
-  __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
+  __device__ __forceinline__ void row4(int r, int c, f32x4 x) const {
     const int which = c / D;
     const int cc = c - which * D;
     const int h = cc / d;
     const int dd = cc - h * d;
     int b, t; map.token(r, b, t);
     const size_t bh = (size_t)b * H + h;
-    if (which < 2) {
-      const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
-      f32x4 o;
-      o[0] = v[0] * cs[0] - v[1] * cs[1];
-      o[1] = v[0] * cs[1] + v[1] * cs[0];
-      o[2] = v[2] * cs[2] - v[3] * cs[3];
-      o[3] = v[2] * cs[3] + v[3] * cs[2];
-      *(f32x4*)((which == 0 ? q : k) + (bh * map.L + t) * d + dd) = o;
-    } else {
-      float* dst = vt + (bh * d + dd) * map.L + t;
-      for (int i = 0; i < 4; ++i) dst[(size_t)i * map.L] = v[i];
+    float* dst = (which == 0 ? q : which == 1 ? k : v) + (bh * map.L + t) * d + dd;
+    if (which == 2) {
+      *(f32x4*)dst = x;
+      return;
     }
+    const f32x4 cs = *(const f32x4*)(rope + ((size_t)t * (d >> 1) + (dd >> 1)) * 2);
+    f32x4 o;
+    o[0] = x[0] * cs[0] - x[1] * cs[1];
+    o[1] = x[0] * cs[1] + x[1] * cs[0];
+    o[2] = x[2] * cs[2] - x[3] * cs[3];
+    o[3] = x[2] * cs[3] + x[3] * cs[2];
+    *(f32x4*)dst = o;
   }
   __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
@@ -1183,14 +1169,14 @@ hipError_t gemm32_gated_residual(const GemmProblem* g, int ng, float* x, int D,
 hipError_t gemm32_qkv(const GemmProblem* g, int ng, const QKVOut32& o, const RowMap* map,
                       hipStream_t st) {
   EpiQKV32 e[2];
-  for (int i = 0; i < ng; ++i) e[i] = EpiQKV32{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i]};
+  for (int i = 0; i < ng; ++i) e[i] = EpiQKV32{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map[i]};
   return launch32(g, e, ng, st, KS_GEMM_QKV);
 }
 
 hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap& map, float* cat,
                           int ldcat, hipStream_t st) {
   EpiLinear1F32 e;
-  e.qkv = EpiQKV32{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map};
+  e.qkv = EpiQKV32{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map};
   e.gelu = EpiGeluF32{cat, ldcat, o.D};
   e.n_qkv = 3 * o.D;
   return launch32(&g, &e, 1, st, KS_GEMM_LIN1);
@@ -1312,12 +1298,12 @@ hipError_t gemm_qkv(const GemmProblem* g, int ng, const QKVOut& o, const RowMap*
   if (o.amax) {
     EpiQKVT<true> e[2];
     for (int i = 0; i < ng; ++i)
-      e[i] = EpiQKVT<true>{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i], o.amax};
+      e[i] = EpiQKVT<true>{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map[i], o.amax};
     return launch(g, e, ng, st, KS_GEMM_QKV);
   }
   EpiQKV e[2];
   for (int i = 0; i < ng; ++i)
-    e[i] = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map[i], nullptr};
+    e[i] = EpiQKV{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map[i], nullptr};
   return launch(g, e, ng, st, KS_GEMM_QKV);
 }
 
@@ -1325,13 +1311,13 @@ hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map
                         bf16_t* cat, int ldcat, hipStream_t st) {
   if (o.amax) {
     EpiLinear1T<true> e;
-    e.qkv = EpiQKVT<true>{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map, o.amax};
+    e.qkv = EpiQKVT<true>{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map, o.amax};
     e.gelu = EpiGeluBf16{cat, ldcat, o.D};
     e.n_qkv = 3 * o.D;
     return launch(&g, &e, 1, st, KS_GEMM_LIN1);
   }
   EpiLinear1 e;
-  e.qkv = EpiQKV{o.q, o.k, o.vt, o.rope, o.D, o.H, o.d, map, nullptr};
+  e.qkv = EpiQKV{o.q, o.k, o.v, o.rope, o.D, o.H, o.d, map, nullptr};
   e.gelu = EpiGeluBf16{cat, ldcat, o.D};
   e.n_qkv = 3 * o.D;
   return launch(&g, &e, 1, st, KS_GEMM_LIN1);

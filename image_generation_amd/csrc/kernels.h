@@ -61,9 +61,9 @@ struct GemmProblem {
 
 // Destinations of the fused QKV epilogue.
 struct QKVOut {
-  bf16_t* q;          // [B, H, L, d]
-  bf16_t* k;          // [B, H, L, d]
-  f16_t* vt;          // [B, H, d, L] fp16
+  bf16_t* q;          // [B, H, L, d] (rotated)
+  bf16_t* k;          // [B, H, L, d] (rotated)
+  bf16_t* v;          // [B, H, L, d]
   const float* rope;  // [L, d/2, 2] (cos, sin)
   int D, H, d;
   // optional [3, B, H]: largest stored |q|, |k|, |v| per (b, h) as fp32 bits,
@@ -89,9 +89,9 @@ hipError_t gemm_linear1(const GemmProblem& g, const QKVOut& o, const RowMap& map
                         bf16_t* cat, int ldcat, hipStream_t st);
 
 // fp32 GEMMs (VALU, 64 x 64 tiles) with the same fused epilogues writing fp32:
-// Q, K, V^T [B, H, L, d] / [B, H, d, L], GELU hidden, gated residual, plain stores.
+// Q, K, V [B, H, L, d], GELU hidden, gated residual, plain stores.
 struct QKVOut32 {
-  float* q; float* k; float* vt; const float* rope; int D, H, d;
+  float* q; float* k; float* v; const float* rope; int D, H, d;
 };
 hipError_t gemm32_store(const GemmProblem& g, float* out, int ldo, hipStream_t st);
 hipError_t gemm32_silu(const GemmProblem& g, float* out, int ldo, hipStream_t st);
@@ -105,14 +105,14 @@ hipError_t gemm32_qkv(const GemmProblem* g, int ng, const QKVOut32& o, const Row
 hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap& map, float* cat,
                           int ldcat, hipStream_t st);
 
-// fp32 attention, head dim 32 or 64: q, k [B, H, L, d], vt [B, H, d, L], o fp32.
-hipError_t attention_f32(const float* q, const float* k, const float* vt, float* o, int ldo,
+// fp32 attention, head dim 32 or 64: q, k, v [B, H, L, d], o fp32.
+hipError_t attention_f32(const float* q, const float* k, const float* v, float* o, int ldo,
                          const RowMap& map, int B, int H, int L, int d, float softmax_scale,
                          hipStream_t st);
 
-// Flash attention: q, k bf16 [B, H, L, d], vt fp16 [B, H, d, L]; output (bf16) of
-// token (b, t), head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
-hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const f16_t* vt, bf16_t* o,
+// Flash attention: q, k, v bf16 [B, H, L, d], d 64 or 128, any L >= 1; output
+// (bf16) of token (b, t), head h goes to o[map.stream_row(b, t) * ldo + h * d + c].
+hipError_t attention_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
                           int ldo, const RowMap& map, int B, int H, int L, int d,
                           float softmax_scale, hipStream_t st);
 
@@ -156,9 +156,9 @@ template <class T>
 hipError_t quant_mxfp4(const T* src, int lds, int rows, int width, uint8_t* codes, uint8_t* scales,
                        int pad_rows, hipStream_t st);
 
-// fp8 attention: q8, k8 e4m3 [B, H, L, d], vt8 e4m3 [B, H, d, L], one fp32 scale per
-// (b, h) for each of q, k, v; output bf16 as attention_bf16.
-hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* vt8, const float* sq,
+// fp8 attention: q8, k8, v8 e4m3 [B, H, L, d], one fp32 scale per (b, h) for each
+// of q, k, v; output bf16 as attention_bf16.
+hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* v8, const float* sq,
                          const float* sk, const float* sv, bf16_t* o, int ldo, const RowMap& map,
                          int B, int H, int L, int d, float softmax_scale, hipStream_t st);
 

@@ -44,6 +44,11 @@ class DitBlock(Structure):
                 ("lin1", DitLinear), ("lin2", DitLinear)]
 
 
+class DitBlockViews(Structure):
+    _fields_ = [(n, c_void_p) for n in ("ln", "ln8", "ln_scale", "q", "k", "v", "q8", "k8", "v8",
+                                        "qkv_scale", "cat", "cat8", "att_scale", "hid_scale")]
+
+
 class DitModel(Structure):
     _fields_ = [("dims", DitDims), ("n_double", c_int), ("n_single", c_int),
                 ("blocks", POINTER(DitBlock)), ("time1", DitLinear), ("time2", DitLinear),
@@ -113,6 +118,7 @@ def _load() -> ctypes.CDLL:
                                         POINTER(c_int)]),
         "dit_loop_graph_reset": (c_int, [P, POINTER(DitFBCache), c_int, P]),
         "dit_loop_graph_destroy": (c_int, [P]),
+        "dit_block_views_of": (c_int, [POINTER(DitDims), P, c_size_t, POINTER(DitBlockViews)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -127,7 +133,8 @@ EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_s
             "fbcache_should_skip", "dit_denoise_step", "dit_set_kernel_timer", "dit_linear_forward",
             "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4",
             "dit_loop_state_bytes", "dit_loop_graph_create", "dit_loop_graph_run",
-            "dit_loop_graph_sync", "dit_loop_graph_reset", "dit_loop_graph_destroy")
+            "dit_loop_graph_sync", "dit_loop_graph_reset", "dit_loop_graph_destroy",
+            "dit_block_views_of")
 
 
 def _check(rc: int) -> None:
@@ -196,39 +203,36 @@ def _codes(t: torch.Tensor, shape, name: str) -> None:
                          f"got {t.dtype} {tuple(t.shape)}")
 
 
-def dit_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, o: torch.Tensor,
+def dit_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                   softmax_scale: Optional[float] = None, q_scale: Optional[torch.Tensor] = None,
                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
-    """bf16: q, k [B, H, L, 128] bf16, vt [B, H, 128, L] fp16, o bf16.
-    fp8: q, k, vt e4m3 codes of the same shapes, scales fp32 [B, H], o bf16.
-    fp32: q, k [B, H, L, d] fp32 (d 32 or 64), vt [B, H, d, L] fp32, o fp32.
-    o [B, L, H*d] (written)."""
+    """q, k, v [B, H, L, d] (any L >= 1), o [B, L, H*d] (written).
+    bf16: q, k, v bf16, d 64 or 128, o bf16.
+    fp8: q, k, v e4m3 codes (d 64 or 128), scales fp32 [B, H], o bf16.
+    fp32: q, k, v fp32 (d 32 or 64), o fp32."""
     B, H, L, d = q.shape
     fp8 = q.dtype in (torch.uint8, torch.float8_e4m3fn)
     f32 = q.dtype == torch.float32
     if f32:
-        _need(q, torch.float32, (B, H, L, d), "q")
-        _need(k, torch.float32, (B, H, L, d), "k")
-        _need(vt, torch.float32, (B, H, d, L), "vt")
+        for n_, t_ in (("q", q), ("k", k), ("v", v)):
+            _need(t_, torch.float32, (B, H, L, d), n_)
         _need(o, torch.float32, (B, L, H * d), "o")
     elif fp8:
-        _codes(q, (B, H, L, d), "q")
-        _codes(k, (B, H, L, d), "k")
-        _codes(vt, (B, H, d, L), "vt")
+        for n_, t_ in (("q", q), ("k", k), ("v", v)):
+            _codes(t_, (B, H, L, d), n_)
         for n_, t_ in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
             if t_ is None:
                 raise ValueError(f"{n_} is required for fp8 attention")
             _need(t_, torch.float32, (B, H), n_)
     else:
-        _need(q, torch.bfloat16, (B, H, L, d), "q")
-        _need(k, torch.bfloat16, (B, H, L, d), "k")
-        _need(vt, torch.float16, (B, H, d, L), "vt")
+        for n_, t_ in (("q", q), ("k", k), ("v", v)):
+            _need(t_, torch.bfloat16, (B, H, L, d), n_)
     if not f32:
         _need(o, torch.bfloat16, (B, L, H * d), "o")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(q_scale), _ptr(k_scale),
+    _check(LIB.dit_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(q_scale), _ptr(k_scale),
                              _ptr(v_scale), B, H, L, d,
                              DIT_F32 if f32 else DIT_FP8 if fp8 else DIT_BF16,
                              float(softmax_scale), _stream(stream)))
@@ -495,6 +499,42 @@ def dit_modulation(gm: GPUModel, sigmas: Sequence[float], out: Optional[torch.Te
     _check(LIB.dit_modulation(ctypes.byref(gm.model), sig, n, _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)))
     return out
+
+
+def block_views(dd: DitDims, ws: torch.Tensor) -> dict:
+    """Tensor views of a block workspace's intermediates (see dit_block_views in
+    include/dit.h), as torch tensors sharing the workspace's memory."""
+    v = DitBlockViews()
+    _check(LIB.dit_block_views_of(ctypes.byref(dd), _ptr(ws), ws.numel(), ctypes.byref(v)))
+    B, L, D, H, F = dd.B, dd.Lt + dd.grid_h * dd.grid_w, dd.D, dd.H, dd.F
+    d = D // H
+    base = ws.data_ptr()
+
+    def view(ptr, dtype, shape):
+        n = 1
+        for s_ in shape:
+            n *= s_
+        es = torch.empty((), dtype=dtype).element_size()
+        off = ptr - base
+        return ws[off:off + n * es].view(dtype).view(shape)
+
+    rows = B * L
+    return {
+        "ln": view(v.ln, torch.bfloat16, (rows, D)),
+        "ln8": view(v.ln8, torch.uint8, (rows, D)),
+        "ln_scale": view(v.ln_scale, torch.float32, (rows,)),
+        "q": view(v.q, torch.bfloat16, (B, H, L, d)),
+        "k": view(v.k, torch.bfloat16, (B, H, L, d)),
+        "v": view(v.v, torch.bfloat16, (B, H, L, d)),
+        "q8": view(v.q8, torch.uint8, (B, H, L, d)),
+        "k8": view(v.k8, torch.uint8, (B, H, L, d)),
+        "v8": view(v.v8, torch.uint8, (B, H, L, d)),
+        "qkv_scale": view(v.qkv_scale, torch.float32, (3, B, H)),
+        "cat": view(v.cat, torch.bfloat16, (rows, D + F)),
+        "cat8": view(v.cat8, torch.uint8, (rows, D + F)),
+        "att_scale": view(v.att_scale, torch.float32, (rows,)),
+        "hid_scale": view(v.hid_scale, torch.float32, (rows,)),
+    }
 
 
 class FBCache:

@@ -86,9 +86,10 @@ extern "C" {
 
 /* Token layout of one denoise problem.
  *   B       batch rows (1, or 2 for a CFG pair: row 0 positive, row 1 negative)
- *   Lt      text tokens (multiple of 8)
- *   grid_h, grid_w  patch grid; Li = grid_h * grid_w image tokens (multiple of 8)
- *   D, H, F hidden size, heads (head dim D / H must be 128), MLP hidden size
+ *   Lt      text tokens (>= 0)
+ *   grid_h, grid_w  patch grid; Li = grid_h * grid_w image tokens
+ *   D, H, F hidden size, heads (head dim D / H: 64 or 128; 32 or 64 for DIT_F32),
+ *           MLP hidden size
  * Joint token order is [text ; image]: token t < Lt is text, token Lt + i is
  * image patch (i / grid_w, i % grid_w). */
 typedef struct dit_dims {
@@ -235,20 +236,27 @@ DIT_API int dit_set_kernel_timer(dit_kernel_timer* timer);
 DIT_API int dit_linear_forward(const void* x, int M, int K, const dit_linear* lin, int N, void* y,
                        int y_dtype, void* stream);
 
-/* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V.
- *   dtype DIT_BF16: q, k device bf16 [B, H, L, 128]; vt device fp16
- *     [B, H, 128, L] (V transposed per head, fp16: the P V product runs on fp16
- *     MFMAs); scales NULL; L % 8 == 0, L >= 8.
- *   dtype DIT_F32: q, k fp32 [B, H, L, d], vt fp32 [B, H, d, L], o fp32, head_dim
- *     32 or 64, any L >= 1.
- *   dtype DIT_FP8: q, k e4m3 [B, H, L, 128], vt e4m3 [B, H, 128, L], each with
- *     one fp32 scale per (b, h) in q_scale / k_scale / v_scale [B * H] (value =
- *     code * scale); with t the scores in exp2 units and r the row maximum of t
- *     rounded up to an integer, P = 2^(t - r) enters P V as e4m3(448 P) / 448 and
- *     the normaliser is the sum of those quantised P; L % 16 == 0, L >= 16.
- *   o: device [B, L, H * head_dim] (token-major), bf16 (fp32 for DIT_F32).  Softmax statistics and both
- *   products accumulate in fp32.  Workspace: none. */
-DIT_API int dit_attention(const void* q, const void* k, const void* vt, void* o,
+/* Joint softmax attention, no mask: O = softmax(Q K^T * softmax_scale) V, per
+ * (batch, head) over all L tokens (the joint text + image attention of a block:
+ * VisualGen article on FLUX Klein, section on why the speed-ups differ, where
+ * BF16 attention is the largest part of the DiT's kernel time; cuDNN FP8
+ * attention is the low-precision variant there).
+ *   q, k, v: device [B, H, L, head_dim] row-major, all three the same layout;
+ *   o: device [B, L, H * head_dim] (token-major), bf16 (fp32 for DIT_F32).
+ *   L >= 1, any value (keys past the last tile are masked; no padding needed).
+ *   dtype DIT_BF16: q, k, v bf16, head_dim 64 or 128; scales NULL.  P enters the
+ *     P V product as bf16.
+ *   dtype DIT_FP8: q, k, v OCP e4m3, head_dim 64 or 128, each with one fp32
+ *     scale per (b, h) in q_scale / k_scale / v_scale [B * H] (value = code *
+ *     scale); with t the scores in exp2 units and r the row maximum of t rounded
+ *     up to an integer, P = 2^(t - r) enters P V as e4m3(448 P) / 448 and the
+ *     normaliser is the sum of those quantised P.
+ *   dtype DIT_F32: q, k, v, o fp32, head_dim 32 or 64 (reference precision).
+ *   Softmax statistics and both products accumulate in fp32.  Workspace: none.
+ *   Errors: DIT_ERR_INVALID_ARG for NULL / misaligned pointers, B, H or L < 1,
+ *   a non-finite scale or missing fp8 scales; DIT_ERR_UNSUPPORTED for another
+ *   head_dim or dtype.  The caller keeps ownership of every buffer. */
+DIT_API int dit_attention(const void* q, const void* k, const void* v, void* o,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           int B, int H, int L, int head_dim, int dtype, float softmax_scale,
                           void* stream);
@@ -310,12 +318,39 @@ DIT_API int dit_linear_mxfp4(const void* x_codes, const unsigned char* x_scales,
  *   linears with w_mx set: each linear's bf16 input is quantised to MXFP4 on the
  *   fly, 32-value blocks along the input dimension; attention in bf16; D and F
  *   multiples of 256); DIT_MXFP4_FP8ATTN (the same linears, attention in e4m3 as
- *   for DIT_FP8; joint length a multiple of 16); DIT_F32 (fp32 weights, head dim
- *   32 or 64).
+ *   for DIT_FP8); DIT_F32 (fp32 weights, head dim 32 or 64).  bf16 / fp8 /
+ *   MXFP4 blocks take head dim 64 or 128 and any token counts.
  *   workspace >= DIT_WS_BLOCK bytes. */
 DIT_API int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, void* x, int x_dtype,
                       const float* mod, long mod_bstride, const float* rope, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Where a block leaves its intermediates in a DIT_WS_BLOCK workspace, for tests
+ * and debugging (the stage-by-stage comparison of a block with a reference).
+ * After dit_block_forward() the buffers hold that block's values.  Row order
+ * of the [rows, *] buffers: a single-stream block uses the joint order (b, t);
+ * a double-stream block puts all image rows first (batch-major), then all
+ * text rows.  Pointers are into the caller's workspace; nothing is copied. */
+typedef struct dit_block_views {
+  void* ln;          /* bf16 [B L, D]: LN-modulate output (bf16 blocks; the      */
+                     /* second LN of a double block once the block has run)      */
+  void* ln8;         /* e4m3 [B L, D] and                                         */
+  float* ln_scale;   /* fp32 [B L]: the same for fp8 blocks                       */
+  void* q;           /* bf16 [B, H, L, d]: Q (rotated)                            */
+  void* k;           /* bf16 [B, H, L, d]: K (rotated)                            */
+  void* v;           /* bf16 [B, H, L, d]: V                                      */
+  void* q8;          /* e4m3 [B, H, L, d] codes of Q, K, V (fp8 attention) with   */
+  void* k8;
+  void* v8;
+  float* qkv_scale;  /* fp32 [3, B H]: one scale per (b, h) for Q, K, V           */
+  void* cat;         /* bf16 [B L, D + F]: attention output | GELU hidden         */
+  void* cat8;        /* e4m3 [B L, D + F]: their codes (fp8 blocks), with         */
+  float* att_scale;  /* fp32 [B L]: attention-output row scales (single-stream:   */
+                     /* one scale over the whole D + F row)                       */
+  float* hid_scale;  /* fp32 [B L]: GELU-hidden row scales (double-stream)        */
+} dit_block_views;
+DIT_API int dit_block_views_of(const dit_dims* dims, void* workspace, size_t ws_bytes,
+                               dit_block_views* out);
 
 /* Modulation vectors of the whole model for n sigmas at once:
  *   out[i] = mod.W SiLU(c_i) + mod.b,  c_i = time2(SiLU(time1(emb(sigma_i)))),

@@ -74,21 +74,25 @@ def test_invalid_arguments_rejected_before_launch():
     N = None
     rc = L.dit_attention(N, N, N, N, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
-    # ragged L (not a multiple of 8) with fake aligned pointers: rejected before any launch
+    # empty L, a head size the kernels do not run: rejected before any launch
     fake = P(4096)
-    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 63, 128, dit.DIT_BF16, 0.1, N)
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 0, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 63, 96, dit.DIT_BF16, 0.1, N)
+    assert rc == dit.DIT_ERR_UNSUPPORTED
+    rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 63, 128, dit.DIT_F32, 0.1, N)
+    assert rc == dit.DIT_ERR_UNSUPPORTED
     rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, math.nan, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
     # misaligned pointer
     rc = L.dit_attention(P(4098), fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_BF16, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
-    # fp8: scales required, L a multiple of 16
+    # fp8: scales required; head dim 64 or 128
     rc = L.dit_attention(fake, fake, fake, fake, N, N, N, 1, 1, 64, 128, dit.DIT_FP8, 0.1, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
-    rc = L.dit_attention(fake, fake, fake, fake, fake, fake, fake, 1, 1, 72, 128, dit.DIT_FP8,
+    rc = L.dit_attention(fake, fake, fake, fake, fake, fake, fake, 1, 1, 72, 32, dit.DIT_FP8,
                          0.1, N)
-    assert rc == dit.DIT_ERR_INVALID_ARG
+    assert rc == dit.DIT_ERR_UNSUPPORTED
     # row quantisation: width not a multiple of 8, stride below width, unsupported source
     rc = L.dit_quantize_rows(fake, dit.DIT_BF16, 12, 4, 12, fake, 16, fake, N)
     assert rc == dit.DIT_ERR_INVALID_ARG
@@ -121,16 +125,19 @@ def test_invalid_arguments_rejected_before_launch():
     rc = L.dit_block_forward(ctypes.byref(d16), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
                              fake, 0, fake, fake, 1 << 30, None)
     assert rc == dit.DIT_ERR_INVALID_ARG
-    # fp8 needs the joint length to be a multiple of 16 (8 + 8*2 = 24 is not)
-    d24 = dit.dims_of(1, 8, 2, 8, 256, 2, 512)
+    # bf16 / fp8 blocks run head dim 64 or 128 (256 / 8 = 32 is not)
+    d32 = dit.dims_of(1, 8, 2, 8, 256, 8, 512)
     blk.lin1 = dit.DitLinear(4096, 4096, 4096)
     blk.lin2 = blk.lin1
-    rc = L.dit_block_forward(ctypes.byref(d24), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
+    rc = L.dit_block_forward(ctypes.byref(d32), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
                              fake, 0, fake, fake, 1 << 30, None)
     assert rc == dit.DIT_ERR_UNSUPPORTED
-    # token counts that are not multiples of 8
-    d = dit.dims_of(1, 7, 2, 4, 256, 2, 512)
+    # a negative token count
+    d = dit.dims_of(1, -1, 2, 4, 256, 2, 512)
     assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
+    # ragged token counts are valid shapes
+    d = dit.dims_of(1, 7, 3, 5, 256, 2, 512)
+    assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) > 0
 
 
 def test_loop_graph_arguments_rejected_on_the_host():

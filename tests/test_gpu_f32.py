@@ -45,7 +45,7 @@ def test_attention_f32(dit, B, H, L, d):
     _say(f"attention fp32 B={B} H={H} L={L} d={d}")
     q, k, v = _f32((B, H, L, d), 81), _f32((B, H, L, d), 82), _f32((B, H, L, d), 83)
     o = torch.empty((B, L, H * d), dtype=torch.float32, device="cuda")
-    dit.dit_attention(q.cuda(), k.cuda(), v.transpose(2, 3).contiguous().cuda(), o)
+    dit.dit_attention(q.cuda(), k.cuda(), v.cuda(), o)
     torch.cuda.synchronize()
     got = o.cpu().double().numpy().reshape(B, L, H, d).transpose(0, 2, 1, 3)
     err = parity_err(got, O.attention(O.to64(q), O.to64(k), O.to64(v)))
@@ -59,7 +59,7 @@ def test_attention_f32_identical_keys(dit):
     k = _f32((B, H, 1, d), 85).expand(B, H, L, d).contiguous()
     v = _f32((B, H, L, d), 86)
     o = torch.empty((B, L, H * d), dtype=torch.float32, device="cuda")
-    dit.dit_attention(q.cuda(), k.cuda(), v.transpose(2, 3).contiguous().cuda(), o)
+    dit.dit_attention(q.cuda(), k.cuda(), v.cuda(), o)
     torch.cuda.synchronize()
     got = o.cpu().double().numpy().reshape(B, L, H, d).transpose(0, 2, 1, 3)
     mean = O.to64(v).mean(axis=2, keepdims=True)

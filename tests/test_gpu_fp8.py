@@ -76,14 +76,14 @@ def test_quantize_rows_bit_exact(dit, rows, width):
 # ---------------------------------------------------------------- attention
 
 def _fp8_operands(dit, q, k, v):
-    """Per-(b, h) e4m3 codes and scales of q, k and V^T, quantised by the library."""
+    """Per-(b, h) e4m3 codes and scales of q, k and v, quantised by the library
+    (one row per head: the [L, d] slice; rows padded to a multiple of 8 values)."""
     B, H, L, d = q.shape
-    q8, sq = dit.dit_quantize_rows(q.reshape(B * H, L * d).cuda())
-    k8, sk = dit.dit_quantize_rows(k.reshape(B * H, L * d).cuda())
-    vt = v.transpose(2, 3).contiguous()
-    v8, sv = dit.dit_quantize_rows(vt.reshape(B * H, d * L).cuda())
-    return (q8.view(B, H, L, d), k8.view(B, H, L, d), v8.view(B, H, d, L),
-            sq.view(B, H), sk.view(B, H), sv.view(B, H))
+    out = []
+    for t in (q, k, v):
+        codes, sc = dit.dit_quantize_rows(t.reshape(B * H, L * d).cuda())
+        out.append((codes.view(B, H, L, d), sc.view(B, H)))
+    return out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1]
 
 
 def _run_fp8_attention(dit, q, k, v):
@@ -95,10 +95,11 @@ def _run_fp8_attention(dit, q, k, v):
     return o.float().cpu().double().numpy().reshape(B, L, H, d).transpose(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("B,H,L", [(1, 1, 16), (1, 2, 272), (2, 1, 528), (1, 3, 1040)])
-def test_attention_fp8_small(dit, B, H, L):
-    _say(f"attention fp8 B={B} H={H} L={L}")
-    d = 128
+@pytest.mark.parametrize("B,H,L,d", [(1, 1, 16, 128), (1, 2, 272, 128), (2, 1, 528, 64),
+                                     (1, 3, 1040, 128), (1, 1, 1, 128), (2, 2, 37, 64),
+                                     (1, 2, 333, 128), (1, 1, 4097, 64)])
+def test_attention_fp8_small(dit, B, H, L, d):
+    _say(f"attention fp8 B={B} H={H} L={L} d={d}")
     q, k, v = _bf16((B, H, L, d), 51), _bf16((B, H, L, d), 52), _bf16((B, H, L, d), 53)
     got = _run_fp8_attention(dit, q, k, v)
     ref, slack = O.attention_fp8(O.to64(q), O.to64(k), O.to64(v), tie_rel=TIE_REL)
@@ -107,8 +108,9 @@ def test_attention_fp8_small(dit, B, H, L):
     assert err <= TOL_FP8
 
 
-def test_attention_fp8_identical_keys(dit):
-    B, H, L, d = 1, 2, 208, 128
+@pytest.mark.parametrize("L,d", [(208, 128), (99, 64)])
+def test_attention_fp8_identical_keys(dit, L, d):
+    B, H = 1, 2
     q = _bf16((B, H, L, d), 61)
     k = _bf16((B, H, 1, d), 62).expand(B, H, L, d).contiguous()
     v = _bf16((B, H, L, d), 63)

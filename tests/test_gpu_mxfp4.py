@@ -191,8 +191,6 @@ def _check_mx4_property(got, ref4, exact, x0):
 @pytest.mark.parametrize("attn8", [False, True])
 @pytest.mark.parametrize("D,H,F,B,Lt,gh,gw,kind", MX4_BLOCK_CASES)
 def test_block_forward_mxfp4(dit, D, H, F, B, Lt, gh, gw, kind, attn8):
-    if attn8 and (Lt + gh * gw) % 16:
-        pytest.skip("e4m3 attention needs a joint length that is a multiple of 16")
     _say(f"mxfp4 block {kind} D={D} B={B} Lt={Lt} grid={gh}x{gw} e4m3 attention={attn8}")
     dims = DI.Dims(D=D, H=H, F=F, n_double=1, n_single=0)
     w = DI.Workload("t", dims, B=B, grid_h=gh, grid_w=gw, Lt=Lt, dtype="bf16")

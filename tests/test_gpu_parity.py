@@ -60,15 +60,18 @@ def _attn_ref_rows(q, k, v, rows):
     return out
 
 
-@pytest.mark.parametrize("B,H,L", [(1, 1, 8), (1, 2, 264), (2, 1, 520), (1, 3, 1032)])
-def test_attention_small(dit, B, H, L):
-    _say(f"attention B={B} H={H} L={L}")
-    d = 128
+@pytest.mark.parametrize("B,H,L,d", [
+    (1, 1, 1, 128), (1, 2, 7, 64), (1, 1, 8, 128), (2, 2, 65, 64), (1, 2, 264, 128),
+    (2, 1, 520, 64), (1, 3, 1032, 128), (2, 2, 333, 128), (1, 1, 4097, 64), (1, 2, 4601, 128)])
+def test_attention_small(dit, B, H, L, d):
+    """Every tile path with ragged tails (L not a multiple of the 64-key tile or
+    the 256-query tile, down to a single token) and both head sizes."""
+    _say(f"attention B={B} H={H} L={L} d={d}")
     q = _bf16((B, H, L, d), 11)
     k = _bf16((B, H, L, d), 12)
     v = _bf16((B, H, L, d), 13)
     o = torch.empty((B, L, H * d), dtype=torch.bfloat16, device="cuda")
-    dit.dit_attention(q.cuda(), k.cuda(), v.transpose(2, 3).contiguous().to(torch.float16).cuda(), o)
+    dit.dit_attention(q.cuda(), k.cuda(), v.cuda(), o)
     torch.cuda.synchronize()
     ref = O.attention(O.to64(q), O.to64(k), O.to64(v))          # [B, H, L, d]
     got = o.float().cpu().double().numpy().reshape(B, L, H, d).transpose(0, 2, 1, 3)
@@ -77,32 +80,35 @@ def test_attention_small(dit, B, H, L):
     assert err <= TOL_BF16
 
 
-def test_attention_identical_keys(dit):
-    B, H, L, d = 1, 2, 200, 128
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_identical_keys(dit, d):
+    B, H, L = 1, 2, 200
     q = _bf16((B, H, L, d), 21)
     k = _bf16((B, H, 1, d), 22).expand(B, H, L, d).contiguous()
     v = _bf16((B, H, L, d), 23)
     o = torch.empty((B, L, H * d), dtype=torch.bfloat16, device="cuda")
-    dit.dit_attention(q.cuda(), k.cuda(), v.transpose(2, 3).contiguous().to(torch.float16).cuda(), o)
+    dit.dit_attention(q.cuda(), k.cuda(), v.cuda(), o)
     torch.cuda.synchronize()
     got = o.float().cpu().double().numpy().reshape(B, L, H, d).transpose(0, 2, 1, 3)
     mean = O.to64(v).mean(axis=2, keepdims=True)
     assert parity_err_bf16_stored(got, np.broadcast_to(mean, got.shape)) <= TOL_BF16
 
 
-@pytest.mark.parametrize("B,L", [(1, 4608), (2, 16896)])
-def test_attention_full_size_sampled(dit, B, L):
-    """FLUX head layout at 1024px (4608 tokens) and 2048px CFG pair (16896), 24 heads."""
-    _say(f"attention full B={B} L={L}")
-    H, d = 24, 128
+@pytest.mark.parametrize("B,L,H,d", [(1, 4608, 24, 128), (2, 16896, 24, 128),
+                                     (1, 4097, 24, 128), (1, 4601, 48, 64)])
+def test_attention_full_size_sampled(dit, B, L, H, d):
+    """FLUX head layout at 1024px (4608 tokens) and the 2048px CFG pair (16896),
+    24 heads; ragged full-size lengths 4097 and 4601 (head dim 128 and 64)."""
+    _say(f"attention full B={B} L={L} H={H} d={d}")
     q = _bf16((B, H, L, d), 31)
     k = _bf16((B, H, L, d), 32)
     v = _bf16((B, H, L, d), 33)
     o = torch.empty((B, L, H * d), dtype=torch.bfloat16, device="cuda")
-    dit.dit_attention(q.cuda(), k.cuda(), v.transpose(2, 3).contiguous().to(torch.float16).cuda(), o)
+    dit.dit_attention(q.cuda(), k.cuda(), v.cuda(), o)
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    rows = np.sort(np.concatenate([rng.choice(L, 60, replace=False), [0, L - 1, 511, 512]]))
+    rows = np.unique(np.concatenate([rng.choice(L, 60, replace=False),
+                                     [0, L - 1, 255, 256, 511, 512, L - 2]]))
     ref = _attn_ref_rows(O.to64(q), O.to64(k), O.to64(v), rows)
     got = o.float().cpu().double().numpy().reshape(B, L, H, d)[:, rows].transpose(0, 2, 1, 3)
     err = parity_err_bf16_stored(got, ref)
