@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -1022,35 +1023,41 @@ int dit_block_forward(const dit_dims* dims, const dit_block* blk, int dtype, voi
   return DIT_OK;
 }
 
-int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* out,
-                   void* workspace, size_t ws_bytes, void* stream) {
-  if (!m || !sigmas_host || !out || !workspace || n < 1)
-    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: NULL pointer or n < 1");
-  Dims dm;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the modulation entry points; *need receives the scratch bytes.
+int check_modulation(const dit_model* m, const double* sigmas_host, int n, const float* out,
+                     Dims* dm, long long* nmod, size_t* need, const char* fn) {
+  if (!m || !sigmas_host || !out || n < 1)
+    return fail(DIT_ERR_INVALID_ARG, "%s: NULL pointer or n < 1", fn);
   int rc;
-  if ((rc = make_dims(&m->dims, &dm))) return rc;
+  if ((rc = make_dims(&m->dims, dm))) return rc;
   if ((rc = check_linear(m->time1, "time1")) || (rc = check_linear(m->time2, "time2")) ||
       (rc = check_linear(m->mod, "mod")))
     return rc;
-  if (!aligned16(out) || !aligned16(workspace))
-    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: pointers must be 16-byte aligned");
+  if (!aligned16(out)) return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   if (m->n_double < 0 || m->n_single < 0)
-    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: negative block count");
-  if (dm.D % 64) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: D %% 64 != 0");
+    return fail(DIT_ERR_INVALID_ARG, "%s: negative block count", fn);
+  if (dm->D % 64) return fail(DIT_ERR_UNSUPPORTED, "%s: D %% 64 != 0", fn);
   for (int i = 0; i < n; ++i)
-    if (!std::isfinite(sigmas_host[i]))
-      return fail(DIT_ERR_INVALID_ARG, "dit_modulation: non-finite sigma");
-  const size_t need = ws_size(dm, DIT_WS_MODULATION, n);
-  if (ws_bytes < need)
-    return fail(DIT_ERR_WORKSPACE, "dit_modulation: workspace %zu < %zu bytes", ws_bytes, need);
-  const long long nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm.D;
-  if (nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "dit_modulation: too many vectors");
+    if (!std::isfinite(sigmas_host[i])) return fail(DIT_ERR_INVALID_ARG, "%s: non-finite sigma", fn);
+  *nmod = (12LL * m->n_double + 3LL * m->n_single + 2) * dm->D;
+  if (*nmod > (1LL << 31) - 1) return fail(DIT_ERR_UNSUPPORTED, "%s: too many vectors", fn);
   if (m->dtype != DIT_BF16 && m->dtype != DIT_FP8 && m->dtype != DIT_F32 &&
       m->dtype != DIT_MXFP4 && m->dtype != DIT_MXFP4_FP8ATTN)
-    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: model dtype %d", m->dtype);
-  if ((rc = check_device())) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  Carver c{(char*)workspace, 0};
+    return fail(DIT_ERR_INVALID_ARG, "%s: model dtype %d", fn, m->dtype);
+  *need = ws_size(*dm, DIT_WS_MODULATION, n);
+  return DIT_OK;
+}
+
+// The modulation kernels with their intermediates (timestep sinusoid, hidden
+// activation, SiLU(c)) carved from scratch; every intermediate is written in
+// full before it is read, so the scratch needs no clearing.
+int modulation_run(const dit_model* m, const Dims& dm, long long nmod, const double* sigmas_host,
+                   int n, float* out, void* scratch_base, hipStream_t st) {
+  Carver c{(char*)scratch_base, 0};
   const ModWS w = carve_mod(c, dm, n);
   if (m->dtype == DIT_F32) {
     float *emb = (float*)w.emb, *h = (float*)w.h, *cs = (float*)w.cs;
@@ -1066,6 +1073,72 @@ int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* 
   DIT_CHECK_HIP(gemm_silu_bf16(gp(h, dm.D, m->time2, dm.D, n, dm.D), cs, dm.D, st));
   DIT_CHECK_HIP(gemm_store_f32(gp(cs, dm.D, m->mod, dm.D, n, (int)nmod), out, (int)nmod, st));
   return DIT_OK;
+}
+
+// Static scratch of dit_modulation_static: one copy per GPU, kept until the
+// process ends.  Host code never passes `scratch` itself (its host-side name is
+// a stand-in, not a device address): the device address of each GPU's copy is
+// looked up once per device with that device current and kept in
+// g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[DIT_MOD_STATIC_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DIT_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(DIT_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DIT_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* out,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  Dims dm;
+  long long nmod = 0;
+  size_t need = 0;
+  int rc;
+  if ((rc = check_modulation(m, sigmas_host, n, out, &dm, &nmod, &need, "dit_modulation")))
+    return rc;
+  if (!workspace) return fail(DIT_ERR_INVALID_ARG, "dit_modulation: NULL workspace");
+  if (!aligned16(workspace))
+    return fail(DIT_ERR_INVALID_ARG, "dit_modulation: pointers must be 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "dit_modulation: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((rc = check_device())) return rc;
+  return modulation_run(m, dm, nmod, sigmas_host, n, out, workspace, (hipStream_t)stream);
+}
+
+int dit_modulation_static(const dit_model* m, const double* sigmas_host, int n, float* out,
+                          void* stream) {
+  Dims dm;
+  long long nmod = 0;
+  size_t need = 0;
+  int rc;
+  if ((rc = check_modulation(m, sigmas_host, n, out, &dm, &nmod, &need, "dit_modulation_static")))
+    return rc;
+  if (need > (size_t)DIT_MOD_STATIC_BYTES)
+    return fail(DIT_ERR_WORKSPACE,
+                "dit_modulation_static: %d steps at D %d need %zu bytes of scratch, more than "
+                "the library's static %u bytes (call dit_modulation with a workspace, or fewer "
+                "steps per call)",
+                n, dm.D, need, (unsigned)DIT_MOD_STATIC_BYTES);
+  if ((rc = check_device())) return rc;
+  void* base = nullptr;
+  if ((rc = static_scratch(&base))) return rc;
+  return modulation_run(m, dm, nmod, sigmas_host, n, out, base, (hipStream_t)stream);
 }
 
 int fbcache_should_skip(const float* x_after, const float* x_before, const float* anchor,

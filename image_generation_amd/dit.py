@@ -27,6 +27,7 @@ DIT_ERR_NONFINITE = -5
 DIT_F32, DIT_BF16, DIT_FP8, DIT_MXFP4, DIT_MXFP4_FP8ATTN = 0, 1, 2, 3, 4
 DIT_BLOCK_DOUBLE, DIT_BLOCK_SINGLE = 0, 1
 DIT_WS_ATTENTION, DIT_WS_BLOCK, DIT_WS_STEP, DIT_WS_MODULATION, DIT_WS_FBCACHE = range(5)
+DIT_MOD_STATIC_BYTES = 8 << 20   # static scratch of dit_modulation_static (include/dit.h)
 
 
 class DitDims(Structure):
@@ -118,6 +119,7 @@ def _load() -> ctypes.CDLL:
                                         POINTER(c_int)]),
         "dit_loop_graph_reset": (c_int, [P, POINTER(DitFBCache), c_int, P]),
         "dit_loop_graph_destroy": (c_int, [P]),
+        "dit_modulation_static": (c_int, [POINTER(DitModel), POINTER(c_double), c_int, P, P]),
         "dit_block_views_of": (c_int, [POINTER(DitDims), P, c_size_t, POINTER(DitBlockViews)]),
     }
     for name, (res, args) in sig.items():
@@ -134,7 +136,7 @@ EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_s
             "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4",
             "dit_loop_state_bytes", "dit_loop_graph_create", "dit_loop_graph_run",
             "dit_loop_graph_sync", "dit_loop_graph_reset", "dit_loop_graph_destroy",
-            "dit_block_views_of")
+            "dit_modulation_static", "dit_block_views_of")
 
 
 def _check(rc: int) -> None:
@@ -535,6 +537,17 @@ def block_views(dd: DitDims, ws: torch.Tensor) -> dict:
         "att_scale": view(v.att_scale, torch.float32, (rows,)),
         "hid_scale": view(v.hid_scale, torch.float32, (rows,)),
     }
+
+
+def dit_modulation_static(gm: GPUModel, sigmas: Sequence[float], out: torch.Tensor,
+                          stream=None) -> torch.Tensor:
+    """dit_modulation without a workspace: the library's static device scratch
+    holds the intermediates.  ``out`` is caller-allocated (fp32 [n, N_mod])."""
+    n = len(sigmas)
+    _need(out, torch.float32, (n, gm.n_mod), "out")
+    sig = (c_double * n)(*[float(s) for s in sigmas])
+    _check(LIB.dit_modulation_static(ctypes.byref(gm.model), sig, n, _ptr(out), _stream(stream)))
+    return out
 
 
 class FBCache:

@@ -29,8 +29,9 @@
  *     pointers (e.g. torch tensor data_ptr()), 16-byte aligned, contiguous,
  *     row-major.  The library allocates nothing and keeps no state between
  *     calls; scratch comes from a caller workspace sized by
- *     dit_workspace_bytes().  (One exception: the handle of a replayed loop,
- *     dit_loop_graph_create() to dit_loop_graph_destroy().)
+ *     dit_workspace_bytes().  (Two exceptions: the handle of a replayed loop,
+ *     dit_loop_graph_create() to dit_loop_graph_destroy(); and the static
+ *     device array that dit_modulation_static() uses instead of a workspace.)
  *   - stream: a hipStream_t (NULL = default stream).  Work is enqueued
  *     asynchronously; only fbcache_should_skip() and dit_denoise_step() with an
  *     enabled cache synchronise that stream, to hand the skip decision to the
@@ -359,6 +360,25 @@ DIT_API int dit_block_views_of(const dit_dims* dims, void* workspace, size_t ws_
  *   workspace >= DIT_WS_MODULATION bytes (for n). */
 DIT_API int dit_modulation(const dit_model* m, const double* sigmas_host, int n, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/* dit_modulation with no workspace argument and no allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same kernels and results as
+ * dit_modulation; their intermediates (the n x 256 timestep sinusoids and two
+ * n x D activations) live in a static device array of DIT_MOD_STATIC_BYTES
+ * that the library holds on each GPU it runs on until the process ends.
+ *   n steps need dit_workspace_bytes(dims, DIT_WS_MODULATION, n) bytes of it
+ *   (about n (256 + 2 D) 4 bytes: 327 steps at D 3072); a larger n returns
+ *   DIT_ERR_WORKSPACE before anything is enqueued.
+ *   Calls on one GPU share that GPU's array: calls that overlap on one GPU (on
+ *   different streams, or from several threads, before the earlier one's kernels
+ *   have finished) race and must be serialised by the caller.  Every
+ *   intermediate is written in full before it is read, so nothing carries over
+ *   from an earlier call.  The first call on a device looks up that device's
+ *   copy of the array (hipGetSymbolAddress); no call allocates or frees. */
+#define DIT_MOD_STATIC_BYTES (8u << 20)
+DIT_API int dit_modulation_static(const dit_model* m, const double* sigmas_host, int n,
+                                  float* out, void* stream);
 
 /* First-Block-Cache test.
  *   x_after: device fp32 joint stream [B, Lt + Li, D] after the first block

@@ -132,6 +132,18 @@ def test_invalid_arguments_rejected_before_launch():
     rc = L.dit_block_forward(ctypes.byref(d32), ctypes.byref(blk), dit.DIT_FP8, fake, dit.DIT_F32,
                              fake, 0, fake, fake, 1 << 30, None)
     assert rc == dit.DIT_ERR_UNSUPPORTED
+    # static-scratch modulation: more steps than its array holds, refused on the host
+    m = dit.DitModel()
+    m.dims = dit.dims_of(1, 8, 2, 4, 3072, 24, 12288)
+    m.n_double, m.n_single = 1, 0
+    m.time1 = m.time2 = m.mod = dit.DitLinear(4096, 4096, None)
+    m.dtype = dit.DIT_BF16
+    n = 400
+    assert dit.dit_workspace_bytes(m.dims, dit.DIT_WS_MODULATION, n) > dit.DIT_MOD_STATIC_BYTES
+    sig = (ctypes.c_double * n)(*([0.5] * n))
+    rc = L.dit_modulation_static(ctypes.byref(m), sig, n, fake, None)
+    assert rc == dit.DIT_ERR_WORKSPACE
+    assert b"static" in L.dit_last_error()
     # a negative token count
     d = dit.dims_of(1, -1, 2, 4, 256, 2, 512)
     assert dit.dit_workspace_bytes(d, dit.DIT_WS_BLOCK) == 0
