@@ -57,6 +57,8 @@ term, a wrong sign or index, a transposed operand:
   linear_mxfp4        test_mx4_blocks_route_every_linear_through_mxfp4,
                       test_mx4_double_block_zero_weights_keeps_biases_exact,
                       test_mxfp4_reproduces_representable_blocks
+  p448_fp32_window    test_attention_fp8_fp32_window_covers_fp32_decisions (an fp32
+                      evaluation emulated on the CPU flips only codes inside it)
   attention_fp8       test_attention_fp8_identical_keys_mean_of_v,
                       test_attention_fp8_identical_values_returned_exactly,
                       test_attention_fp8_exact_when_p_is_representable,
@@ -96,7 +98,7 @@ __all__ = [
     "double_block", "double_block_rows", "single_block", "single_block_rows", "final_layer", "fbcache_rel",
     "fbcache_decide", "fbcache_policy", "euler_update", "cfg_combine", "time_embed",
     "modulation_vectors", "denoise_step", "FBCacheState", "to64",
-    "linear_fp8", "linear_fp8_codes", "linear_mxfp4", "attention_fp8", "image_positions",
+    "linear_fp8", "linear_fp8_codes", "linear_mxfp4", "attention_fp8", "p448_fp32_window", "image_positions",
 ]
 
 LN_EPS = 1e-6
@@ -302,8 +304,24 @@ def linear_fp8_codes(qx, sx, w, b):
         * sw.astype(np.float64)[None, :] + b
 
 
+def p448_fp32_window(t, r, T, d):
+    """Relative error bound of 448 P = 2^(t - r + log2 448) formed in fp32 (R43):
+    t the score in log2 units, r the integer row reference, T the same score
+    with every product taken in magnitude (sum_c |q_c k_c| scale log2 e), d the
+    number of products.  Terms: the score summed in fp32 from exact products
+    (d roundings of partial sums no larger than T), the fp32 score scale (4
+    roundings of |t|), the fp32 reference minus log2 448 (the constant within
+    2^-21, one rounding), one fused multiply-add and exp2 within 2 ulps; an
+    error e in the exponent is a relative error ln 2 e of 448 P."""
+    u = 2.0 ** -24
+    l448 = math.log2(E4M3_MAX)
+    arg = t - r + l448
+    return math.log(2.0) * (d * u * T + 4 * u * np.abs(t) + u * np.abs(r - l448) + 2.0 ** -21
+                            + u * np.abs(arg)) + 2 * u
+
+
 def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
-                  tie_rel: Optional[float] = None):
+                  tie_rel: Optional[float] = None, tie_fp32: bool = False):
     """fp8 attention (R27).
 
     Q, K and V each get one e4m3 scale per (batch, head), taken over that head's
@@ -318,10 +336,19 @@ def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
     output is then the mean of the dequantised V.  ``rows`` restricts the
     output to those query rows (each row is independent of the others).
 
-    With ``tie_rel`` the call returns (out, slack): slack bounds, to first
-    order, how far the output moves when every P code whose 448 P lies within
-    tie_rel (relative) of an e4m3 rounding boundary rounds the other way -- the
-    spread of equally valid results that a computation of P in fp32 can give.
+    Slack (returned as (out, slack) when a window is asked for): a first-order
+    bound on how far the output moves when every P code whose 448 P lies within
+    its window of an e4m3 rounding boundary rounds the other way -- the spread
+    of equally valid results that an evaluation of 448 P in fp32 can give.  The
+    window is either the constant relative width ``tie_rel``, or, with
+    ``tie_fp32``, each score's own bound on the relative error of 448 P formed
+    in fp32 (R43): the score summed from exact e4m3 products in fp32 (at most d
+    roundings, each within u = 2^-24 of a partial sum no larger than
+    sum_c |q_c k_c|), times the fp32 score scale (4 roundings of |t|), minus the
+    reference shifted by log2 448 (an fp32 constant within 2^-21, one rounding
+    of |r - log2 448|), one fused multiply-add (u |arg|) and an exp2 within 2
+    ulps: rel = ln 2 (d u T + 4 u |t| + u |r - 8.8| + 2^-21 + u |arg|) + 2 u,
+    T = scale log2(e) sum_c |q_c k_c| in the dequantised values.
     """
     d = q.shape[-1]
     if scale is None:
@@ -329,7 +356,8 @@ def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
     B, H, L, _ = q.shape
     sel = np.arange(L) if rows is None else np.asarray(rows)
     out = np.empty((B, H, len(sel), d))
-    slack = np.zeros_like(out) if tie_rel is not None else None
+    want_slack = tie_rel is not None or tie_fp32
+    slack = np.zeros_like(out) if want_slack else None
 
     def deq(t):
         codes, sc = quantize_rows_e4m3(t.reshape(1, -1))
@@ -339,13 +367,19 @@ def attention_fp8(q, k, v, scale: Optional[float] = None, rows=None,
         for h in range(H):
             qd, kd, vd = deq(q[bi, h]), deq(k[bi, h]), deq(v[bi, h])
             t = (qd[sel] @ kd.T) * (scale / math.log(2.0))
-            p = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)))
+            r = np.ceil(t.max(axis=1, keepdims=True))
+            p = np.exp2(t - r)
             pq = round_e4m3(p * E4M3_MAX) / E4M3_MAX
             lq = pq.sum(axis=1, keepdims=True)
             out[bi, h] = (pq @ vd) / lq
-            if slack is not None:
+            if want_slack:
+                if tie_fp32:
+                    T = (np.abs(qd[sel]) @ np.abs(kd).T) * (scale / math.log(2.0))
+                    rel = p448_fp32_window(t, r, T, d)
+                else:
+                    rel = tie_rel
                 # moving one weight by a step changes the output by step * (v_j - out) / l
-                tie, step = e4m3_tie_mask(p * E4M3_MAX, tie_rel)
+                tie, step = e4m3_tie_mask(p * E4M3_MAX, rel)
                 w = np.where(tie, step / E4M3_MAX, 0.0)
                 slack[bi, h] = (w @ np.abs(vd) + w.sum(axis=1, keepdims=True)
                                 * np.abs(out[bi, h])) / lq

@@ -90,11 +90,12 @@ def round_fp16(x) -> np.ndarray:
     return np.where(np.isnan(x), np.nan, out)
 
 
-def e4m3_tie_mask(y, rel: float):
+def e4m3_tie_mask(y, rel):
     """(mask, step): mask marks the y (>= 0, <= 448) that lie within rel * y of
     an e4m3 rounding boundary (a midpoint between neighbouring codes), where a
     computation carried in a different precision may round the other way;
-    step is the spacing of e4m3 values around y."""
+    step is the spacing of e4m3 values around y.  rel: a scalar or an array
+    broadcast against y."""
     y = np.asarray(y, dtype=np.float64)
     _, e = np.frexp(y)
     step = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)

@@ -667,6 +667,49 @@ def test_modulation_vectors_hand_derived():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
 
 
+
+def test_attention_fp8_fp32_window_covers_fp32_decisions():
+    # p448_fp32_window must bound the relative error of 448 P evaluated in fp32,
+    # score by score: scores summed sequentially in fp32 from the exact e4m3
+    # products (the worst ordering), the fp32 score scale, one fused multiply-add
+    # against the fp32 reference, exp2 in fp32 -- so every P code such an
+    # evaluation can decide differently lies inside the window.  Small and large
+    # score magnitudes both occur.
+    rng = np.random.default_rng(21)
+    d, L = 128, 256
+    worst = 0.0
+    for trial in range(3):
+        q = rng.standard_normal((1, 1, L, d)) * (1.0 + 2 * trial)
+        k = rng.standard_normal((1, 1, L, d))
+        qc, sq = quantize_rows_e4m3(q[0, 0].reshape(1, -1))
+        kc, sk = quantize_rows_e4m3(k[0, 0].reshape(1, -1))
+        qc = qc.reshape(L, d).astype(np.float32)
+        kc = kc.reshape(L, d).astype(np.float32)
+        s32 = np.zeros((L, L), dtype=np.float32)
+        for c in range(d):                                # fp32, one rounding per add
+            s32 = (s32 + np.outer(qc[:, c], kc[:, c]).astype(np.float32)).astype(np.float32)
+        scale = 1.0 / math.sqrt(d)
+        scale_log2 = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+        cs = np.float32(np.float32(scale_log2 * sq[0]) * sk[0])
+        qd = qc.astype(np.float64) * float(sq[0])
+        kd = kc.astype(np.float64) * float(sk[0])
+        t64 = qd @ kd.T * (scale / math.log(2.0))
+        r = np.ceil(t64.max(axis=1, keepdims=True))
+        moff = (r.astype(np.float32) - np.float32(math.log2(448.0))).astype(np.float32)
+        arg = (s32.astype(np.float64) * float(cs) - moff.astype(np.float64)).astype(np.float32)
+        y32 = np.exp2(arg).astype(np.float64)
+        y64 = np.exp2(t64 - r) * 448.0
+        T = np.abs(qd) @ np.abs(kd).T * (scale / math.log(2.0))
+        rel = O.p448_fp32_window(t64, r, T, d)
+        err = np.abs(y32 - y64) / y64
+        worst = max(worst, float(np.max(err / rel)))
+        assert np.all(err <= rel), (trial, float(np.max(err / rel)))
+        # and the window stays narrow: a small share of codes lies inside it
+        tie, _ = e4m3_tie_mask(y64, rel)
+        assert tie.mean() < 0.02
+    print(f"largest fp32 error / window: {worst:.3f}")
+    assert worst > 1e-3            # the emulation's error is measured, not zero
+
 # ---------------------------------------------------------------- FBC
 
 def test_fbcache_rel_vs_python_loop():
