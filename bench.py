@@ -208,8 +208,11 @@ def mxfp4_gemms(dit, device, reps=10):
     return out
 
 
-def loop_2048_fp8(dit, DI, device, K, warmup):
-    """K steps of the fp8 W8A8 model at 2048px (CFG pair), FBC threshold 0."""
+def loop_2048_fp8(dit, DI, device, K, warmup, k_shares=2):
+    """The fp8 W8A8 model at 2048px (CFG pair, guidance 3.5, 50-step schedule with
+    shift 3): K steps through the replayed step graph at FBC threshold 0 (every
+    step computed) and the same K steps at the workload's threshold 0.2; kernel
+    shares from a separate instrumented eager pass of k_shares steps."""
     import torch
     w = DI.WORKLOADS["flux_2048_fp8_cfg"]
     dims = w.dims
@@ -221,9 +224,12 @@ def loop_2048_fp8(dit, DI, device, K, warmup):
     ws = dit.workspace(gm.model.dims, dit.DIT_WS_STEP)
     if warmup:
         run_loop(dit, gm, sig, txt, lat0, ws, 0.0, warmup)
-    timer = dit.KernelTimer(ALL_SITES, capacity=40 * (dims.n_double + dims.n_single) * K + 256)
-    log(f"[bench] fp8 timed: {K} steps")
-    secs, skipped, _ = run_loop(dit, gm, sig, txt, lat0, ws, 0.0, K, timer)
+    log(f"[bench] fp8 2048px: {K} replayed steps at threshold 0, then at {w.threshold}")
+    secs, skipped, _ = run_replayed(dit, gm, sig, txt, lat0, 0.0, K)
+    assert skipped == 0
+    secs_c, skipped_c, rels_c = run_replayed(dit, gm, sig, txt, lat0, w.threshold, K)
+    timer = dit.KernelTimer(ALL_SITES, capacity=40 * (dims.n_double + dims.n_single) * k_shares + 256)
+    run_loop(dit, gm, sig, txt, lat0, ws, 0.0, k_shares, timer)
     by = site_totals(timer.durations_ms())
     timer.close()
     del gm, ws
@@ -231,19 +237,53 @@ def loop_2048_fp8(dit, DI, device, K, warmup):
     B, L, Li = w.B, w.L, w.Li
     att_n, att_ms = by.get("attention", [0, 0.0])
     att_f = attn_flops_per_launch(B, dims.H, L, dims.d)
-    gemm_f = (gemm_flops_per_step(dims, B, w.Lt, Li, dims.C_in) - 2.0 * B * Li * dims.D * dims.C_in) * K
+    gemm_f = (gemm_flops_per_step(dims, B, w.Lt, Li, dims.C_in) - 2.0 * B * Li * dims.D * dims.C_in) * k_shares
     gemm_ms = sum(by.get(s_, [0, 0.0])[1] for s_ in BLOCK_GEMM_SITES)
     att_tf = att_f * att_n / (att_ms * 1e-3) / 1e12
     gemm_tf = gemm_f / (gemm_ms * 1e-3) / 1e12
+    nb = dims.n_double + dims.n_single
     return {"workload": w.name, "image_px": w.image_px, "tokens": [w.Lt, Li], "batch": B,
-            "guidance": w.guidance, "dtype": "fp8 e4m3 (W8A8)", "steps": K, "warmup": warmup,
+            "guidance": w.guidance, "dtype": "fp8 e4m3 (W8A8)", "euler_steps": w.steps,
+            "shift": w.shift, "loop": "replayed step graph", "steps": K, "warmup": warmup,
             "steps_per_s": round(K / secs, 4), "ms_per_step": round(1e3 * secs / K, 2),
+            "fbcache": {"threshold": w.threshold, "steps_per_s": round(K / secs_c, 4),
+                        "skipped_steps": skipped_c,
+                        "rel_l1": [None if not math.isfinite(r) else round(r, 5) for r in rels_c]},
             "attention_tflops": round(att_tf, 1),
             "attention_frac_fp8_peak": round(att_tf / PEAK_FP8_TFLOPS, 4),
             "block_gemm_tflops": round(gemm_tf, 1),
             "block_gemm_frac_fp8_peak": round(gemm_tf / PEAK_FP8_TFLOPS, 4),
-            "quant_ms_per_step": round(by.get("quant", [0, 0.0])[1] / K, 3),
+            "quant_ms_per_step": round(by.get("quant", [0, 0.0])[1] / k_shares, 3),
+            "hbm_kernels": hbm_rates(by, B, w.Lt, Li, dims, nb, k_shares, fp8=True),
             "kernels": kernel_table(by)}
+
+
+def hbm_rates(by, B, Lt, Li, dims, nblocks, steps, fp8=False):
+    """Achieved GB/s of the bandwidth-bound kernels from their algorithmic bytes
+    (what each must read and write once) and the instrumented pass's times:
+      LN-modulate: fp32 residual row in, bf16 (or e4m3 + row scale) out, two per
+        double block and one per single block, over all B L rows, and the
+        velocity head's over the image rows;
+      First-Block-Cache test: the first block's image rows (after and before)
+        and the anchor read, the residual written (16 B per element; the first
+        step has no anchor: 12 B);
+      fp8 quantisation: bf16 in, e4m3 out (3 B per element) for Q, K, V, the
+        attention output and the GELU hidden of every block."""
+    D, F = dims.D, dims.F
+    L = Lt + Li
+    ln_calls = (2 * dims.n_double + dims.n_single) * steps
+    ln_bytes = ln_calls * B * L * D * (4 + (1 if fp8 else 2))
+    ln_bytes += steps * B * Li * D * (4 + 2)         # the velocity head's LN (image rows)
+    fbc_bytes = B * Li * D * (12 + 16 * (steps - 1))
+    quant_bytes = nblocks * steps * B * L * (4 * D + F) * 3 if fp8 else 0
+    out = {}
+    for site, nbytes in (("ln", ln_bytes), ("fbc", fbc_bytes), ("quant", quant_bytes)):
+        n, ms = by.get(site, [0, 0.0])
+        if n and nbytes:
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[site] = {"launch_sites": n, "bytes": int(nbytes), "total_ms": round(ms, 3),
+                         "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def loop_1024_mxfp4(dit, DI, device, K, warmup, bf16_steps_per_s=None, fp8_attention=False):
@@ -406,7 +446,7 @@ def main():
                     help="skip the 1024px loop with MXFP4 block linears")
     ap.add_argument("--no-tiny", action="store_true",
                     help="skip the tiny-model loop latency (eager vs replayed step graph)")
-    ap.add_argument("--fp8-steps", type=int, default=3)
+    ap.add_argument("--fp8-steps", type=int, default=10)
     ap.add_argument("--only-2048", action="store_true",
                     help="run only the 2048px block and fp8 loop (profiling runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -532,6 +572,8 @@ def main():
         "block_gemm_frac_peak": (round(block_gemm_tflops / PEAK_BF16_TFLOPS, 4)
                                  if block_gemm_tflops else None),
         "linear1_tflops": round(lin1_tflops, 1) if lin1_tflops else None,
+        "linear1_frac_peak": round(lin1_tflops / PEAK_BF16_TFLOPS, 4) if lin1_tflops else None,
+        "hbm_kernels": hbm_rates(by_site, B, w.Lt, Li, dims, dims.n_double + dims.n_single, K),
         "kernels": kernels,
         "roofline": roofline,
     }

@@ -19,9 +19,10 @@ from _helpers import parity_err, parity_err_bf16_stored, sampled_block_rows
 pytestmark = pytest.mark.gpu
 
 TOL_FP8 = 6e-2
-# P codes: the kernel forms 448 P in fp32 (a few ulps from the fp64 value), so a
-# code within 2e-5 (relative) of an e4m3 rounding boundary may round either way
-TIE_REL = 2e-5
+# P codes: the kernel forms 448 P in fp32, so a code whose 448 P lies within the
+# fp32 evaluation's error bound of an e4m3 rounding boundary may round either way;
+# the oracle derives that bound score by score (p448_fp32_window) and returns the
+# spread such codes can cause as a per-element slack
 
 
 def _err_with_slack(got, ref, slack):
@@ -102,7 +103,7 @@ def test_attention_fp8_small(dit, B, H, L, d):
     _say(f"attention fp8 B={B} H={H} L={L} d={d}")
     q, k, v = _bf16((B, H, L, d), 51), _bf16((B, H, L, d), 52), _bf16((B, H, L, d), 53)
     got = _run_fp8_attention(dit, q, k, v)
-    ref, slack = O.attention_fp8(O.to64(q), O.to64(k), O.to64(v), tie_rel=TIE_REL)
+    ref, slack = O.attention_fp8(O.to64(q), O.to64(k), O.to64(v), tie_fp32=True)
     err = _err_with_slack(got, ref, slack)
     _say(f"  err {err:.3e} (without slack {parity_err_bf16_stored(got, ref):.3e})")
     assert err <= TOL_FP8
@@ -128,7 +129,7 @@ def test_attention_fp8_full_size_sampled(dit, B, L):
     got = _run_fp8_attention(dit, q, k, v)
     rng = np.random.default_rng(1)
     rows = np.sort(np.concatenate([rng.choice(L, 40, replace=False), [0, L - 1, 511, 512]]))
-    ref, slack = O.attention_fp8(O.to64(q), O.to64(k), O.to64(v), rows=rows, tie_rel=TIE_REL)
+    ref, slack = O.attention_fp8(O.to64(q), O.to64(k), O.to64(v), rows=rows, tie_fp32=True)
     err = _err_with_slack(got[:, :, rows], ref, slack)
     _say(f"  err {err:.3e} (without slack {parity_err_bf16_stored(got[:, :, rows], ref):.3e})")
     assert err <= TOL_FP8
@@ -151,16 +152,46 @@ def _block_fp8_setup(dit, dims, w, kind, x_dtype):
     return params, dev8, inp, blk, dd, rope, ws, x
 
 
-def _oracle_block_fp8(params, inp, w, dims, kind):
+def _oracle_block_fp8(params, inp, w, dims, kind, fp8=True):
     P = {k: O.to64(v) for k, v in params.items()}
     x = O.to64(inp["x"])
     mod = O.to64(inp["mod"])
     ang = O.rope_table(O.image_positions(w.grid_h, w.grid_w, w.Lt), dims.d)
     if kind == "double":
         xt, xi = O.double_block(x[:, :w.Lt], x[:, w.Lt:], mod[:, :6], mod[:, 6:], P, ang, dims.H,
-                                fp8=True)
+                                fp8=fp8)
         return np.concatenate([xt, xi], axis=1)
-    return O.single_block(x, mod, P, ang, dims.H, fp8=True)
+    return O.single_block(x, mod, P, ang, dims.H, fp8=fp8)
+
+
+# The fp8 branch (x_out - x_in) end to end.  Each stage of an fp8 block agrees
+# with the oracle on identical inputs (codes bit-exact, floats within 1e-4:
+# test_gpu_fp8_stages.py); end to end the two differ only where near-tie codes
+# (LN output, attention's P) were decided the other way and moved later
+# quantisation inputs -- one such P code moves an fp8 attention output by up to
+# ~0.2 of its RMS, so the largest element of the difference is not a stable
+# measure (it varies by tens of percent between equally valid evaluations).  The
+# branch is therefore held to RMS properties against the unquantised oracle
+# branch E, like the MXFP4 blocks: RMS(kernel - oracle) <= FP8_TIE_SHARE x
+# RMS(oracle - E), and RMS(kernel - E) <= 1.05 x RMS(oracle - E).  A wrong scale,
+# a skipped quantisation or a mixed-up head fails both.
+FP8_TIE_SHARE = 0.5
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def _check_fp8_branch(got, ref8, exact, x0):
+    b_gpu, b_orc, b_ex = got - x0, ref8 - x0, exact - x0
+    q_orc = _rms(b_orc - b_ex)
+    d_rms = _rms(b_gpu - b_orc)
+    e_gpu = _rms(b_gpu - b_ex)
+    _say(f"  branch RMS: kernel vs oracle fp8 {d_rms:.3e} ({d_rms / q_orc:.3f} of the fp8 effect "
+         f"{q_orc:.3e}); kernel vs unquantised {e_gpu:.3e}; max-norm kernel vs oracle "
+         f"{parity_err(b_gpu, b_orc):.3e}")
+    assert d_rms <= FP8_TIE_SHARE * q_orc
+    assert e_gpu <= 1.05 * q_orc
 
 
 FP8_BLOCK_CASES = [
@@ -189,22 +220,18 @@ def test_block_forward_fp8(dit, D, H, F, B, Lt, gh, gw, kind, xdt):
     ref = _oracle_block_fp8(params, inp, w, dims, kind)
     got = x.double().cpu().numpy()
     err = parity_err_bf16_stored(got, ref) if xdt == torch.bfloat16 else parity_err(got, ref)
-    derr = parity_err(got - x_in.double().cpu().numpy(), ref - O.to64(inp["x"]))
-    _say(f"  x_out err {err:.3e} branch err {derr:.3e}")
+    _say(f"  x_out err {err:.3e}")
     assert err <= TOL_FP8
+    if xdt == torch.float32:
+        exact = _oracle_block_fp8(params, inp, w, dims, kind, fp8=False)
+        _check_fp8_branch(got, ref, exact, O.to64(inp["x"]))
 
 
 @pytest.mark.parametrize("half", ["attention", "mlp"])
 def test_block_forward_fp8_double_halves(dit, half):
-    """Each half of the fp8 double block on its own (the other half's gates set to 0).
-
-    e4m3 rounding is far from exact here (the oracle's own fp8 branch sits at
-    max-norm ~0.7-1.3 from the unquantised branch) and near-tie codes that the
-    fp32 kernel and the fp64 oracle round differently move later quantisation
-    inputs, so the branch is checked as a property: the kernel's branch is no
-    further from the unquantised branch than the oracle's fp8 branch (10%
-    margin), and the block output meets the fp8 bound.
-    """
+    """Each half of the fp8 double block on its own (the other half's gates set
+    to 0): the block output meets the fp8 bound and the branch is held to the
+    share of the oracle's own quantisation effect described above."""
     _say(f"fp8 double block, {half} half only")
     dims = DI.Dims(D=3072, H=24, F=12288, n_double=1, n_single=0)
     w = DI.Workload("t", dims, B=1, grid_h=12, grid_w=20, Lt=32, dtype="fp8")
@@ -223,15 +250,13 @@ def test_block_forward_fp8_double_halves(dit, half):
     ang = O.rope_table(O.image_positions(w.grid_h, w.grid_w, w.Lt), dims.d)
     xt, xi = O.double_block(x0[:, :w.Lt], x0[:, w.Lt:], mod[:, :6], mod[:, 6:], P, ang, dims.H)
     exact = np.concatenate([xt, xi], axis=1)
-    e_gpu = parity_err(got - x0, exact - x0)
-    e_orc = parity_err(ref8 - x0, exact - x0)
     err = parity_err(got, ref8)
-    _say(f"  branch vs unquantised: kernel {e_gpu:.3e} oracle fp8 {e_orc:.3e}; "
-         f"x_out err {err:.3e} (branch vs oracle {parity_err(got - x0, ref8 - x0):.3e})")
-    assert e_gpu <= 1.1 * e_orc
+    _say(f"  x_out err {err:.3e}")
+    _check_fp8_branch(got, ref8, exact, x0)
     assert err <= TOL_FP8
 
 
+@pytest.mark.timeout(400)
 def test_block_forward_fp8_flux_1024(dit):
     """The full fp8 double block at the 1024px shape (4096 image + 512 text tokens)."""
     _say("fp8 block double full 1024px")
@@ -245,12 +270,14 @@ def test_block_forward_fp8_flux_1024(dit):
     del dev8, ws
     ref = _oracle_block_fp8(params, inp, w, dims, "double")
     err = parity_err(got, ref)
-    _say(f"  err {err:.3e}")
+    _say(f"  x_out err {err:.3e}")
     assert err <= TOL_FP8
+    exact = _oracle_block_fp8(params, inp, w, dims, "double", fp8=False)
+    _check_fp8_branch(got, ref, exact, O.to64(inp["x"]))
 
 
 
-@pytest.mark.timeout(300)        # the fp64 oracle's share takes ~1 min on 8 cores
+@pytest.mark.timeout(600)        # the fp64 oracle's share takes ~2 min on 8 cores
 def test_block_forward_fp8_2048_cfg_sampled(dit):
     """The fp8 double block at the 2048px CFG-pair shape of the fp8 model step
     (2 x (16384 image + 512 text) tokens, D 3072, fp32 residual stream, per-batch
@@ -274,9 +301,11 @@ def test_block_forward_fp8_2048_cfg_sampled(dit):
     ref = O.double_block_rows(x64[:, :w.Lt], x64[:, w.Lt:], m64[:, :6], m64[:, 6:], P, ang,
                               dims.H, rows, fp8=True)
     err = parity_err(got, ref)
-    derr = parity_err(got - x64[:, rows], ref - x64[:, rows])
-    _say(f"  rows {len(rows)} x_out err {err:.3e} branch err {derr:.3e}")
+    _say(f"  rows {len(rows)} x_out err {err:.3e}")
     assert err <= TOL_FP8
+    exact = O.double_block_rows(x64[:, :w.Lt], x64[:, w.Lt:], m64[:, :6], m64[:, 6:], P, ang,
+                                dims.H, rows)
+    _check_fp8_branch(got, ref, exact, x64[:, rows])
 
 
 # ---------------------------------------------------------------- full step
