@@ -51,16 +51,11 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 1070525 * 1024 + 241488 * 1024,
+    "gemm_lin1": {"bytes": 525236 * 2 * 1024 + 250799 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "c1da96acaf660510a751270e7e1aa35607be8801"},
-    "attention": {"bytes": 101508 * 1024 + 27688 * 1024,
-                  "source": "image_generation_amd/csrc/attention.hip",
-                  "begin": "constexpr int ATT_D = 128;",
-                  "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
-                  "sha1": "d448700a0993f9c3df91abae76e9dc17cd5d50f2"},
+                  "sha1": "2cf4b36ad553ff5326b8856da6424e5c5043fedd"},
 }
 
 
@@ -433,6 +428,80 @@ def cpu_baseline(DI, w):
                        f"({t_block:.2f} s), extrapolated to the {nblk} blocks of a step")}
 
 
+GEMM_SHAPES = {"lin1": (4608, 3072, 21504), "lin2": (4608, 15360, 3072),
+               "oproj": (4608, 3072, 3072), "qkv": (4608, 3072, 9216),
+               "fc1": (4608, 3072, 12288)}
+ATTN_SHAPES = {"1024": (1, 4608), "2048": (2, 16896)}
+
+
+def event_time_us(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def micro_gemm(dit, reps, shapes):
+    """The library's bf16 tiled GEMM (dit_linear_forward, bf16 out) at the 1024px
+    block shapes (M x K x N), beside torch.matmul (hipBLASLt) on the same operands."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name in shapes:
+        M, K, N = GEMM_SHAPES[name]
+        x = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+        w = (torch.randn((N, K), device="cuda", generator=g) * K ** -0.5).to(torch.bfloat16)
+        b = torch.zeros((N,), device="cuda", dtype=torch.float32)
+        y = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+        wt = w.t()
+        res = {"mkn": [M, K, N]}
+        for impl, fn in (("library", lambda: dit.dit_linear_forward(x, w, b, y)),
+                         ("hipblaslt", lambda: torch.matmul(x, wt, out=y))):
+            us = event_time_us(fn, reps)
+            tf = 2.0 * M * N * K / us / 1e6
+            res[impl] = {"us": round(us, 1), "tflops": round(tf, 1),
+                         "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        out[name] = res
+        log(f"[micro] gemm {name} {res}")
+    return out
+
+
+def micro_attention(dit, reps, shapes, dtypes):
+    """dit_attention alone, 24 heads x 128, at the 1024px (1 x 4608 tokens) and 2048px
+    CFG-pair (2 x 16896) shapes; fp8 takes per-(b, h) e4m3 codes from dit_quantize_rows."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name in shapes:
+        B, L = ATTN_SHAPES[name]
+        H, d = 24, 128
+        for dt in dtypes:
+            q, k, v = (torch.randn((B, H, L, d), device="cuda", generator=g).to(torch.bfloat16)
+                       for _ in range(3))
+            o = torch.empty((B, L, H * d), device="cuda", dtype=torch.bfloat16)
+            kw = {}
+            if dt == "fp8":
+                ops = []
+                for t in (q, k, v):
+                    c, sc = dit.dit_quantize_rows(t.reshape(B * H, L * d))
+                    ops.append((c.view(B, H, L, d), sc.view(B, H)))
+                (q, sq), (k, sk), (v, sv) = ops
+                kw = dict(q_scale=sq, k_scale=sk, v_scale=sv)
+            us = event_time_us(lambda: dit.dit_attention(q, k, v, o, **kw), reps)
+            tf = attn_flops_per_launch(B, H, L, d) / (us * 1e-6) / 1e12
+            peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_FP8_TFLOPS
+            out[f"{name}_{dt}"] = {"B": B, "L": L, "us": round(us, 1), "tflops": round(tf, 1),
+                                   "frac_peak": round(tf / peak, 4)}
+            log(f"[micro] attention {name} {dt} {out[name + '_' + dt]}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,6 +521,12 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES of device memory 3 times (calibrates the HBM "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--micro", choices=["gemm", "attention"],
+                    help="only time one kernel family alone at the block shapes (profiling)")
+    ap.add_argument("--reps", type=int, default=20, help="launches per --micro shape")
+    ap.add_argument("--shapes", default=None,
+                    help="comma list: gemm lin1,lin2,oproj,qkv,fc1; attention 1024,2048")
+    ap.add_argument("--dtypes", default="bf16,fp8", help="--micro attention: bf16,fp8")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -469,6 +544,17 @@ def main():
         return
     import dit_inputs as DI
     from image_generation_amd import dit
+
+    if args.micro:
+        torch.cuda.set_device(0)
+        if args.micro == "gemm":
+            shapes = args.shapes.split(",") if args.shapes else list(GEMM_SHAPES)
+            res = micro_gemm(dit, args.reps, shapes)
+        else:
+            shapes = args.shapes.split(",") if args.shapes else list(ATTN_SHAPES)
+            res = micro_attention(dit, args.reps, shapes, args.dtypes.split(","))
+        print(json.dumps({"micro": args.micro, "reps": args.reps, "results": res}), flush=True)
+        return
 
     w = DI.WORKLOADS[args.workload]
     if w.dtype != "bf16":

@@ -6,8 +6,9 @@
 // Q, K and V arrive in the same layout, [B, H, L, d] row-major.
 //
 // Work split: one workgroup = 8 wave64s = 256 queries of one (b, h); each wave
-// owns 32 queries, two waves share a SIMD so one wave's softmax arithmetic runs
-// while the other's MFMAs do.  Scores are computed transposed, S^T = K Q^T, so
+// owns 32 queries and two waves share a SIMD.  In the bf16 kernel the two waves
+// of a SIMD run half a tile apart (see the kernel), so one's softmax arithmetic
+// runs while the other's score MFMAs do.  Scores are computed transposed, S^T = K Q^T, so
 // every lane owns a query column: the softmax max is an in-lane reduction plus
 // one exchange with lane ^ 32, and the row sum needs no exchange until the end.
 // K rows are fed to the MFMA in the order (r with bits 2 and 3 swapped), which
@@ -35,9 +36,9 @@
 // skipped.  The reference cancels exactly in O / l.  P enters P V^T as bf16.
 //
 // K/V tiles of 64 keys are double-buffered in LDS, filled by direct
-// global->LDS loads (each wave instruction writes 1 KB contiguously; the padded
-// K rows and the permuted V rows are built by giving each lane the chunk that
-// belongs at its slot).  Keys past L load row L - 1 and are masked to -inf;
+// global->LDS loads (each wave instruction writes 1 KB contiguously; padded or
+// permuted K rows and permuted V rows are built by giving each lane the chunk
+// that belongs at its slot).  Keys past L load row L - 1 and are masked to -inf;
 // queries past L are computed on clamped rows and not stored.
 #include "common.h"
 #include "kernels.h"
@@ -133,19 +134,96 @@ struct AttLoads {
   }
 };
 
+// One 64-key tile of K or V in LDS: 64 unpadded rows of D elements whose 16-byte
+// chunks sit permuted by an XOR with a function of the row.  K's permutation puts
+// the 16 rows that one LDS cycle serves to a fragment read (16 lanes x 16 bytes,
+// one chunk of 16 different keys) in 16 distinct bank groups; V's serves the
+// transposing reads (see vswz).  A tile is NI 1-KB direct-to-LDS loads, IPW per wave.
+template <int D, int ES>
+struct KVTile {
+  static constexpr int ROW = D * ES;
+  static constexpr int CPR = ROW / 16;
+  static constexpr int BYTES = ATT_BN * ROW;
+  static constexpr int NI = BYTES / 1024;
+  static constexpr int IPW = NI / ATT_WAVES;
+  static_assert(NI % ATT_WAVES == 0, "tile loads split evenly over the waves");
+  static __device__ __forceinline__ int kswz(int r) {
+    return ROW == 256 ? (r & 15) : ((r >> 1) & 7);
+  }
+};
+
+// Per-lane source of a tile's direct-to-LDS loads: instruction wave + 8 j covers
+// LDS chunks (wave + 8 j) * 64 + lane, i.e. row `row[j]` and the logical chunk
+// whose elements start at `off[j]`.
+template <int D, int ES, bool IS_K>
+struct TileLoads {
+  using T = KVTile<D, ES>;
+  int row[T::IPW];
+  int off[T::IPW];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < T::IPW; ++j) {
+      const int sl = (wave + j * ATT_WAVES) * 64 + lane;
+      const int r = sl / T::CPR, pc = sl - r * T::CPR;
+      const int lc = pc ^ (IS_K ? T::kswz(r) : AttGeo<D, ES>::vswz(r));
+      row[j] = r;
+      off[j] = lc * (16 / ES);
+    }
+  }
+  // rows kv0 .. kv0 + 63 of one (b, h) into dst; rows past L load row L - 1
+  template <class E>
+  __device__ __forceinline__ void issue(char* dst, const E* base, int kv0, int L, int wave) const {
+#pragma unroll
+    for (int j = 0; j < T::IPW; ++j) {
+      const int r = min(kv0 + row[j], L - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)r * D + off[j]),
+                                       (void*)(dst + (wave + j * ATT_WAVES) * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a wave-uniform n in 0..3
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+  if (n >= 3) __builtin_amdgcn_s_waitcnt(3 | 0x0070);
+  else if (n == 2) __builtin_amdgcn_s_waitcnt(2 | 0x0070);
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(1 | 0x0070);
+  else __builtin_amdgcn_s_waitcnt(0x0070);
+}
+
+// Two wave groups in ping-pong: waves 0-3 and 4-7 (one of each per SIMD) run the
+// same work one segment apart.  Each tile takes two barrier-separated segments;
+// in each segment one group computes a tile's scores (MFMA-bound) while the other
+// turns the previous tile's scores into P and P V^T (exp2-bound, with the P V^T
+// MFMAs), so a SIMD's MFMA and vector units both have work at once instead of its
+// two waves queueing on the same unit.  Segment hs runs, for group r, step hs - r:
+// the scores of tile (hs - r)/2 when even, its P V^T when odd.
+//
+// K and V each have two LDS buffers, four arrays always named statically (the
+// loop is unrolled over two tiles), so the compiler knows which array a pending
+// direct-to-LDS load writes and lets reads of the others proceed.  K(t) is loaded
+// in segment 2t - 2, after its buffer's last reader (group 1's scores of tile
+// t - 2, segment 2t - 3); V(t) in segment 2t - 1, after group 1's P V^T of tile
+// t - 2.  A batch has landed by the end of the segment after the one issuing it,
+// one segment before its first reader.  Segments end in a plain s_barrier after
+// the wave's own waits (__syncthreads()' fence would also wait for the batch in
+// flight).
 template <int D>
 __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
     const int* __restrict__ gate) {
+  using T = KVTile<D, 2>;
   using G = AttGeo<D, 2>;
   if (gate_closed(gate)) return;
-  __shared__ __attribute__((aligned(1024))) char st0[G::SB];
-  __shared__ __attribute__((aligned(1024))) char st1[G::SB];
+  __shared__ __attribute__((aligned(1024))) char sk0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[T::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave >> 2;         // ping-pong group
   const int g = lane >> 5;           // lane group
   const int l32 = lane & 31;
 
@@ -182,8 +260,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   float mref = -INFINITY;     // reference max (raw score units)
   float lsum = 0.f;           // this lane's partial row sum, relative to mref
 
-  AttLoads<D, 2> ld;
-  ld.init(wave, lane);
+  TileLoads<D, 2, true> ldk;
+  TileLoads<D, 2, false> ldv;
+  ldk.init(wave, lane);
+  ldv.init(wave, lane);
 
   // transposing V reads: lane 4e + q of its 16-lane group sources key
   // (chunk base) + e, channels db*32 + (group & 1)*16 + 4q .. + 3
@@ -192,25 +272,21 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   int vbase[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
-    vbase[db] = (g * 8 + te) * G::VROW +
+    vbase[db] = (g * 8 + te) * T::ROW +
                 (((4 * db + 2 * (tg & 1) + (tq >> 1)) ^ vsw) << 4) + 8 * (tq & 1);
 
   const int ntiles = (L + ATT_BN - 1) / ATT_BN;
-  const int krow_perm = swap23(l32);
-  ld.issue(st0, Kb, Vb, 0, L, wave);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
+  // K fragment of key block kb, d-chunk c: row kb*32 + swap23(l32), logical
+  // 16-byte chunk 2c + g, stored at chunk (2c + g) ^ kswz(row) = kc0 ^ 2c
+  const int krow = swap23(l32);
+  const int kbase = krow * T::ROW;
+  const int kc0 = g ^ T::kswz(krow);   // the same for krow + 32
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    char* cur = (kt & 1) ? st1 : st0;
-    char* nxt = (kt & 1) ? st0 : st1;
-    if (kt + 1 < ntiles) ld.issue(nxt, Kb, Vb, kt + 1, L, wave);
-    const char* sK = cur;
-    const char* sV = cur + G::KB;
+  f32x16 sacc[2];
+  // ---- scores of tile kt from K buffer sK: element e of sacc[kb] is key kv0 +
+  // kb*32 + (e/8)*16 + g*8 + e%8 of query column l32; then the reference max
+  auto scores = [&](const char* sK, int kt) {
     const int kv0 = kt * ATT_BN;
-
-    // S^T for 2 key blocks of 32
-    f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -219,12 +295,11 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(sK + (kb * 32 + krow_perm) * G::KROW + c * 32 + g * 16);
+        const bf16x8 kf =
+            *(const bf16x8*)(sK + kbase + kb * 32 * T::ROW + ((kc0 ^ (2 * c)) << 4));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
       }
     }
-
-    // element e of sacc[kb] is key kv0 + kb*32 + (e/8)*16 + g*8 + e%8 of query column l32
     if (kv0 + ATT_BN > L) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -234,15 +309,14 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
           if (kv >= L) sacc[kb][e] = -INFINITY;
         }
     }
-
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     // move the reference only when some query of the wave would overflow 2^8; a
-    // lane's half of the keys decides that as well as the whole row does (the
-    // test is wave-wide), so the two halves exchange maxima only when it moves
+    // lane's half of the keys decides that as well as the whole row does (the test
+    // is wave-wide), so the two halves exchange maxima only when it moves
     if (__any((mx - mref) * scale_log2 > ATT_RESCALE_LOG2)) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mref, mx);
@@ -254,8 +328,13 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
+  };
+  // ---- P of the scores in sacc (bf16, the B operand of O^T += V^T P^T) and P V^T
+  // over its 4 chunks of 16 keys from V buffer sV; the V^T fragment of chunk ch
+  // (keys ch*16 + g*8 .. + 7 of channel db*32 + l32) is two transposing reads
+  auto pv = [&](const char* sV) {
     const float moff = mref * scale_log2;
-    bf16x8 pf[4];   // [16-key chunk]
+    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -263,31 +342,84 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
         bf16x8 t;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(fmaf(sacc[kb][ch * 8 + e], scale_log2, -moff));
-          lsum += pv;
-          t[e] = (__bf16)pv;
+          const float pv_ = fast_exp2(fmaf(sacc[kb][ch * 8 + e], scale_log2, -moff));
+          lsum += pv_;
+          t[e] = (__bf16)pv_;
         }
         pf[kb * 2 + ch] = t;
       }
-
-    // O^T += V^T P^T over the 4 chunks of 16 keys; the V^T fragment of chunk ch
-    // (keys ch*16 + g*8 .. + 7 of channel db*32 + l32) is two transposing reads
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const char* vp = sV + vbase[db] + ch * 16 * G::VROW;
+        const char* vp = sV + vbase[db] + ch * 16 * T::ROW;
         const s16x4v lo = lds_tr16(vp);
-        const s16x4v hi = lds_tr16(vp + 4 * G::VROW);
+        const s16x4v hi = lds_tr16(vp + 4 * T::ROW);
         const s16x8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[ch],
                                                            oacc[db], 0, 0, 0);
       }
     }
+  };
+  // end of a segment: this wave's LDS reads have returned and the batch it issued
+  // one segment earlier has landed (`inflight`: this segment's own batch, which
+  // may stay in flight); then the barrier.  The "memory" clobber keeps the
+  // compiler from moving LDS accesses across it.
+  auto seg_end = [&](int inflight) {
+    wait_vm_lgkm0(inflight);
+    asm volatile("s_barrier" ::: "memory");
+  };
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next tile landed
-    __syncthreads();
+  ldk.issue(sk0, Kb, 0, L, wave);
+  ldv.issue(sv0, Vb, 0, L, wave);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+
+  // segments 2 t0 .. 2 t0 + 3 cover tiles t0 (buffers 0) and t0 + 1 (buffers 1);
+  // group 1 runs one segment behind group 0.  Each group runs its own copy of the
+  // loop (both pass the same barriers in the same order).  Every segment issues
+  // one batch (past the last tile it reloads the last tile into a buffer no one
+  // reads again), so the outstanding-load count is the same on every path.
+  const int tlast = ntiles - 1;
+  if (grp == 0) {
+    for (int t0 = 0; t0 <= ntiles; t0 += 2) {
+      ldk.issue(sk1, Kb, min(t0 + 1, tlast) * ATT_BN, L, wave);        // hs = 2 t0
+      if (t0 < ntiles) scores(sk0, t0);
+      seg_end(T::IPW);
+      if (2 * t0 + 1 > 2 * ntiles) break;
+      ldv.issue(sv1, Vb, min(t0 + 1, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 1
+      pv(sv0);
+      seg_end(T::IPW);
+      if (2 * t0 + 2 > 2 * ntiles) break;
+      ldk.issue(sk0, Kb, min(t0 + 2, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 2
+      if (t0 + 1 < ntiles) scores(sk1, t0 + 1);
+      seg_end(T::IPW);
+      if (2 * t0 + 3 > 2 * ntiles) break;
+      ldv.issue(sv0, Vb, min(t0 + 2, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 3
+      pv(sv1);
+      seg_end(T::IPW);
+    }
+  } else {
+    for (int t0 = 0; t0 <= ntiles; t0 += 2) {
+      ldk.issue(sk1, Kb, min(t0 + 1, tlast) * ATT_BN, L, wave);        // hs = 2 t0
+      if (t0 >= 1) pv(sv1);
+      seg_end(T::IPW);
+      if (2 * t0 + 1 > 2 * ntiles) break;
+      ldv.issue(sv1, Vb, min(t0 + 1, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 1
+      scores(sk0, t0);
+      seg_end(T::IPW);
+      if (2 * t0 + 2 > 2 * ntiles) break;
+      ldk.issue(sk0, Kb, min(t0 + 2, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 2
+      pv(sv0);
+      seg_end(T::IPW);
+      if (2 * t0 + 3 > 2 * ntiles) break;
+      ldv.issue(sv0, Vb, min(t0 + 2, tlast) * ATT_BN, L, wave);        // hs = 2 t0 + 3
+      scores(sk1, t0 + 1);
+      seg_end(T::IPW);
+    }
   }
+  // no direct-to-LDS load may outlive the workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- normalise and store: O^T element e of block db is
   // d = db*32 + (e/4)*8 + g*4 + e%4 of query column l32
