@@ -33,7 +33,8 @@
 // Softmax reference max (bf16): exp2 is taken relative to a per-query reference
 // m that only moves when a tile's maximum exceeds it by more than 2^8 (in exp2
 // units); otherwise P <= 256 and the rescale of O and of the row sum is
-// skipped.  The reference cancels exactly in O / l.  P enters P V^T as bf16.
+// skipped.  The reference cancels exactly in O / l.  P enters P V^T as bf16, and
+// the row sum l adds up those same bf16 values.
 //
 // K/V tiles of 64 keys are double-buffered in LDS, filled by direct
 // global->LDS loads (each wave instruction writes 1 KB contiguously; padded or
@@ -52,6 +53,7 @@ constexpr int ATT_BM = ATT_QW * ATT_WAVES;
 constexpr float ATT_RESCALE_LOG2 = 8.0f;        // P stays <= 2^8 between rescales
 
 typedef short s16x4v __attribute__((vector_size(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2v __attribute__((vector_size(8)));
 typedef short s16x8v __attribute__((vector_size(16)));
 #define DIT_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -147,8 +149,11 @@ struct KVTile {
   static constexpr int NI = BYTES / 1024;
   static constexpr int IPW = NI / ATT_WAVES;
   static_assert(NI % ATT_WAVES == 0, "tile loads split evenly over the waves");
+  // bf16 reads take rows swap23(l) (+ 32 kb): 16 consecutive rows per cycle; e4m3
+  // reads take rows ((l >> 2) & 1) * 32 + (l >> 3) * 4 + (l & 3) (+ 16 kb)
   static __device__ __forceinline__ int kswz(int r) {
-    return ROW == 256 ? (r & 15) : ((r >> 1) & 7);
+    if constexpr (ES == 2) return ROW == 256 ? (r & 15) : ((r >> 1) & 7);
+    else return ROW == 128 ? (((r >> 1) & 3) | ((r >> 3) & 4)) : (((r >> 2) & 1) | ((r >> 4) & 2));
   }
 };
 
@@ -335,17 +340,20 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
   auto pv = [&](const char* sV) {
     const float moff = mref * scale_log2;
     bf16x8 pf[4];
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         bf16x8 t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv_ = fast_exp2(fmaf(sacc[kb][ch * 8 + e], scale_log2, -moff));
-          lsum += pv_;
-          t[e] = (__bf16)pv_;
-        }
+        for (int e = 0; e < 8; ++e)
+          t[e] = (__bf16)fast_exp2(fmaf(sacc[kb][ch * 8 + e], scale_log2, -moff));
+        // the row sum takes the same bf16 weights that multiply V (two per
+        // instruction, fp32 accumulation), so the weights applied sum to one
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{t[e], t[e + 1]}, one2, lsum, false);
         pf[kb * 2 + ch] = t;
       }
 #pragma unroll
@@ -459,7 +467,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
 // sum is that of the quantised P, taken by one more MFMA of the P codes against
 // an all-ones operand, so the weights that multiply V sum to one.
 template <int D>
-__global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
+__global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_db_kernel(
     const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ V,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
     bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
@@ -631,6 +639,237 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   }
 }
 
+// The e4m3 kernel for head dim 128 in the bf16 kernel's ping-pong form (see there):
+// unpadded K tiles with the e4m3 row permutation, one 1-KB load per wave for each
+// of K and V, four statically named LDS buffers.  (Head dim 64 has 4-KB tiles,
+// fewer loads than waves, and uses the double-buffered kernel above.)
+template <int D>
+__global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
+    const fp8_t* __restrict__ Q, const fp8_t* __restrict__ K, const fp8_t* __restrict__ V,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    bf16_t* __restrict__ O, int ldo, RowMap map, int H, int L, float scale_log2,
+    const int* __restrict__ gate) {
+  static_assert(D == 128, "head dim 128");
+  using T = KVTile<D, 1>;
+  using G = AttGeo<D, 1>;
+  if (gate_closed(gate)) return;
+  __shared__ __attribute__((aligned(1024))) char sk0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[T::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave >> 2;         // ping-pong group
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int nqt = (L + ATT_BM - 1) / ATT_BM;
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
+  const int lid = xcd * xq + min(xcd, xr) + (bid >> 3);
+  const int bh = lid / nqt;
+  const int qt = lid - bh * nqt;
+  const int b = bh / H;
+  const int h = bh - b * H;
+
+  const fp8_t* Qb = Q + (size_t)bh * L * D;
+  const fp8_t* Kb = K + (size_t)bh * L * D;
+  const fp8_t* Vb = V + (size_t)bh * L * D;
+  const float cs = scale_log2 * sq[bh] * sk[bh];   // raw score -> exp2 units
+
+  // Q fragments: lane holds Q[q][c*64 + g*32 .. +32]
+  const int q0 = qt * ATT_BM + wave * ATT_QW;
+  i32x8 qf[D / 64];
+  {
+    const int qr = min(q0 + l32, L - 1);
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      const i32x4 lo = *(const i32x4*)(Qb + (size_t)qr * D + c * 64 + g * 32);
+      const i32x4 hi = *(const i32x4*)(Qb + (size_t)qr * D + c * 64 + g * 32 + 16);
+      qf[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float mref = -INFINITY;    // integer-valued reference, exp2 units
+  // row sums of the quantised 448 P, accumulated by one more MFMA against an
+  // all-ones e4m3 operand (every row of the result is the column's sum)
+  f32x16 lacc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                           0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+
+  TileLoads<D, 1, true> ldk;
+  TileLoads<D, 1, false> ldv;
+  ldk.init(wave, lane);
+  ldv.init(wave, lane);
+
+  // transposing V reads: lane 2e + q of its 16-lane group sources key
+  // g*32 + 8t + e, channels db*32 + (group & 1)*16 + 8q .. + 7
+  const int tg = lane >> 4, ts = lane & 15, te = ts >> 1, tq = ts & 1;
+  const int vsw = G::vswz(te);   // the rows a lane sources are all = te (mod 8)
+  int vbase[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    vbase[db] = (g * 32 + te) * T::ROW + (((2 * db + (tg & 1)) ^ vsw) << 4) + 8 * tq;
+
+  const int ntiles = (L + ATT_BN - 1) / ATT_BN;
+  // K row fed to MFMA row l32 of key block kb: krow0 + 16 kb; its logical 16-byte
+  // chunks 4c + 2g and 4c + 2g + 1 sit at those XOR kswz(row) (the same for both kb)
+  const int krow0 = ((l32 >> 2) & 1) * 32 + (l32 >> 3) * 4 + (l32 & 3);
+  const int kbase = krow0 * T::ROW;
+  const int ksw = T::kswz(krow0);
+
+  f32x16 sacc[2];
+  // ---- scores of tile kt from K buffer sK: element e of sacc[kb] is key kv0 +
+  // g*32 + kb*16 + e of query column l32; then the reference
+  auto scores = [&](const char* sK, int kt) {
+    const int kv0 = kt * ATT_BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) {
+        const char* r_ = sK + kbase + kb * 16 * T::ROW;
+        const i32x4 lo = *(const i32x4*)(r_ + (((4 * c + 2 * g) ^ ksw) << 4));
+        const i32x4 hi = *(const i32x4*)(r_ + (((4 * c + 2 * g + 1) ^ ksw) << 4));
+        const i32x8 kf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[c], sacc[kb], 0, 0, 0,
+                                                                   127, 0, 127);
+      }
+    }
+    if (kv0 + ATT_BN > L) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kv0 + g * 32 + kb * 16 + e >= L) sacc[kb][e] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    // as in the bf16 kernel: the halves exchange maxima only when the reference moves
+    if (__any(mx * cs > mref)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxl = mx * cs;
+      const float mnew = fmaxf(mref, ceilf(mxl));
+      // 2^(mref - mnew): an exact power of two (0 before the first tile)
+      const float alpha = mref == -INFINITY ? 0.f : ldexpf(1.0f, (int)(mref - mnew));
+      mref = mnew;
+      lacc *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+  };
+  // ---- the e4m3 codes of 448 P = 2^(t - mref + log2 448) and P V^T from V buffer sV
+  auto pv = [&](const char* sV) {
+    const float moff = mref - 8.807354922057604f;
+    int pw[8];   // 32 e4m3 codes of P * 448, keys g*32 + 0..31
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p[e] = fast_exp2(fmaf(sacc[kb][w4 * 4 + e], cs, -moff));
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        pw[kb * 4 + w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+      }
+    const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const char* vp = sV + vbase[db];
+      const i32x2v t0 = lds_tr8(vp), t1 = lds_tr8(vp + 8 * T::ROW);
+      const i32x2v t2 = lds_tr8(vp + 16 * T::ROW), t3 = lds_tr8(vp + 24 * T::ROW);
+      const i32x8 vf = i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[db], 0, 0, 0, 127,
+                                                                 0, 127);
+    }
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 127, 0, 127);
+  };
+  auto seg_end = [&]() {
+    wait_vm_lgkm0(T::IPW);
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  ldk.issue(sk0, Kb, 0, L, wave);
+  ldv.issue(sv0, Vb, 0, L, wave);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+
+  // the same segment schedule as the bf16 kernel
+  const int tlast = ntiles - 1;
+  if (grp == 0) {
+    for (int t0 = 0; t0 <= ntiles; t0 += 2) {
+      ldk.issue(sk1, Kb, min(t0 + 1, tlast) * ATT_BN, L, wave);   // hs = 2 t0
+      if (t0 < ntiles) scores(sk0, t0);
+      seg_end();
+      if (2 * t0 + 1 > 2 * ntiles) break;
+      ldv.issue(sv1, Vb, min(t0 + 1, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 1
+      pv(sv0);
+      seg_end();
+      if (2 * t0 + 2 > 2 * ntiles) break;
+      ldk.issue(sk0, Kb, min(t0 + 2, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 2
+      if (t0 + 1 < ntiles) scores(sk1, t0 + 1);
+      seg_end();
+      if (2 * t0 + 3 > 2 * ntiles) break;
+      ldv.issue(sv0, Vb, min(t0 + 2, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 3
+      pv(sv1);
+      seg_end();
+    }
+  } else {
+    for (int t0 = 0; t0 <= ntiles; t0 += 2) {
+      ldk.issue(sk1, Kb, min(t0 + 1, tlast) * ATT_BN, L, wave);   // hs = 2 t0
+      if (t0 >= 1) pv(sv1);
+      seg_end();
+      if (2 * t0 + 1 > 2 * ntiles) break;
+      ldv.issue(sv1, Vb, min(t0 + 1, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 1
+      scores(sk0, t0);
+      seg_end();
+      if (2 * t0 + 2 > 2 * ntiles) break;
+      ldk.issue(sk0, Kb, min(t0 + 2, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 2
+      pv(sv0);
+      seg_end();
+      if (2 * t0 + 3 > 2 * ntiles) break;
+      ldv.issue(sv0, Vb, min(t0 + 2, tlast) * ATT_BN, L, wave);   // hs = 2 t0 + 3
+      scores(sk1, t0 + 1);
+      seg_end();
+    }
+  }
+  // no direct-to-LDS load may outlive the workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const float inv = sv[bh] / lacc[0];
+  const int t = q0 + l32;
+  if (t < L) {
+    bf16_t* orow = O + (size_t)map.stream_row(b, t) * ldo + h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int dd = db * 32 + e4 * 8 + g * 4;
+        uint2 u;
+        u.x = pack_bf16x2(oacc[db][e4 * 4 + 0] * inv, oacc[db][e4 * 4 + 1] * inv);
+        u.y = pack_bf16x2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv);
+        *(uint2*)(orow + dd) = u;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 // Reference-precision attention for small models (head dim 32 or 64): one wave
 // per 64 queries of one (b, h), one query per lane, 64-key K and V tiles in LDS
@@ -729,7 +968,7 @@ hipError_t attention_fp8(const fp8_t* q8, const fp8_t* k8, const fp8_t* v8, cons
   if (nblk == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   KTimerScope timer(KS_ATTENTION, st);
-  auto kern = d == 128 ? attention_fp8_kernel<128> : attention_fp8_kernel<64>;
+  auto kern = d == 128 ? attention_fp8_kernel<128> : attention_fp8_db_kernel<64>;
   hipLaunchKernelGGL(kern, dim3(nblk), dim3(ATT_WAVES * 64), 0, st, q8, k8, v8, sq, sk, sv, o, ldo,
                      map, H, L, scale_log2, launch_gate());
   return hipGetLastError();
