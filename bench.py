@@ -56,6 +56,11 @@ TRAFFIC_1024 = {
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
                   "sha1": "2cf4b36ad553ff5326b8856da6424e5c5043fedd"},
+    "attention": {"bytes": 50799 * 2 * 1024 + 28203 * 1024,
+                  "source": "image_generation_amd/csrc/attention.hip",
+                  "begin": "constexpr int ATT_BN = 64;",
+                  "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
+                  "sha1": "1c823a5e078da2f6878defec9f66c96cf30422d9"},
 }
 
 
