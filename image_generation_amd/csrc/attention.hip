@@ -296,6 +296,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+    // reads and MFMAs interleaved a pair at a time (measured 4-7% faster here than
+    // all reads of a batch first, unlike the e4m3 kernel)
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
@@ -733,20 +735,31 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attention_fp8_kernel(
   // g*32 + kb*16 + e of query column l32; then the reference
   auto scores = [&](const char* sK, int kt) {
     const int kv0 = kt * ATT_BN;
+    // all 8 K fragment reads of the tile before its 4 MFMAs: while a direct-to-LDS
+    // load is pending the compiler can only wait for all of a wave's LDS reads at
+    // once, so one wait here instead of one per MFMA (measured 1-2% faster; the
+    // bf16 kernel is faster with its reads interleaved)
+    i32x8 kf[2][D / 64];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int c = 0; c < D / 64; ++c) {
         const char* r_ = sK + kbase + kb * 16 * T::ROW;
         const i32x4 lo = *(const i32x4*)(r_ + (((4 * c + 2 * g) ^ ksw) << 4));
         const i32x4 hi = *(const i32x4*)(r_ + (((4 * c + 2 * g + 1) ^ ksw) << 4));
-        const i32x8 kf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[c], sacc[kb], 0, 0, 0,
-                                                                   127, 0, 127);
+        kf[kb][c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c)
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kb][c], qf[c], sacc[kb], 0,
+                                                                   0, 0, 127, 0, 127);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 64), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 64), 0);
     if (kv0 + ATT_BN > L) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
