@@ -159,6 +159,55 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T* __restrict
   if (lane == 0) scale[r] = sc;
 }
 
+// One workgroup (4 waves) per row, the row split over the waves and held in
+// registers (4 x NCH x 512 elements at most; NCH chunks of 512 per wave): the
+// row's amax combines the waves' maxima through LDS, then each wave quantises its
+// part.  Splitting a row keeps the registers per wave low, so more rows are in
+// flight than with one wave per row.
+template <class T, int NCH>
+__global__ __launch_bounds__(256) void quant_rows_split_kernel(const T* __restrict__ src, int lds,
+                                                               fp8_t* __restrict__ dst, int ldd,
+                                                               float* __restrict__ scale,
+                                                               int rows, int width,
+                                                               const int* __restrict__ gate) {
+  if (gate_closed(gate)) return;
+  __shared__ float wmax[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = blockIdx.x;
+  const T* s = src + (size_t)r * lds;
+  i32x4 raw[NCH];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (wave * NCH + i) * 512 + lane * 8;
+    if (c < width) {
+      raw[i] = *(const i32x4*)(s + c);
+      float v[8];
+      decode8<T>(raw[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float sc, inv;
+  scale_of(amax, sc, inv);
+  fp8_t* d = dst + (size_t)r * ldd;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (wave * NCH + i) * 512 + lane * 8;
+    if (c < width) {
+      float v[8];
+      decode8<T>(raw[i], v);
+      store_fp8x8(d + c, v, inv);
+    }
+  }
+  if (threadIdx.x == 0) scale[r] = sc;
+}
+
 // e4m3 codes of one contiguous slice per blockIdx.y, scaled by that slice's given
 // amax (fp32 bits; a non-negative float's bits order like its value).
 template <class T>
@@ -196,9 +245,9 @@ hipError_t quant_rows(const T* src, int lds, fp8_t* dst, int ldd, float* scale, 
   if (width <= 8 * 512)
     hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8>), grid, dim3(256), 0, st, src, lds, dst, ldd,
                        scale, rows, width, launch_gate());
-  else if (width <= 32 * 512)
-    hipLaunchKernelGGL((quant_rows_reg_kernel<T, 32>), grid, dim3(256), 0, st, src, lds, dst, ldd,
-                       scale, rows, width, launch_gate());
+  else if (width <= 4 * 8 * 512)
+    hipLaunchKernelGGL((quant_rows_split_kernel<T, 8>), dim3(rows), dim3(256), 0, st, src, lds,
+                       dst, ldd, scale, rows, width, launch_gate());
   else
     hipLaunchKernelGGL(quant_rows_kernel<T>, grid, dim3(256), 0, st, src, lds, dst, ldd, scale,
                        rows, width, launch_gate());
