@@ -678,6 +678,18 @@ def main():
                           "skipped_steps": skipped_c, "eager_skipped_steps": skipped_ce,
                           "rel_l1": [None if not math.isfinite(r) else round(r, 5)
                                      for r in rels_c]}
+        # the cached path's own cost: a threshold no rel-L1 reaches, so every step
+        # after the first reuses the cached residual (first block, the test, the
+        # cache apply; in the replayed graph the other blocks' kernels are still
+        # launched and return at once)
+        log("[bench] FBC runs: every step after the first cached, replayed and eager")
+        secs_s, skipped_s, _ = run_replayed(dit, gm, sig, txt, lat0, 1e30, K)
+        secs_se, skipped_se, _ = run_loop(dit, gm, sig, txt, lat0, ws, 1e30, K)
+        out["fbcache_all_cached"] = {
+            "threshold": 1e30, "steps": K, "skipped_steps": skipped_s,
+            "eager_skipped_steps": skipped_se,
+            "ms_per_cached_step": round(1e3 * (secs_s - secs / K) / max(skipped_s, 1), 3),
+            "eager_ms_per_cached_step": round(1e3 * (secs_se - secs_e / K) / max(skipped_se, 1), 3)}
     del gm, ws
     torch.cuda.empty_cache()
     if not args.no_mxfp4_loop:
