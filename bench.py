@@ -22,7 +22,7 @@ double block of the 2048px CFG-pair shape (16384 + 512 tokens, batch 2:
 attention and GEMM TFLOP/s) and a few steps of the fp8 W8A8 model at 2048px
 (batch 2, CFG 3.5), whose TFLOP/s are taken against the fp8 peak.
 
-Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 exits: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -534,7 +534,7 @@ def main():
     ap.add_argument("--dtypes", default="bf16,fp8", help="--micro attention: bf16,fp8")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 

@@ -63,7 +63,7 @@ extern "C" {
 /* ------------------------------------------------------------------ status */
 #define DIT_OK 0
 #define DIT_ERR_INVALID_ARG (-1)  /* bad pointer, shape, alignment or value        */
-#define DIT_ERR_UNSUPPORTED (-2)  /* dtype / shape / device this build does not run */
+#define DIT_ERR_UNSUPPORTED (-2)  /* dtype / shape / device the library does not support */
 #define DIT_ERR_WORKSPACE (-3)    /* workspace smaller than dit_workspace_bytes()   */
 #define DIT_ERR_HIP (-4)          /* the HIP runtime reported an error              */
 #define DIT_ERR_NONFINITE (-5)    /* NaN / Inf reached the First-Block-Cache test   */
