@@ -406,11 +406,9 @@ def tiny_loop_latency(dit, DI, device, reps=20):
 
 
 def cpu_baseline(DI, w):
-    """The fp64 oracle on the host: one double-stream block of the workload's
-    shape, extrapolated to a whole step.  Both block kinds carry the same
-    24 D^2 GEMM flops per token and the same joint attention, so a step costs
-    about (n_double + n_single) double blocks; the embeddings, modulation and
-    velocity head add well under 1%."""
+    """The fp64 oracle on the host: one double-stream and one single-stream block
+    of the workload's shape (about 10 s together), weighted by the step's block
+    counts; the embeddings, modulation and velocity head add well under 1%."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -421,16 +419,21 @@ def cpu_baseline(DI, w):
     D, H = dims.D, dims.H
     ang = O.rope_table(O.image_positions(w.grid_h, w.grid_w, w.Lt), D // H)
     x = O.to64(DI.randn((1, w.L, D), DI.SEED_ACT, 1.0, "bf16"))
-    P = {k: O.to64(v) for k, v in DI.block_params(dims, "bf16", "double").items()}
     mod = O.to64(DI.randn((1, 12, D), DI.SEED_MOD, 0.1, "f32"))
+    P = {k: O.to64(v) for k, v in DI.block_params(dims, "bf16", "double").items()}
     t0 = time.perf_counter()
     O.double_block(x[:, :w.Lt], x[:, w.Lt:], mod[:, :6], mod[:, 6:], P, ang, H)
-    t_block = time.perf_counter() - t0
-    nblk = dims.n_double + dims.n_single
-    return {"value": 1.0 / (nblk * t_block), "unit": "steps/s", "cores": int(threads),
+    t_double = time.perf_counter() - t0
+    P = {k: O.to64(v) for k, v in DI.block_params(dims, "bf16", "single").items()}
+    t0 = time.perf_counter()
+    O.single_block(x, mod[:, :3], P, ang, H)
+    t_single = time.perf_counter() - t0
+    t_step = dims.n_double * t_double + dims.n_single * t_single
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"one double-stream block of the {w.Lt}+{w.Li}-token shape in fp64 "
-                       f"({t_block:.2f} s), extrapolated to the {nblk} blocks of a step")}
+            "sample": (f"one double-stream block ({t_double:.2f} s) and one single-stream "
+                       f"block ({t_single:.2f} s) of the {w.Lt}+{w.Li}-token shape in fp64, "
+                       f"weighted by the step's {dims.n_double} + {dims.n_single} blocks")}
 
 
 GEMM_SHAPES = {"lin1": (4608, 3072, 21504), "lin2": (4608, 15360, 3072),
