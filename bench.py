@@ -51,16 +51,16 @@ BLOCK_GEMM_SITES = ("gemm_qkv", "gemm_resid", "gemm_gelu", "gemm_lin1")
 # of that code's source region (from the `begin` marker up to the `end` marker) is
 # checked at run time and traffic is reported as null once it differs.
 TRAFFIC_1024 = {
-    "gemm_lin1": {"bytes": 525236 * 2 * 1024 + 250799 * 1024,
+    "gemm_lin1": {"bytes": 522535 * 2 * 1024 + 251286 * 1024,
                   "source": "image_generation_amd/csrc/gemm.hip",
                   "begin": "// ---------------------------------------------------------------- epilogues",
                   "end": "// ---------------------------------------------------------------- fp32 path",
-                  "sha1": "2cf4b36ad553ff5326b8856da6424e5c5043fedd"},
-    "attention": {"bytes": 50799 * 2 * 1024 + 28203 * 1024,
+                  "sha1": "3cfebb6d5a89ac05967a09b11264363640aa7b6f"},
+    "attention": {"bytes": 50799 * 2 * 1024 + 28199 * 1024,
                   "source": "image_generation_amd/csrc/attention.hip",
                   "begin": "constexpr int ATT_BN = 64;",
                   "end": "// ---------------------------------------------------------------- fp8 (e4m3)",
-                  "sha1": "1c823a5e078da2f6878defec9f66c96cf30422d9"},
+                  "sha1": "548d5e07803ec885633257dad74a7329f5068982"},
 }
 
 

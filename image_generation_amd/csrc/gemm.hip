@@ -9,9 +9,8 @@
 // double block, each with its own weights) share one launch.
 //
 // Epilogue: each wave parks one 32-column slice of its accumulators in LDS at a
-// time and reads it back either row-wise (4 consecutive columns of one row per
-// lane: coalesced stores, RoPE pairs in-register) or column-wise (4 consecutive
-// rows of one column per lane), then calls the fused
+// time and reads it back row-wise (4 consecutive columns of one row per lane:
+// coalesced stores, RoPE pairs in-register), then calls the fused
 // epilogue functor; a pass wholly in bounds hands the functor all of a lane's rows
 // at once, so the loads they need (RoPE entries, residual rows, gates) are in
 // flight together.
@@ -28,8 +27,6 @@ constexpr int EPI_LDS = 36;             // padded fp32 row of a parked 32-column
 
 // ---------------------------------------------------------------- epilogues
 // row4(r, c, v): v = C[r, c..c+3] (bias added), c % 4 == 0
-// col4(r, c, v): v = C[r..r+3, c] (bias added), r % 4 == 0
-// colmajor(n0, BN): true if the tile starting at column n0 wants col4
 // rows<NR>(r0, rs, c, v) (optional): v[i] = C[r0 + i rs, c..c+3] for i < NR, every
 //   row in bounds and the calling wave's columns inside one tensor and head, so
 //   branches on c agree across the wave; the functor issues all its loads before
@@ -37,11 +34,9 @@ constexpr int EPI_LDS = 36;             // padded fp32 row of a parked 32-column
 
 struct EpiStoreF32 {
   float* out; int ldo;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     *(f32x4*)(out + (size_t)r * ldo + c) = v;
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 __device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
@@ -53,37 +48,30 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float 
 
 struct EpiStoreBf16 {
   bf16_t* out; int ldo;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     store_bf16x4(out + (size_t)r * ldo + c, v[0], v[1], v[2], v[3]);
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 struct EpiSiluBf16 {
   bf16_t* out; int ldo;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     store_bf16x4(out + (size_t)r * ldo + c, silu_f(v[0]), silu_f(v[1]), silu_f(v[2]), silu_f(v[3]));
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 struct EpiGeluBf16 {
   bf16_t* out; int ldo; int col_off;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     store_bf16x4(out + (size_t)r * ldo + col_off + c, gelu_tanh_f(v[0]), gelu_tanh_f(v[1]),
                  gelu_tanh_f(v[2]), gelu_tanh_f(v[3]));
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 // x[token] += gate[b] * v, x being the joint residual stream [B, L, D].
 template <class XT>
 struct EpiGatedResidual {
   XT* x; int D; const float* gate; int gate_bstride; RowMap map;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     int b, t; map.token(r, b, t);
     XT* p = x + ((size_t)b * map.L + t) * D + c;
@@ -129,11 +117,10 @@ struct EpiGatedResidual {
     }
     return 0.f;
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 // Epilogues that also report the largest magnitude they stored, per slot
-// (kTrackAmax): row4 / col4 return the largest |value| before the store's rounding,
+// (kTrackAmax): row4 returns the largest |value| before the store's rounding,
 // slot(r, c) names the slot of an output (-1: not tracked) and stored(slot, m)
 // applies that slot's rounding (round-to-nearest is monotonic, so rounding the
 // largest magnitude gives the largest stored magnitude).  The kernel folds these
@@ -191,7 +178,6 @@ struct EpiQKVT {
   int D, H, d; RowMap map;
   unsigned int* amax;
   __device__ __forceinline__ unsigned int* amax_ptr() const { return amax; }
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ int slot(int r, int c) const {
     const int which = c / D;
     const int h = (c - which * D) / d;
@@ -273,7 +259,6 @@ struct EpiQKVT {
   }
   // every slot stores bf16
   __device__ __forceinline__ float stored(int, float m) const { return bf2f(f2bf(m)); }
-  __device__ __forceinline__ float col4(int, int, f32x4) const { return 0.f; }
 };
 
 using EpiQKV = EpiQKVT<false>;
@@ -284,7 +269,6 @@ struct EpiLinear1T {
   static constexpr bool kTrackAmax = AMAX;
   EpiQKVT<AMAX> qkv; EpiGeluBf16 gelu; int n_qkv;
   __device__ __forceinline__ unsigned int* amax_ptr() const { return qkv.amax; }
-  __device__ __forceinline__ bool colmajor(int n0, int bn) const { return qkv.colmajor(n0, bn); }
   __device__ __forceinline__ int slot(int r, int c) const { return c < n_qkv ? qkv.slot(r, c) : -1; }
   __device__ __forceinline__ int slot_span(int r0, int r1, int c) const {
     return c < n_qkv ? qkv.slot_span(r0, r1, c) : -1;
@@ -301,7 +285,6 @@ struct EpiLinear1T {
     for (int i = 0; i < NR; ++i) gelu.row4(r0 + i * rs, c - n_qkv, v[i]);
     return 0.f;
   }
-  __device__ __forceinline__ float col4(int r, int c, f32x4 v) const { return qkv.col4(r, c, v); }
   __device__ __forceinline__ float stored(int slot, float m) const { return qkv.stored(slot, m); }
 };
 using EpiLinear1 = EpiLinear1T<false>;
@@ -445,7 +428,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
   // ---- epilogue (the loop above ended with a barrier: operand LDS is free)
   const Epi epi = g1 ? p.e[1] : p.e[0];
   float* slice = (float*)smem + wave * WROWS * EPI_LDS;
-  const bool cmaj = epi.colmajor(n0, BN);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     // accumulator element e of block (i, j): row i*32 + (e/4)*8 + (lane/32)*4 + e%4,
@@ -460,38 +442,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi>
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int cbase = n0 + wcol + j * 32;
-    if (!cmaj) {
-      // 8 lanes per row, 4 columns each
+    // 8 lanes per row, 4 columns each
 #pragma unroll
-      for (int ps = 0; ps < WROWS / 8; ++ps) {
-        const int rl = ps * 8 + (lane >> 3);
-        const int cl = (lane & 7) * 4;
-        const int row = m0 + wrow + rl;
-        const int col = cbase + cl;
-        if (row < g.M && col < g.N) {
-          f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
-          if (g.bias) v += *(const f32x4*)(g.bias + col);
-          epi.row4(row, col, v);
-        }
-      }
-    } else {
-      // 32 row-quads x 2 columns per pass: lanes 0..31 write 32 consecutive quads
-#pragma unroll
-      for (int ps = 0; ps < WROWS / 4 * 32 / 64; ++ps) {
-        const int idx = ps * 64 + lane;
-        const int rq = idx % (WROWS / 4);
-        const int cl = idx / (WROWS / 4);
-        const int row = m0 + wrow + rq * 4;
-        const int col = cbase + cl;
-        if (row < g.M && col < g.N) {
-          f32x4 v;
-          v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
-          v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
-          v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
-          v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
-          if (g.bias) v += g.bias[col];
-          epi.col4(row, col, v);
-        }
+    for (int ps = 0; ps < WROWS / 8; ++ps) {
+      const int rl = ps * 8 + (lane >> 3);
+      const int cl = (lane & 7) * 4;
+      const int row = m0 + wrow + rl;
+      const int col = cbase + cl;
+      if (row < g.M && col < g.N) {
+        f32x4 v = *(const f32x4*)&slice[rl * EPI_LDS + cl];
+        if (g.bias) v += *(const f32x4*)(g.bias + col);
+        epi.row4(row, col, v);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -531,8 +492,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Epilogue of the direct-to-LDS kernels: a wave parks its accumulators, 32
-// columns by PR = WROWS / EH rows at a time, in its LDS slice, then hands row- or
-// column-contiguous quads to the epilogue functor (dequantised first for e4m3).
+// columns by PR = WROWS / EH rows at a time, in its LDS slice, then hands
+// row-contiguous quads to the epilogue functor (dequantised first for e4m3).
 // Accumulator element e of block (i, j) is row i*32 + (e/4)*8 + (lane/32)*4 + e%4,
 // column j*32 + lane%32 of the wave's tile.
 template <int BN, int WN, int TM, int TN, int WROWS, int EH, bool F8, class Epi>
@@ -540,7 +501,6 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
                                              f32x16 (&acc)[TM][TN], float* slice, int m0, int n0,
                                              int wrow, int wcol, int lane) {
   constexpr int PR = WROWS / EH;
-  const bool cmaj = epi.colmajor(n0, BN);
   constexpr bool kAmax = TracksAmax<Epi>::value;
   unsigned int* const amax_p = amax_of(epi);
   // A wave's BN / WN = 64 columns start on a multiple of 64, so with head size and
@@ -576,7 +536,7 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
       // the functor gets all PR / 8 rows of a lane at once, with no branch between
       // them, so their loads are issued together
       const bool whole = rbase + PR <= g.M && cbase + 32 <= g.N && (!kAmax || one_slot);
-      if (!cmaj && whole) {
+      if (whole) {
         const int cl = (lane & 7) * 4;
         const int col = cbase + cl;
         const int row0 = rbase + (lane >> 3);
@@ -601,7 +561,7 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
           const float m = epi_rows<NRB>(epi, row0 + bt * NRB * 8, 8, col, vb);
           if constexpr (kAmax) am = fmaxf(am, m);
         }
-      } else if (!cmaj) {
+      } else {
 #pragma unroll
         for (int ps = 0; ps < PR / 8; ++ps) {
           const int rl = ps * 8 + (lane >> 3);
@@ -618,58 +578,6 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& g, const Epi& ep
               else track_amax(epi, epi.slot(row, col), m, amax_p);
             } else {
               epi.row4(row, col, v);
-            }
-          }
-        }
-      } else if (whole) {
-        // column quads, all in bounds: operands and bias first, then the stores
-        constexpr int NP = PR / 4 * 32 / 64;
-        f32x4 v[NP];
-#pragma unroll
-        for (int ps = 0; ps < NP; ++ps) {
-          const int idx = ps * 64 + lane;
-          const int rq = idx % (PR / 4);
-          const int cl = idx / (PR / 4);
-          v[ps][0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
-          v[ps][1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
-          v[ps][2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
-          v[ps][3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
-          if constexpr (F8) v[ps] *= *(const f32x4*)(g.sa + rbase + rq * 4) * g.sw[cbase + cl];
-        }
-        if (g.bias) {
-#pragma unroll
-          for (int ps = 0; ps < NP; ++ps) v[ps] += g.bias[cbase + (ps * 64 + lane) / (PR / 4)];
-        }
-#pragma unroll
-        for (int ps = 0; ps < NP; ++ps) {
-          const int idx = ps * 64 + lane;
-          const int row = rbase + (idx % (PR / 4)) * 4;
-          const int col = cbase + idx / (PR / 4);
-          if constexpr (kAmax) am = fmaxf(am, epi.col4(row, col, v[ps]));
-          else epi.col4(row, col, v[ps]);
-        }
-      } else {
-#pragma unroll
-        for (int ps = 0; ps < PR / 4 * 32 / 64; ++ps) {
-          const int idx = ps * 64 + lane;
-          const int rq = idx % (PR / 4);
-          const int cl = idx / (PR / 4);
-          const int row = rbase + rq * 4;
-          const int col = cbase + cl;
-          if (row + 3 < g.M && col < g.N) {
-            f32x4 v;
-            v[0] = slice[(rq * 4 + 0) * EPI_LDS + cl];
-            v[1] = slice[(rq * 4 + 1) * EPI_LDS + cl];
-            v[2] = slice[(rq * 4 + 2) * EPI_LDS + cl];
-            v[3] = slice[(rq * 4 + 3) * EPI_LDS + cl];
-            if constexpr (F8) v *= *(const f32x4*)(g.sa + row) * g.sw[col];
-            if (g.bias) v += g.bias[col];
-            if constexpr (kAmax) {
-              const float m = epi.col4(row, col, v);
-              if (one_slot) am = fmaxf(am, m);
-              else track_amax(epi, epi.slot(row, col), m, amax_p);
-            } else {
-              epi.col4(row, col, v);
             }
           }
         }
@@ -1009,31 +917,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
 
 struct EpiSiluF32 {
   float* out; int ldo;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     f32x4 o;
     for (int i = 0; i < 4; ++i) o[i] = silu_f(v[i]);
     *(f32x4*)(out + (size_t)r * ldo + c) = o;
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 struct EpiGeluF32 {
   float* out; int ldo; int col_off;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     f32x4 o;
     for (int i = 0; i < 4; ++i) o[i] = gelu_tanh_f(v[i]);
     *(f32x4*)(out + (size_t)r * ldo + col_off + c) = o;
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 // Q, K (rotated) and V [B, H, L, d], all fp32.
 struct EpiQKV32 {
   float* q; float* k; float* v; const float* rope;
   int D, H, d; RowMap map;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 x) const {
     const int which = c / D;
     const int cc = c - which * D;
@@ -1054,17 +957,14 @@ struct EpiQKV32 {
     o[3] = x[2] * cs[3] + x[3] * cs[2];
     *(f32x4*)dst = o;
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 struct EpiLinear1F32 {
   EpiQKV32 qkv; EpiGeluF32 gelu; int n_qkv;
-  __device__ __forceinline__ bool colmajor(int, int) const { return false; }
   __device__ __forceinline__ void row4(int r, int c, f32x4 v) const {
     if (c < n_qkv) qkv.row4(r, c, v);
     else gelu.row4(r, c - n_qkv, v);
   }
-  __device__ __forceinline__ void col4(int, int, f32x4) const {}
 };
 
 constexpr int G32_T = 64;    // output tile edge
