@@ -1242,6 +1242,65 @@ int dit_denoise_step(const dit_model* m, const float* mod_step, const void* txt,
   return DIT_OK;
 }
 
+// Workspace of dit_denoise_step_at: the step's own workspace, then the step's
+// modulation row, then the modulation scratch for one row.
+struct StepAtLayout {
+  size_t step, row_off, mod_off, total;
+};
+
+static bool step_at_layout(const dit_model* m, StepAtLayout* o) {
+  Dims dm;
+  if (!m || m->n_double < 0 || m->n_single < 0) return false;
+  if (make_dims(&m->dims, &dm) != DIT_OK) return false;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  o->step = ws_size(dm, DIT_WS_STEP, 0);
+  o->row_off = up(o->step);
+  o->mod_off = o->row_off + up(n_mod_of(m) * sizeof(float));
+  o->total = o->mod_off + ws_size(dm, DIT_WS_MODULATION, 1);
+  return true;
+}
+
+size_t dit_step_at_workspace_bytes(const dit_model* m) {
+  StepAtLayout lay;
+  return step_at_layout(m, &lay) ? lay.total : 0;
+}
+
+int dit_denoise_step_at(const dit_model* m, float* latents, const void* txt, int step,
+                        int num_steps, const double* sigmas_host, dit_fbcache* cache,
+                        void* workspace, size_t ws_bytes, void* stream,
+                        dit_step_info* info_out) {
+  const char* fn = "dit_denoise_step_at";
+  if (!m || !sigmas_host || !workspace) return fail(DIT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (num_steps < 1 || step < 0 || step >= num_steps)
+    return fail(DIT_ERR_INVALID_ARG, "%s: step %d of %d", fn, step, num_steps);
+  if (!aligned16(workspace))
+    return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  Dims dm;
+  int rc;
+  if ((rc = check_model(m, &dm, fn))) return rc;
+  StepAtLayout lay;
+  if (!step_at_layout(m, &lay)) return fail(DIT_ERR_INVALID_ARG, "%s: bad model dimensions", fn);
+  if (ws_bytes < lay.total)
+    return fail(DIT_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, lay.total);
+  float* row = (float*)((char*)workspace + lay.row_off);
+  long long nmod = 0;
+  size_t mod_need = 0;
+  if ((rc = check_modulation(m, sigmas_host + step, 1, row, &dm, &nmod, &mod_need, fn))) return rc;
+  if (!std::isfinite(sigmas_host[step + 1]))
+    return fail(DIT_ERR_INVALID_ARG, "%s: non-finite sigma", fn);
+  // the step's own checks run before anything is enqueued; the row is written next
+  if (!latents || (m->dims.Lt > 0 && !txt)) return fail(DIT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(latents) || (txt && !aligned16(txt)))
+    return fail(DIT_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  if ((rc = check_cache(cache, fn))) return rc;
+  if ((rc = check_device())) return rc;
+  if ((rc = modulation_run(m, dm, nmod, sigmas_host + step, 1, row,
+                           (char*)workspace + lay.mod_off, (hipStream_t)stream)))
+    return rc;
+  return dit_denoise_step(m, row, txt, latents, sigmas_host[step], sigmas_host[step + 1], cache,
+                          workspace, lay.step, stream, info_out);
+}
+
 size_t dit_loop_state_bytes(const dit_model* m, int n_steps) {
   if (!m || n_steps < 1 || m->n_double < 0 || m->n_single < 0 || m->dims.D <= 0) return 0;
   Carver c{nullptr, 0};

@@ -105,6 +105,10 @@ def _load() -> ctypes.CDLL:
                                         P, c_size_t, P, POINTER(c_double), POINTER(c_int)]),
         "dit_denoise_step": (c_int, [POINTER(DitModel), P, P, P, c_double, c_double,
                                      POINTER(DitFBCache), P, c_size_t, P, POINTER(DitStepInfo)]),
+        "dit_denoise_step_at": (c_int, [POINTER(DitModel), P, P, c_int, c_int, POINTER(c_double),
+                                        POINTER(DitFBCache), P, c_size_t, P,
+                                        POINTER(DitStepInfo)]),
+        "dit_step_at_workspace_bytes": (c_size_t, [POINTER(DitModel)]),
         "dit_set_kernel_timer": (c_int, [POINTER(DitKernelTimer)]),
         "dit_linear_forward": (c_int, [P, c_int, c_int, POINTER(DitLinear), c_int, P, c_int, P]),
         "dit_quantize_mxfp4": (c_int, [P, c_int, c_int, c_int, c_int, P, P, P]),
@@ -136,7 +140,8 @@ EXPORTED = ("dit_status_string", "dit_last_error", "dit_workspace_bytes", "dit_s
             "dit_quantize_rows", "dit_quantize_mxfp4", "dit_mx_rows", "dit_linear_mxfp4",
             "dit_loop_state_bytes", "dit_loop_graph_create", "dit_loop_graph_run",
             "dit_loop_graph_sync", "dit_loop_graph_reset", "dit_loop_graph_destroy",
-            "dit_modulation_static", "dit_block_views_of")
+            "dit_modulation_static", "dit_block_views_of", "dit_denoise_step_at",
+            "dit_step_at_workspace_bytes")
 
 
 def _check(rc: int) -> None:
@@ -589,6 +594,34 @@ def dit_denoise_step(gm: GPUModel, mod_step: torch.Tensor, txt: torch.Tensor,
     _check(LIB.dit_denoise_step(ctypes.byref(gm.model), _ptr(mod_step), _ptr(txt), _ptr(latents),
                                 float(sigma), float(sigma_next), cp, _ptr(ws), ws.numel(),
                                 _stream(stream), ctypes.byref(info)))
+    return info.rel, bool(info.skipped)
+
+
+def step_at_workspace(gm: GPUModel, device=None) -> torch.Tensor:
+    """A device workspace of dit_step_at_workspace_bytes(model) bytes."""
+    nb = int(LIB.dit_step_at_workspace_bytes(ctypes.byref(gm.model)))
+    if nb == 0:
+        raise ValueError("dit_step_at_workspace_bytes rejected the model")
+    return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
+
+
+def dit_denoise_step_at(gm: GPUModel, txt: torch.Tensor, latents: torch.Tensor, step: int,
+                        sigmas: Sequence[float], cache: Optional[FBCache], ws: torch.Tensor,
+                        stream=None):
+    """Step `step` of the schedule `sigmas` (n_steps + 1 entries) in place on latents,
+    computing that step's modulation vectors itself.  -> (rel, skipped)."""
+    dm = gm.model.dims
+    Li = dm.grid_h * dm.grid_w
+    _need(txt, torch.float32 if gm.dtype == DIT_F32 else torch.bfloat16, (dm.B, dm.Lt, dm.D),
+          "txt")
+    _need(latents, torch.float32, (Li, gm.model.C_in), "latents")
+    n = len(sigmas) - 1
+    sig = (c_double * len(sigmas))(*[float(x) for x in sigmas])
+    info = DitStepInfo()
+    cp = ctypes.byref(cache.c) if cache is not None else None
+    _check(LIB.dit_denoise_step_at(ctypes.byref(gm.model), _ptr(latents), _ptr(txt), int(step), n,
+                                   sig, cp, _ptr(ws), ws.numel(), _stream(stream),
+                                   ctypes.byref(info)))
     return info.rel, bool(info.skipped)
 
 

@@ -409,6 +409,33 @@ DIT_API int dit_denoise_step(const dit_model* m, const float* mod_step, const vo
                      double sigma, double sigma_next, dit_fbcache* cache, void* workspace,
                      size_t ws_bytes, void* stream, dit_step_info* info_out);
 
+/* One Euler step addressed by its place in the schedule: step `step` of
+ * `num_steps` (0 <= step < num_steps), with sigma = sigmas_host[step] and
+ * sigma_next = sigmas_host[step + 1] from a host table of num_steps + 1 entries
+ * (dit_sigmas()).  This step's adaLN modulation vectors are computed here by the
+ * kernels of dit_modulation() (timestep MLP, then one pass over the stacked
+ * modulation weights; the per-row arithmetic is the same, so the row equals row
+ * `step` of dit_modulation() over the table), then the step runs exactly as
+ * dit_denoise_step().  Calling this once per step reads the modulation weights
+ * once per step; precomputing every row once with dit_modulation() and calling
+ * dit_denoise_step() (or the replayed loop) reads them once per loop.
+ *   latents, txt, cache, info_out: as dit_denoise_step();
+ *   workspace >= dit_step_at_workspace_bytes(m) bytes (device), 16-byte aligned.
+ * Sources: the loop calls the transformer once per scheduler step, with the cache
+ * deciding per step (unsloth studio diffusion.py commit log, commit "Add opt-in
+ * step caching (First-Block-Cache)"); the sigma table is the flow-shift
+ * schedule (vflash "Optimization ledger", section "Fewer steps require a new
+ * contract"). */
+DIT_API int dit_denoise_step_at(const dit_model* m, float* latents, const void* txt, int step,
+                                int num_steps, const double* sigmas_host, dit_fbcache* cache,
+                                void* workspace, size_t ws_bytes, void* stream,
+                                dit_step_info* info_out);
+
+/* Device workspace bytes dit_denoise_step_at() needs for this model (the step's
+ * own workspace, one modulation row and the modulation scratch); 0 for NULL or
+ * invalid dimensions. */
+DIT_API size_t dit_step_at_workspace_bytes(const dit_model* m);
+
 /* ------------------------------------------------------------------ replayed loop
  *
  * The denoise loop as one captured HIP graph per step, replayed with no host

@@ -185,6 +185,33 @@ def test_loop_graph_arguments_rejected_on_the_host():
     assert L.dit_loop_graph_destroy(N) == dit.DIT_OK
 
 
+def test_step_at_arguments_rejected_on_the_host():
+    """dit_denoise_step_at refuses a step outside its table and a NULL model or
+    table before touching the device; its workspace query covers the step's own
+    workspace plus one modulation row."""
+    from image_generation_amd import dit
+    L = dit.LIB
+    N = None
+    assert L.dit_step_at_workspace_bytes(N) == 0
+    m = dit.DitModel()
+    m.dims = dit.dims_of(1, 8, 2, 4, 256, 2, 512)
+    m.n_double, m.n_single = 2, 1
+    nb = L.dit_step_at_workspace_bytes(ctypes.byref(m))
+    step = dit.dit_workspace_bytes(m.dims, dit.DIT_WS_STEP)
+    assert nb >= step + (24 + 3 + 2) * 256 * 4
+    assert nb % 256 == 0
+    sig = (ctypes.c_double * 5)(1.0, 0.75, 0.5, 0.25, 0.0)
+    fake = ctypes.c_void_p(4096)
+    for step_i, n in ((-1, 4), (4, 4), (0, 0)):
+        rc = L.dit_denoise_step_at(ctypes.byref(m), fake, fake, step_i, n, sig, N, fake, 1 << 30,
+                                   N, N)
+        assert rc == dit.DIT_ERR_INVALID_ARG
+    assert L.dit_denoise_step_at(N, fake, fake, 0, 4, sig, N, fake, 1 << 30, N, N) == \
+        dit.DIT_ERR_INVALID_ARG
+    assert L.dit_denoise_step_at(ctypes.byref(m), fake, fake, 0, 4, N, N, fake, 1 << 30, N, N) == \
+        dit.DIT_ERR_INVALID_ARG
+
+
 def test_struct_layouts_match_the_header(tmp_path):
     """Every ctypes mirror in the binding has the size and field offsets that a C
     compiler gives the header's struct (compiled here with gcc)."""
