@@ -438,8 +438,12 @@ def cpu_baseline(DI, w):
 
 GEMM_SHAPES = {"lin1": (4608, 3072, 21504), "lin2": (4608, 15360, 3072),
                "oproj": (4608, 3072, 3072), "qkv": (4608, 3072, 9216),
-               "fc1": (4608, 3072, 12288)}
-ATTN_SHAPES = {"1024": (1, 4608), "2048": (2, 16896)}
+               "fc1": (4608, 3072, 12288),
+               # one rank's share of the 2048px CFG pair under 8-way sequence
+               # parallelism: 2 x 16896 / 8 = 4224 token rows
+               "lin1_u8": (4224, 3072, 21504), "lin2_u8": (4224, 15360, 3072)}
+# (B, L, heads): 24 heads, and one rank's 3 heads under 8-way head sharding
+ATTN_SHAPES = {"1024": (1, 4608, 24), "2048": (2, 16896, 24), "2048_u8": (2, 16896, 3)}
 
 
 def event_time_us(fn, reps):
@@ -481,14 +485,15 @@ def micro_gemm(dit, reps, shapes):
 
 
 def micro_attention(dit, reps, shapes, dtypes):
-    """dit_attention alone, 24 heads x 128, at the 1024px (1 x 4608 tokens) and 2048px
-    CFG-pair (2 x 16896) shapes; fp8 takes per-(b, h) e4m3 codes from dit_quantize_rows."""
+    """dit_attention alone, head dim 128, at the 1024px (1 x 4608 tokens) and 2048px
+    CFG-pair (2 x 16896) shapes with 24 heads, and at one rank's 3 heads of the
+    latter; fp8 takes per-(b, h) e4m3 codes from dit_quantize_rows."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(0)
     out = {}
     for name in shapes:
-        B, L = ATTN_SHAPES[name]
-        H, d = 24, 128
+        B, L, H = ATTN_SHAPES[name]
+        d = 128
         for dt in dtypes:
             q, k, v = (torch.randn((B, H, L, d), device="cuda", generator=g).to(torch.bfloat16)
                        for _ in range(3))
@@ -711,6 +716,11 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] MXFP4 (W4A4) GEMMs")
         out["mxfp4_gemm"] = mxfp4_gemms(dit, device)
+        log("[bench] one rank's kernels under 8-way sequence parallelism at 2048px")
+        out["shard_2048px_u8"] = {
+            "attention": micro_attention(dit, 5, ["2048_u8"], ["bf16", "fp8"]),
+            "gemm": micro_gemm(dit, 5, ["lin1_u8", "lin2_u8"])}
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(DI, w)

@@ -120,11 +120,12 @@ def test_attention_fp8_identical_keys(dit, L, d):
     assert parity_err_bf16_stored(got, ref) <= TOL_FP8
 
 
-@pytest.mark.parametrize("B,L", [(1, 4608), (2, 16896)])
-def test_attention_fp8_full_size_sampled(dit, B, L):
-    """24 heads of 128 at 1024px (4608 tokens) and the 2048px CFG pair (16896)."""
-    _say(f"attention fp8 full B={B} L={L}")
-    H, d = 24, 128
+@pytest.mark.parametrize("B,L,H", [(1, 4608, 24), (2, 16896, 24), (2, 16896, 3)])
+def test_attention_fp8_full_size_sampled(dit, B, L, H):
+    """Heads of 128 at 1024px (4608 tokens) and the 2048px CFG pair (16896): 24
+    heads, and one rank's 3 heads under 8-way head sharding."""
+    _say(f"attention fp8 full B={B} L={L} H={H}")
+    d = 128
     q, k, v = _bf16((B, H, L, d), 71), _bf16((B, H, L, d), 72), _bf16((B, H, L, d), 73)
     got = _run_fp8_attention(dit, q, k, v)
     rng = np.random.default_rng(1)

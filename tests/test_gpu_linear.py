@@ -71,6 +71,33 @@ def test_linear_forward(dit, M, K, N, out_dtype):
     assert err <= tol
 
 
+@pytest.mark.parametrize("K,N", [(3072, 21504), (15360, 3072)])
+def test_linear_forward_shard_shapes_sampled(dit, K, N):
+    """One rank's linear1 and linear2 under 8-way sequence parallelism at the 2048px
+    CFG pair (2 x 16896 / 8 = 4224 token rows), bf16 out, on sampled rows (tile
+    edges and random rows).  The bound grows with the accumulation length like the
+    fp32 rounding of the K-term sum, sqrt(K / 3072) x 1e-5."""
+    M = 4224
+    print(f"linear shard M={M} K={K} N={N}", flush=True)
+    sys.stdout.flush()
+    x = DI.randn((M, K), 94, 1.0, "bf16")
+    w = DI.randn((N, K), 95, K ** -0.5, "bf16")
+    b = DI.randn((N,), 96, 0.1, "f32")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dit.dit_linear_forward(x.cuda(), w.cuda(), b.cuda(), y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(M, 16, replace=False),
+                                     [0, 1, 255, 256, 2047, 2048, 4095, 4096, M - 2, M - 1]]))
+    ref = O.linear(O.to64(x)[rows], O.to64(w), O.to64(b))
+    got = y[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    err = parity_err_bf16_stored(got, ref)
+    tol = TOL_BF16_OUT * (K / 3072) ** 0.5
+    print(f"  err {err:.3e} (bound {tol:.1e})", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= tol
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_linear_forward_epilogue_paths_agree(dit, out_dtype):
     """The tiled kernel's epilogue stores a pass wholly inside the problem through its

@@ -95,10 +95,11 @@ def test_attention_identical_keys(dit, d):
 
 
 @pytest.mark.parametrize("B,L,H,d", [(1, 4608, 24, 128), (2, 16896, 24, 128),
-                                     (1, 4097, 24, 128), (1, 4601, 48, 64)])
+                                     (2, 16896, 3, 128), (1, 4097, 24, 128), (1, 4601, 48, 64)])
 def test_attention_full_size_sampled(dit, B, L, H, d):
     """FLUX head layout at 1024px (4608 tokens) and the 2048px CFG pair (16896),
-    24 heads; ragged full-size lengths 4097 and 4601 (head dim 128 and 64)."""
+    24 heads, and one rank's 3 heads of the latter under 8-way head sharding;
+    ragged full-size lengths 4097 and 4601 (head dim 128 and 64)."""
     _say(f"attention full B={B} L={L} H={H} d={d}")
     q = _bf16((B, H, L, d), 31)
     k = _bf16((B, H, L, d), 32)
