@@ -299,7 +299,42 @@ struct GemmParams {
   int tiles[2];     // tiles per group
   int tiles_n[2];   // n-tiles per group
   const int* gate;  // launch gate (nullptr: always run)
+  // tiled kernel: the groups' tiles as one grid of grid_m x grid_n (group 1's rows
+  // after split_m), cut into `bands` row bands (0: per-group raster instead)
+  int grid_m, grid_n, split_m, bands;
 };
+
+// Logical tile lid -> (row, column) of a grid_m x grid_n tile grid cut into
+// P row bands x Q = min(8 / P, grid_n) column bands, visited region by region.
+// The 8 XCDs each receive a contiguous run of logical tiles, so each one works
+// through one compact region and streams the A rows and W columns of that region
+// only (an XCD's L2 is its own).  Inside a region: columns of up to 16 rows, or
+// for taller regions groups of 8 rows sweeping the region's columns, so the 32
+// tiles an XCD runs at once share their operand blocks.
+__device__ __forceinline__ void grid_tile(int lid, int grid_m, int grid_n, int P, int& tm,
+                                          int& tn) {
+  const int Q = min(8 / P, grid_n);
+  tm = tn = 0;
+  for (int c = 0; c < Q; ++c)
+    for (int r = 0; r < P; ++r) {
+      const int r0 = grid_m * r / P, r1 = grid_m * (r + 1) / P;
+      const int c0 = grid_n * c / Q, c1 = grid_n * (c + 1) / Q;
+      const int h = r1 - r0, w = c1 - c0;
+      if (lid < h * w) {
+        if (h <= 16) {
+          tm = r0 + lid % h;
+          tn = c0 + lid / h;
+        } else {
+          const int in_group = 8 * w, first = (lid / in_group) * 8;
+          const int gsize = min(h - first, 8);
+          tm = r0 + first + (lid % in_group) % gsize;
+          tn = c0 + (lid % in_group) / gsize;
+        }
+        return;
+      }
+      lid -= h * w;
+    }
+}
 
 template <int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmParams<Epi> p) {
@@ -647,18 +682,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmParams<Epi> 
   const int bid = blockIdx.x;
   const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
   int lid = xcd * xq + min(xcd, xr) + (bid >> 3);
-  const bool g1 = p.ngroups > 1 && lid >= p.tiles[0];
-  if (g1) lid -= p.tiles[0];
+  bool g1;
+  int m0, n0;
+  if (p.bands > 0) {
+    int tm, tn;
+    grid_tile(lid, p.grid_m, p.grid_n, p.bands, tm, tn);
+    g1 = tm >= p.split_m;
+    m0 = (g1 ? tm - p.split_m : tm) * BM;
+    n0 = tn * BN;
+  } else {
+    g1 = p.ngroups > 1 && lid >= p.tiles[0];
+    if (g1) lid -= p.tiles[0];
+    const int tiles_n = g1 ? p.tiles_n[1] : p.tiles_n[0];
+    const int tiles_m = ((g1 ? p.g[1] : p.g[0]).M + BM - 1) / BM;
+    constexpr int GROUP_M = 8;
+    const int in_group = GROUP_M * tiles_n;
+    const int first_m = (lid / in_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    m0 = (first_m + (lid % in_group) % gsize) * BM;
+    n0 = ((lid % in_group) / gsize) * BN;
+  }
   const GemmProblem g = g1 ? p.g[1] : p.g[0];
-  const int tiles_n = g1 ? p.tiles_n[1] : p.tiles_n[0];
-  const int tiles_m = (g.M + BM - 1) / BM;
-  constexpr int GROUP_M = 8;
-  const int in_group = GROUP_M * tiles_n;
-  const int gid = lid / in_group;
-  const int first_m = gid * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int m0 = (first_m + (lid % in_group) % gsize) * BM;
-  const int n0 = ((lid % in_group) / gsize) * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1084,6 +1128,25 @@ hipError_t gemm32_linear1(const GemmProblem& g, const QKVOut32& o, const RowMap&
 
 // ---------------------------------------------------------------- launch
 
+// Row bands of the tiled kernels' region raster (grid_tile): of 1, 2, 4 and 8 bands
+// (times 8, 4, 2, 1 column bands), the split that divides the grid exactly, then the
+// one with the squarest regions (smallest region rows + columns).
+static int grid_bands(int gm, int gn) {
+  int best = 1;
+  double best_score = 1e30;
+  for (int P = 1; P <= 8; P *= 2) {
+    const int Q = 8 / P;
+    if (P > gm || Q > gn) continue;
+    const bool exact = gm % P == 0 && gn % Q == 0;
+    const double score = (exact ? 0.0 : 1e9) + (double)gm / P + (double)gn / Q;
+    if (score < best_score) {
+      best_score = score;
+      best = P;
+    }
+  }
+  return min(best, gm);
+}
+
 // KV: 4 = MXFP4 tiled kernel, 2 = fp8 tiled kernel, 1 = bf16 tiled kernel (256 x 256
 // tiles, see above), 0 = the 32 x 256 / 128 x 128 register-staged kernel; NS stages
 // of SLAB bytes per row for the tiled kernels
@@ -1101,6 +1164,14 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
     total += p.tiles[i];
   }
   if (total == 0) return hipSuccess;
+  p.bands = 0;
+  if (KV > 0 && (ng == 1 || p.tiles_n[0] == p.tiles_n[1])) {
+    const int tm0 = (gp[0].M + BM - 1) / BM;
+    p.grid_m = tm0 + (ng > 1 ? (gp[1].M + BM - 1) / BM : 0);
+    p.grid_n = p.tiles_n[0];
+    p.split_m = ng > 1 ? tm0 : p.grid_m;
+    p.bands = grid_bands(p.grid_m, p.grid_n);
+  }
   void (*kern)(GemmParams<Epi>);
   if constexpr (KV == 4) kern = &gemm_dma_kernel<BM, BN, WM, WN, 2, NS, SLAB, Epi>;
   else if constexpr (KV == 2) kern = &gemm_dma_kernel<BM, BN, WM, WN, 1, NS, SLAB, Epi>;
