@@ -1165,7 +1165,7 @@ static hipError_t launch_cfg(const GemmProblem* gp, const Epi* ep, int ng, hipSt
   }
   if (total == 0) return hipSuccess;
   // the region raster for the bf16 and e4m3 tiled kernels; the MXFP4 kernel keeps
-  // the 8-row raster (measured 2% faster there, 2% slower with regions)
+  // the 8-row raster (it measured 2% slower with regions)
   p.bands = 0;
   if ((KV == 1 || KV == 2) && (ng == 1 || p.tiles_n[0] == p.tiles_n[1])) {
     const int tm0 = (gp[0].M + BM - 1) / BM;
