@@ -29,7 +29,8 @@
  *     pointers (e.g. torch tensor data_ptr()), 16-byte aligned, contiguous,
  *     row-major.  The library allocates nothing and keeps no state between
  *     calls; scratch comes from a caller workspace sized by
- *     dit_workspace_bytes().  (Two exceptions: the handle of a replayed loop,
+ *     dit_workspace_bytes() (dit_step_at_workspace_bytes() for
+ *     dit_denoise_step_at()).  (Two exceptions: the handle of a replayed loop,
  *     dit_loop_graph_create() to dit_loop_graph_destroy(); and the static
  *     device array that dit_modulation_static() uses instead of a workspace.)
  *   - stream: a hipStream_t (NULL = default stream).  Work is enqueued
