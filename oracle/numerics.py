@@ -32,8 +32,7 @@ Pins (tests/test_oracle_pins.py):
                       test_e4m3_representable_values_are_fixed_points
   e4m3_tie_mask       test_e4m3_tie_mask_against_code_table
   quant_scale_f32,    test_quantize_rows_scale_and_roundtrip
-  quantize_rows_e4m3,
-  quantize_cols_e4m3
+  quantize_rows_e4m3
   round_e2m1          test_e2m1_rounding_cases, test_e2m1_value_set
   mx_block_exponent   test_mx_block_exponent_cases
   quantize_mxfp4,     test_mxfp4_reproduces_representable_blocks, test_mxfp4_error_bound
@@ -44,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["round_bf16", "round_fp16", "e4m3_tie_mask", "round_e4m3", "E4M3_MAX", "quant_scale_f32",
-           "quantize_rows_e4m3", "quantize_cols_e4m3", "round_e2m1", "E2M1_MAX", "MX_BLOCK",
+           "quantize_rows_e4m3", "round_e2m1", "E2M1_MAX", "MX_BLOCK",
            "mx_block_exponent", "quantize_mxfp4", "dequantize_mxfp4"]
 
 E2M1_MAX = 6.0
@@ -136,11 +135,6 @@ def quantize_rows_e4m3(x: np.ndarray):
     scale, inv = quant_scale_f32(amax)
     y = (x32 * inv[..., None]).astype(np.float32)
     return round_e4m3(y.astype(np.float64)), scale
-
-
-def quantize_cols_e4m3(w: np.ndarray):
-    """Per-output-channel quantisation of a weight [out, in] (one scale per row)."""
-    return quantize_rows_e4m3(w)
 
 
 def round_e2m1(x) -> np.ndarray:
